@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+Default workload: 70B-shaped decode, bf16, B=16, n_h=64, n_kv=8, d_h=128,
+every context 8192 tokens, block 16, 80 layers, each layer its own pool of
+8192 randomly permuted physical blocks (40 GiB of K+V in HBM).  One step is
+the whole decode step of the path over the 80 layers: for each layer the new
+token's K/V is written through reshape_and_cache (position 8191 of every
+sequence, overwritten each step) and paged_decode_attention runs over the
+layer's cache.  Inputs are seeded N(0,1) synthetic data resident in HBM
+before timing starts.
+
+Prints one JSON line:  KV GB/s (value), % of the 8 TB/s HBM peak, tokens/s,
+token*heads/s, a roofline record of the dominant kernel (timed with HIP
+events on the launch stream) and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn KV GB/s + % of MI355X HBM peak; tokens/s at 70B-shaped B=16 S=8K"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=80, help="layers of the 70B-shaped model (80)")
+    ap.add_argument("--split-tokens", type=int, default=0, help="0 = library's automatic split")
+    ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    ap.add_argument("--kernel-reps", type=int, default=3,
+                    help="passes over the layers when timing the attention kernel alone")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU budget of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or KV head with no exchange, see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    from synth import CONFIGS, structure, device_normal_
+    from synth.workloads import decode_positions
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS["llama70b"]
+    L = args.layers
+    B, n_h, n_kv, d = cfg.B, cfg.n_h, cfg.n_kv, cfg.d_k
+    bs = cfg.block_size
+
+    print(f"[bench] building {L} layers of {cfg.desc}", file=sys.stderr, flush=True)
+    layers = []
+    seq_ids, positions = decode_positions(np.full(B, 8192, dtype=np.int32))
+    for l in range(L):
+        s = structure(cfg, layer=l)
+        pool = pk.kv_pool_create(s.num_blocks, bs, n_kv, d, d, torch.bfloat16, device=dev)
+        device_normal_(pool.k, cfg.seed * 1000 + 4 * l)
+        device_normal_(pool.v, cfg.seed * 1000 + 4 * l + 1)
+        q = device_normal_(torch.empty((B, n_h, d), dtype=torch.bfloat16, device=dev), cfg.seed * 1000 + 4 * l + 2)
+        kv_new = device_normal_(torch.empty((2, B, n_kv, d), dtype=torch.bfloat16, device=dev),
+                                cfg.seed * 1000 + 4 * l + 3)
+        bt = torch.from_numpy(s.block_table).to(dev)
+        ctx = torch.from_numpy(s.context_lens).to(dev)
+        slots = pk.paged_slot_mapping(bt, torch.from_numpy(seq_ids).to(dev),
+                                      torch.from_numpy(positions).to(dev), bs)
+        out = torch.empty((B, n_h, d), dtype=torch.bfloat16, device=dev)
+        layers.append(dict(pool=pool, q=q, k_new=kv_new[0], v_new=kv_new[1], bt=bt, ctx=ctx,
+                           slots=slots, out=out, s=s))
+    ws_bytes = 0
+    calls_rc, calls_dec = [], []
+    workspace = None
+    for ly in layers:
+        desc = pk.make_desc(B=B, n_h=n_h, n_kv=n_kv, d_k=d, d_v=d, block_size=bs,
+                            max_blocks_per_seq=ly["bt"].shape[1], max_context_len=8192,
+                            q_dtype=pk.KVP_BF16, kv_dtype=pk.KVP_BF16, split_tokens=args.split_tokens)
+        ws_bytes = pk.decode_workspace_size(desc)
+        if workspace is None and ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        calls_rc.append(pk.prepare_reshape_and_cache(ly["pool"], ly["k_new"], ly["v_new"], ly["slots"]))
+        calls_dec.append(pk.prepare_decode(ly["q"], ly["pool"].k, ly["pool"].v, ly["bt"], ly["ctx"],
+                                           cfg.scale, ly["out"], max_context_len=8192,
+                                           split_tokens=args.split_tokens, workspace=workspace))
+    split = pk.decode_split_tokens(pk.make_desc(
+        B=B, n_h=n_h, n_kv=n_kv, d_k=d, d_v=d, block_size=bs, max_blocks_per_seq=512,
+        max_context_len=8192, q_dtype=pk.KVP_BF16, kv_dtype=pk.KVP_BF16, split_tokens=args.split_tokens))
+    torch.cuda.synchronize()
+
+    def step():
+        for rc, dec in zip(calls_rc, calls_dec):
+            rc()
+            dec()
+
+    stream = torch.cuda.current_stream(dev)
+    run = step
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        step()                                   # warm before capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        run = g.replay
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    # ---- the timed region: exactly K steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f})",
+          file=sys.stderr, flush=True)
+
+    # ---- dominant kernel alone: attention launches over all layers, HIP events
+    # on the launch stream; average duration per launch
+    reps = args.kernel_reps
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(reps):
+        for dec in calls_dec:
+            dec()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    us_launch = 1e3 * k0.elapsed_time(k1) / (reps * L)
+
+    kv_bytes_layer = B * 8192 * n_kv * d * 2 * 2            # K + V, bf16
+    kv_bytes_step = kv_bytes_layer * L
+    gbs = kv_bytes_step / (ms_step * 1e-3) / 1e9
+    tokens_per_s = B / (ms_step * 1e-3)
+    tok_heads = B * 8192 * n_h * L / (ms_step * 1e-3)
+    achieved = kv_bytes_layer / (us_launch * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "70B-shaped paged decode attention, 80 layers",
+                   "B": B, "n_h": n_h, "n_kv": n_kv, "d_h": d, "context": 8192, "block_size": bs,
+                   "layers": L, "kv_bytes_per_step": kv_bytes_step, "split_tokens": split,
+                   "graph": bool(args.graph), "parallelism": "single GPU"},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(tokens_per_s, 1),
+        "token_heads_per_s": float(f"{tok_heads:.4g}"),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_decode_attention (decode_gqa_kernel<128,8,bf16> + split reduce)",
+                     "avg_launch_us": round(us_launch, 2),
+                     "bytes_per_launch": kv_bytes_layer},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(layers[0], cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(layer, cfg, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same
+    workload: whole sequences of layer 0 (all 64 query heads) until the CPU
+    budget is spent; single-threaded BLAS."""
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
+    except Exception:                                   # pragma: no cover
+        limit = None
+    s = layer["s"]
+    kh = layer["pool"].k.cpu().view(torch.int16).numpy().view(np.uint16)
+    vh = layer["pool"].v.cpu().view(torch.int16).numpy().view(np.uint16)
+    qh = layer["q"].cpu().view(torch.int16).numpy().view(np.uint16)
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(cfg.B):
+        oracle.paged_decode_attention(qh[b:b + 1], kh, vh, s.block_table[b:b + 1],
+                                      s.context_lens[b:b + 1], cfg.scale)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    if limit is not None:
+        limit.unregister() if hasattr(limit, "unregister") else None
+    kv_bytes = done * int(s.context_lens[0]) * cfg.n_kv * cfg.d_k * 2 * 2
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0, {done} of {cfg.B} sequences x 8192 tokens x {cfg.n_kv} KV heads, "
+                      f"all {cfg.n_h} query heads ({kv_bytes} KV bytes in {dt:.2f} s)",
+            "tokens_per_s_equiv": round(done / dt / 80.0, 6)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,244 @@
+/*
+ * pagedkv.h -- C ABI of a paged-KV-cache single-token decode attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (page citations name a page by its site; the same five
+ * pages are cited throughout the sources):
+ *   faulkner -- "LLM 推理底层：KV Cache 显存几何、GQA/MLA 压缩与 PagedAttention 调度"
+ *               (blog.faulkner.fun/posts/llm-kv-cache-and-paged-attention)
+ *   qwbw     -- "【infra之路】10-PagedAttention 与 KV Cache 管理" (www.qwbw.cn/news/28817)
+ *   guijiagi -- KV cache guide (guijiagi.com/posts/kv-cache-guide/)
+ *   talentme -- "KV Cache 显存管理全景 ..." (talentme.airsota.com/.../kv-cache-and-paged-attention)
+ *   hx       -- "LLM 推理引擎设计：KV Cache、PagedAttention 与连续批处理"
+ *               (hx.sn.cn/archives/llm-inference-engine)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument named as device memory must point to memory of
+ *   the current HIP device.  Host pointers are named as such.
+ * - Work is enqueued on the caller's stream (a hipStream_t passed as
+ *   void*; NULL is the null stream) and the call returns without waiting
+ *   for it, except where a function says it synchronises.
+ * - The library never frees caller memory and never allocates device
+ *   memory outside kv_pool_create (storage == NULL).
+ * - Errors: argument and shape checks happen on the host before anything
+ *   is enqueued; a failing call returns a negative kvp_status, enqueues
+ *   nothing and leaves a message for kvp_last_error() (per thread).
+ *   Device data that breaks a documented precondition (a block id out of
+ *   range, a context longer than the block table covers) is not checked in
+ *   the fast path; paged_decode_validate() checks it on request.
+ * - No C++ exception crosses this interface.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVP_OK = 0,
+  KVP_ERR_INVALID_ARG = -1,   /* a null pointer, a bad size or a shape mismatch */
+  KVP_ERR_OUT_OF_MEMORY = -2, /* the pool could not be allocated */
+  KVP_ERR_UNSUPPORTED = -3,   /* a valid shape/type this build has no kernel for */
+  KVP_ERR_HIP = -4            /* the HIP runtime reported an error */
+} kvp_status;
+
+typedef enum {
+  KVP_F32 = 0,   /* IEEE binary32 */
+  KVP_BF16 = 1,  /* bfloat16 (top half of binary32), round-to-nearest-even */
+  KVP_INT8 = 2   /* signed 8-bit codes with one fp32 scale per (slot, KV head) */
+} kvp_dtype;
+
+/* ------------------------------------------------------------------------
+ * KV pool
+ *
+ * A pool of num_blocks physical blocks, each holding block_size token
+ * slots (faulkner, section on logical/physical block mapping; qwbw 3.2).
+ * Layout, row-major (talentme chapter 3, the NumPy pool class):
+ *   K codes/values  [num_blocks, block_size, n_kv, d_k]
+ *   V codes/values  [num_blocks, block_size, n_kv, d_v]
+ *   K, V scales     [num_blocks, block_size, n_kv] float   (KVP_INT8 only)
+ * Slot s is block s / block_size, offset s % block_size.  A latent pool
+ * (latent = 1, absorbed MLA; faulkner, matrix absorption section) has
+ * n_kv = 1 and no V array: the value of a token is the first d_v columns
+ * of its K row.  Each region starts 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+typedef struct kvp_pool kvp_pool;
+
+typedef struct {
+  int64_t num_blocks;   /* > 0 */
+  int32_t block_size;   /* power of two, 1 ... 256 */
+  int32_t n_kv;         /* KV heads, > 0 */
+  int32_t d_k;          /* K row width in elements, > 0 */
+  int32_t d_v;          /* V row width in elements, > 0 (<= d_k when latent) */
+  kvp_dtype dtype;      /* element type of the pool */
+  int32_t latent;       /* 1: V aliases K[..., :d_v]; requires n_kv == 1 */
+} kvp_pool_desc;
+
+typedef struct {
+  void* k;              /* device: K region */
+  void* v;              /* device: V region (== k for a latent pool) */
+  float* k_scale;       /* device: K scales (KVP_INT8), else NULL */
+  float* v_scale;       /* device: V scales (KVP_INT8, not latent), else NULL */
+  size_t total_bytes;   /* bytes the pool occupies from k onward */
+  kvp_pool_desc desc;
+} kvp_pool_view;
+
+/* Bytes of device storage a pool with this description needs (0 if the
+ * description is invalid). */
+size_t kv_pool_required_bytes(const kvp_pool_desc* desc);
+
+/* Create a pool.  If storage is NULL the library allocates the memory with
+ * hipMalloc on the current device and frees it in kv_pool_destroy
+ * (KVP_ERR_OUT_OF_MEMORY if that fails -- the analogue of the allocator
+ * running out of physical blocks, faulkner allocator code).  Otherwise
+ * storage (device, 256-byte aligned, at least kv_pool_required_bytes) is
+ * caller-owned and must outlive the pool.  Contents are not initialised. */
+kvp_status kv_pool_create(const kvp_pool_desc* desc, void* storage,
+                          size_t storage_bytes, kvp_pool** out);
+
+/* Release the handle (and the memory, if the library allocated it).
+ * NULL is a no-op. */
+void kv_pool_destroy(kvp_pool* pool);
+
+/* Device addresses and shape of a pool. */
+kvp_status kv_pool_view_get(const kvp_pool* pool, kvp_pool_view* out);
+
+/* ------------------------------------------------------------------------
+ * Slot mapping (faulkner, logical/physical block mapping; talentme
+ * chapter 3, the write_kv lookup): for each token t,
+ *   slots[t] = block_table[seq_ids[t]][positions[t] / block_size] * block_size
+ *              + positions[t] % block_size
+ * as int64.  block_table: device int32 [*, max_blocks_per_seq] row-major.
+ * seq_ids, positions: device int32 [num_tokens]; slots: device int64
+ * [num_tokens].  A negative seq id or position, or a position whose
+ * logical block is >= max_blocks_per_seq, or a negative table entry,
+ * yields slot -1 (which reshape_and_cache skips).
+ * ---------------------------------------------------------------------- */
+kvp_status paged_slot_mapping(const int32_t* block_table, int32_t max_blocks_per_seq,
+                              int32_t block_size, const int32_t* seq_ids,
+                              const int32_t* positions, int64_t num_tokens,
+                              int64_t* slots, void* stream);
+
+/* ------------------------------------------------------------------------
+ * reshape_and_cache: scatter the K/V rows of new tokens into their slots
+ * (talentme chapter 3, write_kv; qwbw 1.2 appends each step's K/V before
+ * attending).
+ *   k_new: device [num_tokens, n_kv, d_k] of in_dtype, contiguous
+ *   v_new: device [num_tokens, n_kv, d_v] of in_dtype (ignored, may be
+ *          NULL, for a latent pool)
+ *   slot_mapping: device int64 [num_tokens]; a negative slot skips the
+ *          token; a slot >= num_blocks * block_size is a precondition
+ *          violation.
+ * F32 and BF16 pools store the rows bit for bit (in_dtype must equal the
+ * pool dtype).  An INT8 pool quantizes on write (guijiagi 4.2): per (token,
+ * head) row, scale = fl32(absmax / 127) and code = clamp(rint(fl32(x /
+ * scale)), -128, 127) in IEEE binary32 with round-half-to-even; a zero row
+ * gets scale 0 and codes 0.  in_dtype F32 or BF16 (widened exactly).
+ * Two tokens mapped to one slot race; the result is one of the rows.
+ * ---------------------------------------------------------------------- */
+kvp_status reshape_and_cache(kvp_pool* pool, const void* k_new, const void* v_new,
+                             kvp_dtype in_dtype, const int64_t* slot_mapping,
+                             int64_t num_tokens, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention
+ *
+ * For every sequence b and query head h (faulkner, first section, o_t;
+ * qwbw 3.4 walks the block table; faulkner's MHA/GQA/MLA table for head
+ * sharing):
+ *   kvh = h / (n_h / n_kv)                  (consecutive head groups)
+ *   K_j = k_pool[block_table[b][j / bs]][j % bs][kvh]   for 0 <= j < L,
+ *   L   = context_lens[b] (the token being decoded included)
+ *   out[b][h] = softmax_j(scale * q[b][h] . K_j) weighted sum of V_j
+ * Slots at or beyond L are never read.  L == 0 gives a zero output.
+ * The result is unique; kernels accumulate in fp32 (online softmax over
+ * context splits merged by log-sum-exp), so it matches the exact value to
+ * within rounding.
+ *
+ *   q:   device [B, n_h, d_k], q_dtype      out: device [B, n_h, d_v], q_dtype
+ *   block_table: device int32 [B, max_blocks_per_seq]
+ *   context_lens: device int32 [B], each in [0, max_context_len]
+ *   max_context_len: a host-side upper bound of every context_lens[b]
+ *          (used to size the launch without reading device memory);
+ *          must be <= max_blocks_per_seq * block_size.
+ *   workspace: device scratch of at least paged_decode_workspace_size()
+ *          bytes (may be NULL when that is 0), 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t B, n_h, n_kv, d_k, d_v;
+  int32_t block_size;          /* power of two */
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;     /* host upper bound of context_lens */
+  kvp_dtype q_dtype;           /* F32 or BF16; also the output type */
+  kvp_dtype kv_dtype;          /* F32, BF16 or INT8 */
+  int32_t split_tokens;        /* tokens per context split; 0 = automatic */
+  int64_t total_context_len;   /* optional host hint: sum of context_lens
+                                  (0 = unknown; then B * max_context_len is
+                                  assumed when sizing splits) */
+} kvp_decode_desc;
+
+/* Workspace bytes the call needs for this description (split partials). */
+size_t paged_decode_workspace_size(const kvp_decode_desc* desc);
+
+/* Tokens per context split the automatic policy picks (for reporting). */
+int32_t paged_decode_split_tokens(const kvp_decode_desc* desc);
+
+/* Float pools (F32/BF16 K and V of the same dtype as q; GQA, MQA, MHA). */
+kvp_status paged_decode_attention(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* context_lens,
+                                  float scale, void* out, const kvp_decode_desc* desc,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* INT8 pools: codes as in the pool layout plus fp32 scales
+ * [num_blocks, block_size, n_kv]; dequantization (code * scale,
+ * guijiagi 4.2) happens inside the kernel.  desc->kv_dtype == KVP_INT8. */
+kvp_status paged_decode_attention_int8(const void* q, const int8_t* k_codes,
+                                       const float* k_scale, const int8_t* v_codes,
+                                       const float* v_scale, const int32_t* block_table,
+                                       const int32_t* context_lens, float scale, void* out,
+                                       const kvp_decode_desc* desc, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* Absorbed MLA over a latent pool (faulkner, matrix absorption and
+ * decoupled RoPE): q [B, n_h, d_k] already carries W^UK; the pool holds
+ * one [c | k_rope] row of d_k bf16 per token (n_kv = 1); the value is the
+ * first d_v columns of that row; out [B, n_h, d_v] is in latent space. */
+kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
+                                      const int32_t* block_table, const int32_t* context_lens,
+                                      float scale, void* out, const kvp_decode_desc* desc,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Gather (qwbw 3.4: read each physical block through the table): copies
+ * rows 0 .. context_lens[b]-1 of every sequence, bit for bit, into
+ * out [B, max_context_len, n_kv, d] (device, elem_bytes per element);
+ * rows at or beyond a sequence's length are left untouched.
+ * ---------------------------------------------------------------------- */
+kvp_status paged_gather(const void* pool, int32_t elem_bytes, int32_t block_size,
+                        int32_t n_kv, int32_t d, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t B, int32_t max_context_len, void* out, void* stream);
+
+/* Debug check (synchronises the stream, copies the tables to the host):
+ * every context length within [0, max_context_len] and every table entry
+ * a sequence uses within [0, num_blocks).  KVP_ERR_INVALID_ARG names the
+ * first violation. */
+kvp_status paged_decode_validate(const int32_t* block_table, const int32_t* context_lens,
+                                 const kvp_decode_desc* desc, int64_t num_blocks,
+                                 void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* kvp_last_error(void);
+
+/* Library version string. */
+const char* kvp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

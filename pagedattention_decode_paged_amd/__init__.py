@@ -1,0 +1,369 @@
+"""Paged decode attention for AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libpagedkv.so`` (the C ABI in
+``include/pagedkv.h``).  It only marshals arguments: every step of the path
+runs in the library's HIP kernels.  PyTorch is used to hold device memory and
+to name the current stream.  There is no fallback: if the library is missing
+or fails to load, importing the binding raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+KVP_OK, KVP_ERR_INVALID_ARG, KVP_ERR_OUT_OF_MEMORY, KVP_ERR_UNSUPPORTED, KVP_ERR_HIP = 0, -1, -2, -3, -4
+KVP_F32, KVP_BF16, KVP_INT8 = 0, 1, 2
+
+_TORCH_TO_KVP = {torch.float32: KVP_F32, torch.bfloat16: KVP_BF16, torch.int8: KVP_INT8}
+_KVP_TO_TORCH = {v: k for k, v in _TORCH_TO_KVP.items()}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+class _PoolDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
+                ("n_kv", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("latent", ctypes.c_int32)]
+
+
+class _PoolView(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("total_bytes", ctypes.c_size_t),
+                ("desc", _PoolDesc)]
+
+
+class _DecodeDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("n_h", ctypes.c_int32), ("n_kv", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
+                ("split_tokens", ctypes.c_int32), ("total_context_len", ctypes.c_int64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m pagedattention_decode_paged_amd.build`"
+            " (or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "kvp_last_error": (ctypes.c_char_p, []),
+        "kvp_version": (ctypes.c_char_p, []),
+        "kv_pool_required_bytes": (SZ, [ctypes.POINTER(_PoolDesc)]),
+        "kv_pool_create": (ctypes.c_int, [ctypes.POINTER(_PoolDesc), P, SZ, ctypes.POINTER(P)]),
+        "kv_pool_destroy": (None, [P]),
+        "kv_pool_view_get": (ctypes.c_int, [P, ctypes.POINTER(_PoolView)]),
+        "paged_slot_mapping": (ctypes.c_int, [P, I32, I32, P, P, I64, P, P]),
+        "reshape_and_cache": (ctypes.c_int, [P, P, P, ctypes.c_int, P, I64, P]),
+        "paged_decode_workspace_size": (SZ, [ctypes.POINTER(_DecodeDesc)]),
+        "paged_decode_split_tokens": (I32, [ctypes.POINTER(_DecodeDesc)]),
+        "paged_decode_attention": (ctypes.c_int, [P, P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc), P, SZ, P]),
+        "paged_decode_attention_int8": (ctypes.c_int, [P, P, P, P, P, P, P, F, P,
+                                                       ctypes.POINTER(_DecodeDesc), P, SZ, P]),
+        "paged_decode_attention_mla": (ctypes.c_int, [P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc), P, SZ, P]),
+        "paged_gather": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P]),
+        "paged_decode_validate": (ctypes.c_int, [P, P, ctypes.POINTER(_DecodeDesc), I64, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+EXPORTED_SYMBOLS = (
+    "kvp_last_error", "kvp_version", "kv_pool_required_bytes", "kv_pool_create", "kv_pool_destroy",
+    "kv_pool_view_get", "paged_slot_mapping", "reshape_and_cache", "paged_decode_workspace_size",
+    "paged_decode_split_tokens", "paged_decode_attention", "paged_decode_attention_int8",
+    "paged_decode_attention_mla", "paged_gather", "paged_decode_validate",
+)
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def version() -> str:
+    return _lib.kvp_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != KVP_OK:
+        raise PagedKVError(status, _lib.kvp_last_error().decode())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p | None:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(*ts: torch.Tensor) -> torch.device:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        dev = t.device if dev is None else dev
+    return dev
+
+
+# --------------------------------------------------------------------- pool
+
+@dataclass
+class KVPool:
+    """A pool created by ``kv_pool_create``; its memory is a torch uint8
+    tensor owned by this object, and ``k``/``v``/``k_scale``/``v_scale`` are
+    views of it in the pool layout ``[num_blocks, block_size, n_kv, d]``."""
+    handle: ctypes.c_void_p
+    storage: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    k_scale: torch.Tensor | None
+    v_scale: torch.Tensor | None
+    num_blocks: int
+    block_size: int
+    n_kv: int
+    d_k: int
+    d_v: int
+    dtype: torch.dtype
+    latent: bool
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            _lib.kv_pool_destroy(h)
+            self.handle = ctypes.c_void_p(None)
+
+
+def kv_pool_required_bytes(num_blocks, block_size, n_kv, d_k, d_v, dtype, latent=False) -> int:
+    d = _PoolDesc(num_blocks, block_size, n_kv, d_k, d_v, _TORCH_TO_KVP[dtype], int(latent))
+    return int(_lib.kv_pool_required_bytes(ctypes.byref(d)))
+
+
+def kv_pool_create(num_blocks: int, block_size: int, n_kv: int, d_k: int, d_v: int,
+                   dtype: torch.dtype, latent: bool = False, device="cuda") -> KVPool:
+    if dtype not in _TORCH_TO_KVP:
+        raise ValueError(f"unsupported pool dtype {dtype}")
+    d = _PoolDesc(num_blocks, block_size, n_kv, d_k, d_v, _TORCH_TO_KVP[dtype], int(latent))
+    nbytes = int(_lib.kv_pool_required_bytes(ctypes.byref(d)))
+    if nbytes == 0:
+        # let the library name the problem
+        h = ctypes.c_void_p()
+        _check(_lib.kv_pool_create(ctypes.byref(d), None, 0, ctypes.byref(h)))
+    storage = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    h = ctypes.c_void_p()
+    _check(_lib.kv_pool_create(ctypes.byref(d), _ptr(storage), nbytes, ctypes.byref(h)))
+    view = _PoolView()
+    _check(_lib.kv_pool_view_get(h, ctypes.byref(view)))
+    base = storage.data_ptr()
+
+    def sub(addr, count, dt, shape):
+        if addr is None:
+            return None
+        off = addr - base
+        nb = count * torch.empty((), dtype=dt).element_size()
+        return storage[off:off + nb].view(dt).view(shape)
+
+    slots = num_blocks * block_size
+    k = sub(view.k, slots * n_kv * d_k, dtype, (num_blocks, block_size, n_kv, d_k))
+    v = k if latent else sub(view.v, slots * n_kv * d_v, dtype, (num_blocks, block_size, n_kv, d_v))
+    ks = sub(view.k_scale, slots * n_kv, torch.float32, (num_blocks, block_size, n_kv))
+    vs = sub(view.v_scale, slots * n_kv, torch.float32, (num_blocks, block_size, n_kv))
+    return KVPool(h, storage, k, v, ks, vs, num_blocks, block_size, n_kv, d_k, d_v, dtype, latent)
+
+
+# --------------------------------------------------------------------- cache ops
+
+def paged_slot_mapping(block_table: torch.Tensor, seq_ids: torch.Tensor, positions: torch.Tensor,
+                       block_size: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    dev = _need_cuda(block_table, seq_ids, positions)
+    if block_table.dtype != torch.int32 or seq_ids.dtype != torch.int32 or positions.dtype != torch.int32:
+        raise TypeError("block_table, seq_ids and positions must be int32")
+    n = seq_ids.numel()
+    if positions.numel() != n:
+        raise ValueError("seq_ids and positions differ in length")
+    if out is None:
+        out = torch.empty(n, dtype=torch.int64, device=dev)
+    _check(_lib.paged_slot_mapping(_ptr(block_table), block_table.shape[1], block_size,
+                                   _ptr(seq_ids), _ptr(positions), n, _ptr(out), _stream(dev)))
+    return out
+
+
+def reshape_and_cache(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor | None,
+                      slot_mapping: torch.Tensor) -> None:
+    dev = _need_cuda(k_new, v_new, slot_mapping)
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    n = slot_mapping.numel()
+    if k_new.shape != (n, pool.n_kv, pool.d_k):
+        raise ValueError(f"k_new must be [{n}, {pool.n_kv}, {pool.d_k}]")
+    if not pool.latent and (v_new is None or v_new.shape != (n, pool.n_kv, pool.d_v)):
+        raise ValueError(f"v_new must be [{n}, {pool.n_kv}, {pool.d_v}]")
+    if v_new is not None and v_new.dtype != k_new.dtype:
+        raise TypeError("k_new and v_new must share a dtype")
+    _check(_lib.reshape_and_cache(pool.handle, _ptr(k_new), _ptr(v_new), _TORCH_TO_KVP[k_new.dtype],
+                                  _ptr(slot_mapping), n, _stream(dev)))
+
+
+def paged_gather(pool: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
+                 max_context_len: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows 0..ctx-1 of each sequence in logical order, bit for bit:
+    ``[B, max_context_len, n_kv, d]``; rows past a sequence's length keep
+    ``out``'s previous contents (zeros when ``out`` is None)."""
+    dev = _need_cuda(pool, block_table, context_lens)
+    nb, bs, n_kv, d = pool.shape
+    B = context_lens.numel()
+    if out is None:
+        out = torch.zeros((B, max_context_len, n_kv, d), dtype=pool.dtype, device=dev)
+    _check(_lib.paged_gather(_ptr(pool), pool.element_size(), bs, n_kv, d, _ptr(block_table),
+                             block_table.shape[1], _ptr(context_lens), B, max_context_len, _ptr(out),
+                             _stream(dev)))
+    return out
+
+
+# --------------------------------------------------------------------- decode
+
+def _desc(q, block_table, context_lens, n_kv, d_k, d_v, block_size, kv_dtype, max_context_len,
+          split_tokens, total_context_len) -> _DecodeDesc:
+    B, n_h, _ = q.shape
+    return _DecodeDesc(B, n_h, n_kv, d_k, d_v, block_size, block_table.shape[1], int(max_context_len),
+                       _TORCH_TO_KVP[q.dtype], kv_dtype, int(split_tokens), int(total_context_len))
+
+
+def decode_workspace_size(desc: _DecodeDesc) -> int:
+    return int(_lib.paged_decode_workspace_size(ctypes.byref(desc)))
+
+
+def decode_split_tokens(desc: _DecodeDesc) -> int:
+    return int(_lib.paged_decode_split_tokens(ctypes.byref(desc)))
+
+
+def _workspace(desc, workspace, dev):
+    need = decode_workspace_size(desc)
+    if need == 0:
+        return None, 0
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return workspace, workspace.numel()
+
+
+def paged_decode_attention(q, k_pool, v_pool, block_table, context_lens, scale, out=None, *,
+                           max_context_len, split_tokens=0, total_context_len=0, workspace=None):
+    """``out[b, h] = softmax(scale * q[b, h] . K) V`` over each sequence's
+    paged K/V (pools ``[num_blocks, block_size, n_kv, d]``)."""
+    dev = _need_cuda(q, k_pool, v_pool, block_table, context_lens)
+    _, bs, n_kv, d_k = k_pool.shape
+    d_v = v_pool.shape[3]
+    desc = _desc(q, block_table, context_lens, n_kv, d_k, d_v, bs, _TORCH_TO_KVP[k_pool.dtype],
+                 max_context_len, split_tokens, total_context_len)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=dev)
+    ws, wsb = _workspace(desc, workspace, dev)
+    _check(_lib.paged_decode_attention(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                       _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(desc),
+                                       _ptr(ws), wsb, _stream(dev)))
+    return out
+
+
+def paged_decode_attention_int8(q, k_codes, k_scale, v_codes, v_scale, block_table, context_lens,
+                                scale, out=None, *, max_context_len, split_tokens=0,
+                                total_context_len=0, workspace=None):
+    dev = _need_cuda(q, k_codes, k_scale, v_codes, v_scale, block_table, context_lens)
+    _, bs, n_kv, d_k = k_codes.shape
+    d_v = v_codes.shape[3]
+    desc = _desc(q, block_table, context_lens, n_kv, d_k, d_v, bs, KVP_INT8, max_context_len,
+                 split_tokens, total_context_len)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=dev)
+    ws, wsb = _workspace(desc, workspace, dev)
+    _check(_lib.paged_decode_attention_int8(_ptr(q), _ptr(k_codes), _ptr(k_scale), _ptr(v_codes),
+                                            _ptr(v_scale), _ptr(block_table), _ptr(context_lens),
+                                            float(scale), _ptr(out), ctypes.byref(desc), _ptr(ws), wsb,
+                                            _stream(dev)))
+    return out
+
+
+def paged_decode_attention_mla(q, latent_pool, block_table, context_lens, scale, d_v, out=None, *,
+                               max_context_len, split_tokens=0, total_context_len=0, workspace=None):
+    dev = _need_cuda(q, latent_pool, block_table, context_lens)
+    _, bs, n_kv, d_k = latent_pool.shape
+    desc = _desc(q, block_table, context_lens, n_kv, d_k, d_v, bs, _TORCH_TO_KVP[latent_pool.dtype],
+                 max_context_len, split_tokens, total_context_len)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=dev)
+    ws, wsb = _workspace(desc, workspace, dev)
+    _check(_lib.paged_decode_attention_mla(_ptr(q), _ptr(latent_pool), _ptr(block_table),
+                                           _ptr(context_lens), float(scale), _ptr(out),
+                                           ctypes.byref(desc), _ptr(ws), wsb, _stream(dev)))
+    return out
+
+
+def make_desc(*, B, n_h, n_kv, d_k, d_v, block_size, max_blocks_per_seq, max_context_len,
+              q_dtype, kv_dtype, split_tokens=0, total_context_len=0) -> _DecodeDesc:
+    """A decode description from plain values (dtype codes KVP_F32/BF16/INT8)."""
+    return _DecodeDesc(B, n_h, n_kv, d_k, d_v, block_size, max_blocks_per_seq, max_context_len,
+                       q_dtype, kv_dtype, split_tokens, total_context_len)
+
+
+def paged_decode_validate(block_table, context_lens, desc: _DecodeDesc, num_blocks: int) -> None:
+    dev = _need_cuda(block_table, context_lens)
+    _check(_lib.paged_decode_validate(_ptr(block_table), _ptr(context_lens), ctypes.byref(desc),
+                                      int(num_blocks), _stream(dev)))
+
+
+# --------------------------------------------------------------------- prepared calls
+
+class PreparedCall:
+    """A library call with its arguments marshalled once (for tight loops:
+    decode steps over many layers).  Calling it enqueues the same work on
+    the current stream of the tensors' device."""
+
+    def __init__(self, fn, args, device, keep):
+        self._fn = fn
+        self._args = list(args)
+        self._device = device
+        self._keep = keep          # tensors that must stay alive
+
+    def __call__(self) -> None:
+        self._args[-1] = _stream(self._device)
+        _check(self._fn(*self._args))
+
+
+def prepare_decode(q, k_pool, v_pool, block_table, context_lens, scale, out, *, max_context_len,
+                   split_tokens=0, total_context_len=0, workspace=None) -> PreparedCall:
+    dev = _need_cuda(q, k_pool, v_pool, block_table, context_lens, out)
+    _, bs, n_kv, d_k = k_pool.shape
+    desc = _desc(q, block_table, context_lens, n_kv, d_k, v_pool.shape[3], bs,
+                 _TORCH_TO_KVP[k_pool.dtype], max_context_len, split_tokens, total_context_len)
+    ws, wsb = _workspace(desc, workspace, dev)
+    args = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(context_lens),
+            ctypes.c_float(scale), _ptr(out), ctypes.byref(desc), _ptr(ws), wsb, None)
+    return PreparedCall(_lib.paged_decode_attention, args, dev,
+                        (q, k_pool, v_pool, block_table, context_lens, out, ws, desc))
+
+
+def prepare_reshape_and_cache(pool: KVPool, k_new, v_new, slot_mapping) -> PreparedCall:
+    dev = _need_cuda(k_new, v_new, slot_mapping)
+    n = slot_mapping.numel()
+    args = (pool.handle, _ptr(k_new), _ptr(v_new), _TORCH_TO_KVP[k_new.dtype], _ptr(slot_mapping), n, None)
+    return PreparedCall(_lib.reshape_and_cache, args, dev, (pool, k_new, v_new, slot_mapping))

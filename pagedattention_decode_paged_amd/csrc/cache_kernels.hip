@@ -1,0 +1,164 @@
+// Cache-side kernels: slot mapping, the K/V write (plain and INT8
+// quantize-on-write) and the block-table gather used to check addressing.
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+// faulkner, logical/physical block mapping: logical block = pos >> shift,
+// offset = pos & (bs - 1), physical block from the table; slot numbers the
+// pool's (block, offset) cells row-major.
+__global__ void slot_mapping_kernel(const int32_t* __restrict__ bt, int32_t mb, int32_t shift,
+                                    const int32_t* __restrict__ seq_ids,
+                                    const int32_t* __restrict__ positions, int64_t n,
+                                    int64_t* __restrict__ slots) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  int32_t b = seq_ids[t];
+  int32_t pos = positions[t];
+  int64_t out = -1;
+  if (b >= 0 && pos >= 0) {
+    int32_t lb = pos >> shift;
+    if (lb < mb) {
+      int32_t phys = bt[(int64_t)b * mb + lb];
+      if (phys >= 0) out = ((int64_t)phys << shift) + (pos & ((1 << shift) - 1));
+    }
+  }
+  slots[t] = out;
+}
+
+// One workgroup per token row; 16-byte moves when the row allows it.
+template <typename V>
+__global__ void cache_copy_kernel(uint8_t* __restrict__ pool, const uint8_t* __restrict__ src,
+                                  const int64_t* __restrict__ slots, int64_t row_bytes) {
+  int64_t t = blockIdx.x;
+  int64_t s = slots[t];
+  if (s < 0) return;
+  const V* in = reinterpret_cast<const V*>(src + t * row_bytes);
+  V* out = reinterpret_cast<V*>(pool + s * row_bytes);
+  int64_t n = row_bytes / (int64_t)sizeof(V);
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) out[i] = in[i];
+}
+
+__device__ __forceinline__ float load_as_f32(const void* src, int64_t i, bool bf16) {
+  if (bf16) {
+    uint32_t bits = reinterpret_cast<const uint16_t*>(src)[i];
+    return __uint_as_float(bits << 16);
+  }
+  return reinterpret_cast<const float*>(src)[i];
+}
+
+// guijiagi 4.2, 8-bit branch, in binary32: one wavefront per (token, head)
+// row.  The absolute maximum is exact; the scale and the quotients are IEEE
+// divisions (HIP's default float division is correctly rounded); rintf
+// rounds half to even.
+__global__ void cache_quant_int8_kernel(int8_t* __restrict__ codes, float* __restrict__ scales,
+                                        const void* __restrict__ src, int bf16,
+                                        const int64_t* __restrict__ slots, int64_t num_rows,
+                                        int32_t n_kv, int32_t d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= num_rows) return;
+  const int64_t t = row / n_kv;
+  const int32_t h = (int32_t)(row - t * n_kv);
+  const int64_t s = slots[t];
+  if (s < 0) return;
+  const int64_t in_base = row * d;
+  float amax = 0.f;
+  for (int i = lane; i < d; i += 64) amax = fmaxf(amax, fabsf(load_as_f32(src, in_base + i, bf16)));
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax / 127.0f;
+  const int64_t out_row = s * n_kv + h;
+  int8_t* crow = codes + out_row * d;
+  for (int i = lane; i < d; i += 64) {
+    int c = 0;
+    if (scale > 0.f) {
+      float r = rintf(load_as_f32(src, in_base + i, bf16) / scale);
+      r = fminf(fmaxf(r, -128.f), 127.f);
+      c = (int)r;
+    }
+    crow[i] = (int8_t)c;
+  }
+  if (lane == 0) scales[out_row] = scale;
+}
+
+// qwbw 3.4: walk each sequence's table and copy its rows in logical order.
+template <typename V>
+__global__ void gather_kernel(const uint8_t* __restrict__ pool, int64_t row_bytes, int32_t shift,
+                              const int32_t* __restrict__ bt, int32_t mb,
+                              const int32_t* __restrict__ ctx, int32_t max_ctx,
+                              uint8_t* __restrict__ out) {
+  const int32_t j = blockIdx.x;
+  const int32_t b = blockIdx.y;
+  if (j >= ctx[b]) return;
+  const int32_t phys = bt[(int64_t)b * mb + (j >> shift)];
+  const int64_t slot = ((int64_t)phys << shift) + (j & ((1 << shift) - 1));
+  const V* in = reinterpret_cast<const V*>(pool + slot * row_bytes);
+  V* o = reinterpret_cast<V*>(out + ((int64_t)b * max_ctx + j) * row_bytes);
+  int64_t n = row_bytes / (int64_t)sizeof(V);
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) o[i] = in[i];
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(const int32_t* block_table, int32_t mb, int32_t shift,
+                               const int32_t* seq_ids, const int32_t* positions,
+                               int64_t n, int64_t* slots, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int threads = 256;
+  dim3 grid((unsigned)((n + threads - 1) / threads));
+  hipLaunchKernelGGL(slot_mapping_kernel, grid, dim3(threads), 0, stream, block_table, mb, shift,
+                     seq_ids, positions, n, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_copy(void* pool, const void* src, const int64_t* slots,
+                             int64_t num_tokens, int64_t row_bytes, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  dim3 grid((unsigned)num_tokens);
+  const bool v16 = (row_bytes % 16 == 0) && ((uintptr_t)pool % 16 == 0) &&
+                   ((uintptr_t)src % 16 == 0);
+  int64_t nvec = v16 ? row_bytes / 16 : row_bytes / 4;
+  int threads = nvec >= 256 ? 256 : (int)((nvec + 63) / 64) * 64;
+  if (v16)
+    hipLaunchKernelGGL(cache_copy_kernel<uint4>, grid, dim3(threads), 0, stream,
+                       (uint8_t*)pool, (const uint8_t*)src, slots, row_bytes);
+  else
+    hipLaunchKernelGGL(cache_copy_kernel<uint32_t>, grid, dim3(threads), 0, stream,
+                       (uint8_t*)pool, (const uint8_t*)src, slots, row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_quant_int8(int8_t* codes, float* scales, const void* src, bool src_bf16,
+                                   const int64_t* slots, int64_t num_tokens, int32_t n_kv,
+                                   int32_t d, hipStream_t stream) {
+  const int64_t rows = num_tokens * n_kv;
+  if (rows == 0) return hipSuccess;
+  const int waves = 4;
+  dim3 grid((unsigned)((rows + waves - 1) / waves));
+  hipLaunchKernelGGL(cache_quant_int8_kernel, grid, dim3(64 * waves), 0, stream, codes, scales,
+                     src, src_bf16 ? 1 : 0, slots, rows, n_kv, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* pool, int64_t row_bytes, int32_t shift,
+                         const int32_t* block_table, int32_t mb, const int32_t* context_lens,
+                         int32_t B, int32_t max_ctx, void* out, hipStream_t stream) {
+  if (B == 0 || max_ctx == 0) return hipSuccess;
+  dim3 grid((unsigned)max_ctx, (unsigned)B);
+  const bool v16 = (row_bytes % 16 == 0) && ((uintptr_t)pool % 16 == 0) &&
+                   ((uintptr_t)out % 16 == 0);
+  int64_t nvec = v16 ? row_bytes / 16 : row_bytes / 4;
+  int threads = nvec >= 256 ? 256 : (int)((nvec + 63) / 64) * 64;
+  if (v16)
+    hipLaunchKernelGGL(gather_kernel<uint4>, grid, dim3(threads), 0, stream,
+                       (const uint8_t*)pool, row_bytes, shift, block_table, mb, context_lens,
+                       max_ctx, (uint8_t*)out);
+  else
+    hipLaunchKernelGGL(gather_kernel<uint32_t>, grid, dim3(threads), 0, stream,
+                       (const uint8_t*)pool, row_bytes, shift, block_table, mb, context_lens,
+                       max_ctx, (uint8_t*)out);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI host layer (pagedkv_api.cpp) and the
+// kernel translation units.  Launchers return hipError_t; the host layer has
+// already validated every shape and pointer they receive.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// ---------------------------------------------------------------- cache ops
+hipError_t launch_slot_mapping(const int32_t* block_table, int32_t max_blocks_per_seq,
+                               int32_t block_shift, const int32_t* seq_ids,
+                               const int32_t* positions, int64_t num_tokens,
+                               int64_t* slots, hipStream_t stream);
+
+// Bit copy of num_tokens rows of row_bytes each (row_bytes % 4 == 0).
+hipError_t launch_cache_copy(void* pool, const void* src, const int64_t* slots,
+                             int64_t num_tokens, int64_t row_bytes, hipStream_t stream);
+
+// Quantize-on-write: src rows [num_tokens, n_kv, d] (f32 or bf16 bits),
+// codes [slots, n_kv, d] int8, scales [slots, n_kv] f32.
+hipError_t launch_cache_quant_int8(int8_t* codes, float* scales, const void* src,
+                                   bool src_bf16, const int64_t* slots, int64_t num_tokens,
+                                   int32_t n_kv, int32_t d, hipStream_t stream);
+
+hipError_t launch_gather(const void* pool, int64_t row_bytes, int32_t block_shift,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t B, int32_t max_context_len,
+                         void* out, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode
+enum class KV { F32, BF16, INT8 };
+
+struct DecodeParams {
+  const void* q;
+  const void* k;            // K values or codes
+  const void* v;            // V values or codes (== k for latent)
+  const float* k_scale;     // INT8 only
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  void* out;
+  float* part_o;            // [B, n_h, num_splits, d_v] (num_splits > 1)
+  float* part_ml;           // [B, n_h, num_splits, 2]  (max, sum)
+  float scale;
+  int32_t B, n_h, n_kv, d_k, d_v;
+  int32_t block_shift;      // log2(block_size)
+  int32_t max_blocks_per_seq;
+  int32_t split_tokens;     // multiple of the kernel's per-split granule
+  int32_t num_splits;
+  bool q_bf16;
+  KV kv;
+};
+
+// GQA/MQA/MHA over float or INT8 pools (VALU kernels).  Returns
+// hipErrorInvalidValue for a (d, g, dtype) combination with no instance.
+hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream);
+
+// Absorbed MLA over a bf16 latent pool (MFMA kernel).
+hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
+
+// Whether an instance exists (host-side check before launch).
+bool gqa_supported(KV kv, bool q_bf16, int d_k, int d_v, int g);
+bool mla_supported(int d_k, int d_v, int n_h, int block_size);
+
+// Context tokens each workgroup of the GQA kernel walks per split must be a
+// multiple of this.
+constexpr int kGqaSplitGranule = 256;
+constexpr int kMlaSplitGranule = 64;
+
+}  // namespace pkv

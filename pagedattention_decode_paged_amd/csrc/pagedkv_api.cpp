@@ -1,0 +1,472 @@
+// C-ABI host layer: argument validation, pool management, split planning,
+// workspace sizing and kernel dispatch.  Every check runs on the host before
+// anything is enqueued; failures return a status and set a per-thread message.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvp_status fail(kvp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kvp_status ok() {
+  g_last_error.clear();
+  return KVP_OK;
+}
+
+kvp_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t dtype_bytes(kvp_dtype t) {
+  switch (t) {
+    case KVP_F32: return 4;
+    case KVP_BF16: return 2;
+    case KVP_INT8: return 1;
+  }
+  return 0;
+}
+
+bool dtype_valid(int t) { return t == KVP_F32 || t == KVP_BF16 || t == KVP_INT8; }
+
+struct PoolLayout {
+  size_t k_off = 0, v_off = 0, ks_off = 0, vs_off = 0, total = 0;
+  size_t k_bytes = 0, v_bytes = 0, s_bytes = 0;
+};
+
+const char* pool_desc_error(const kvp_pool_desc* d) {
+  if (!d) return "pool description is NULL";
+  if (d->num_blocks <= 0) return "num_blocks must be > 0";
+  if (!is_pow2(d->block_size) || d->block_size > 256) return "block_size must be a power of two in [1, 256]";
+  if (d->n_kv <= 0) return "n_kv must be > 0";
+  if (d->d_k <= 0 || d->d_v <= 0) return "d_k and d_v must be > 0";
+  if (!dtype_valid(d->dtype)) return "unknown pool dtype";
+  if (d->latent != 0 && d->latent != 1) return "latent must be 0 or 1";
+  if (d->latent && d->n_kv != 1) return "a latent pool has n_kv == 1";
+  if (d->latent && d->d_v > d->d_k) return "a latent pool needs d_v <= d_k";
+  if (d->latent && d->dtype == KVP_INT8) return "INT8 latent pools are not supported";
+  const size_t eb = dtype_bytes(d->dtype);
+  if ((d->d_k * eb) % 4 || (d->d_v * eb) % 4) return "row bytes must be a multiple of 4";
+  return nullptr;
+}
+
+PoolLayout pool_layout(const kvp_pool_desc* d) {
+  PoolLayout L;
+  const size_t eb = dtype_bytes(d->dtype);
+  const size_t slots = (size_t)d->num_blocks * (size_t)d->block_size;
+  L.k_bytes = slots * d->n_kv * d->d_k * eb;
+  L.v_bytes = d->latent ? 0 : slots * d->n_kv * d->d_v * eb;
+  L.s_bytes = d->dtype == KVP_INT8 ? slots * d->n_kv * sizeof(float) : 0;
+  size_t off = 0;
+  L.k_off = off; off = round_up(off + L.k_bytes, 256);
+  L.v_off = off; off = round_up(off + L.v_bytes, 256);
+  L.ks_off = off; off = round_up(off + L.s_bytes, 256);
+  L.vs_off = off; off = round_up(off + (d->latent ? 0 : L.s_bytes), 256);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct kvp_pool {
+  kvp_pool_desc desc;
+  PoolLayout layout;
+  uint8_t* base = nullptr;
+  bool owned = false;
+};
+
+extern "C" {
+
+const char* kvp_last_error(void) { return g_last_error.c_str(); }
+
+const char* kvp_version(void) { return "pagedkv 0.1 (gfx950)"; }
+
+size_t kv_pool_required_bytes(const kvp_pool_desc* desc) {
+  if (pool_desc_error(desc)) return 0;
+  return pool_layout(desc).total;
+}
+
+kvp_status kv_pool_create(const kvp_pool_desc* desc, void* storage, size_t storage_bytes,
+                          kvp_pool** out) {
+  if (!out) return fail(KVP_ERR_INVALID_ARG, "kv_pool_create: out is NULL");
+  *out = nullptr;
+  if (const char* e = pool_desc_error(desc)) return fail(KVP_ERR_INVALID_ARG, "kv_pool_create: %s", e);
+  PoolLayout L = pool_layout(desc);
+  uint8_t* base = nullptr;
+  bool owned = false;
+  if (storage) {
+    if (!aligned(storage, 256)) return fail(KVP_ERR_INVALID_ARG, "kv_pool_create: storage must be 256-byte aligned");
+    if (storage_bytes < L.total)
+      return fail(KVP_ERR_INVALID_ARG, "kv_pool_create: storage has %zu bytes, pool needs %zu",
+                  storage_bytes, L.total);
+    base = static_cast<uint8_t*>(storage);
+  } else {
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, L.total);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(KVP_ERR_OUT_OF_MEMORY, "kv_pool_create: out of device memory for %zu bytes (%s)",
+                  L.total, hipGetErrorString(e));
+    }
+    base = static_cast<uint8_t*>(p);
+    owned = true;
+  }
+  kvp_pool* pool = new (std::nothrow) kvp_pool;
+  if (!pool) {
+    if (owned) (void)hipFree(base);
+    return fail(KVP_ERR_OUT_OF_MEMORY, "kv_pool_create: host allocation failed");
+  }
+  pool->desc = *desc;
+  pool->layout = L;
+  pool->base = base;
+  pool->owned = owned;
+  *out = pool;
+  return ok();
+}
+
+void kv_pool_destroy(kvp_pool* pool) {
+  if (!pool) return;
+  if (pool->owned && pool->base) (void)hipFree(pool->base);
+  delete pool;
+}
+
+kvp_status kv_pool_view_get(const kvp_pool* pool, kvp_pool_view* out) {
+  if (!pool || !out) return fail(KVP_ERR_INVALID_ARG, "kv_pool_view_get: NULL argument");
+  const PoolLayout& L = pool->layout;
+  out->k = pool->base + L.k_off;
+  out->v = pool->desc.latent ? out->k : pool->base + L.v_off;
+  out->k_scale = pool->desc.dtype == KVP_INT8 ? reinterpret_cast<float*>(pool->base + L.ks_off) : nullptr;
+  out->v_scale = (pool->desc.dtype == KVP_INT8 && !pool->desc.latent)
+                     ? reinterpret_cast<float*>(pool->base + L.vs_off) : nullptr;
+  out->total_bytes = L.total;
+  out->desc = pool->desc;
+  return ok();
+}
+
+kvp_status paged_slot_mapping(const int32_t* block_table, int32_t max_blocks_per_seq,
+                              int32_t block_size, const int32_t* seq_ids, const int32_t* positions,
+                              int64_t num_tokens, int64_t* slots, void* stream) {
+  if (num_tokens < 0) return fail(KVP_ERR_INVALID_ARG, "paged_slot_mapping: num_tokens < 0");
+  if (num_tokens == 0) return ok();
+  if (!block_table || !seq_ids || !positions || !slots)
+    return fail(KVP_ERR_INVALID_ARG, "paged_slot_mapping: NULL pointer");
+  if (max_blocks_per_seq <= 0) return fail(KVP_ERR_INVALID_ARG, "paged_slot_mapping: max_blocks_per_seq must be > 0");
+  if (!is_pow2(block_size) || block_size > 256)
+    return fail(KVP_ERR_INVALID_ARG, "paged_slot_mapping: block_size must be a power of two in [1, 256]");
+  return hip_status(pkv::launch_slot_mapping(block_table, max_blocks_per_seq, log2i(block_size),
+                                             seq_ids, positions, num_tokens, slots,
+                                             static_cast<hipStream_t>(stream)),
+                    "paged_slot_mapping");
+}
+
+kvp_status reshape_and_cache(kvp_pool* pool, const void* k_new, const void* v_new,
+                             kvp_dtype in_dtype, const int64_t* slot_mapping, int64_t num_tokens,
+                             void* stream) {
+  if (!pool) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: pool is NULL");
+  if (num_tokens < 0) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: num_tokens < 0");
+  if (num_tokens == 0) return ok();
+  const kvp_pool_desc& d = pool->desc;
+  if (!k_new || !slot_mapping) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: NULL pointer");
+  if (!d.latent && !v_new) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: v_new is NULL");
+  if (!dtype_valid(in_dtype)) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: unknown in_dtype");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  kvp_pool_view v;
+  kv_pool_view_get(pool, &v);
+  if (d.dtype == KVP_INT8) {
+    if (in_dtype == KVP_INT8) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: INT8 pools take F32 or BF16 rows");
+    const bool bf = in_dtype == KVP_BF16;
+    hipError_t e = pkv::launch_cache_quant_int8(static_cast<int8_t*>(v.k), v.k_scale, k_new, bf,
+                                               slot_mapping, num_tokens, d.n_kv, d.d_k, st);
+    if (e != hipSuccess) return hip_status(e, "reshape_and_cache (K)");
+    e = pkv::launch_cache_quant_int8(static_cast<int8_t*>(v.v), v.v_scale, v_new, bf, slot_mapping,
+                                     num_tokens, d.n_kv, d.d_v, st);
+    return hip_status(e, "reshape_and_cache (V)");
+  }
+  if (in_dtype != d.dtype)
+    return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: rows must have the pool's dtype");
+  const size_t eb = dtype_bytes(d.dtype);
+  hipError_t e = pkv::launch_cache_copy(v.k, k_new, slot_mapping, num_tokens,
+                                        (int64_t)d.n_kv * d.d_k * eb, st);
+  if (e != hipSuccess || d.latent) return hip_status(e, "reshape_and_cache (K)");
+  e = pkv::launch_cache_copy(v.v, v_new, slot_mapping, num_tokens, (int64_t)d.n_kv * d.d_v * eb, st);
+  return hip_status(e, "reshape_and_cache (V)");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- decode
+namespace {
+
+enum class Variant { Float, Int8, Mla };
+
+const char* decode_desc_error(const kvp_decode_desc* d) {
+  if (!d) return "decode description is NULL";
+  if (d->B < 0) return "B must be >= 0";
+  if (d->n_h <= 0 || d->n_kv <= 0) return "n_h and n_kv must be > 0";
+  if (d->n_h % d->n_kv) return "n_h must be a multiple of n_kv";
+  if (d->d_k <= 0 || d->d_v <= 0) return "d_k and d_v must be > 0";
+  if (!is_pow2(d->block_size) || d->block_size > 256) return "block_size must be a power of two in [1, 256]";
+  if (d->max_blocks_per_seq <= 0) return "max_blocks_per_seq must be > 0";
+  if (d->max_context_len < 0) return "max_context_len must be >= 0";
+  if ((int64_t)d->max_context_len > (int64_t)d->max_blocks_per_seq * d->block_size)
+    return "max_context_len exceeds max_blocks_per_seq * block_size";
+  if (d->q_dtype != KVP_F32 && d->q_dtype != KVP_BF16) return "q_dtype must be F32 or BF16";
+  if (!dtype_valid(d->kv_dtype)) return "unknown kv_dtype";
+  if (d->split_tokens < 0) return "split_tokens must be >= 0";
+  if (d->total_context_len < 0) return "total_context_len must be >= 0";
+  return nullptr;
+}
+
+Variant variant_of(const kvp_decode_desc* d) {
+  if (d->kv_dtype == KVP_INT8) return Variant::Int8;
+  if (d->n_kv == 1 && d->d_k != d->d_v) return Variant::Mla;
+  return Variant::Float;
+}
+
+int granule(Variant v) { return v == Variant::Mla ? pkv::kMlaSplitGranule : pkv::kGqaSplitGranule; }
+
+// Context split size: aim for about kTargetUnits workgroups doing real work
+// (8 per compute unit on 256 CUs), in multiples of the kernel's granule.
+constexpr int64_t kTargetUnits = 2048;
+constexpr int32_t kMaxSplit = 2048;
+
+int32_t plan_split(const kvp_decode_desc* d, Variant v) {
+  const int g = granule(v);
+  if (d->split_tokens > 0) return d->split_tokens;
+  const int64_t total = d->total_context_len > 0 ? d->total_context_len
+                                                 : (int64_t)d->B * d->max_context_len;
+  const int64_t heads = v == Variant::Mla ? 1 : d->n_kv;
+  const int64_t work = total * heads;
+  int64_t split = (work + kTargetUnits - 1) / kTargetUnits;
+  split = (split + g - 1) / g * g;
+  if (split < g) split = g;
+  if (split > kMaxSplit) split = kMaxSplit;
+  return (int32_t)split;
+}
+
+int32_t num_splits_of(const kvp_decode_desc* d, int32_t split) {
+  if (d->max_context_len <= 0) return 1;
+  return (d->max_context_len + split - 1) / split;
+}
+
+size_t workspace_for(const kvp_decode_desc* d, Variant v) {
+  const int32_t split = plan_split(d, v);
+  const int32_t ns = num_splits_of(d, split);
+  if (ns <= 1) return 0;
+  const size_t rows = (size_t)d->B * d->n_h * ns;
+  return round_up(rows * d->d_v * sizeof(float), 256) + round_up(rows * 2 * sizeof(float), 256);
+}
+
+kvp_status decode_common(Variant var, const char* fn, const void* q, const void* k,
+                         const void* v, const float* ks, const float* vs,
+                         const int32_t* block_table, const int32_t* context_lens, float scale,
+                         void* out, const kvp_decode_desc* d, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (const char* e = decode_desc_error(d)) return fail(KVP_ERR_INVALID_ARG, "%s: %s", fn, e);
+  if (variant_of(d) != var) {
+    if (var == Variant::Int8) return fail(KVP_ERR_INVALID_ARG, "%s: desc->kv_dtype must be KVP_INT8", fn);
+    if (var == Variant::Mla) return fail(KVP_ERR_INVALID_ARG, "%s: MLA needs n_kv == 1 and d_v < d_k", fn);
+    if (d->kv_dtype == KVP_INT8) return fail(KVP_ERR_INVALID_ARG, "%s: use paged_decode_attention_int8 for INT8 pools", fn);
+    return fail(KVP_ERR_INVALID_ARG, "%s: n_kv == 1 with d_v != d_k is the MLA layout; use paged_decode_attention_mla", fn);
+  }
+  if (d->B == 0) return ok();
+  if (!q || !k || !block_table || !context_lens || !out) return fail(KVP_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (var != Variant::Mla && !v) return fail(KVP_ERR_INVALID_ARG, "%s: v pool is NULL", fn);
+  if (var == Variant::Int8 && (!ks || !vs)) return fail(KVP_ERR_INVALID_ARG, "%s: NULL scale array", fn);
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return fail(KVP_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k, 16) || (v && !aligned(v, 16)))
+    return fail(KVP_ERR_INVALID_ARG, "%s: q, out and pools must be 16-byte aligned", fn);
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4))
+    return fail(KVP_ERR_INVALID_ARG, "%s: tables must be 4-byte aligned", fn);
+  if (d->B > 65535 || d->n_kv > 65535) return fail(KVP_ERR_UNSUPPORTED, "%s: B and n_kv must be <= 65535", fn);
+
+  const int g = d->n_h / d->n_kv;
+  const bool q_bf16 = d->q_dtype == KVP_BF16;
+  if (var == Variant::Float) {
+    if (d->kv_dtype != d->q_dtype)
+      return fail(KVP_ERR_UNSUPPORTED, "%s: q and the pools must have the same dtype", fn);
+    const pkv::KV kv = d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32;
+    if (!pkv::gqa_supported(kv, q_bf16, d->d_k, d->d_v, g))
+      return fail(KVP_ERR_UNSUPPORTED, "%s: no kernel for dtype %d, d_k %d, d_v %d, g %d", fn,
+                  (int)d->kv_dtype, d->d_k, d->d_v, g);
+  } else if (var == Variant::Int8) {
+    if (!pkv::gqa_supported(pkv::KV::INT8, q_bf16, d->d_k, d->d_v, g))
+      return fail(KVP_ERR_UNSUPPORTED, "%s: no INT8 kernel for q dtype %d, d_k %d, d_v %d, g %d", fn,
+                  (int)d->q_dtype, d->d_k, d->d_v, g);
+  } else {
+    if (d->kv_dtype != KVP_BF16 || !q_bf16 || !pkv::mla_supported(d->d_k, d->d_v, d->n_h, d->block_size))
+      return fail(KVP_ERR_UNSUPPORTED, "%s: no MLA kernel for n_h %d, d_k %d, d_v %d, block %d", fn,
+                  d->n_h, d->d_k, d->d_v, d->block_size);
+  }
+
+  const int gr = granule(var);
+  if (d->split_tokens > 0 && (d->split_tokens % gr || d->split_tokens > kMaxSplit))
+    return fail(KVP_ERR_INVALID_ARG, "%s: split_tokens must be a multiple of %d and <= %d", fn, gr, kMaxSplit);
+  const int32_t split = plan_split(d, var);
+  const int32_t ns = num_splits_of(d, split);
+  const size_t need = workspace_for(d, var);
+  if (need > 0) {
+    if (!workspace) return fail(KVP_ERR_INVALID_ARG, "%s: workspace of %zu bytes required", fn, need);
+    if (workspace_bytes < need)
+      return fail(KVP_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(KVP_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  }
+  if (ns > 65535 * 1024) return fail(KVP_ERR_UNSUPPORTED, "%s: too many splits", fn);
+
+  pkv::DecodeParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = var == Variant::Mla ? k : v;
+  p.k_scale = ks;
+  p.v_scale = vs;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.out = out;
+  if (need > 0) {
+    const size_t rows = (size_t)d->B * d->n_h * ns;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                         round_up(rows * d->d_v * sizeof(float), 256));
+  }
+  p.scale = scale;
+  p.B = d->B;
+  p.n_h = d->n_h;
+  p.n_kv = d->n_kv;
+  p.d_k = d->d_k;
+  p.d_v = d->d_v;
+  p.block_shift = log2i(d->block_size);
+  p.max_blocks_per_seq = d->max_blocks_per_seq;
+  p.split_tokens = split;
+  p.num_splits = ns;
+  p.q_bf16 = q_bf16;
+  p.kv = var == Variant::Int8 ? pkv::KV::INT8 : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = var == Variant::Mla ? pkv::launch_decode_mla(p, st) : pkv::launch_decode_gqa(p, st);
+  return hip_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_decode_workspace_size(const kvp_decode_desc* desc) {
+  if (decode_desc_error(desc)) return 0;
+  return workspace_for(desc, variant_of(desc));
+}
+
+int32_t paged_decode_split_tokens(const kvp_decode_desc* desc) {
+  if (decode_desc_error(desc)) return 0;
+  return plan_split(desc, variant_of(desc));
+}
+
+kvp_status paged_decode_attention(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* context_lens,
+                                  float scale, void* out, const kvp_decode_desc* desc,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(Variant::Float, "paged_decode_attention", q, k_pool, v_pool, nullptr,
+                       nullptr, block_table, context_lens, scale, out, desc, workspace,
+                       workspace_bytes, stream);
+}
+
+kvp_status paged_decode_attention_int8(const void* q, const int8_t* k_codes, const float* k_scale,
+                                       const int8_t* v_codes, const float* v_scale,
+                                       const int32_t* block_table, const int32_t* context_lens,
+                                       float scale, void* out, const kvp_decode_desc* desc,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(Variant::Int8, "paged_decode_attention_int8", q, k_codes, v_codes, k_scale,
+                       v_scale, block_table, context_lens, scale, out, desc, workspace,
+                       workspace_bytes, stream);
+}
+
+kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
+                                      const int32_t* block_table, const int32_t* context_lens,
+                                      float scale, void* out, const kvp_decode_desc* desc,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(Variant::Mla, "paged_decode_attention_mla", q, latent_pool, latent_pool,
+                       nullptr, nullptr, block_table, context_lens, scale, out, desc, workspace,
+                       workspace_bytes, stream);
+}
+
+kvp_status paged_gather(const void* pool, int32_t elem_bytes, int32_t block_size, int32_t n_kv,
+                        int32_t d, const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t B, int32_t max_context_len, void* out,
+                        void* stream) {
+  if (B < 0 || max_context_len < 0) return fail(KVP_ERR_INVALID_ARG, "paged_gather: negative size");
+  if (B == 0 || max_context_len == 0) return ok();
+  if (!pool || !block_table || !context_lens || !out) return fail(KVP_ERR_INVALID_ARG, "paged_gather: NULL pointer");
+  if (!(elem_bytes == 1 || elem_bytes == 2 || elem_bytes == 4))
+    return fail(KVP_ERR_INVALID_ARG, "paged_gather: elem_bytes must be 1, 2 or 4");
+  if (!is_pow2(block_size) || block_size > 256)
+    return fail(KVP_ERR_INVALID_ARG, "paged_gather: block_size must be a power of two in [1, 256]");
+  if (n_kv <= 0 || d <= 0 || max_blocks_per_seq <= 0) return fail(KVP_ERR_INVALID_ARG, "paged_gather: bad shape");
+  const int64_t row_bytes = (int64_t)n_kv * d * elem_bytes;
+  if (row_bytes % 4) return fail(KVP_ERR_INVALID_ARG, "paged_gather: row bytes must be a multiple of 4");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(KVP_ERR_INVALID_ARG, "paged_gather: max_context_len exceeds the table");
+  if (B > 65535) return fail(KVP_ERR_UNSUPPORTED, "paged_gather: B must be <= 65535");
+  return hip_status(pkv::launch_gather(pool, row_bytes, log2i(block_size), block_table,
+                                       max_blocks_per_seq, context_lens, B, max_context_len, out,
+                                       static_cast<hipStream_t>(stream)),
+                    "paged_gather");
+}
+
+kvp_status paged_decode_validate(const int32_t* block_table, const int32_t* context_lens,
+                                 const kvp_decode_desc* desc, int64_t num_blocks, void* stream) {
+  if (const char* e = decode_desc_error(desc)) return fail(KVP_ERR_INVALID_ARG, "paged_decode_validate: %s", e);
+  if (desc->B == 0) return ok();
+  if (!block_table || !context_lens) return fail(KVP_ERR_INVALID_ARG, "paged_decode_validate: NULL pointer");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> ctx(desc->B);
+  std::vector<int32_t> bt((size_t)desc->B * desc->max_blocks_per_seq);
+  hipError_t e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(bt.data(), block_table, bt.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_status(e, "paged_decode_validate");
+  for (int32_t b = 0; b < desc->B; ++b) {
+    const int32_t c = ctx[b];
+    if (c < 0 || c > desc->max_context_len)
+      return fail(KVP_ERR_INVALID_ARG, "paged_decode_validate: context_lens[%d] = %d outside [0, %d]", b, c,
+                  desc->max_context_len);
+    const int32_t nb = (c + desc->block_size - 1) / desc->block_size;
+    for (int32_t j = 0; j < nb; ++j) {
+      const int32_t p = bt[(size_t)b * desc->max_blocks_per_seq + j];
+      if (p < 0 || p >= num_blocks)
+        return fail(KVP_ERR_INVALID_ARG, "paged_decode_validate: block_table[%d][%d] = %d outside [0, %lld)", b, j,
+                    p, (long long)num_blocks);
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

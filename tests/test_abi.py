@@ -1,0 +1,127 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before any GPU work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+pk = pytest.importorskip("pagedattention_decode_paged_amd",
+                         reason="libpagedkv.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    skip = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in skip})
+
+
+def test_every_declared_function_is_exported():
+    lib = pk.lib()
+    declared = _declared_functions()
+    assert "paged_decode_attention" in declared and "kv_pool_create" in declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in pagedkv.h but not exported"
+    assert set(pk.EXPORTED_SYMBOLS) <= set(declared)
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in pk.version()
+
+
+def test_pool_sizes():
+    # 16 blocks x 16 slots x 2 heads x 64 fp32, K and V, 256-byte aligned regions
+    n = pk.kv_pool_required_bytes(16, 16, 2, 64, 64, pk.torch.float32)
+    assert n == 2 * 16 * 16 * 2 * 64 * 4
+    # INT8 adds fp32 scales per (slot, head) for K and V
+    n8 = pk.kv_pool_required_bytes(10, 16, 8, 128, 128, pk.torch.int8)
+    codes = 10 * 16 * 8 * 128
+    scales = 10 * 16 * 8 * 4
+    assert n8 == 2 * codes + 2 * ((scales + 255) // 256 * 256)
+    # latent pool: one region
+    nl = pk.kv_pool_required_bytes(4, 64, 1, 576, 512, pk.torch.bfloat16, latent=True)
+    assert nl == 4 * 64 * 576 * 2
+    # invalid descriptions size to 0
+    assert pk.kv_pool_required_bytes(16, 12, 2, 64, 64, pk.torch.float32) == 0   # block not pow2
+    assert pk.kv_pool_required_bytes(0, 16, 2, 64, 64, pk.torch.float32) == 0
+    assert pk.kv_pool_required_bytes(4, 64, 2, 576, 512, pk.torch.bfloat16, latent=True) == 0
+
+
+def _desc(**kw):
+    base = dict(B=16, n_h=64, n_kv=8, d_k=128, d_v=128, block_size=16, max_blocks_per_seq=512,
+                max_context_len=8192, q_dtype=pk.KVP_BF16, kv_dtype=pk.KVP_BF16)
+    base.update(kw)
+    return pk.make_desc(**base)
+
+
+def test_split_planning_and_workspace():
+    d = _desc()
+    split = pk.decode_split_tokens(d)
+    assert split % 256 == 0 and 256 <= split <= 2048
+    ns = -(-8192 // split)
+    ws = pk.decode_workspace_size(d)
+    if ns > 1:
+        rows = 16 * 64 * ns
+        assert ws >= rows * 128 * 4 + rows * 8
+    # one split, no workspace
+    d1 = _desc(max_context_len=200, split_tokens=256)
+    assert pk.decode_workspace_size(d1) == 0
+    # explicit split respected
+    d2 = _desc(split_tokens=512)
+    assert pk.decode_split_tokens(d2) == 512
+    assert pk.decode_workspace_size(d2) == (16 * 64 * 16 * 128 * 4) + (16 * 64 * 16 * 2 * 4)
+    # MLA uses 64-token granules
+    dm = _desc(B=64, n_h=128, n_kv=1, d_k=576, d_v=512, block_size=64, max_blocks_per_seq=128,
+               max_context_len=8192)
+    assert pk.decode_split_tokens(dm) % 64 == 0
+
+
+def _call_decode(desc, **ptrs):
+    lib = pk.lib()
+    P = ctypes.c_void_p
+    args = dict(q=P(16), k=P(16), v=P(16), bt=P(16), ctx=P(16), out=P(16))
+    args.update(ptrs)
+    return lib.paged_decode_attention(args["q"], args["k"], args["v"], args["bt"], args["ctx"],
+                                      ctypes.c_float(0.1), args["out"], ctypes.byref(desc),
+                                      None, 0, None)
+
+
+def test_decode_rejects_bad_arguments_on_host():
+    lib = pk.lib()
+    assert _call_decode(_desc(n_h=63)) == pk.KVP_ERR_INVALID_ARG
+    assert b"multiple of n_kv" in lib.kvp_last_error()
+    assert _call_decode(_desc(block_size=12)) == pk.KVP_ERR_INVALID_ARG
+    assert _call_decode(_desc(max_context_len=512 * 16 + 1)) == pk.KVP_ERR_INVALID_ARG
+    assert _call_decode(_desc(split_tokens=300, max_context_len=200)) == pk.KVP_ERR_INVALID_ARG
+    assert _call_decode(_desc(max_context_len=200), q=None) == pk.KVP_ERR_INVALID_ARG
+    assert _call_decode(_desc(max_context_len=200), q=ctypes.c_void_p(18)) == pk.KVP_ERR_INVALID_ARG
+    assert b"aligned" in lib.kvp_last_error()
+    # the default split of an 8K context needs a workspace
+    assert _call_decode(_desc()) == pk.KVP_ERR_INVALID_ARG
+    assert b"workspace" in lib.kvp_last_error()
+    # shapes without a kernel
+    assert _call_decode(_desc(d_k=96, d_v=96, max_context_len=200)) == pk.KVP_ERR_UNSUPPORTED
+    assert _call_decode(_desc(q_dtype=pk.KVP_F32, max_context_len=200)) == pk.KVP_ERR_UNSUPPORTED
+    # INT8 pools must go through the INT8 entry point; MLA shapes through MLA
+    assert _call_decode(_desc(kv_dtype=pk.KVP_INT8, max_context_len=200)) == pk.KVP_ERR_INVALID_ARG
+    assert _call_decode(_desc(n_kv=1, d_k=576, d_v=512, max_context_len=200)) == pk.KVP_ERR_INVALID_ARG
+    # B == 0 is a no-op
+    assert _call_decode(_desc(B=0)) == pk.KVP_OK
+
+
+def test_cache_ops_reject_bad_arguments_on_host():
+    lib = pk.lib()
+    P = ctypes.c_void_p
+    assert lib.paged_slot_mapping(P(16), 4, 12, P(16), P(16), 3, P(16), None) == pk.KVP_ERR_INVALID_ARG
+    assert lib.paged_slot_mapping(None, 4, 16, P(16), P(16), 3, P(16), None) == pk.KVP_ERR_INVALID_ARG
+    assert lib.paged_slot_mapping(None, 4, 16, None, None, 0, None, None) == pk.KVP_OK
+    assert lib.reshape_and_cache(None, P(16), P(16), pk.KVP_F32, P(16), 1, None) == pk.KVP_ERR_INVALID_ARG
+    assert lib.paged_gather(P(16), 3, 16, 2, 64, P(16), 4, P(16), 2, 50, P(16), None) == pk.KVP_ERR_INVALID_ARG
+    assert lib.paged_gather(P(16), 4, 16, 2, 64, P(16), 4, P(16), 2, 65, P(16), None) == pk.KVP_ERR_INVALID_ARG
+    assert lib.kv_pool_create(None, None, 0, ctypes.byref(P())) == pk.KVP_ERR_INVALID_ARG
