@@ -97,7 +97,7 @@ def main():
                             q_dtype=pk.KVP_BF16, kv_dtype=pk.KVP_BF16, split_tokens=args.split_tokens)
         ws_bytes = pk.decode_workspace_size(desc)
         if workspace is None and ws_bytes:
-            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
         calls_rc.append(pk.prepare_reshape_and_cache(ly["pool"], ly["k_new"], ly["v_new"], ly["slots"]))
         calls_dec.append(pk.prepare_decode(ly["q"], ly["pool"].k, ly["pool"].v, ly["bt"], ly["ctx"],
                                            cfg.scale, ly["out"], max_context_len=8192,
@@ -182,7 +182,7 @@ def main():
         "token_heads_per_s": float(f"{tok_heads:.4g}"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_decode_attention (decode_gqa_kernel<128,8,bf16> + split reduce)",
+                     "kernel": "decode_gqa_kernel<128,8,bf16> (split merge fused)",
                      "avg_launch_us": round(us_launch, 2),
                      "bytes_per_launch": kv_bytes_layer},
     }

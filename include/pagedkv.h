@@ -167,7 +167,9 @@ kvp_status reshape_and_cache(kvp_pool* pool, const void* k_new, const void* v_ne
  *          (used to size the launch without reading device memory);
  *          must be <= max_blocks_per_seq * block_size.
  *   workspace: device scratch of at least paged_decode_workspace_size()
- *          bytes (may be NULL when that is 0), 256-byte aligned.
+ *          bytes (may be NULL when that is 0), 256-byte aligned; it holds
+ *          the split partials.  Calls that share a workspace must not
+ *          overlap (use one stream, or one workspace per stream).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t B, n_h, n_kv, d_k, d_v;

@@ -263,7 +263,9 @@ def _workspace(desc, workspace, dev):
     if need == 0:
         return None, 0
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        # zero once: the split counters inside start at zero and every call
+        # leaves them at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     return workspace, workspace.numel()
 
 

@@ -26,6 +26,7 @@
 //   -inf and their V registers are zero, so NaN in unused slots cannot leak.
 #include "internal.h"
 #include "device_common.h"
+#include "decode_epilogue.h"
 
 namespace pkv {
 namespace {
@@ -44,14 +45,33 @@ struct Geo {
   static_assert(kRowBytes == 128 || kRowBytes == 256, "row must be 128 or 256 bytes");
 };
 
-template <int D, int G, bool BF16>
-__global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeParams p) {
+// PAIR (bf16 rows, blocks of at least kWave / kRowQ slots): K and V are read
+// row-coalesced with one uniform block base per load, K reaches the
+// lane-per-token score phase through a swizzled LDS tile, and the value phase
+// multiplies token pairs with v_dot2 against bf16 probability pairs.
+template <int D, int G, bool BF16, bool PAIR>
+__global__ __launch_bounds__(kThreads, 2) void decode_gqa_kernel(const DecodeParams p) {
   using Gm = Geo<D, BF16>;
-  __shared__ __align__(16) int32_t s_bt[kMaxSplitTokens];
-  __shared__ __align__(16) float s_p[kWaves][kTile * G];
+  static_assert(!PAIR || BF16, "pair mode is for bf16 rows");
+  constexpr int kPairs = kTile / 2;                 // token pairs per tile
+  constexpr int kGh = (G + 1) / 2;                  // pair dwords written by first lanes
+  // value phase: PAIR reads V in 8-byte pieces (kAccLpr lanes per row,
+  // kAccTpi rows per load) and pairs token t with t + kAccTpi in one lane
+  constexpr int kAccE = PAIR ? 4 : Gm::kEpl;                       // accumulator columns per lane
+  constexpr int kAccLpr = PAIR ? Gm::kRowBytes / 8 : Gm::kLpr;     // lanes per V row
+  constexpr int kAccTpi = kWave / kAccLpr;                         // V rows per load
+  constexpr int kVL = PAIR ? kTile / kAccTpi : Gm::kSteps;         // V loads per tile
+  __shared__ __align__(16) int32_t s_bt[kBtSlots];
+  __shared__ __align__(16) float s_p[kWaves][PAIR ? 1 : kTile * G];
+  __shared__ __align__(16) uint32_t s_pp[kWaves][PAIR ? kPairs * G : 1];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
-  __shared__ __align__(16) float s_acc[kWaves][G * D];
+  // PAIR: each wave's K tile (kTile rows) is staged here by direct-to-LDS
+  // loads; after the tile loop the same bytes hold the waves' accumulators.
+  constexpr int kKBytes = PAIR ? kWaves * kTile * Gm::kRowBytes : 16;
+  constexpr int kAccBytes = kWaves * G * D * 4;
+  __shared__ __align__(16) uint8_t s_kbuf[kKBytes > kAccBytes ? kKBytes : kAccBytes];
+  float (&s_acc)[kWaves][G * D] = *reinterpret_cast<float (*)[kWaves][G * D]>(s_kbuf);
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -64,15 +84,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeParams
   const int n_h = p.n_h;
 
   if (t_begin >= ctx) {
-    // Only the first split of an empty sequence has anything to write.
-    if (split == 0 && p.num_splits == 1) {
-      for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int h = idx / D, d = idx % D;
-        const int64_t o = ((int64_t)b * n_h + kvh * G + h) * D + d;
-        if (p.q_bf16) reinterpret_cast<uint16_t*>(p.out)[o] = 0;
-        else reinterpret_cast<float*>(p.out)[o] = 0.f;
-      }
-    }
+    if (split == 0) write_zero_rows<G, D>(p, b, kvh);   // empty sequence
     return;
   }
   const int t_end = min(ctx, t_begin + p.split_tokens);
@@ -103,41 +115,98 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeParams
   const int64_t q_dw0 = ((int64_t)b * n_h + (int64_t)kvh * G) * Gm::kRowDw;
 
   float m_run[G], l_run[G];
-  float acc[G][Gm::kEpl];
+  float acc[G][kAccE];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < Gm::kEpl; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < kAccE; ++e) acc[h][e] = 0.f;
   }
 
-  const int vj = lane / Gm::kLpr;      // row within a value load
-  const int ve = lane % Gm::kLpr;      // 16-byte piece within the row
+  const int vj = lane / kAccLpr;       // row within a value load
+  const int ve = lane % kAccLpr;       // piece within the row
 
-  uint4 kreg[Gm::kRowQ];
+  u32x4_t kreg[Gm::kRowQ];
   int tile_start = t_begin + wave * kTile;
-  if (tile_start < t_end) {
+
+  // PAIR: K rows are loaded row-coalesced (kRpi rows of kPr 16-byte pieces
+  // per instruction, one block per instruction) into kreg, stored to this
+  // wave's LDS tile with row r's piece P in slot P ^ swz(r), and read back
+  // one token row per lane; both LDS passes touch every bank once per 16
+  // lanes.  Rows past the context re-read the last valid row (finite data
+  // that gets a masked score and probability 0).
+  constexpr int kPr = Gm::kRowQ;                    // 16-byte pieces per row
+  constexpr int kRpi = kWave / kPr;                 // rows per load instruction
+  constexpr int kRows256 = 256 / Gm::kRowBytes;     // rows per 256 bytes of LDS
+  uint8_t* const kl = s_kbuf + (PAIR ? wave * kTile * Gm::kRowBytes : 0);
+  const int lj = lane / kPr, le = lane % kPr;
+  auto swz = [](int r) { return (r / kRows256) % kPr; };
+  const int t_last = t_end - 1;
+  auto load_k_rows = [&](int ts) {
+#pragma unroll
+    for (int k = 0; k < kPr; ++k) {
+      const int tg = min(ts + k * kRpi, t_last);    // first (valid) token of the instruction
+      const int32_t phys = __builtin_amdgcn_readfirstlane(s_bt[(tg >> shift) - lb0]);
+      const uint8_t* gb = kbase + ((int64_t)phys << shift) * slot_stride;
+      const int tr = min(ts + k * kRpi + lj, t_last);
+      kreg[k] = *reinterpret_cast<const u32x4_t*>(gb + (uint32_t)(tr & bmask) * (uint32_t)slot_stride + (uint32_t)le * 16u);
+    }
+  };
+
+  if constexpr (PAIR) {
+    if (tile_start < t_end) load_k_rows(tile_start);
+  } else if (tile_start < t_end) {
     const int t = tile_start + lane;
     if (t < t_end) {
-      const uint4* src = reinterpret_cast<const uint4*>(row_addr(kbase, t));
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(row_addr(kbase, t));
 #pragma unroll
       for (int i = 0; i < Gm::kRowQ; ++i) kreg[i] = src[i];
     } else {
 #pragma unroll
-      for (int i = 0; i < Gm::kRowQ; ++i) kreg[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < Gm::kRowQ; ++i) kreg[i] = (u32x4_t){0u, 0u, 0u, 0u};
     }
   }
 
   for (; tile_start < t_end; tile_start += kWaves * kTile) {
-    // ---- issue the value loads of this tile
-    uint4 vreg[Gm::kSteps];
+    if constexpr (PAIR) {
+      // rows -> swizzled LDS tile -> this lane's token row
 #pragma unroll
-    for (int k = 0; k < Gm::kSteps; ++k) {
-      const int t = tile_start + k * Gm::kTpi + vj;
-      if (t < t_end) vreg[k] = reinterpret_cast<const uint4*>(row_addr(vbase, t))[ve];
-      else vreg[k] = make_uint4(0, 0, 0, 0);
+      for (int k = 0; k < kPr; ++k) {
+        const int r = k * kRpi + lj;
+        *reinterpret_cast<u32x4_t*>(kl + r * Gm::kRowBytes + ((le ^ swz(r)) * 16)) = kreg[k];
+      }
+      wave_sync_lds();
+      int sw = swz(lane);
+      asm volatile("" : "+v"(sw));          // keep the 16 addresses out of the loop preheader
+      const uint8_t* krow = kl + lane * Gm::kRowBytes;
+#pragma unroll
+      for (int i = 0; i < kPr; ++i)
+        kreg[i] = *reinterpret_cast<const u32x4_t*>(krow + ((i ^ sw) * 16));
     }
+
+    // ---- issue the value loads of this tile (they fly during the scores)
+    uint4 vreg[PAIR ? 1 : Gm::kSteps];
+    u32x2_t vreg2[PAIR ? kVL : 1];
+    if constexpr (PAIR) {
+      // load k covers rows k*kAccTpi .. +kAccTpi-1 of the tile (one block)
+#pragma unroll
+      for (int k = 0; k < kVL; ++k) {
+        const int t_grp = min(tile_start + k * kAccTpi, t_last);
+        const int32_t phys = __builtin_amdgcn_readfirstlane(s_bt[(t_grp >> shift) - lb0]);
+        const uint8_t* gbase = vbase + ((int64_t)phys << shift) * slot_stride;
+        const int t = min(tile_start + k * kAccTpi + vj, t_last);
+        vreg2[k] = *reinterpret_cast<const u32x2_t*>(gbase + (uint32_t)(t & bmask) * (uint32_t)slot_stride + (uint32_t)ve * 8u);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < Gm::kSteps; ++k) {
+        const int t = tile_start + k * Gm::kTpi + vj;
+        if (t < t_end) vreg[k] = reinterpret_cast<const uint4*>(row_addr(vbase, t))[ve];
+        else vreg[k] = make_uint4(0, 0, 0, 0);
+      }
+    }
+
 
     // ---- scores of this lane's token for the G heads
     // q is uniform and never written here, so it is read with scalar loads
@@ -199,81 +268,150 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeParams
 
     // ---- prefetch the next tile's K rows (the registers are free now)
     const int next = tile_start + kWaves * kTile;
-    if (next < t_end) {
+    if constexpr (PAIR) {
+      if (next < t_end) load_k_rows(next);
+    } else if (next < t_end) {
       const int t = next + lane;
       if (t < t_end) {
-        const uint4* src = reinterpret_cast<const uint4*>(row_addr(kbase, t));
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(row_addr(kbase, t));
 #pragma unroll
         for (int i = 0; i < Gm::kRowQ; ++i) kreg[i] = src[i];
       } else {
 #pragma unroll
-        for (int i = 0; i < Gm::kRowQ; ++i) kreg[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < Gm::kRowQ; ++i) kreg[i] = (u32x4_t){0u, 0u, 0u, 0u};
       }
     }
 
-    // ---- online softmax update (base 2)
+    // ---- online softmax update (base 2); the rescale is skipped while the
+    // running maximum of a head does not move
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float tmax = wave_max(s[h]);           // finite: token tile_start is valid
-      const float m_new = fmaxf(m_run[h], tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
-      const float pr = __builtin_amdgcn_exp2f(s[h] - m_new);
-      l_run[h] = l_run[h] * alpha + pr;
-      m_run[h] = m_new;
+      if (tmax > m_run[h]) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[h] - tmax);
+        l_run[h] *= alpha;
 #pragma unroll
-      for (int e = 0; e < Gm::kEpl; ++e) acc[h][e] *= alpha;
+        for (int e = 0; e < kAccE; ++e) acc[h][e] *= alpha;
+        m_run[h] = tmax;
+      }
+      const float pr = __builtin_amdgcn_exp2f(s[h] - m_run[h]);
+      l_run[h] += pr;
       s[h] = pr;
     }
-    if constexpr (G % 4 == 0) {
-#pragma unroll
-      for (int h = 0; h < G; h += 4)
-        *reinterpret_cast<float4*>(&s_p[wave][lane * G + h]) = make_float4(s[h], s[h + 1], s[h + 2], s[h + 3]);
-    } else {
-#pragma unroll
-      for (int h = 0; h < G; ++h) s_p[wave][lane * G + h] = s[h];
-    }
-    wave_sync_lds();
 
-    // ---- acc += p * V
+    if constexpr (PAIR) {
+      // bf16 probability pairs of tokens (t, t + kAccTpi): the first lane of a
+      // pair packs heads [0, kGh), the second heads [kGh, G), exchanging
+      // values with its partner lane t ^ kAccTpi; pair id of token t is
+      // (t / (2 kAccTpi)) * kAccTpi + t % kAccTpi
+      const bool first = ((lane / kAccTpi) & 1) == 0;
+      uint32_t packed[kGh];
 #pragma unroll
-    for (int k = 0; k < Gm::kSteps; ++k) {
-      const int i = k * Gm::kTpi + vj;
-      float pr[G];
+      for (int j = 0; j < kGh; ++j) {
+        const int ho = kGh + j;
+        const float mine_e = s[j];
+        const float mine_o = ho < G ? s[ho < G ? ho : 0] : 0.f;
+        const float send = first ? mine_o : mine_e;
+        float recv;
+        if constexpr (kAccTpi == 2) recv = dpp<0x4E>(send);                 // quad_perm [2,3,0,1]
+        else recv = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(send), 0x101F));  // lane ^ 4
+        const float keep = first ? mine_e : mine_o;
+        typedef float f2_t __attribute__((ext_vector_type(2)));
+        const f2_t v2 = {first ? keep : recv, first ? recv : keep};
+        packed[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2_t));
+      }
+      const int pid = (lane / (2 * kAccTpi)) * kAccTpi + lane % kAccTpi;
+      uint32_t* dst = &s_pp[wave][pid * G + (first ? 0 : kGh)];
+      const int nw = first ? kGh : G - kGh;
+#pragma unroll
+      for (int j = 0; j < kGh; ++j)
+        if (j < nw) dst[j] = packed[j];
+      wave_sync_lds();
+
+      // ---- acc += p * V over token pairs: (p_t0, p_t1) . (V_t0[e], V_t1[e])
+#pragma unroll
+      for (int m = 0; m < kVL / 2; ++m) {
+        const int i = m * kAccTpi + vj;            // pair id of tokens 2m*kAccTpi + vj, +kAccTpi
+        uint32_t pp[G];
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+          for (int h = 0; h < G; h += 4) {
+            const uint4 v4 = *reinterpret_cast<const uint4*>(&s_pp[wave][i * G + h]);
+            pp[h] = v4.x; pp[h + 1] = v4.y; pp[h + 2] = v4.z; pp[h + 3] = v4.w;
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h) pp[h] = s_pp[wave][i * G + h];
+        }
+        const u32x2_t a = vreg2[2 * m], c = vreg2[2 * m + 1];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const uint32_t lo = __builtin_amdgcn_perm(c[x], a[x], 0x05040100u);   // (V_t0[2x], V_t1[2x])
+          const uint32_t hi = __builtin_amdgcn_perm(c[x], a[x], 0x07060302u);   // (V_t0[2x+1], V_t1[2x+1])
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[h][2 * x] = dot2_bf16(pp[h], lo, acc[h][2 * x]);
+            acc[h][2 * x + 1] = dot2_bf16(pp[h], hi, acc[h][2 * x + 1]);
+          }
+        }
+      }
+      wave_sync_lds();   // s_pp is rewritten by the next tile
+    } else {
       if constexpr (G % 4 == 0) {
 #pragma unroll
-        for (int h = 0; h < G; h += 4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(&s_p[wave][i * G + h]);
-          pr[h] = v4.x; pr[h + 1] = v4.y; pr[h + 2] = v4.z; pr[h + 3] = v4.w;
+        for (int h = 0; h < G; h += 4)
+          *reinterpret_cast<float4*>(&s_p[wave][lane * G + h]) = make_float4(s[h], s[h + 1], s[h + 2], s[h + 3]);
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_p[wave][lane * G + h] = s[h];
+      }
+      wave_sync_lds();
+
+      // ---- acc += p * V
+#pragma unroll
+      for (int k = 0; k < Gm::kSteps; ++k) {
+        const int i = k * Gm::kTpi + vj;
+        float pr[G];
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+          for (int h = 0; h < G; h += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(&s_p[wave][i * G + h]);
+            pr[h] = v4.x; pr[h + 1] = v4.y; pr[h + 2] = v4.z; pr[h + 3] = v4.w;
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h) pr[h] = s_p[wave][i * G + h];
         }
-      } else {
+        float v[Gm::kEpl];
+        if constexpr (BF16) {
+          const uint32_t w[4] = {vreg[k].x, vreg[k].y, vreg[k].z, vreg[k].w};
 #pragma unroll
-        for (int h = 0; h < G; ++h) pr[h] = s_p[wave][i * G + h];
+          for (int x = 0; x < 4; ++x) { v[2 * x] = bf_lo(w[x]); v[2 * x + 1] = bf_hi(w[x]); }
+        } else {
+          v[0] = __uint_as_float(vreg[k].x); v[1] = __uint_as_float(vreg[k].y);
+          v[2] = __uint_as_float(vreg[k].z); v[3] = __uint_as_float(vreg[k].w);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < Gm::kEpl; ++e) acc[h][e] = fmaf(pr[h], v[e], acc[h][e]);
       }
-      float v[Gm::kEpl];
-      if constexpr (BF16) {
-        const uint32_t w[4] = {vreg[k].x, vreg[k].y, vreg[k].z, vreg[k].w};
-#pragma unroll
-        for (int x = 0; x < 4; ++x) { v[2 * x] = bf_lo(w[x]); v[2 * x + 1] = bf_hi(w[x]); }
-      } else {
-        v[0] = __uint_as_float(vreg[k].x); v[1] = __uint_as_float(vreg[k].y);
-        v[2] = __uint_as_float(vreg[k].z); v[3] = __uint_as_float(vreg[k].w);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < Gm::kEpl; ++e) acc[h][e] = fmaf(pr[h], v[e], acc[h][e]);
+      wave_sync_lds();   // s_p is rewritten by the next tile
     }
-    wave_sync_lds();   // s_p is rewritten by the next tile
   }
+
+  // every wave has left the tile loop before s_acc (aliasing the K staging
+  // area) is written
+  __syncthreads();
 
   // ---- merge within the wave: rows sharing a 16-byte piece, and the sums
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     l_run[h] = wave_sum(l_run[h]);
 #pragma unroll
-    for (int e = 0; e < Gm::kEpl; ++e) {
+    for (int e = 0; e < kAccE; ++e) {
 #pragma unroll
-      for (int off = Gm::kLpr; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
+      for (int off = kAccLpr; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
     }
   }
   if (lane == 0) {
@@ -284,83 +422,98 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeParams
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < Gm::kEpl; ++e) s_acc[wave][h * D + ve * Gm::kEpl + e] = acc[h][e];
+      for (int e = 0; e < kAccE; ++e) s_acc[wave][h * D + ve * kAccE + e] = acc[h][e];
   }
   __syncthreads();
-
-  // ---- merge the 4 waves and write
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
-    float M = s_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = (s_m[w][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
-      L = fmaf(s_l[w][h], f, L);
-      O = fmaf(s_acc[w][idx], f, O);
-    }
-    const int hq = kvh * G + h;
-    if (p.num_splits == 1) {
-      const float r = O / L;
-      const int64_t o = ((int64_t)b * n_h + hq) * D + d;
-      if (p.q_bf16) reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(r);
-      else reinterpret_cast<float*>(p.out)[o] = r;
-    } else {
-      const int64_t pi = ((int64_t)b * n_h + hq) * p.num_splits + split;
-      p.part_o[pi * D + d] = O / L;
-      if (d == 0) { p.part_ml[2 * pi] = M; p.part_ml[2 * pi + 1] = L; }
-    }
-  }
+  finish_split<G, D>(p, b, kvh, split, ctx, s_m, s_l, s_acc);
 }
 
-// Log-sum-exp merge of split partials (FlashDecoding-style, qwbw 8 Q2/Q3
-// name the idea): with M the largest split maximum (base-2 scores),
-// out = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.
-__global__ void decode_reduce_kernel(const float* __restrict__ part_o,
-                                     const float* __restrict__ part_ml,
-                                     const int32_t* __restrict__ context_lens, void* out,
-                                     int n_h, int d_v, int num_splits, int split_tokens,
-                                     int out_bf16) {
+// Log-sum-exp merge of split partials (the split-context reduction that
+// qwbw 8 Q2/Q3 name FlashDecoding): with M the largest split maximum (scores
+// in base 2), out = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.
+// One workgroup per (sequence, query head); the split weights are formed
+// once in LDS, then every thread owns output columns and streams the
+// partials with several loads in flight.
+constexpr int kReduceThreads = 128;
+constexpr int kMaxSplits = 1024;
+
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ context_lens, void* __restrict__ out, int n_h, int d_v,
+    int num_splits, int split_tokens, int out_bf16) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[kReduceThreads / kWave];
   const int bh = blockIdx.x;
   const int b = bh / n_h;
+  const int tid = threadIdx.x;
   const int ctx = context_lens[b];
   const int nsp = min(num_splits, (ctx + split_tokens - 1) / split_tokens);
-  const int64_t pbase = (int64_t)bh * num_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, part_ml[2 * (pbase + s)]);
+  const int64_t base = (int64_t)bh * num_splits;
+  if (nsp <= 1) return;                 // written by the decode kernel itself
+
+  float mx = -INFINITY;
+  for (int s = tid; s < nsp; s += kReduceThreads) mx = fmaxf(mx, part_ml[2 * (base + s)]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  float M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kReduceThreads / kWave; ++w) M = fmaxf(M, s_red[w]);
+  __syncthreads();
+  float lsum = 0.f;
+  for (int s = tid; s < nsp; s += kReduceThreads) {
+    const float w = part_ml[2 * (base + s) + 1] * __builtin_amdgcn_exp2f(part_ml[2 * (base + s)] - M);
+    s_w[s] = w;
+    lsum += w;
+  }
+  lsum = wave_sum(lsum);
+  if ((tid & 63) == 0) s_red[tid >> 6] = lsum;
+  __syncthreads();
   float L = 0.f;
-  for (int s = 0; s < nsp; ++s) L += part_ml[2 * (pbase + s) + 1] * __builtin_amdgcn_exp2f(part_ml[2 * (pbase + s)] - M);
-  for (int d = threadIdx.x; d < d_v; d += blockDim.x) {
-    float O = 0.f;
-    for (int s = 0; s < nsp; ++s) {
-      const float w = part_ml[2 * (pbase + s) + 1] * __builtin_amdgcn_exp2f(part_ml[2 * (pbase + s)] - M);
-      O = fmaf(part_o[(pbase + s) * d_v + d], w, O);
+#pragma unroll
+  for (int w = 0; w < kReduceThreads / kWave; ++w) L += s_red[w];
+  const float inv = 1.0f / L;
+  for (int d = tid; d < d_v; d += kReduceThreads) {
+    const float* po = part_o + base * d_v + d;
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int s = 0;
+    for (; s + 4 <= nsp; s += 4) {
+      o0 = fmaf(po[(int64_t)(s + 0) * d_v], s_w[s + 0], o0);
+      o1 = fmaf(po[(int64_t)(s + 1) * d_v], s_w[s + 1], o1);
+      o2 = fmaf(po[(int64_t)(s + 2) * d_v], s_w[s + 2], o2);
+      o3 = fmaf(po[(int64_t)(s + 3) * d_v], s_w[s + 3], o3);
     }
-    const float r = nsp > 0 ? O / L : 0.f;
+    for (; s < nsp; ++s) o0 = fmaf(po[(int64_t)s * d_v], s_w[s], o0);
+    const float r = ((o0 + o1) + (o2 + o3)) * inv;
     const int64_t o = (int64_t)bh * d_v + d;
     if (out_bf16) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(r);
     else reinterpret_cast<float*>(out)[o] = r;
   }
 }
 
-template <int D, int G, bool BF16>
+template <int D, int G, bool BF16, bool PAIR>
 hipError_t launch_inst(const DecodeParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.num_splits, (unsigned)p.n_kv, (unsigned)p.B);
-  hipLaunchKernelGGL((decode_gqa_kernel<D, G, BF16>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_gqa_kernel<D, G, BF16, PAIR>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool PAIR>
 hipError_t dispatch_g(const DecodeParams& p, int g, hipStream_t stream) {
   switch (g) {
-    case 1: return launch_inst<D, 1, BF16>(p, stream);
-    case 2: return launch_inst<D, 2, BF16>(p, stream);
-    case 4: return launch_inst<D, 4, BF16>(p, stream);
-    case 8: return launch_inst<D, 8, BF16>(p, stream);
+    case 1: return launch_inst<D, 1, BF16, PAIR>(p, stream);
+    case 2: return launch_inst<D, 2, BF16, PAIR>(p, stream);
+    case 4: return launch_inst<D, 4, BF16, PAIR>(p, stream);
+    case 8: return launch_inst<D, 8, BF16, PAIR>(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Pair mode needs the rows of every K load (kWave / kRowQ of them) inside
+// one block (the V loads cover fewer rows).
+template <int D>
+bool pair_ok(const DecodeParams& p) {
+  return (1 << p.block_shift) >= kWave / Geo<D, true>::kRowQ;
 }
 
 }  // namespace
@@ -370,23 +523,33 @@ bool gqa_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
   if (!(g == 1 || g == 2 || g == 4 || g == 8)) return false;
   if (kv == KV::BF16) return q_bf16 && (d_k == 64 || d_k == 128);
   if (kv == KV::F32) return !q_bf16 && (d_k == 32 || d_k == 64);
+  if (kv == KV::INT8) return int8_supported(q_bf16, d_k, d_v, g);
   return false;
 }
 
 hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
-  if (p.split_tokens > kMaxSplitTokens || p.split_tokens % kGqaSplitGranule) return hipErrorInvalidValue;
+  if (p.split_tokens > kMaxSplitTokens || p.split_tokens % kGqaSplitGranule ||
+      (p.split_tokens >> p.block_shift) > kBtSlots)
+    return hipErrorInvalidValue;
   const int g = p.n_h / p.n_kv;
   hipError_t e = hipErrorInvalidValue;
-  if (p.kv == KV::BF16) {
-    if (p.d_k == 128) e = dispatch_g<128, true>(p, g, stream);
-    else if (p.d_k == 64) e = dispatch_g<64, true>(p, g, stream);
+  if (p.deep && deep_supported(p)) {
+    e = launch_decode_deep(p, stream);
+  } else if (p.kv == KV::BF16) {
+    if (p.d_k == 128) e = pair_ok<128>(p) ? dispatch_g<128, true, true>(p, g, stream)
+                                          : dispatch_g<128, true, false>(p, g, stream);
+    else if (p.d_k == 64) e = pair_ok<64>(p) ? dispatch_g<64, true, true>(p, g, stream)
+                                             : dispatch_g<64, true, false>(p, g, stream);
   } else if (p.kv == KV::F32) {
-    if (p.d_k == 64) e = dispatch_g<64, false>(p, g, stream);
-    else if (p.d_k == 32) e = dispatch_g<32, false>(p, g, stream);
+    if (p.d_k == 64) e = dispatch_g<64, false, false>(p, g, stream);
+    else if (p.d_k == 32) e = dispatch_g<32, false, false>(p, g, stream);
+  } else if (p.kv == KV::INT8) {
+    e = launch_decode_int8(p, g, stream);
   }
   if (e != hipSuccess || p.num_splits == 1) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(p.B * p.n_h)), dim3(64), 0, stream,
-                     (const float*)p.part_o, (const float*)p.part_ml, p.context_lens, p.out,
+  if (p.num_splits > kMaxSplits) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(p.B * p.n_h)), dim3(kReduceThreads), 0,
+                     stream, (const float*)p.part_o, (const float*)p.part_ml, p.context_lens, p.out,
                      p.n_h, p.d_v, p.num_splits, p.split_tokens, p.q_bf16 ? 1 : 0);
   return hipGetLastError();
 }

@@ -13,6 +13,7 @@
 // while the softmax denominator sums p_j itself.
 #include "internal.h"
 #include "device_common.h"
+#include "decode_epilogue.h"
 
 namespace pkv {
 namespace {
@@ -43,7 +44,7 @@ struct Geo8 {
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_int8_kernel(const DecodeParams p) {
   using Gm = Geo8<D>;
-  __shared__ __align__(16) int32_t s_bt[kMaxSplitTokens];
+  __shared__ __align__(16) int32_t s_bt[kBtSlots];
   __shared__ __align__(16) float s_p[kWaves][kTile * G];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
@@ -60,13 +61,7 @@ __global__ __launch_bounds__(kThreads) void decode_int8_kernel(const DecodeParam
   const int n_h = p.n_h;
 
   if (t_begin >= ctx) {
-    if (split == 0 && p.num_splits == 1) {
-      for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int64_t o = ((int64_t)b * n_h + kvh * G) * D + idx;
-        if (p.q_bf16) reinterpret_cast<uint16_t*>(p.out)[o] = 0;
-        else reinterpret_cast<float*>(p.out)[o] = 0.f;
-      }
-    }
+    if (split == 0) write_zero_rows<G, D>(p, b, kvh);   // empty sequence
     return;
   }
   const int t_end = min(ctx, t_begin + p.split_tokens);
@@ -249,30 +244,7 @@ __global__ __launch_bounds__(kThreads) void decode_int8_kernel(const DecodeParam
       for (int e = 0; e < 8; ++e) s_acc[wave][h * D + ve * 8 + e] = acc[h][e];
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
-    float M = s_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = (s_m[w][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
-      L = fmaf(s_l[w][h], f, L);
-      O = fmaf(s_acc[w][idx], f, O);
-    }
-    const int hq = kvh * G + h;
-    if (p.num_splits == 1) {
-      const float r = O / L;
-      const int64_t o = ((int64_t)b * n_h + hq) * D + d;
-      if (p.q_bf16) reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(r);
-      else reinterpret_cast<float*>(p.out)[o] = r;
-    } else {
-      const int64_t pi = ((int64_t)b * n_h + hq) * p.num_splits + split;
-      p.part_o[pi * D + d] = O / L;
-      if (d == 0) { p.part_ml[2 * pi] = M; p.part_ml[2 * pi + 1] = L; }
-    }
-  }
+  finish_split<G, D>(p, b, kvh, split, ctx, s_m, s_l, s_acc);
 }
 
 template <int D, int G>

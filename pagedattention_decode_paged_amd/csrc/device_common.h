@@ -12,7 +12,8 @@ static constexpr int kWave = 64;
 static constexpr int kWaves = 4;
 static constexpr int kThreads = kWave * kWaves;
 static constexpr int kTile = 64;                   // tokens per wave tile
-static constexpr int kMaxSplitTokens = 2048;       // LDS block-table slice bound (bs = 1)
+static constexpr int kMaxSplitTokens = 8192;       // longest context split
+static constexpr int kBtSlots = 512;               // block-table entries staged per split
 static constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -40,7 +41,7 @@ static __device__ __forceinline__ float wave_max(float x) {
   const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
   const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
   const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fmaxf(fmaxf(a, b), fmaxf(c, d)))));
 }
 
 static __device__ __forceinline__ float wave_sum(float x) {
@@ -66,6 +67,14 @@ static __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int N>
+static __device__ __forceinline__ uint32_t kdw(const u32x4_t (&k)[N], int w) {
+  return k[w >> 2][w & 3];
 }
 
 // Dword w (compile-time after unrolling) of a K row held as 16-byte pieces.

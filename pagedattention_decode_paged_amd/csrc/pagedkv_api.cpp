@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -258,7 +259,15 @@ int granule(Variant v) { return v == Variant::Mla ? pkv::kMlaSplitGranule : pkv:
 // Context split size: aim for about kTargetUnits workgroups doing real work
 // (8 per compute unit on 256 CUs), in multiples of the kernel's granule.
 constexpr int64_t kTargetUnits = 2048;
-constexpr int32_t kMaxSplit = 2048;
+constexpr int32_t kMaxSplit = 8192;
+
+// A split stages at most kBtSlots block-table entries in LDS.
+constexpr int32_t kBtSlots = 512;
+
+int32_t max_split(const kvp_decode_desc* d) {
+  const int64_t cap = (int64_t)kBtSlots * d->block_size;
+  return (int32_t)(cap < kMaxSplit ? cap : kMaxSplit);
+}
 
 int32_t plan_split(const kvp_decode_desc* d, Variant v) {
   const int g = granule(v);
@@ -270,7 +279,7 @@ int32_t plan_split(const kvp_decode_desc* d, Variant v) {
   int64_t split = (work + kTargetUnits - 1) / kTargetUnits;
   split = (split + g - 1) / g * g;
   if (split < g) split = g;
-  if (split > kMaxSplit) split = kMaxSplit;
+  if (split > max_split(d)) split = max_split(d);
   return (int32_t)split;
 }
 
@@ -331,8 +340,8 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   }
 
   const int gr = granule(var);
-  if (d->split_tokens > 0 && (d->split_tokens % gr || d->split_tokens > kMaxSplit))
-    return fail(KVP_ERR_INVALID_ARG, "%s: split_tokens must be a multiple of %d and <= %d", fn, gr, kMaxSplit);
+  if (d->split_tokens > 0 && (d->split_tokens % gr || d->split_tokens > max_split(d)))
+    return fail(KVP_ERR_INVALID_ARG, "%s: split_tokens must be a multiple of %d and <= %d", fn, gr, max_split(d));
   const int32_t split = plan_split(d, var);
   const int32_t ns = num_splits_of(d, split);
   const size_t need = workspace_for(d, var);
@@ -342,7 +351,7 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
       return fail(KVP_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
     if (!aligned(workspace, 256)) return fail(KVP_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   }
-  if (ns > 65535 * 1024) return fail(KVP_ERR_UNSUPPORTED, "%s: too many splits", fn);
+  if (ns > 1024) return fail(KVP_ERR_UNSUPPORTED, "%s: more than 1024 context splits (raise split_tokens)", fn);
 
   pkv::DecodeParams p{};
   p.q = q;
@@ -356,8 +365,11 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   if (need > 0) {
     const size_t rows = (size_t)d->B * d->n_h * ns;
     p.part_o = static_cast<float*>(workspace);
-    p.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                         round_up(rows * d->d_v * sizeof(float), 256));
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    const size_t o_bytes = round_up(rows * d->d_v * sizeof(float), 256);
+    const size_t ml_bytes = round_up(rows * 2 * sizeof(float), 256);
+    (void)ml_bytes;
+    p.part_ml = reinterpret_cast<float*>(w + o_bytes);
   }
   p.scale = scale;
   p.B = d->B;
@@ -371,6 +383,7 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   p.num_splits = ns;
   p.q_bf16 = q_bf16;
   p.kv = var == Variant::Int8 ? pkv::KV::INT8 : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
+  p.deep = getenv("PAGEDKV_SHALLOW") == nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = var == Variant::Mla ? pkv::launch_decode_mla(p, st) : pkv::launch_decode_gqa(p, st);
   return hip_status(e, fn);
