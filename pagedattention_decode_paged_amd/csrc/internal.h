@@ -51,16 +51,11 @@ struct DecodeParams {
   int32_t num_splits;
   bool q_bf16;
   KV kv;
-  bool deep;                // use the deep-pipelined kernel when it applies
 };
 
 // GQA/MQA/MHA over float or INT8 pools (VALU kernels).  Returns
 // hipErrorInvalidValue for a (d, g, dtype) combination with no instance.
 hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream);
-
-// Deep-pipelined bf16 kernel (d = 128, block >= 8); called by launch_decode_gqa.
-bool deep_supported(const DecodeParams& p);
-hipError_t launch_decode_deep(const DecodeParams& p, hipStream_t stream);
 
 // INT8 pools (fused dequant); called by launch_decode_gqa.
 bool int8_supported(bool q_bf16, int d_k, int d_v, int g);

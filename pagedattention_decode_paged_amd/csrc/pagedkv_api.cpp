@@ -257,8 +257,9 @@ Variant variant_of(const kvp_decode_desc* d) {
 int granule(Variant v) { return v == Variant::Mla ? pkv::kMlaSplitGranule : pkv::kGqaSplitGranule; }
 
 // Context split size: aim for about kTargetUnits workgroups doing real work
-// (8 per compute unit on 256 CUs), in multiples of the kernel's granule.
-constexpr int64_t kTargetUnits = 2048;
+// (two 4-wave workgroups per compute unit on 256 CUs), in multiples of the
+// kernel's granule; longer splits amortise each workgroup's set-up and merge.
+constexpr int64_t kTargetUnits = 512;
 constexpr int32_t kMaxSplit = 8192;
 
 // A split stages at most kBtSlots block-table entries in LDS.
@@ -383,7 +384,6 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   p.num_splits = ns;
   p.q_bf16 = q_bf16;
   p.kv = var == Variant::Int8 ? pkv::KV::INT8 : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
-  p.deep = getenv("PAGEDKV_SHALLOW") == nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = var == Variant::Mla ? pkv::launch_decode_mla(p, st) : pkv::launch_decode_gqa(p, st);
   return hip_status(e, fn);

@@ -77,7 +77,9 @@ def test_int8_properties(seed):
     nz = scale > 0
     assert np.all(np.abs(codes.astype(np.int32)).max(axis=-1)[nz] == 127)
     err = np.abs(x.astype(np.float64) - oracle.dequantize_int8(codes, scale))
-    bound = scale.astype(np.float64)[..., None] * 0.5 * (1 + 1e-6)
+    # rint adds at most 1/2; the binary32 quotient x / scale (|x / scale| <= 128)
+    # carries at most half an ulp of 128, i.e. 2^-17, in units of the scale
+    bound = scale.astype(np.float64)[..., None] * (0.5 + 2.0 ** -17)
     assert np.all(err <= bound)
 
 
