@@ -182,13 +182,24 @@ typedef struct {
   int64_t total_context_len;   /* optional host hint: sum of context_lens
                                   (0 = unknown; then B * max_context_len is
                                   assumed when sizing splits) */
+  int32_t workgroups;          /* MLA only: persistent workgroups per group
+                                  of 128 heads; 0 = one per compute unit of
+                                  the current device (at most the number of
+                                  32-token context tiles).  Ignored by the
+                                  other entry points. */
 } kvp_decode_desc;
 
 /* Workspace bytes the call needs for this description (split partials). */
 size_t paged_decode_workspace_size(const kvp_decode_desc* desc);
 
-/* Tokens per context split the automatic policy picks (for reporting). */
+/* Tokens per context split the automatic policy picks (for reporting);
+ * for an MLA description, the 32-token tile the work is divided in. */
 int32_t paged_decode_split_tokens(const kvp_decode_desc* desc);
+
+/* MLA: persistent workgroups per head group the call launches (0 for a
+ * description that is not MLA or is invalid).  The workspace size of an
+ * MLA call depends on it, so query both with the same device current. */
+int32_t paged_decode_mla_workgroups(const kvp_decode_desc* desc);
 
 /* Float pools (F32/BF16 K and V of the same dtype as q; GQA, MQA, MHA). */
 kvp_status paged_decode_attention(const void* q, const void* k_pool, const void* v_pool,
@@ -209,7 +220,15 @@ kvp_status paged_decode_attention_int8(const void* q, const int8_t* k_codes,
 /* Absorbed MLA over a latent pool (faulkner, matrix absorption and
  * decoupled RoPE): q [B, n_h, d_k] already carries W^UK; the pool holds
  * one [c | k_rope] row of d_k bf16 per token (n_kv = 1); the value is the
- * first d_v columns of that row; out [B, n_h, d_v] is in latent space. */
+ * first d_v columns of that row; out [B, n_h, d_v] is in latent space.
+ * This build has the kernel for d_k = 576, d_v = 512 (a 512-wide latent
+ * plus a 64-wide rope part), bf16 q, pool and output, block_size >= 16,
+ * any n_h, B <= 4096; other shapes return KVP_ERR_UNSUPPORTED.  The
+ * context of the batch is cut into 32-token tiles that desc->workgroups
+ * persistent workgroups share in equal contiguous ranges; a sequence cut
+ * between workgroups is merged by log-sum-exp in a second kernel.  The
+ * workspace (always needed for MLA) holds a per-sequence record and, when
+ * more than one workgroup runs, the fp32 partials of the cut sequences. */
 kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
                                       const int32_t* block_table, const int32_t* context_lens,
                                       float scale, void* out, const kvp_decode_desc* desc,

@@ -48,13 +48,14 @@ class _DecodeDesc(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
-                ("split_tokens", ctypes.c_int32), ("total_context_len", ctypes.c_int64)]
+                ("split_tokens", ctypes.c_int32), ("total_context_len", ctypes.c_int64),
+                ("workgroups", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m pagedattention_decode_paged_amd.build`"
+            f"{LIB_PATH} is missing: build it with `python pagedattention_decode_paged_amd/build.py`"
             " (or __graft_entry__.build()); there is no fallback implementation")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -69,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "reshape_and_cache": (ctypes.c_int, [P, P, P, ctypes.c_int, P, I64, P]),
         "paged_decode_workspace_size": (SZ, [ctypes.POINTER(_DecodeDesc)]),
         "paged_decode_split_tokens": (I32, [ctypes.POINTER(_DecodeDesc)]),
+        "paged_decode_mla_workgroups": (I32, [ctypes.POINTER(_DecodeDesc)]),
         "paged_decode_attention": (ctypes.c_int, [P, P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc), P, SZ, P]),
         "paged_decode_attention_int8": (ctypes.c_int, [P, P, P, P, P, P, P, F, P,
                                                        ctypes.POINTER(_DecodeDesc), P, SZ, P]),
@@ -88,7 +90,8 @@ _lib = _load()
 EXPORTED_SYMBOLS = (
     "kvp_last_error", "kvp_version", "kv_pool_required_bytes", "kv_pool_create", "kv_pool_destroy",
     "kv_pool_view_get", "paged_slot_mapping", "reshape_and_cache", "paged_decode_workspace_size",
-    "paged_decode_split_tokens", "paged_decode_attention", "paged_decode_attention_int8",
+    "paged_decode_split_tokens", "paged_decode_mla_workgroups", "paged_decode_attention",
+    "paged_decode_attention_int8",
     "paged_decode_attention_mla", "paged_gather", "paged_decode_validate",
 )
 
@@ -244,10 +247,11 @@ def paged_gather(pool: torch.Tensor, block_table: torch.Tensor, context_lens: to
 # --------------------------------------------------------------------- decode
 
 def _desc(q, block_table, context_lens, n_kv, d_k, d_v, block_size, kv_dtype, max_context_len,
-          split_tokens, total_context_len) -> _DecodeDesc:
+          split_tokens, total_context_len, workgroups=0) -> _DecodeDesc:
     B, n_h, _ = q.shape
     return _DecodeDesc(B, n_h, n_kv, d_k, d_v, block_size, block_table.shape[1], int(max_context_len),
-                       _TORCH_TO_KVP[q.dtype], kv_dtype, int(split_tokens), int(total_context_len))
+                       _TORCH_TO_KVP[q.dtype], kv_dtype, int(split_tokens), int(total_context_len),
+                       int(workgroups))
 
 
 def decode_workspace_size(desc: _DecodeDesc) -> int:
@@ -258,14 +262,16 @@ def decode_split_tokens(desc: _DecodeDesc) -> int:
     return int(_lib.paged_decode_split_tokens(ctypes.byref(desc)))
 
 
+def decode_mla_workgroups(desc: _DecodeDesc) -> int:
+    return int(_lib.paged_decode_mla_workgroups(ctypes.byref(desc)))
+
+
 def _workspace(desc, workspace, dev):
     need = decode_workspace_size(desc)
     if need == 0:
         return None, 0
     if workspace is None or workspace.numel() < need:
-        # zero once: the split counters inside start at zero and every call
-        # leaves them at zero
-        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     return workspace, workspace.numel()
 
 
@@ -306,11 +312,14 @@ def paged_decode_attention_int8(q, k_codes, k_scale, v_codes, v_scale, block_tab
 
 
 def paged_decode_attention_mla(q, latent_pool, block_table, context_lens, scale, d_v, out=None, *,
-                               max_context_len, split_tokens=0, total_context_len=0, workspace=None):
+                               max_context_len, total_context_len=0, workgroups=0, workspace=None):
+    """Absorbed MLA: ``out[b, h] = softmax(scale * q[b, h] . C) C[:, :d_v]``
+    over each sequence's paged latent rows (pool ``[num_blocks, block_size,
+    1, d_k]``).  ``workgroups`` = persistent workgroups (0 = one per CU)."""
     dev = _need_cuda(q, latent_pool, block_table, context_lens)
     _, bs, n_kv, d_k = latent_pool.shape
     desc = _desc(q, block_table, context_lens, n_kv, d_k, d_v, bs, _TORCH_TO_KVP[latent_pool.dtype],
-                 max_context_len, split_tokens, total_context_len)
+                 max_context_len, 0, total_context_len, workgroups)
     if out is None:
         out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=dev)
     ws, wsb = _workspace(desc, workspace, dev)
@@ -321,10 +330,10 @@ def paged_decode_attention_mla(q, latent_pool, block_table, context_lens, scale,
 
 
 def make_desc(*, B, n_h, n_kv, d_k, d_v, block_size, max_blocks_per_seq, max_context_len,
-              q_dtype, kv_dtype, split_tokens=0, total_context_len=0) -> _DecodeDesc:
+              q_dtype, kv_dtype, split_tokens=0, total_context_len=0, workgroups=0) -> _DecodeDesc:
     """A decode description from plain values (dtype codes KVP_F32/BF16/INT8)."""
     return _DecodeDesc(B, n_h, n_kv, d_k, d_v, block_size, max_blocks_per_seq, max_context_len,
-                       q_dtype, kv_dtype, split_tokens, total_context_len)
+                       q_dtype, kv_dtype, split_tokens, total_context_len, workgroups)
 
 
 def paged_decode_validate(block_table, context_lens, desc: _DecodeDesc, num_blocks: int) -> None:

@@ -1,6 +1,7 @@
 """Build libpagedkv.so (HIP for gfx950) in-tree with hipcc.
 
-Usage: python -m pagedattention_decode_paged_amd.build [--jobs N] [--keep-asm DIR]
+Usage: python pagedattention_decode_paged_amd/build.py [--jobs N] [--keep-asm DIR]
+(run as a file: importing the package loads the library being rebuilt)
 """
 
 from __future__ import annotations

@@ -51,6 +51,10 @@ struct DecodeParams {
   int32_t num_splits;
   bool q_bf16;
   KV kv;
+  // MLA only: persistent workgroups per head group, and the per-sequence
+  // record of which workgroups hold a sequence ([B, 2], in the workspace).
+  int32_t workgroups;
+  int32_t* seq_meta;
 };
 
 // GQA/MQA/MHA over float or INT8 pools (VALU kernels).  Returns
@@ -61,8 +65,10 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream);
 bool int8_supported(bool q_bf16, int d_k, int d_v, int g);
 hipError_t launch_decode_int8(const DecodeParams& p, int g, hipStream_t stream);
 
-// Absorbed MLA over a bf16 latent pool (MFMA kernel).
+// Absorbed MLA over a bf16 latent pool (MFMA kernel) plus the merge of
+// sequences cut across workgroups.
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
+int mla_head_groups(int n_h);
 
 // Whether an instance exists (host-side check before launch).
 bool gqa_supported(KV kv, bool q_bf16, int d_k, int d_v, int g);
@@ -71,6 +77,10 @@ bool mla_supported(int d_k, int d_v, int n_h, int block_size);
 // Context tokens each workgroup of the GQA kernel walks per split must be a
 // multiple of this.
 constexpr int kGqaSplitGranule = 256;
-constexpr int kMlaSplitGranule = 64;
+
+// MLA: context tiles of 32 tokens; every workgroup stages the batch's tile
+// prefix in LDS, which bounds the batch.
+constexpr int kMlaTileTokens = 32;
+constexpr int kMlaMaxBatch = 4096;
 
 }  // namespace pkv

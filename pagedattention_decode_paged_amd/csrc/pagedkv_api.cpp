@@ -245,6 +245,7 @@ const char* decode_desc_error(const kvp_decode_desc* d) {
   if (!dtype_valid(d->kv_dtype)) return "unknown kv_dtype";
   if (d->split_tokens < 0) return "split_tokens must be >= 0";
   if (d->total_context_len < 0) return "total_context_len must be >= 0";
+  if (d->workgroups < 0) return "workgroups must be >= 0";
   return nullptr;
 }
 
@@ -254,7 +255,64 @@ Variant variant_of(const kvp_decode_desc* d) {
   return Variant::Float;
 }
 
-int granule(Variant v) { return v == Variant::Mla ? pkv::kMlaSplitGranule : pkv::kGqaSplitGranule; }
+int granule(Variant) { return pkv::kGqaSplitGranule; }
+
+// Compute units of the current device (cached per device; 256 when no
+// device can be queried, e.g. on a host without a GPU).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) {
+      (void)hipGetLastError();
+      cu = 256;
+    }
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
+// MLA: tiles of 32 tokens over the whole batch, split into W contiguous
+// ranges.  An upper bound of the tile count comes from the host-side sizes.
+int64_t mla_tile_bound(const kvp_decode_desc* d) {
+  const int64_t per_seq = ((int64_t)d->max_context_len + pkv::kMlaTileTokens - 1) / pkv::kMlaTileTokens;
+  int64_t bound = (int64_t)d->B * per_seq;
+  if (d->total_context_len > 0) {
+    const int64_t hint = (d->total_context_len + pkv::kMlaTileTokens - 1) / pkv::kMlaTileTokens + d->B;
+    if (hint < bound) bound = hint;
+  }
+  return bound;
+}
+
+int32_t mla_workgroups(const kvp_decode_desc* d) {
+  if (d->workgroups > 0) return d->workgroups;
+  int64_t w = device_cus();
+  const int64_t bound = mla_tile_bound(d);
+  if (bound < w) w = bound;
+  return (int32_t)(w < 1 ? 1 : w);
+}
+
+struct MlaWorkspace {
+  size_t meta = 0, ml = 0, o = 0;
+  size_t total() const { return meta + ml + o; }
+};
+
+MlaWorkspace mla_workspace(const kvp_decode_desc* d) {
+  MlaWorkspace m;
+  const int32_t W = mla_workgroups(d);
+  m.meta = round_up((size_t)d->B * 2 * sizeof(int32_t), 256);
+  if (W > 1) {
+    const size_t rows = (size_t)(W + d->B) * d->n_h;
+    m.ml = round_up(rows * 2 * sizeof(float), 256);
+    m.o = round_up(rows * d->d_v * sizeof(float), 256);
+  }
+  return m;
+}
 
 // Context split size: aim for about kTargetUnits workgroups doing real work
 // (two 4-wave workgroups per compute unit on 256 CUs), in multiples of the
@@ -290,11 +348,60 @@ int32_t num_splits_of(const kvp_decode_desc* d, int32_t split) {
 }
 
 size_t workspace_for(const kvp_decode_desc* d, Variant v) {
+  if (v == Variant::Mla) return d->B > 0 ? mla_workspace(d).total() : 0;
   const int32_t split = plan_split(d, v);
   const int32_t ns = num_splits_of(d, split);
   if (ns <= 1) return 0;
   const size_t rows = (size_t)d->B * d->n_h * ns;
   return round_up(rows * d->d_v * sizeof(float), 256) + round_up(rows * 2 * sizeof(float), 256);
+}
+
+kvp_status check_workspace(const char* fn, size_t need, const void* workspace, size_t workspace_bytes) {
+  if (need == 0) return KVP_OK;
+  if (!workspace) return fail(KVP_ERR_INVALID_ARG, "%s: workspace of %zu bytes required", fn, need);
+  if (workspace_bytes < need)
+    return fail(KVP_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(KVP_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  return KVP_OK;
+}
+
+// The MLA kernel: persistent workgroups over the batch's 32-token tiles
+// (shape checks already done by decode_common).
+kvp_status launch_mla(const char* fn, const void* q, const void* pool, const int32_t* block_table,
+                      const int32_t* context_lens, float scale, void* out,
+                      const kvp_decode_desc* d, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (d->B > pkv::kMlaMaxBatch) return fail(KVP_ERR_UNSUPPORTED, "%s: MLA batch must be <= %d", fn, pkv::kMlaMaxBatch);
+  const int64_t per_seq = ((int64_t)d->max_context_len + pkv::kMlaTileTokens - 1) / pkv::kMlaTileTokens;
+  if ((int64_t)d->B * per_seq >= ((int64_t)1 << 31))
+    return fail(KVP_ERR_UNSUPPORTED, "%s: too many context tiles in one batch", fn);
+  if (d->workgroups > 65535) return fail(KVP_ERR_INVALID_ARG, "%s: workgroups must be <= 65535", fn);
+  const MlaWorkspace m = mla_workspace(d);
+  const kvp_status ws = check_workspace(fn, m.total(), workspace, workspace_bytes);
+  if (ws != KVP_OK) return ws;
+  uint8_t* wsb = static_cast<uint8_t*>(workspace);
+  pkv::DecodeParams p{};
+  p.q = q;
+  p.k = pool;
+  p.v = pool;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.seq_meta = reinterpret_cast<int32_t*>(wsb);
+  p.part_ml = m.ml ? reinterpret_cast<float*>(wsb + m.meta) : nullptr;
+  p.part_o = m.o ? reinterpret_cast<float*>(wsb + m.meta + m.ml) : nullptr;
+  p.scale = scale;
+  p.B = d->B;
+  p.n_h = d->n_h;
+  p.n_kv = 1;
+  p.d_k = d->d_k;
+  p.d_v = d->d_v;
+  p.block_shift = log2i(d->block_size);
+  p.max_blocks_per_seq = d->max_blocks_per_seq;
+  p.q_bf16 = true;
+  p.kv = pkv::KV::BF16;
+  p.workgroups = mla_workgroups(d);
+  return hip_status(pkv::launch_decode_mla(p, static_cast<hipStream_t>(stream)), fn);
 }
 
 kvp_status decode_common(Variant var, const char* fn, const void* q, const void* k,
@@ -340,6 +447,8 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
                   d->n_h, d->d_k, d->d_v, d->block_size);
   }
 
+  if (var == Variant::Mla) return launch_mla(fn, q, k, block_table, context_lens, scale, out, d,
+                                             workspace, workspace_bytes, stream);
   const int gr = granule(var);
   if (d->split_tokens > 0 && (d->split_tokens % gr || d->split_tokens > max_split(d)))
     return fail(KVP_ERR_INVALID_ARG, "%s: split_tokens must be a multiple of %d and <= %d", fn, gr, max_split(d));
@@ -385,8 +494,7 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   p.q_bf16 = q_bf16;
   p.kv = var == Variant::Int8 ? pkv::KV::INT8 : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = var == Variant::Mla ? pkv::launch_decode_mla(p, st) : pkv::launch_decode_gqa(p, st);
-  return hip_status(e, fn);
+  return hip_status(pkv::launch_decode_gqa(p, st), fn);
 }
 
 }  // namespace
@@ -400,7 +508,13 @@ size_t paged_decode_workspace_size(const kvp_decode_desc* desc) {
 
 int32_t paged_decode_split_tokens(const kvp_decode_desc* desc) {
   if (decode_desc_error(desc)) return 0;
+  if (variant_of(desc) == Variant::Mla) return pkv::kMlaTileTokens;
   return plan_split(desc, variant_of(desc));
+}
+
+int32_t paged_decode_mla_workgroups(const kvp_decode_desc* desc) {
+  if (decode_desc_error(desc) || variant_of(desc) != Variant::Mla) return 0;
+  return mla_workgroups(desc);
 }
 
 kvp_status paged_decode_attention(const void* q, const void* k_pool, const void* v_pool,

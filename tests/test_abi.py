@@ -76,10 +76,24 @@ def test_split_planning_and_workspace():
     d2 = _desc(split_tokens=512)
     assert pk.decode_split_tokens(d2) == 512
     assert pk.decode_workspace_size(d2) == (16 * 64 * 16 * 128 * 4) + (16 * 64 * 16 * 2 * 4)
-    # MLA uses 64-token granules
+    # MLA: 32-token tiles shared out to persistent workgroups; never more
+    # workgroups than tiles, and a workspace for the per-sequence records
+    # plus the partials of (workgroups + B) pieces
     dm = _desc(B=64, n_h=128, n_kv=1, d_k=576, d_v=512, block_size=64, max_blocks_per_seq=128,
                max_context_len=8192)
-    assert pk.decode_split_tokens(dm) % 64 == 0
+    assert pk.decode_split_tokens(dm) == 32
+    W = pk.decode_mla_workgroups(dm)
+    assert 1 <= W <= 64 * 256
+    rows = (W + 64) * 128
+    assert pk.decode_workspace_size(dm) >= 64 * 2 * 4 + rows * 2 * 4 + rows * 512 * 4
+    dm1 = _desc(B=2, n_h=128, n_kv=1, d_k=576, d_v=512, block_size=64, max_blocks_per_seq=1,
+                max_context_len=20, workgroups=0)
+    assert pk.decode_mla_workgroups(dm1) == 2          # two tiles in the whole batch
+    dm2 = _desc(B=2, n_h=128, n_kv=1, d_k=576, d_v=512, block_size=64, max_blocks_per_seq=1,
+                max_context_len=20, workgroups=1)
+    assert pk.decode_mla_workgroups(dm2) == 1
+    assert pk.decode_workspace_size(dm2) == 256        # records only: nothing is cut
+    assert pk.decode_mla_workgroups(d) == 0            # not an MLA description
 
 
 def _call_decode(desc, **ptrs):
