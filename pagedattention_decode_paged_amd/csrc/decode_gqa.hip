@@ -533,7 +533,9 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
     return hipErrorInvalidValue;
   const int g = p.n_h / p.n_kv;
   hipError_t e = hipErrorInvalidValue;
-  if (p.kv == KV::BF16) {
+  if (gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)) {
+    e = launch_decode_gqa_ring(p, stream);
+  } else if (p.kv == KV::BF16) {
     if (p.d_k == 128) e = pair_ok<128>(p) ? dispatch_g<128, true, true>(p, g, stream)
                                           : dispatch_g<128, true, false>(p, g, stream);
     else if (p.d_k == 64) e = pair_ok<64>(p) ? dispatch_g<64, true, true>(p, g, stream)

@@ -1,0 +1,401 @@
+// Paged decode attention for GQA on bf16 pools, g = n_h / n_kv in {4, 8}:
+// the kernel for the bandwidth-bound shapes (8B- and 70B-shaped layers).
+//
+// What is computed: for each sequence b and query head h,
+//   out[b][h] = sum_j softmax_j(scale * q[b][h] . K_j) V_j ,  j < context_lens[b],
+// with K_j, V_j reached through the block table (faulkner, first section and
+// the logical/physical block mapping; qwbw 3.4) and the g query heads of a
+// group sharing KV head h / g (faulkner's MHA/GQA/MLA table).
+//
+// How (gfx950, wave64, one workgroup of 4 waves per (split, KV head, seq)):
+// * K and V rows reach LDS through the LDS DMA path (global_load_lds_dwordx4)
+//   in 64-token stages (one 64-row K tile and one V tile), RING stages
+//   deep: while a stage is computed, the next RING - 1 are in flight, so
+//   the reads outstanding live in LDS, not in registers (with two 2-stage
+//   rings per compute unit, 64 KiB per CU).  Each DMA instruction moves four (d = 128) or
+//   eight (d = 64) whole rows, 16 bytes per lane, every lane with its own
+//   row address from the block table (any block size works).
+// * The waves split the g heads (g / 4 each) and every wave walks all
+//   tokens of the stage, so a K/V byte crosses HBM once and feeds all g
+//   heads, and each wave's softmax state is final at the end (no merge
+//   between waves).
+// * Scores: lane i owns token i of the stage and reads its K row from LDS
+//   (rows are stored with their 16-byte pieces permuted by the row index, so
+//   the 16 lanes of a read phase hit distinct banks); q is uniform per wave
+//   and streamed through scalar registers; v_dot2 on bf16 pairs, fp32 sums.
+// * Online softmax per stage in base 2 (scale * log2 e folded into q.K);
+//   the stage maximum comes from DPP, the probabilities are rounded to bf16
+//   (the same values feed the numerator and the running sum) and packed in
+//   token pairs into a per-wave LDS slice.
+// * Values: lane (group j, index i) owns output column 16 k + i of every
+//   head of the wave, k = j (+ 4 for the upper half of d = 128); one
+//   transposed LDS read (ds_read_b64_tr_b16) returns that column for four
+//   consecutive tokens, i.e. two bf16 token pairs that v_dot2 multiplies
+//   with the matching probability pairs.  Each lane accumulates whole
+//   columns, so no cross-lane reduction is needed at the end.
+// * Tokens at or past the context length re-read the last valid row (finite
+//   data): their scores are -inf and probabilities 0, so unused slots (NaN
+//   in the tests) are never read.
+#include "internal.h"
+#include "device_common.h"
+
+// Launch shapes (measured on the 70B-shaped layer): two 64 KiB rings per
+// compute unit (two workgroups resident) beat one 128 KiB ring; g = 8 runs
+// 8 waves (one head each), g = 4 runs 4 waves.
+#ifndef PKV_G8_NW
+#define PKV_G8_NW 8
+#endif
+#ifndef PKV_G8_RING
+#define PKV_G8_RING 2
+#endif
+#ifndef PKV_G4_RING
+#define PKV_G4_RING 2
+#endif
+
+namespace pkv {
+namespace {
+
+using namespace dev;
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kStageTok = 64;    // tokens per stage (one per lane in the score phase)
+
+template <int D, int NW>
+struct Ring {
+  static constexpr int kRowBytes = D * 2;                     // bf16 row
+  static constexpr int kPieces = kRowBytes / 16;              // 16-byte pieces per row
+  static constexpr int kRowsPerDma = kWave / kPieces;         // rows per DMA instruction
+  static constexpr int kDmaPerMat = kStageTok / kRowsPerDma;  // per stage, per matrix
+  static constexpr int kDmaPerWave = 2 * kDmaPerMat / NW;     // each wave's share (K or V)
+  static constexpr int kMatBytes = kStageTok * kRowBytes;
+  static constexpr int kHalves = D / 64;                      // 64-column passes of the value phase
+  static constexpr int kRows256 = 256 / kRowBytes;            // rows per 256 bytes
+  static_assert(D == 64 || D == 128, "row must be 128 or 256 bytes");
+  static_assert(kDmaPerMat % kDmaPerWave == 0, "a wave issues K or V instructions only");
+  // Piece permutations (row r's logical piece p sits at position p ^ swz(r)):
+  // K rows are read one row per lane, 16 lanes per LDS phase; V is read
+  // transposed, 4 rows x 2 pieces per 16 lanes, 32 lanes per phase.
+  static __device__ __forceinline__ int swz_k(int r) { return (r / kRows256) % kPieces; }
+  static __device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Every LDS access of this wave has completed, then the workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS DMA, 16 bytes per lane to LDS m0 + 16 * lane.  The address is either
+// a per-lane 64-bit pointer or a wave-uniform 64-bit base plus a per-lane
+// 32-bit offset (the block's address computed once on the scalar unit).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+template <int D, int G, int NW, int RING>
+__global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodeParams p) {
+  using R = Ring<D, NW>;
+  constexpr int kThr = 64 * NW;
+  constexpr int kHpw = G / NW;                     // heads per wave
+  static_assert(G % NW == 0, "g must be a multiple of the wave count");
+  __shared__ __attribute__((aligned(1024))) uint8_t s_k[RING][R::kMatBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_v[RING][R::kMatBytes];
+  __shared__ __align__(16) int32_t s_bt[kBtSlots];
+  __shared__ __align__(16) uint32_t s_pp[NW][kHpw][kStageTok / 2];
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ctx = p.context_lens[b];
+  const int t_begin = split * p.split_tokens;
+  const int n_h = p.n_h;
+  const int h0 = kvh * G + wave * kHpw;            // first query head of this wave
+
+  if (t_begin >= ctx) {
+    if (split == 0) {                               // empty sequence: zero output
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)b * n_h + (int64_t)kvh * G) * D;
+      for (int i = tid; i < G * D; i += kThr) o[i] = 0;
+    }
+    return;
+  }
+  const int t_end = min(ctx, t_begin + p.split_tokens);
+  const int t_last = t_end - 1;
+  const int shift = p.block_shift;
+  const int bmask = (1 << shift) - 1;
+  const int lb0 = t_begin >> shift;
+  {
+    const int nblk = (t_last >> shift) - lb0 + 1;
+    const int32_t* row = p.block_table + (int64_t)b * p.max_blocks_per_seq + lb0;
+    for (int i = tid; i < nblk; i += kThr) s_bt[i] = row[i];
+  }
+  __syncthreads();
+
+  const int64_t slot_stride = (int64_t)p.n_kv * R::kRowBytes;
+  const int n_stages = (t_end - t_begin + kStageTok - 1) / kStageTok;
+
+  // ---- this wave's DMA share: instructions j0 .. j0 + kDmaPerWave - 1 of a
+  // stage, all on K (first half of the waves) or all on V.  Lane l moves
+  // piece l % kPieces of row l / kPieces of the instruction's rows.
+  const int j0 = wave * R::kDmaPerWave;
+  const bool dma_v = j0 >= R::kDmaPerMat;
+  const int jbase = j0 % R::kDmaPerMat;
+  const uint8_t* mat = reinterpret_cast<const uint8_t*>(dma_v ? p.v : p.k) + (int64_t)kvh * R::kRowBytes;
+  const uint32_t lds_mat = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(dma_v ? &s_v[0][0] : &s_k[0][0]);
+  const int lrow = lane / R::kPieces, lpiece = lane % R::kPieces;
+  // per-lane offsets inside a block for the fast path (rows of an
+  // instruction share a block); the piece permutation depends on the row
+  // only through jm mod kSwzPeriod
+  constexpr int kSwzPeriod = D == 128 ? 4 : 2;
+  uint32_t voff[kSwzPeriod];
+#pragma unroll
+  for (int i = 0; i < kSwzPeriod; ++i) {
+    const int r = i * R::kRowsPerDma + lrow;
+    const int piece = lpiece ^ (dma_v ? R::swz_v(r) : R::swz_k(r));
+    voff[i] = (uint32_t)(lrow * slot_stride) + (uint32_t)piece * 16u;
+  }
+  const bool fast_ok = (1 << shift) >= R::kRowsPerDma;
+
+  auto issue = [&](int s, int slot) {
+    const int tile0 = t_begin + s * kStageTok;
+    const uint32_t dst0 = lds_mat + (uint32_t)(slot * R::kMatBytes);
+    if (fast_ok && tile0 + kStageTok <= t_end) {
+      // whole stage: one block per instruction, address base on the scalar unit
+#pragma unroll
+      for (int jj = 0; jj < R::kDmaPerWave; ++jj) {
+        const int jm = jbase + jj;
+        const int t0 = tile0 + jm * R::kRowsPerDma;
+        const int32_t phys = __builtin_amdgcn_readfirstlane(s_bt[(t0 >> shift) - lb0]);
+        const uint8_t* sb = mat + (((int64_t)phys << shift) + (t0 & bmask)) * slot_stride;
+        dma16(sb, voff[jm % kSwzPeriod], dst0 + (uint32_t)(jm * 1024));
+      }
+    } else {
+      // last (partial) stage or tiny blocks: per-lane rows, clamped to the
+      // last valid token
+      int32_t ph[R::kDmaPerWave];
+#pragma unroll
+      for (int jj = 0; jj < R::kDmaPerWave; ++jj) {
+        const int r = (jbase + jj) * R::kRowsPerDma + lrow;
+        ph[jj] = s_bt[(min(tile0 + r, t_last) >> shift) - lb0];
+      }
+#pragma unroll
+      for (int jj = 0; jj < R::kDmaPerWave; ++jj) {
+        const int jm = jbase + jj;
+        const int r = jm * R::kRowsPerDma + lrow;
+        const int t = min(tile0 + r, t_last);
+        const int64_t sl = ((int64_t)ph[jj] << shift) + (t & bmask);
+        const int piece = lpiece ^ (dma_v ? R::swz_v(r) : R::swz_k(r));
+        dma16(mat + sl * slot_stride + piece * 16, dst0 + (uint32_t)(jm * 1024));
+      }
+    }
+  };
+
+  float m_run[kHpw], l_run[kHpw];
+  float acc[kHpw][R::kHalves];
+#pragma unroll
+  for (int h = 0; h < kHpw; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < R::kHalves; ++e) acc[h][e] = 0.f;
+  }
+  const float qscale = p.scale * kLog2e;
+  const int64_t q_dw0 = ((int64_t)b * n_h + h0) * (D / 2);   // this wave's q rows (contiguous)
+
+  // loop-invariant LDS offsets: K row pieces of this lane's token, and the
+  // transposed V reads (lane = 16-lane group vg, index vi: token vt of a
+  // quad, 4-column chunk vc; output column 16 k + vi, k = 4 e + vg)
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vt = vi >> 2, vc = vi & 3;
+  uint32_t koff[R::kPieces];
+  {
+    const int sw = R::swz_k(lane);
+#pragma unroll
+    for (int i = 0; i < R::kPieces; ++i) koff[i] = (uint32_t)(lane * R::kRowBytes + ((i ^ sw) * 16));
+  }
+  uint32_t vofs[R::kHalves];
+#pragma unroll
+  for (int e = 0; e < R::kHalves; ++e) {
+    const int k = 4 * e + vg;
+    const int piece = (2 * k + (vc >> 1)) ^ R::swz_v(vt);   // swz_v of rows 4 m + vt depends on vt only
+    vofs[e] = (uint32_t)(vt * R::kRowBytes + piece * 16 + 8 * (vc & 1));
+  }
+
+#pragma unroll
+  for (int s = 0; s < RING - 1; ++s)
+    if (s < n_stages) issue(s, s);
+
+  auto stage = [&](int s, int slot) {
+    // this wave's DMA for stage s has landed (later stages may still fly),
+    // then every wave's has, and every wave is done with stage s - 1
+    const int ahead = min(RING - 2, n_stages - 1 - s);
+    if (RING > 3 && ahead >= 2) wait_vmcnt<2 * R::kDmaPerWave>();
+    else if (RING > 2 && ahead >= 1) wait_vmcnt<R::kDmaPerWave>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (s + RING - 1 < n_stages) issue(s + RING - 1, (slot + RING - 1) % RING);
+
+    const uint8_t* kst = &s_k[slot][0];
+    const uint8_t* vst = &s_v[slot][0];
+    const int tile0 = t_begin + s * kStageTok;
+    const bool valid = tile0 + lane < t_end;
+
+    // ---- scores: this lane's token row against the wave's heads
+    u32x4_t kreg[R::kPieces];
+#pragma unroll
+    for (int i = 0; i < R::kPieces; ++i) kreg[i] = *reinterpret_cast<const u32x4_t*>(kst + koff[i]);
+    float sc[kHpw];
+    {
+      // q is uniform and read with scalar loads in 16-dword chunks, one chunk
+      // ahead of its use; the opaque base (tied to the finished sums) keeps
+      // the compiler from hoisting every q dword into scalar registers.
+      using QPtr = const __attribute__((address_space(4))) uint32_t*;
+      constexpr int kQch = 16;
+      constexpr int kCph = (D / 2) / kQch;           // chunks per head
+      constexpr int kNch = kHpw * kCph;
+      float ax[kHpw], ay[kHpw];
+#pragma unroll
+      for (int h = 0; h < kHpw; ++h) { ax[h] = 0.f; ay[h] = 0.f; }
+      uintptr_t qaddr = (uintptr_t)p.q + (uintptr_t)q_dw0 * 4u;
+      asm volatile("" : "+s"(qaddr));
+      uint32_t qa[kQch], qb[kQch];
+      auto load_chunk = [&](uint32_t (&dst)[kQch], int c) {
+        const QPtr qp = (QPtr)qaddr;
+        const int off = c * kQch;
+#pragma unroll
+        for (int i = 0; i < kQch; ++i) dst[i] = qp[off + i];
+      };
+      load_chunk(qa, 0);
+#pragma unroll
+      for (int c = 0; c < kNch; ++c) {
+        if (c > 0) {
+          const int hp = (c - 1) / kCph;
+          asm volatile("" : "+s"(qaddr) : "v"(ax[hp]), "v"(ay[hp]));
+        }
+        if (c + 1 < kNch) load_chunk(qb, c + 1);
+        const int h = c / kCph;
+        const int w0 = (c % kCph) * kQch;
+#pragma unroll
+        for (int i = 0; i < kQch; i += 2) {
+          ax[h] = dot2_bf16(qa[i], kdw(kreg, w0 + i), ax[h]);
+          ay[h] = dot2_bf16(qa[i + 1], kdw(kreg, w0 + i + 1), ay[h]);
+        }
+#pragma unroll
+        for (int i = 0; i < kQch; ++i) qa[i] = qb[i];
+      }
+#pragma unroll
+      for (int h = 0; h < kHpw; ++h) sc[h] = valid ? (ax[h] + ay[h]) * qscale : -INFINITY;
+    }
+
+    // ---- online softmax; probabilities as bf16 token pairs in LDS (the
+    // rounded values also feed the running sum)
+#pragma unroll
+    for (int h = 0; h < kHpw; ++h) {
+      const float tmax = wave_max(sc[h]);          // finite: the stage's first token is valid
+      if (tmax > m_run[h]) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[h] - tmax);
+        l_run[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < R::kHalves; ++e) acc[h][e] *= alpha;
+        m_run[h] = tmax;
+      }
+      const float pr = __builtin_amdgcn_exp2f(sc[h] - m_run[h]);
+      const float pn = dpp<0xB1>(pr);              // token lane ^ 1
+      const f32x2_t two = {pr, pn};
+      const uint32_t pair = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_t));
+      l_run[h] += __uint_as_float(pair << 16);
+      if ((lane & 1) == 0) s_pp[wave][h][lane >> 1] = pair;
+    }
+    wave_sync_lds();
+
+    // ---- acc += p . V over token quads (transposed reads give token pairs)
+#pragma unroll
+    for (int q8 = 0; q8 < kStageTok / 8; ++q8) {
+      u32x4_t pp[kHpw];                            // pairs of tokens 8 q8 .. 8 q8 + 7 (uniform)
+#pragma unroll
+      for (int h = 0; h < kHpw; ++h) pp[h] = *reinterpret_cast<const u32x4_t*>(&s_pp[wave][h][4 * q8]);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int e = 0; e < R::kHalves; ++e) {
+          const uint8_t* a = vst + (8 * q8 + 4 * half) * R::kRowBytes + vofs[e];
+          const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t*)(uintptr_t)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)a);
+          const u32x2_t w = __builtin_bit_cast(u32x2_t, v);
+#pragma unroll
+          for (int h = 0; h < kHpw; ++h) {
+            acc[h][e] = dot2_bf16(pp[h][2 * half], w[0], acc[h][e]);
+            acc[h][e] = dot2_bf16(pp[h][2 * half + 1], w[1], acc[h][e]);
+          }
+        }
+      }
+    }
+  };
+
+  for (int s0 = 0; s0 < n_stages; s0 += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u)
+      if (s0 + u < n_stages) stage(s0 + u, u);
+  }
+
+  // ---- finish: each wave owns whole heads; lane owns columns 16 k + vi
+  const int nsp = (ctx + p.split_tokens - 1) / p.split_tokens;
+#pragma unroll
+  for (int h = 0; h < kHpw; ++h) {
+    const float L = wave_sum(l_run[h]);
+    const float inv = 1.0f / L;
+    const int64_t row = (int64_t)b * n_h + h0 + h;
+#pragma unroll
+    for (int e = 0; e < R::kHalves; ++e) {
+      const int d = 16 * (4 * e + vg) + vi;
+      const float o = acc[h][e] * inv;
+      if (nsp == 1) {
+        reinterpret_cast<uint16_t*>(p.out)[row * D + d] = f32_to_bf16_rne(o);
+      } else {
+        const int64_t pi = row * p.num_splits + split;
+        p.part_o[pi * D + d] = o;
+        if (lane == 0 && e == 0) { p.part_ml[2 * pi] = m_run[h]; p.part_ml[2 * pi + 1] = L; }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
+  return kv == KV::BF16 && q_bf16 && d_k == d_v && (d_k == 64 || d_k == 128) && (g == 4 || g == 8);
+}
+
+hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.num_splits, (unsigned)p.n_kv, (unsigned)p.B);
+  const int g = p.n_h / p.n_kv;
+#define PKV_RING(D_, G_, NW_, RING_) \
+  hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_>), grid, dim3(64 * NW_), 0, stream, p)
+  if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_G8_NW, PKV_G8_RING);
+  else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_G4_RING);
+  else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_G8_NW, PKV_G8_RING);
+  else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_G4_RING);
+  else return hipErrorInvalidValue;
+#undef PKV_RING
+  return hipGetLastError();
+}
+
+}  // namespace pkv

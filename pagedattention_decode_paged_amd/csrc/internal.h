@@ -70,6 +70,11 @@ hipError_t launch_decode_int8(const DecodeParams& p, int g, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
 int mla_head_groups(int n_h);
 
+// bf16 GQA with g in {4, 8}: the LDS-ring kernel (decode_gqa_ring.hip);
+// launch_decode_gqa routes the shapes it covers there.
+bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g);
+hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream);
+
 // Whether an instance exists (host-side check before launch).
 bool gqa_supported(KV kv, bool q_bf16, int d_k, int d_v, int g);
 bool mla_supported(int d_k, int d_v, int n_h, int block_size);
