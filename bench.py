@@ -46,11 +46,30 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU budget of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of a known size: 1 GiB read, 1 GiB written per copy."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence or KV head with no exchange, see DESIGN.md)",
@@ -181,8 +200,9 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "token_heads_per_s": float(f"{tok_heads:.4g}"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_gqa_kernel<128,8,bf16> (split merge fused)",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "paged_decode_attention: decode_gqa_ring_kernel<128,8,8,2> + decode_reduce_kernel",
                      "avg_launch_us": round(us_launch, 2),
                      "bytes_per_launch": kv_bytes_layer},
     }
@@ -190,6 +210,24 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers[0], cfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record, if the kernel sources it was taken on are unchanged
+    (else None: the counters describe a different kernel)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gqa_ring_70b_traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() == rec["sources_sha256"]:
+            return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
 
 
 def cpu_baseline(layer, cfg, budget_s):
