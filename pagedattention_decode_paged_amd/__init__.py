@@ -266,12 +266,21 @@ def decode_mla_workgroups(desc: _DecodeDesc) -> int:
     return int(_lib.paged_decode_mla_workgroups(ctypes.byref(desc)))
 
 
+def alloc_workspace(desc: _DecodeDesc, device="cuda") -> torch.Tensor | None:
+    """A workspace for calls of this description (reusable by later calls
+    on the same stream that need no more bytes)."""
+    need = decode_workspace_size(desc)
+    return torch.empty(need, dtype=torch.uint8, device=device) if need else None
+
+
 def _workspace(desc, workspace, dev):
     need = decode_workspace_size(desc)
     if need == 0:
         return None, 0
-    if workspace is None or workspace.numel() < need:
+    if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
     return workspace, workspace.numel()
 
 

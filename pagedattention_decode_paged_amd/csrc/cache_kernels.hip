@@ -27,16 +27,24 @@ __global__ void slot_mapping_kernel(const int32_t* __restrict__ bt, int32_t mb, 
   slots[t] = out;
 }
 
-// One workgroup per token row; 16-byte moves when the row allows it.
+// One workgroup per (token, matrix): blockIdx.y = 0 writes the K row,
+// 1 the V row, so one launch scatters both; 16-byte moves when the rows
+// allow it.
+struct CopyJob {
+  uint8_t* pool;
+  const uint8_t* src;
+  int64_t row_bytes;
+};
+
 template <typename V>
-__global__ void cache_copy_kernel(uint8_t* __restrict__ pool, const uint8_t* __restrict__ src,
-                                  const int64_t* __restrict__ slots, int64_t row_bytes) {
-  int64_t t = blockIdx.x;
-  int64_t s = slots[t];
+__global__ void cache_copy_kernel(CopyJob k, CopyJob v, const int64_t* __restrict__ slots) {
+  const CopyJob j = blockIdx.y == 0 ? k : v;
+  const int64_t t = blockIdx.x;
+  const int64_t s = slots[t];
   if (s < 0) return;
-  const V* in = reinterpret_cast<const V*>(src + t * row_bytes);
-  V* out = reinterpret_cast<V*>(pool + s * row_bytes);
-  int64_t n = row_bytes / (int64_t)sizeof(V);
+  const V* in = reinterpret_cast<const V*>(j.src + t * j.row_bytes);
+  V* out = reinterpret_cast<V*>(j.pool + s * j.row_bytes);
+  const int64_t n = j.row_bytes / (int64_t)sizeof(V);
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) out[i] = in[i];
 }
 
@@ -52,10 +60,21 @@ __device__ __forceinline__ float load_as_f32(const void* src, int64_t i, bool bf
 // row.  The absolute maximum is exact; the scale and the quotients are IEEE
 // divisions (HIP's default float division is correctly rounded); rintf
 // rounds half to even.
-__global__ void cache_quant_int8_kernel(int8_t* __restrict__ codes, float* __restrict__ scales,
-                                        const void* __restrict__ src, int bf16,
+struct QuantJob {
+  int8_t* codes;
+  float* scales;
+  const void* src;
+  int32_t d;
+};
+
+__global__ void cache_quant_int8_kernel(QuantJob kj, QuantJob vj, int bf16,
                                         const int64_t* __restrict__ slots, int64_t num_rows,
-                                        int32_t n_kv, int32_t d) {
+                                        int32_t n_kv) {
+  const QuantJob j = blockIdx.y == 0 ? kj : vj;
+  const int32_t d = j.d;
+  int8_t* __restrict__ codes = j.codes;
+  float* __restrict__ scales = j.scales;
+  const void* __restrict__ src = j.src;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= num_rows) return;
@@ -112,32 +131,38 @@ hipError_t launch_slot_mapping(const int32_t* block_table, int32_t mb, int32_t s
   return hipGetLastError();
 }
 
-hipError_t launch_cache_copy(void* pool, const void* src, const int64_t* slots,
-                             int64_t num_tokens, int64_t row_bytes, hipStream_t stream) {
+hipError_t launch_cache_copy(void* k_pool, const void* k_src, int64_t k_row_bytes, void* v_pool,
+                             const void* v_src, int64_t v_row_bytes, const int64_t* slots,
+                             int64_t num_tokens, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  dim3 grid((unsigned)num_tokens);
-  const bool v16 = (row_bytes % 16 == 0) && ((uintptr_t)pool % 16 == 0) &&
-                   ((uintptr_t)src % 16 == 0);
-  int64_t nvec = v16 ? row_bytes / 16 : row_bytes / 4;
-  int threads = nvec >= 256 ? 256 : (int)((nvec + 63) / 64) * 64;
+  const bool two = v_pool != nullptr;
+  dim3 grid((unsigned)num_tokens, two ? 2u : 1u);
+  auto al16 = [](const void* p) { return (uintptr_t)p % 16 == 0; };
+  const bool v16 = k_row_bytes % 16 == 0 && al16(k_pool) && al16(k_src) &&
+                   (!two || (v_row_bytes % 16 == 0 && al16(v_pool) && al16(v_src)));
+  const int64_t row = two && v_row_bytes > k_row_bytes ? v_row_bytes : k_row_bytes;
+  const int64_t nvec = v16 ? row / 16 : row / 4;
+  const int threads = nvec >= 256 ? 256 : (int)((nvec + 63) / 64) * 64;
+  const CopyJob kj{(uint8_t*)k_pool, (const uint8_t*)k_src, k_row_bytes};
+  const CopyJob vj{(uint8_t*)v_pool, (const uint8_t*)v_src, v_row_bytes};
   if (v16)
-    hipLaunchKernelGGL(cache_copy_kernel<uint4>, grid, dim3(threads), 0, stream,
-                       (uint8_t*)pool, (const uint8_t*)src, slots, row_bytes);
+    hipLaunchKernelGGL(cache_copy_kernel<uint4>, grid, dim3(threads), 0, stream, kj, vj, slots);
   else
-    hipLaunchKernelGGL(cache_copy_kernel<uint32_t>, grid, dim3(threads), 0, stream,
-                       (uint8_t*)pool, (const uint8_t*)src, slots, row_bytes);
+    hipLaunchKernelGGL(cache_copy_kernel<uint32_t>, grid, dim3(threads), 0, stream, kj, vj, slots);
   return hipGetLastError();
 }
 
-hipError_t launch_cache_quant_int8(int8_t* codes, float* scales, const void* src, bool src_bf16,
-                                   const int64_t* slots, int64_t num_tokens, int32_t n_kv,
-                                   int32_t d, hipStream_t stream) {
+hipError_t launch_cache_quant_int8(int8_t* k_codes, float* k_scales, const void* k_src, int32_t d_k,
+                                   int8_t* v_codes, float* v_scales, const void* v_src, int32_t d_v,
+                                   bool src_bf16, const int64_t* slots, int64_t num_tokens,
+                                   int32_t n_kv, hipStream_t stream) {
   const int64_t rows = num_tokens * n_kv;
   if (rows == 0) return hipSuccess;
   const int waves = 4;
-  dim3 grid((unsigned)((rows + waves - 1) / waves));
-  hipLaunchKernelGGL(cache_quant_int8_kernel, grid, dim3(64 * waves), 0, stream, codes, scales,
-                     src, src_bf16 ? 1 : 0, slots, rows, n_kv, d);
+  dim3 grid((unsigned)((rows + waves - 1) / waves), 2u);
+  hipLaunchKernelGGL(cache_quant_int8_kernel, grid, dim3(64 * waves), 0, stream,
+                     QuantJob{k_codes, k_scales, k_src, d_k}, QuantJob{v_codes, v_scales, v_src, d_v},
+                     src_bf16 ? 1 : 0, slots, rows, n_kv);
   return hipGetLastError();
 }
 

@@ -431,60 +431,85 @@ __global__ __launch_bounds__(kThreads, 2) void decode_gqa_kernel(const DecodePar
 // Log-sum-exp merge of split partials (the split-context reduction that
 // qwbw 8 Q2/Q3 name FlashDecoding): with M the largest split maximum (scores
 // in base 2), out = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.
-// One workgroup per (sequence, query head); the split weights are formed
-// once in LDS, then every thread owns output columns and streams the
-// partials with several loads in flight.
-constexpr int kReduceThreads = 128;
+// One wavefront per (sequence, query head).  The split (m, l) pairs are
+// uniform and come through the scalar cache; the partial outputs do not
+// depend on them, so all the loads of a batch are in flight at once and the
+// kernel costs about one memory round trip.
+constexpr int kReduceThreads = 64;
 constexpr int kMaxSplits = 1024;
+constexpr int kFewSplits = 8;       // unrolled path: up to this many splits
 
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ context_lens, void* __restrict__ out, int n_h, int d_v,
     int num_splits, int split_tokens, int out_bf16) {
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_red[kReduceThreads / kWave];
   const int bh = blockIdx.x;
   const int b = bh / n_h;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x;
   const int ctx = context_lens[b];
   const int nsp = min(num_splits, (ctx + split_tokens - 1) / split_tokens);
-  const int64_t base = (int64_t)bh * num_splits;
   if (nsp <= 1) return;                 // written by the decode kernel itself
-
-  float mx = -INFINITY;
-  for (int s = tid; s < nsp; s += kReduceThreads) mx = fmaxf(mx, part_ml[2 * (base + s)]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-  __syncthreads();
-  float M = s_red[0];
+  const int64_t base = (int64_t)bh * num_splits;
+  const float* ml = part_ml + 2 * base;
+  if (nsp <= kFewSplits && d_v <= 2 * kReduceThreads) {
+    // every load issued before the first use
+    float m[kFewSplits], l[kFewSplits], v0[kFewSplits], v1[kFewSplits];
+    const float* po = part_o + base * d_v + lane;
+    const bool c1 = lane + kReduceThreads < d_v;
 #pragma unroll
-  for (int w = 1; w < kReduceThreads / kWave; ++w) M = fmaxf(M, s_red[w]);
-  __syncthreads();
-  float lsum = 0.f;
-  for (int s = tid; s < nsp; s += kReduceThreads) {
-    const float w = part_ml[2 * (base + s) + 1] * __builtin_amdgcn_exp2f(part_ml[2 * (base + s)] - M);
-    s_w[s] = w;
-    lsum += w;
-  }
-  lsum = wave_sum(lsum);
-  if ((tid & 63) == 0) s_red[tid >> 6] = lsum;
-  __syncthreads();
-  float L = 0.f;
-#pragma unroll
-  for (int w = 0; w < kReduceThreads / kWave; ++w) L += s_red[w];
-  const float inv = 1.0f / L;
-  for (int d = tid; d < d_v; d += kReduceThreads) {
-    const float* po = part_o + base * d_v + d;
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    int s = 0;
-    for (; s + 4 <= nsp; s += 4) {
-      o0 = fmaf(po[(int64_t)(s + 0) * d_v], s_w[s + 0], o0);
-      o1 = fmaf(po[(int64_t)(s + 1) * d_v], s_w[s + 1], o1);
-      o2 = fmaf(po[(int64_t)(s + 2) * d_v], s_w[s + 2], o2);
-      o3 = fmaf(po[(int64_t)(s + 3) * d_v], s_w[s + 3], o3);
+    for (int s = 0; s < kFewSplits; ++s) {
+      if (s < nsp) {
+        m[s] = ml[2 * s];
+        l[s] = ml[2 * s + 1];
+        v0[s] = lane < d_v ? po[(int64_t)s * d_v] : 0.f;
+        v1[s] = c1 ? po[(int64_t)s * d_v + kReduceThreads] : 0.f;
+      }
     }
-    for (; s < nsp; ++s) o0 = fmaf(po[(int64_t)s * d_v], s_w[s], o0);
-    const float r = ((o0 + o1) + (o2 + o3)) * inv;
+    float M = m[0];
+#pragma unroll
+    for (int s = 1; s < kFewSplits; ++s)
+      if (s < nsp) M = fmaxf(M, m[s]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int s = 0; s < kFewSplits; ++s) {
+      if (s < nsp) {
+        const float w = l[s] * __builtin_amdgcn_exp2f(m[s] - M);
+        L += w;
+        o0 = fmaf(v0[s], w, o0);
+        o1 = fmaf(v1[s], w, o1);
+      }
+    }
+    const float inv = 1.0f / L;
+    const int64_t o = (int64_t)bh * d_v + lane;
+    if (out_bf16) {
+      if (lane < d_v) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(o0 * inv);
+      if (c1) reinterpret_cast<uint16_t*>(out)[o + kReduceThreads] = f32_to_bf16_rne(o1 * inv);
+    } else {
+      if (lane < d_v) reinterpret_cast<float*>(out)[o] = o0 * inv;
+      if (c1) reinterpret_cast<float*>(out)[o + kReduceThreads] = o1 * inv;
+    }
+    return;
+  }
+  float M = -INFINITY;
+  for (int s = 0; s < nsp; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int d = lane; d < d_v; d += kReduceThreads) {
+    const float* po = part_o + base * d_v + d;
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    int s = 0;
+    for (; s + 2 <= nsp; s += 2) {
+      const float v0 = po[(int64_t)s * d_v], v1 = po[(int64_t)(s + 1) * d_v];
+      const float w0 = ml[2 * s + 1] * __builtin_amdgcn_exp2f(ml[2 * s] - M);
+      const float w1 = ml[2 * s + 3] * __builtin_amdgcn_exp2f(ml[2 * s + 2] - M);
+      L += w0 + w1;
+      o0 = fmaf(v0, w0, o0);
+      o1 = fmaf(v1, w1, o1);
+    }
+    if (s < nsp) {
+      const float w = ml[2 * s + 1] * __builtin_amdgcn_exp2f(ml[2 * s] - M);
+      L += w;
+      o0 = fmaf(po[(int64_t)s * d_v], w, o0);
+    }
+    const float r = (o0 + o1) / L;
     const int64_t o = (int64_t)bh * d_v + d;
     if (out_bf16) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(r);
     else reinterpret_cast<float*>(out)[o] = r;

@@ -14,15 +14,18 @@ hipError_t launch_slot_mapping(const int32_t* block_table, int32_t max_blocks_pe
                                const int32_t* positions, int64_t num_tokens,
                                int64_t* slots, hipStream_t stream);
 
-// Bit copy of num_tokens rows of row_bytes each (row_bytes % 4 == 0).
-hipError_t launch_cache_copy(void* pool, const void* src, const int64_t* slots,
-                             int64_t num_tokens, int64_t row_bytes, hipStream_t stream);
+// Bit copy of the K rows (and V rows when v_pool is not null) of num_tokens
+// tokens into their slots, one launch (row bytes % 4 == 0).
+hipError_t launch_cache_copy(void* k_pool, const void* k_src, int64_t k_row_bytes, void* v_pool,
+                             const void* v_src, int64_t v_row_bytes, const int64_t* slots,
+                             int64_t num_tokens, hipStream_t stream);
 
-// Quantize-on-write: src rows [num_tokens, n_kv, d] (f32 or bf16 bits),
-// codes [slots, n_kv, d] int8, scales [slots, n_kv] f32.
-hipError_t launch_cache_quant_int8(int8_t* codes, float* scales, const void* src,
+// Quantize-on-write of K and V, one launch: src rows [num_tokens, n_kv, d]
+// (f32 or bf16 bits), codes [slots, n_kv, d] int8, scales [slots, n_kv] f32.
+hipError_t launch_cache_quant_int8(int8_t* k_codes, float* k_scales, const void* k_src, int32_t d_k,
+                                   int8_t* v_codes, float* v_scales, const void* v_src, int32_t d_v,
                                    bool src_bf16, const int64_t* slots, int64_t num_tokens,
-                                   int32_t n_kv, int32_t d, hipStream_t stream);
+                                   int32_t n_kv, hipStream_t stream);
 
 hipError_t launch_gather(const void* pool, int64_t row_bytes, int32_t block_shift,
                          const int32_t* block_table, int32_t max_blocks_per_seq,

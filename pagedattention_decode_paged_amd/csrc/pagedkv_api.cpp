@@ -206,21 +206,19 @@ kvp_status reshape_and_cache(kvp_pool* pool, const void* k_new, const void* v_ne
   if (d.dtype == KVP_INT8) {
     if (in_dtype == KVP_INT8) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: INT8 pools take F32 or BF16 rows");
     const bool bf = in_dtype == KVP_BF16;
-    hipError_t e = pkv::launch_cache_quant_int8(static_cast<int8_t*>(v.k), v.k_scale, k_new, bf,
-                                               slot_mapping, num_tokens, d.n_kv, d.d_k, st);
-    if (e != hipSuccess) return hip_status(e, "reshape_and_cache (K)");
-    e = pkv::launch_cache_quant_int8(static_cast<int8_t*>(v.v), v.v_scale, v_new, bf, slot_mapping,
-                                     num_tokens, d.n_kv, d.d_v, st);
-    return hip_status(e, "reshape_and_cache (V)");
+    return hip_status(pkv::launch_cache_quant_int8(static_cast<int8_t*>(v.k), v.k_scale, k_new, d.d_k,
+                                                  static_cast<int8_t*>(v.v), v.v_scale, v_new, d.d_v,
+                                                  bf, slot_mapping, num_tokens, d.n_kv, st),
+                      "reshape_and_cache");
   }
   if (in_dtype != d.dtype)
     return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: rows must have the pool's dtype");
   const size_t eb = dtype_bytes(d.dtype);
-  hipError_t e = pkv::launch_cache_copy(v.k, k_new, slot_mapping, num_tokens,
-                                        (int64_t)d.n_kv * d.d_k * eb, st);
-  if (e != hipSuccess || d.latent) return hip_status(e, "reshape_and_cache (K)");
-  e = pkv::launch_cache_copy(v.v, v_new, slot_mapping, num_tokens, (int64_t)d.n_kv * d.d_v * eb, st);
-  return hip_status(e, "reshape_and_cache (V)");
+  // K and V rows in one launch (a latent pool has no V region)
+  return hip_status(pkv::launch_cache_copy(v.k, k_new, (int64_t)d.n_kv * d.d_k * eb,
+                                           d.latent ? nullptr : v.v, v_new,
+                                           (int64_t)d.n_kv * d.d_v * eb, slot_mapping, num_tokens, st),
+                    "reshape_and_cache");
 }
 
 }  // extern "C"
@@ -474,11 +472,10 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   p.out = out;
   if (need > 0) {
     const size_t rows = (size_t)d->B * d->n_h * ns;
-    p.part_o = static_cast<float*>(workspace);
+    // [part_o][part_ml]
     uint8_t* w = static_cast<uint8_t*>(workspace);
     const size_t o_bytes = round_up(rows * d->d_v * sizeof(float), 256);
-    const size_t ml_bytes = round_up(rows * 2 * sizeof(float), 256);
-    (void)ml_bytes;
+    p.part_o = reinterpret_cast<float*>(w);
     p.part_ml = reinterpret_cast<float*>(w + o_bytes);
   }
   p.scale = scale;

@@ -213,3 +213,26 @@ def test_split_count_invariance():
     again = pk.paged_decode_attention(q, k, v, bt, ctx, cfg.scale, max_context_len=s.max_context_len,
                                       split_tokens=256).float()
     assert torch.equal(again, outs[0])
+
+
+
+def test_one_workspace_serves_calls_of_different_shapes():
+    """One workspace, sized for the largest call, serves calls of different
+    split sizes and batch shapes in a row; every result matches the oracle."""
+    cfg = CONFIGS["llama8b"]
+    s = structure(cfg)
+    k, v, q = _big_case(cfg, s, 91)
+    bt, ctx = tables_to_device(s)
+    ref = oracle.paged_decode_attention(host(q), host(k), host(v), s.block_table, s.context_lens,
+                                        cfg.scale)
+    big = pk.make_desc(B=cfg.B, n_h=cfg.n_h, n_kv=cfg.n_kv, d_k=128, d_v=128, block_size=16,
+                       max_blocks_per_seq=s.max_blocks_per_seq, max_context_len=s.max_context_len,
+                       q_dtype=pk.KVP_BF16, kv_dtype=pk.KVP_BF16, split_tokens=256)
+    ws = pk.alloc_workspace(big)
+    for split, rows in [(256, slice(None)), (1024, slice(None)), (512, slice(3, 11)),
+                        (256, slice(0, 5)), (2048, slice(None))]:
+        qq, bb, cc = q[rows].contiguous(), bt[rows].contiguous(), ctx[rows].contiguous()
+        out = pk.paged_decode_attention(qq, k, v, bb, cc, cfg.scale, max_context_len=s.max_context_len,
+                                        split_tokens=split, workspace=ws)
+        torch.cuda.synchronize()
+        assert max_err(out, ref[rows]) <= TOL_BF16, split
