@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU budget of the oracle baseline sample")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the secondary workloads (8B-shaped layer, INT8 cache, MLA)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -207,9 +209,161 @@ def main():
                      "bytes_per_launch": kv_bytes_layer},
     }
 
+    if not args.headline_only:
+        del layers, calls_rc, calls_dec
+        torch.cuda.empty_cache()
+        result["secondary"] = [bench_llama8b(dev), bench_int8(dev), bench_mla(dev)]
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(layers[0], cfg, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _time_calls(calls, cycles, warm=3):
+    """Average device time of one call, cycling through independent
+    instances (so that repeated calls do not find their data in the
+    256 MB last-level cache); HIP events on the launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(cycles):
+        for c in calls:
+            c()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / (cycles * len(calls))
+
+
+def bench_llama8b(dev, instances=16, cycles=20):
+    """8B-shaped layer (B=32, n_h=32, n_kv=8, d=128, contexts U[512, 4096],
+    2K prefix shared by all sequences), 16 instances of identical structure
+    and different contents cycled."""
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    from synth import CONFIGS, structure, device_normal_
+    cfg = CONFIGS["llama8b"]
+    s = structure(cfg)
+    bt = torch.from_numpy(s.block_table).to(dev)
+    ctx = torch.from_numpy(s.context_lens).to(dev)
+    calls = []
+    keep = []
+    for i in range(instances):
+        pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v,
+                                 torch.bfloat16, device=dev)
+        device_normal_(pool.storage.view(torch.bfloat16), cfg.seed * 100 + i)
+        q = device_normal_(torch.empty((cfg.B, cfg.n_h, cfg.d_k), dtype=torch.bfloat16, device=dev),
+                           cfg.seed * 100 + 50 + i)
+        out = torch.empty((cfg.B, cfg.n_h, cfg.d_v), dtype=torch.bfloat16, device=dev)
+        calls.append(pk.prepare_decode(q, pool.k, pool.v, bt, ctx, cfg.scale, out,
+                                       max_context_len=s.max_context_len,
+                                       total_context_len=int(s.context_lens.sum())))
+        keep.append((pool, q, out))
+    us = _time_calls(calls, cycles)
+    row = cfg.n_kv * cfg.d_k * 2 * 2                            # K + V bytes per token
+    total = int(s.context_lens.sum())
+    logical = total * row
+    unique_tokens = int(min(2048, s.context_lens.max())) + int(np.maximum(s.context_lens - 2048, 0).sum())
+    unique = unique_tokens * row
+    return {"workload": cfg.desc, "instances": instances, "us_per_call": round(us, 2),
+            "kv_gbs_logical": round(logical / (us * 1e-6) / 1e9, 1),
+            "kv_gbs_unique": round(unique / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak_logical": round(100 * logical / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "token_heads_per_s": float(f"{total * cfg.n_h / (us * 1e-6):.4g}"),
+            "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+            "note": "logical bytes count every sequence's view of the shared prefix; the prefix "
+                    "blocks are read from cache after the first sequence, so logical GB/s can "
+                    "exceed what HBM alone delivers"}
+
+
+def bench_int8(dev, instances=4, cycles=10):
+    """INT8 cache, 70B-shaped heads (B=32, n_h=64, n_kv=8, d=128), contexts
+    log-uniform in [50, 32768]; codes and scales written by reshape_and_cache
+    from bf16 N(0,1) rows; 4 instances cycled."""
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    from synth import CONFIGS, structure, device_normal_
+    from synth.workloads import prefill_tokens
+    cfg = CONFIGS["int8_70b"]
+    s = structure(cfg)
+    bt = torch.from_numpy(s.block_table).to(dev)
+    ctx = torch.from_numpy(s.context_lens).to(dev)
+    seq, pos = prefill_tokens(s.context_lens)
+    slots = pk.paged_slot_mapping(bt, torch.from_numpy(seq).to(dev), torch.from_numpy(pos).to(dev),
+                                  cfg.block_size)
+    calls, keep = [], []
+    for i in range(instances):
+        pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v, torch.int8,
+                                 device=dev)
+        src = device_normal_(torch.empty((2, len(seq), cfg.n_kv, cfg.d_k), dtype=torch.bfloat16,
+                                         device=dev), cfg.seed * 100 + i)
+        pk.reshape_and_cache(pool, src[0], src[1], slots)
+        del src
+        q = device_normal_(torch.empty((cfg.B, cfg.n_h, cfg.d_k), dtype=torch.bfloat16, device=dev),
+                           cfg.seed * 100 + 50 + i)
+        out = torch.empty((cfg.B, cfg.n_h, cfg.d_v), dtype=torch.bfloat16, device=dev)
+        desc = pk.make_desc(B=cfg.B, n_h=cfg.n_h, n_kv=cfg.n_kv, d_k=cfg.d_k, d_v=cfg.d_v,
+                            block_size=cfg.block_size, max_blocks_per_seq=s.max_blocks_per_seq,
+                            max_context_len=s.max_context_len, q_dtype=pk.KVP_BF16,
+                            kv_dtype=pk.KVP_INT8, total_context_len=int(s.context_lens.sum()))
+        ws = pk.alloc_workspace(desc, dev)
+        calls.append(lambda q=q, pool=pool, out=out, ws=ws: pk.paged_decode_attention_int8(
+            q, pool.k, pool.k_scale, pool.v, pool.v_scale, bt, ctx, cfg.scale, out,
+            max_context_len=s.max_context_len, total_context_len=int(s.context_lens.sum()),
+            workspace=ws))
+        keep.append((pool, q, out, ws))
+    torch.cuda.synchronize()
+    us = _time_calls(calls, cycles)
+    total = int(s.context_lens.sum())
+    kv = total * cfg.n_kv * 2 * (cfg.d_k + 4)                  # codes + one fp32 scale, K and V
+    return {"workload": cfg.desc, "instances": instances, "us_per_call": round(us, 2),
+            "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "token_heads_per_s": float(f"{total * cfg.n_h / (us * 1e-6):.4g}"), "kv_bytes": kv}
+
+
+def bench_mla(dev, instances=4, cycles=10):
+    """Absorbed MLA (B=64, n_h=128, 576-wide latent rows, values = first
+    512 columns, block 64, contexts U[1024, 8192]); 4 instances cycled."""
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    from synth import CONFIGS, structure, device_normal_
+    cfg = CONFIGS["mla"]
+    s = structure(cfg)
+    bt = torch.from_numpy(s.block_table).to(dev)
+    ctx = torch.from_numpy(s.context_lens).to(dev)
+    total = int(s.context_lens.sum())
+    calls, keep = [], []
+    for i in range(instances):
+        pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, 1, cfg.d_k, cfg.d_v, torch.bfloat16,
+                                 latent=True, device=dev)
+        device_normal_(pool.k, cfg.seed * 100 + i)
+        q = device_normal_(torch.empty((cfg.B, cfg.n_h, cfg.d_k), dtype=torch.bfloat16, device=dev),
+                           cfg.seed * 100 + 50 + i)
+        out = torch.empty((cfg.B, cfg.n_h, cfg.d_v), dtype=torch.bfloat16, device=dev)
+        desc = pk.make_desc(B=cfg.B, n_h=cfg.n_h, n_kv=1, d_k=cfg.d_k, d_v=cfg.d_v,
+                            block_size=cfg.block_size, max_blocks_per_seq=s.max_blocks_per_seq,
+                            max_context_len=s.max_context_len, q_dtype=pk.KVP_BF16,
+                            kv_dtype=pk.KVP_BF16, total_context_len=total)
+        ws = pk.alloc_workspace(desc, dev)
+        calls.append(lambda q=q, pool=pool, out=out, ws=ws: pk.paged_decode_attention_mla(
+            q, pool.k, bt, ctx, cfg.scale, cfg.d_v, out, max_context_len=s.max_context_len,
+            total_context_len=total, workspace=ws))
+        keep.append((pool, q, out, ws))
+    torch.cuda.synchronize()
+    us = _time_calls(calls, cycles)
+    kv = total * cfg.d_k * 2
+    flops = total * cfg.n_h * 2 * (cfg.d_k + cfg.d_v)
+    return {"workload": cfg.desc, "instances": instances, "us_per_call": round(us, 2),
+            "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "pct_mfma_bf16_peak": round(100 * flops / (us * 1e-6) / 2.5e15, 2),
+            "token_heads_per_s": float(f"{total * cfg.n_h / (us * 1e-6):.4g}"), "kv_bytes": kv,
+            "flops": flops}
 
 
 def measured_traffic():
@@ -230,12 +384,23 @@ def measured_traffic():
     return None
 
 
-def cpu_baseline(layer, cfg, budget_s):
+def cpu_baseline(budget_s):
     """The fp64 oracle, as it stands, on a bounded sample of the same
-    workload: whole sequences of layer 0 (all 64 query heads) until the CPU
-    budget is spent; single-threaded BLAS."""
+    workload: whole sequences of layer 0 (all 64 query heads, its K/V drawn
+    with the bench's seeds) until the CPU budget is spent; single-threaded
+    BLAS."""
     import torch
     import oracle
+    import pagedattention_decode_paged_amd as pk
+    from synth import CONFIGS, structure, device_normal_
+    cfg = CONFIGS["llama70b"]
+    s = structure(cfg, layer=0)
+    pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v, torch.bfloat16)
+    device_normal_(pool.k, cfg.seed * 1000)
+    device_normal_(pool.v, cfg.seed * 1000 + 1)
+    q = device_normal_(torch.empty((cfg.B, cfg.n_h, cfg.d_k), dtype=torch.bfloat16, device="cuda"),
+                       cfg.seed * 1000 + 2)
+    layer = {"s": s, "pool": pool, "q": q}
     try:
         from threadpoolctl import threadpool_limits
         limit = threadpool_limits(limits=1)
