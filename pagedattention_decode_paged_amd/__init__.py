@@ -153,7 +153,7 @@ class KVPool:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
+        if h is not None and h.value and _lib is not None:   # (None at interpreter exit)
             _lib.kv_pool_destroy(h)
             self.handle = ctypes.c_void_p(None)
 

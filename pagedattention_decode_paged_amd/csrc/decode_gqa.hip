@@ -73,9 +73,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_gqa_kernel(const DecodePar
   __shared__ __align__(16) uint8_t s_kbuf[kKBytes > kAccBytes ? kKBytes : kAccBytes];
   float (&s_acc)[kWaves][G * D] = *reinterpret_cast<float (*)[kWaves][G * D]>(s_kbuf);
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // grid (KV head, sequence, split), KV head fastest: workgroups are dealt
+  // to the 8 XCDs round-robin by linear index, so each XCD serves whole KV
+  // heads (identical work) whatever the context lengths and split count
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int split = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_gqa_kernel(const DecodePar
 // kernel costs about one memory round trip.
 constexpr int kReduceThreads = 64;
 constexpr int kMaxSplits = 1024;
-constexpr int kFewSplits = 8;       // unrolled path: up to this many splits
+constexpr int kFewSplits = 8;       // splits whose loads are issued together (d_v <= 128)
 
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -451,74 +454,57 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(
   if (nsp <= 1) return;                 // written by the decode kernel itself
   const int64_t base = (int64_t)bh * num_splits;
   const float* ml = part_ml + 2 * base;
-  if (nsp <= kFewSplits && d_v <= 2 * kReduceThreads) {
-    // every load issued before the first use
+  const float* po = part_o + base * d_v + lane;
+  const bool c0 = lane < d_v, c1 = lane + kReduceThreads < d_v;
+  // batches of kFewSplits splits, all loads of a batch issued before their
+  // first use; batches merged online (running max M, sum L, outputs o)
+  float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < nsp; s0 += kFewSplits) {
     float m[kFewSplits], l[kFewSplits], v0[kFewSplits], v1[kFewSplits];
-    const float* po = part_o + base * d_v + lane;
-    const bool c1 = lane + kReduceThreads < d_v;
 #pragma unroll
-    for (int s = 0; s < kFewSplits; ++s) {
+    for (int k = 0; k < kFewSplits; ++k) {
+      const int s = s0 + k;
       if (s < nsp) {
-        m[s] = ml[2 * s];
-        l[s] = ml[2 * s + 1];
-        v0[s] = lane < d_v ? po[(int64_t)s * d_v] : 0.f;
-        v1[s] = c1 ? po[(int64_t)s * d_v + kReduceThreads] : 0.f;
+        m[k] = ml[2 * s];
+        l[k] = ml[2 * s + 1];
+        v0[k] = c0 ? po[(int64_t)s * d_v] : 0.f;
+        v1[k] = c1 ? po[(int64_t)s * d_v + kReduceThreads] : 0.f;
+      } else {
+        m[k] = -INFINITY;
+        l[k] = 0.f;
+        v0[k] = v1[k] = 0.f;
       }
     }
-    float M = m[0];
+    float Mb = M;
 #pragma unroll
-    for (int s = 1; s < kFewSplits; ++s)
-      if (s < nsp) M = fmaxf(M, m[s]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int k = 0; k < kFewSplits; ++k) Mb = fmaxf(Mb, m[k]);
+    const float f = __builtin_amdgcn_exp2f(M - Mb);   // 0 for the first batch
+    L *= f;
+    o0 *= f;
+    o1 *= f;
+    M = Mb;
 #pragma unroll
-    for (int s = 0; s < kFewSplits; ++s) {
-      if (s < nsp) {
-        const float w = l[s] * __builtin_amdgcn_exp2f(m[s] - M);
-        L += w;
-        o0 = fmaf(v0[s], w, o0);
-        o1 = fmaf(v1[s], w, o1);
-      }
-    }
-    const float inv = 1.0f / L;
-    const int64_t o = (int64_t)bh * d_v + lane;
-    if (out_bf16) {
-      if (lane < d_v) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(o0 * inv);
-      if (c1) reinterpret_cast<uint16_t*>(out)[o + kReduceThreads] = f32_to_bf16_rne(o1 * inv);
-    } else {
-      if (lane < d_v) reinterpret_cast<float*>(out)[o] = o0 * inv;
-      if (c1) reinterpret_cast<float*>(out)[o + kReduceThreads] = o1 * inv;
-    }
-    return;
-  }
-  float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, ml[2 * s]);
-  for (int d = lane; d < d_v; d += kReduceThreads) {
-    const float* po = part_o + base * d_v + d;
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-    int s = 0;
-    for (; s + 2 <= nsp; s += 2) {
-      const float v0 = po[(int64_t)s * d_v], v1 = po[(int64_t)(s + 1) * d_v];
-      const float w0 = ml[2 * s + 1] * __builtin_amdgcn_exp2f(ml[2 * s] - M);
-      const float w1 = ml[2 * s + 3] * __builtin_amdgcn_exp2f(ml[2 * s + 2] - M);
-      L += w0 + w1;
-      o0 = fmaf(v0, w0, o0);
-      o1 = fmaf(v1, w1, o1);
-    }
-    if (s < nsp) {
-      const float w = ml[2 * s + 1] * __builtin_amdgcn_exp2f(ml[2 * s] - M);
+    for (int k = 0; k < kFewSplits; ++k) {
+      const float w = l[k] * __builtin_amdgcn_exp2f(m[k] - M);   // 0 past the last split
       L += w;
-      o0 = fmaf(po[(int64_t)s * d_v], w, o0);
+      o0 = fmaf(v0[k], w, o0);
+      o1 = fmaf(v1[k], w, o1);
     }
-    const float r = (o0 + o1) / L;
-    const int64_t o = (int64_t)bh * d_v + d;
-    if (out_bf16) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(r);
-    else reinterpret_cast<float*>(out)[o] = r;
+  }
+  const float inv = 1.0f / L;
+  const int64_t o = (int64_t)bh * d_v + lane;
+  if (out_bf16) {
+    if (c0) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(o0 * inv);
+    if (c1) reinterpret_cast<uint16_t*>(out)[o + kReduceThreads] = f32_to_bf16_rne(o1 * inv);
+  } else {
+    if (c0) reinterpret_cast<float*>(out)[o] = o0 * inv;
+    if (c1) reinterpret_cast<float*>(out)[o + kReduceThreads] = o1 * inv;
   }
 }
 
 template <int D, int G, bool BF16, bool PAIR>
 hipError_t launch_inst(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)p.num_splits, (unsigned)p.n_kv, (unsigned)p.B);
+  dim3 grid((unsigned)p.n_kv, (unsigned)p.B, (unsigned)p.num_splits);
   hipLaunchKernelGGL((decode_gqa_kernel<D, G, BF16, PAIR>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -1,41 +1,51 @@
-// Paged decode attention for GQA on bf16 pools, g = n_h / n_kv in {4, 8}:
-// the kernel for the bandwidth-bound shapes (8B- and 70B-shaped layers).
+// Paged decode attention for GQA with g = n_h / n_kv in {4, 8}: bf16 pools,
+// and INT8 pools with the dequantization fused in.  The kernel for the
+// bandwidth-bound shapes (8B- and 70B-shaped layers).
 //
 // What is computed: for each sequence b and query head h,
 //   out[b][h] = sum_j softmax_j(scale * q[b][h] . K_j) V_j ,  j < context_lens[b],
 // with K_j, V_j reached through the block table (faulkner, first section and
 // the logical/physical block mapping; qwbw 3.4) and the g query heads of a
-// group sharing KV head h / g (faulkner's MHA/GQA/MLA table).
+// group sharing KV head h / g (faulkner's MHA/GQA/MLA table).  For an INT8
+// pool K_j = code_j * sK_j and V_j = code_j * sV_j with one fp32 scale per
+// (token, KV head) (guijiagi 4.2).
 //
-// How (gfx950, wave64, one workgroup of 4 waves per (split, KV head, seq)):
+// How (gfx950, wave64, one workgroup of NW waves per (split, KV head, seq)):
 // * K and V rows reach LDS through the LDS DMA path (global_load_lds_dwordx4)
-//   in 64-token stages (one 64-row K tile and one V tile), RING stages
-//   deep: while a stage is computed, the next RING - 1 are in flight, so
-//   the reads outstanding live in LDS, not in registers (with two 2-stage
-//   rings per compute unit, 64 KiB per CU).  Each DMA instruction moves four (d = 128) or
-//   eight (d = 64) whole rows, 16 bytes per lane, every lane with its own
-//   row address from the block table (any block size works).
-// * The waves split the g heads (g / 4 each) and every wave walks all
+//   in 64-token stages, RING stages deep: while a stage is computed the next
+//   RING - 1 are in flight, so the reads outstanding live in LDS, not in
+//   registers.  Each DMA instruction moves whole rows, 16 bytes per lane;
+//   for a whole stage the block's base address is formed on the scalar unit
+//   and each lane adds a loop-invariant 32-bit offset (rows of an
+//   instruction share a block); the last, partial stage (and blocks smaller
+//   than an instruction's rows) use per-lane addresses.
+// * INT8: codes and the per-token scales land in a staging ring; the waves
+//   then widen each stage's codes to bf16 tiles in LDS as u = code + 128
+//   (exact: every integer in [0, 255] is a bf16), and the offset is taken
+//   out exactly afterwards: q . code = q . u - 128 sum(q) for the scores and
+//   sum_t p'_t code_t = sum_t p'_t u_t - 128 sum_t p'_t for the values, with
+//   p'_t = p_t * sV_t.
+// * The waves split the g heads (g / NW each) and every wave walks all
 //   tokens of the stage, so a K/V byte crosses HBM once and feeds all g
-//   heads, and each wave's softmax state is final at the end (no merge
-//   between waves).
+//   heads, and each wave's softmax state is final at the end.
 // * Scores: lane i owns token i of the stage and reads its K row from LDS
 //   (rows are stored with their 16-byte pieces permuted by the row index, so
-//   the 16 lanes of a read phase hit distinct banks); q is uniform per wave
-//   and streamed through scalar registers; v_dot2 on bf16 pairs, fp32 sums.
+//   the 16 lanes of a read phase hit distinct banks of the 64-bank LDS); q
+//   is uniform per wave and streamed through scalar registers; v_dot2 on
+//   bf16 pairs, fp32 sums.
 // * Online softmax per stage in base 2 (scale * log2 e folded into q.K);
-//   the stage maximum comes from DPP, the probabilities are rounded to bf16
-//   (the same values feed the numerator and the running sum) and packed in
-//   token pairs into a per-wave LDS slice.
+//   the stage maximum comes from DPP; the value-phase weights are rounded to
+//   bf16 by v_cvt_pk_bf16_f32 in token pairs into a per-wave LDS slice.
 // * Values: lane (group j, index i) owns output column 16 k + i of every
 //   head of the wave, k = j (+ 4 for the upper half of d = 128); one
 //   transposed LDS read (ds_read_b64_tr_b16) returns that column for four
 //   consecutive tokens, i.e. two bf16 token pairs that v_dot2 multiplies
-//   with the matching probability pairs.  Each lane accumulates whole
-//   columns, so no cross-lane reduction is needed at the end.
+//   with the matching weight pairs.  Each lane accumulates whole columns.
 // * Tokens at or past the context length re-read the last valid row (finite
-//   data): their scores are -inf and probabilities 0, so unused slots (NaN
-//   in the tests) are never read.
+//   data): their scores are -inf and weights 0, so unused slots (NaN in the
+//   tests) are never read.
+#include <utility>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -51,6 +61,12 @@
 #ifndef PKV_G4_RING
 #define PKV_G4_RING 2
 #endif
+#ifndef PKV_Q8_G8_RING
+#define PKV_Q8_G8_RING 2
+#endif
+#ifndef PKV_Q8_G4_RING
+#define PKV_Q8_G4_RING 2
+#endif
 
 namespace pkv {
 namespace {
@@ -63,40 +79,58 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kStageTok = 64;    // tokens per stage (one per lane in the score phase)
 
-template <int D, int NW>
+template <int D, int NW, bool Q8>
 struct Ring {
-  static constexpr int kRowBytes = D * 2;                     // bf16 row
-  static constexpr int kPieces = kRowBytes / 16;              // 16-byte pieces per row
-  static constexpr int kRowsPerDma = kWave / kPieces;         // rows per DMA instruction
+  static constexpr int kRowBytes = D * 2;                     // bf16 row (the LDS tiles)
+  static constexpr int kPieces = kRowBytes / 16;              // 16-byte pieces per bf16 row
+  static constexpr int kSrcRow = Q8 ? D : D * 2;              // bytes per row in the pool
+  static constexpr int kSrcPieces = kSrcRow / 16;
+  static constexpr int kRowsPerDma = kWave / kSrcPieces;      // rows per DMA instruction
   static constexpr int kDmaPerMat = kStageTok / kRowsPerDma;  // per stage, per matrix
-  static constexpr int kDmaPerWave = 2 * kDmaPerMat / NW;     // each wave's share (K or V)
-  static constexpr int kMatBytes = kStageTok * kRowBytes;
+  static constexpr int kDmaPerWave = 2 * kDmaPerMat / NW;     // each wave's row share (K or V)
+  static constexpr int kMatBytes = kStageTok * kRowBytes;     // one bf16 tile
+  static constexpr int kSrcBytes = kStageTok * kSrcRow;       // one matrix of a staged stage
   static constexpr int kHalves = D / 64;                      // 64-column passes of the value phase
-  static constexpr int kRows256 = 256 / kRowBytes;            // rows per 256 bytes
-  static_assert(D == 64 || D == 128, "row must be 128 or 256 bytes");
+  static constexpr int kRows256 = 256 / kRowBytes;            // bf16 rows per 256 bytes
+  // INT8 scales: one 4-byte DMA instruction per matrix per stage, issued by
+  // waves 0 and 1
+  static constexpr int kScaleWaves = Q8 ? 2 : 0;
+  static_assert(D == 64 || D == 128, "row must be 64 or 128 elements");
   static_assert(kDmaPerMat % kDmaPerWave == 0, "a wave issues K or V instructions only");
-  // Piece permutations (row r's logical piece p sits at position p ^ swz(r)):
-  // K rows are read one row per lane, 16 lanes per LDS phase; V is read
-  // transposed, 4 rows x 2 pieces per 16 lanes, 32 lanes per phase.
+  // Piece permutations of the bf16 tiles (row r's logical piece p sits at
+  // position p ^ swz(r)): K rows are read one row per lane, 16 lanes per LDS
+  // phase; V is read transposed, 4 rows x 2 pieces per 16 lanes, 32 lanes
+  // per phase.
   static __device__ __forceinline__ int swz_k(int r) { return (r / kRows256) % kPieces; }
   static __device__ __forceinline__ int swz_v(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
   }
 };
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // Every LDS access of this wave has completed, then the workgroup barrier.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// LDS DMA, 16 bytes per lane to LDS m0 + 16 * lane.  The address is either
-// a per-lane 64-bit pointer or a wave-uniform 64-bit base plus a per-lane
-// 32-bit offset (the block's address computed once on the scalar unit).
+// Wait until at most n of this wave's vector-memory instructions are in
+// flight (the instruction takes an immediate; n is uniform, n < 32).
+template <int N>
+__device__ __forceinline__ void wait_vm_imm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int... Ns>
+__device__ __forceinline__ void wait_vm_sel(int n, std::integer_sequence<int, Ns...>) {
+  ((n == Ns ? (wait_vm_imm<Ns>(), 0) : 0), ...);
+}
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 32) n = 0;                             // stricter than needed, never looser
+  wait_vm_sel(n, std::make_integer_sequence<int, 32>{});
+}
+
+// LDS DMA, 16 (or 4) bytes per lane to LDS m0 + 16 (or 4) * lane.  The
+// address is either a per-lane 64-bit pointer or a wave-uniform 64-bit base
+// plus a per-lane 32-bit offset (the block's address formed on the scalar
+// unit).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -107,21 +141,50 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
 }
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(m0), "v"(src) : "memory", "m0");
+}
 
-template <int D, int G, int NW, int RING>
+// Sixteen int8 codes (a 16-byte piece) -> sixteen bf16 values code + 128
+// (exact), as two 16-byte pieces.
+__device__ __forceinline__ void widen_codes(const u32x4_t c, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t o[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t u = c[w] ^ 0x80808080u;        // code + 128 as unsigned bytes
+    // (byte -> float conversions: v_cvt_f32_ubyte0..3)
+    const f32x2_t a = {(float)(u & 0xffu), (float)((u >> 8) & 0xffu)};
+    const f32x2_t b = {(float)((u >> 16) & 0xffu), (float)(u >> 24)};
+    o[2 * w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_t));
+    o[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2_t));
+  }
+  lo = u32x4_t{o[0], o[1], o[2], o[3]};
+  hi = u32x4_t{o[4], o[5], o[6], o[7]};
+}
+
+template <int D, int G, int NW, int RING, bool Q8>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodeParams p) {
-  using R = Ring<D, NW>;
+  using R = Ring<D, NW, Q8>;
   constexpr int kThr = 64 * NW;
   constexpr int kHpw = G / NW;                     // heads per wave
   static_assert(G % NW == 0, "g must be a multiple of the wave count");
-  __shared__ __attribute__((aligned(1024))) uint8_t s_k[RING][R::kMatBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_v[RING][R::kMatBytes];
+  // bf16: the DMA ring holds the K and V tiles themselves.  INT8: it holds
+  // codes and scales, and one pair of bf16 tiles receives each stage.
+  constexpr int kRingBytes = Q8 ? R::kSrcBytes : R::kMatBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_dma[2][RING][kRingBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_tile[Q8 ? 2 : 1][Q8 ? R::kMatBytes : 16];
+  __shared__ __align__(16) float s_scl[2][Q8 ? RING : 1][Q8 ? kStageTok : 1];
   __shared__ __align__(16) int32_t s_bt[kBtSlots];
   __shared__ __align__(16) uint32_t s_pp[NW][kHpw][kStageTok / 2];
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // grid (KV head, sequence, split), KV head fastest: workgroups are dealt
+  // to the 8 XCDs round-robin by linear index, so each XCD serves whole KV
+  // heads (identical work) whatever the context lengths and split count
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int split = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -149,34 +212,43 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   }
   __syncthreads();
 
-  const int64_t slot_stride = (int64_t)p.n_kv * R::kRowBytes;
+  const int64_t slot_stride = (int64_t)p.n_kv * R::kSrcRow;
   const int n_stages = (t_end - t_begin + kStageTok - 1) / kStageTok;
 
   // ---- this wave's DMA share: instructions j0 .. j0 + kDmaPerWave - 1 of a
   // stage, all on K (first half of the waves) or all on V.  Lane l moves
-  // piece l % kPieces of row l / kPieces of the instruction's rows.
+  // piece l % kSrcPieces of row l / kSrcPieces of the instruction's rows.
   const int j0 = wave * R::kDmaPerWave;
   const bool dma_v = j0 >= R::kDmaPerMat;
   const int jbase = j0 % R::kDmaPerMat;
-  const uint8_t* mat = reinterpret_cast<const uint8_t*>(dma_v ? p.v : p.k) + (int64_t)kvh * R::kRowBytes;
-  const uint32_t lds_mat = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(dma_v ? &s_v[0][0] : &s_k[0][0]);
-  const int lrow = lane / R::kPieces, lpiece = lane % R::kPieces;
-  // per-lane offsets inside a block for the fast path (rows of an
-  // instruction share a block); the piece permutation depends on the row
-  // only through jm mod kSwzPeriod
-  constexpr int kSwzPeriod = D == 128 ? 4 : 2;
+  const uint8_t* mat = reinterpret_cast<const uint8_t*>(dma_v ? p.v : p.k) + (int64_t)kvh * R::kSrcRow;
+  const uint32_t lds_mat =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&s_dma[dma_v ? 1 : 0][0][0];
+  const int lrow = lane / R::kSrcPieces, lpiece = lane % R::kSrcPieces;
+  // source piece a lane moves for row r: bf16 rows go straight to the tile
+  // (permuted); INT8 codes go to the staging ring in order
+  auto src_piece = [&](int r) {
+    if constexpr (Q8) return lpiece;
+    else return lpiece ^ (dma_v ? R::swz_v(r) : R::swz_k(r));
+  };
+  // per-lane offsets inside a block for the fast path; the permutation
+  // depends on the row only through jm mod kSwzPeriod
+  constexpr int kSwzPeriod = Q8 ? 1 : (D == 128 ? 4 : 2);
   uint32_t voff[kSwzPeriod];
 #pragma unroll
-  for (int i = 0; i < kSwzPeriod; ++i) {
-    const int r = i * R::kRowsPerDma + lrow;
-    const int piece = lpiece ^ (dma_v ? R::swz_v(r) : R::swz_k(r));
-    voff[i] = (uint32_t)(lrow * slot_stride) + (uint32_t)piece * 16u;
-  }
+  for (int i = 0; i < kSwzPeriod; ++i)
+    voff[i] = (uint32_t)(lrow * slot_stride) + (uint32_t)src_piece(i * R::kRowsPerDma + lrow) * 16u;
   const bool fast_ok = (1 << shift) >= R::kRowsPerDma;
+  // INT8 scales: wave 0 moves the K scales, wave 1 the V scales, one fp32
+  // per lane and token
+  const float* scl_src = wave == 0 ? p.k_scale : p.v_scale;
+  const uint32_t lds_scl =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&s_scl[wave == 0 ? 0 : 1][0][0];
+  const int dma_per_wave = R::kDmaPerWave + (wave < R::kScaleWaves ? 1 : 0);
 
   auto issue = [&](int s, int slot) {
     const int tile0 = t_begin + s * kStageTok;
-    const uint32_t dst0 = lds_mat + (uint32_t)(slot * R::kMatBytes);
+    const uint32_t dst0 = lds_mat + (uint32_t)(slot * kRingBytes);
     if (fast_ok && tile0 + kStageTok <= t_end) {
       // whole stage: one block per instruction, address base on the scalar unit
 #pragma unroll
@@ -202,23 +274,43 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
         const int r = jm * R::kRowsPerDma + lrow;
         const int t = min(tile0 + r, t_last);
         const int64_t sl = ((int64_t)ph[jj] << shift) + (t & bmask);
-        const int piece = lpiece ^ (dma_v ? R::swz_v(r) : R::swz_k(r));
-        dma16(mat + sl * slot_stride + piece * 16, dst0 + (uint32_t)(jm * 1024));
+        dma16(mat + sl * slot_stride + src_piece(r) * 16, dst0 + (uint32_t)(jm * 1024));
+      }
+    }
+    if constexpr (Q8) {
+      if (wave < R::kScaleWaves) {
+        const int t = min(tile0 + lane, t_last);
+        const int64_t sl = ((int64_t)s_bt[(t >> shift) - lb0] << shift) + (t & bmask);
+        dma4(scl_src + sl * p.n_kv + kvh, lds_scl + (uint32_t)(slot * kStageTok * 4));
       }
     }
   };
 
-  float m_run[kHpw], l_run[kHpw];
+  float m_run[kHpw], l_run[kHpw], ps_run[kHpw];
   float acc[kHpw][R::kHalves];
 #pragma unroll
   for (int h = 0; h < kHpw; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.f;
+    ps_run[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < R::kHalves; ++e) acc[h][e] = 0.f;
   }
   const float qscale = p.scale * kLog2e;
   const int64_t q_dw0 = ((int64_t)b * n_h + h0) * (D / 2);   // this wave's q rows (contiguous)
+  // INT8: sum of each head's q (it multiplies the +128 offset of the codes)
+  float qsum[kHpw];
+#pragma unroll
+  for (int h = 0; h < kHpw; ++h) qsum[h] = 0.f;
+  if constexpr (Q8) {
+#pragma unroll
+    for (int h = 0; h < kHpw; ++h) {
+      float t = 0.f;
+      const uint32_t* qh = reinterpret_cast<const uint32_t*>(p.q) + q_dw0 + h * (D / 2);
+      for (int i = lane; i < D / 2; i += kWave) t += bf_lo(qh[i]) + bf_hi(qh[i]);
+      qsum[h] = wave_sum(t);
+    }
+  }
 
   // loop-invariant LDS offsets: K row pieces of this lane's token, and the
   // transposed V reads (lane = 16-lane group vg, index vi: token vt of a
@@ -246,15 +338,38 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   auto stage = [&](int s, int slot) {
     // this wave's DMA for stage s has landed (later stages may still fly),
     // then every wave's has, and every wave is done with stage s - 1
-    const int ahead = min(RING - 2, n_stages - 1 - s);
-    if (RING > 3 && ahead >= 2) wait_vmcnt<2 * R::kDmaPerWave>();
-    else if (RING > 2 && ahead >= 1) wait_vmcnt<R::kDmaPerWave>();
-    else wait_vmcnt<0>();
+    wait_vm(min(RING - 2, n_stages - 1 - s) * dma_per_wave);
     lds_barrier();
     if (s + RING - 1 < n_stages) issue(s + RING - 1, (slot + RING - 1) % RING);
 
-    const uint8_t* kst = &s_k[slot][0];
-    const uint8_t* vst = &s_v[slot][0];
+    const uint8_t* kst;
+    const uint8_t* vst;
+    if constexpr (Q8) {
+      // widen the stage's codes into the bf16 tiles (each thread its share
+      // of the 16-byte code pieces), then make them visible to every wave
+      constexpr int kCodePieces = 2 * kStageTok * R::kSrcPieces;
+      static_assert(kCodePieces % kThr == 0, "code pieces must split evenly over the threads");
+#pragma unroll
+      for (int i = 0; i < kCodePieces / kThr; ++i) {
+        const int q = i * kThr + tid;
+        const int m = q / (kStageTok * R::kSrcPieces);          // 0: K, 1: V
+        const int r = (q / R::kSrcPieces) % kStageTok;
+        const int e = q % R::kSrcPieces;
+        const u32x4_t c = *reinterpret_cast<const u32x4_t*>(&s_dma[m][slot][(r * R::kSrcPieces + e) * 16]);
+        u32x4_t lo, hi;
+        widen_codes(c, lo, hi);
+        const int sw = m ? R::swz_v(r) : R::swz_k(r);
+        uint8_t* row = &s_tile[m][r * R::kRowBytes];
+        *reinterpret_cast<u32x4_t*>(row + ((2 * e) ^ sw) * 16) = lo;
+        *reinterpret_cast<u32x4_t*>(row + ((2 * e + 1) ^ sw) * 16) = hi;
+      }
+      lds_barrier();
+      kst = &s_tile[0][0];
+      vst = &s_tile[1][0];
+    } else {
+      kst = &s_dma[0][slot][0];
+      vst = &s_dma[1][slot][0];
+    }
     const int tile0 = t_begin + s * kStageTok;
     const bool valid = tile0 + lane < t_end;
 
@@ -301,32 +416,48 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
 #pragma unroll
         for (int i = 0; i < kQch; ++i) qa[i] = qb[i];
       }
+      if constexpr (Q8) {
+        const float sk = s_scl[0][slot][lane] * qscale;
 #pragma unroll
-      for (int h = 0; h < kHpw; ++h) sc[h] = valid ? (ax[h] + ay[h]) * qscale : -INFINITY;
+        for (int h = 0; h < kHpw; ++h)
+          sc[h] = valid ? fmaf(-128.f, qsum[h], ax[h] + ay[h]) * sk : -INFINITY;
+      } else {
+#pragma unroll
+        for (int h = 0; h < kHpw; ++h) sc[h] = valid ? (ax[h] + ay[h]) * qscale : -INFINITY;
+      }
     }
 
-    // ---- online softmax; probabilities as bf16 token pairs in LDS (the
-    // rounded values also feed the running sum)
+    // ---- online softmax; value weights as bf16 token pairs in LDS (bf16:
+    // p, whose rounded value also feeds the running sum; INT8: p * sV)
+    float sv = 1.f;
+    if constexpr (Q8) sv = s_scl[1][slot][lane];
 #pragma unroll
     for (int h = 0; h < kHpw; ++h) {
       const float tmax = wave_max(sc[h]);          // finite: the stage's first token is valid
       if (tmax > m_run[h]) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[h] - tmax);
         l_run[h] *= alpha;
+        ps_run[h] *= alpha;
 #pragma unroll
         for (int e = 0; e < R::kHalves; ++e) acc[h][e] *= alpha;
         m_run[h] = tmax;
       }
       const float pr = __builtin_amdgcn_exp2f(sc[h] - m_run[h]);
-      const float pn = dpp<0xB1>(pr);              // token lane ^ 1
-      const f32x2_t two = {pr, pn};
+      const float pw = Q8 ? pr * sv : pr;
+      const float pn = dpp<0xB1>(pw);              // token lane ^ 1
+      const f32x2_t two = {pw, pn};
       const uint32_t pair = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_t));
-      l_run[h] += __uint_as_float(pair << 16);
+      if constexpr (Q8) {
+        l_run[h] += pr;
+        ps_run[h] += __uint_as_float(pair << 16);
+      } else {
+        l_run[h] += __uint_as_float(pair << 16);
+      }
       if ((lane & 1) == 0) s_pp[wave][h][lane >> 1] = pair;
     }
     wave_sync_lds();
 
-    // ---- acc += p . V over token quads (transposed reads give token pairs)
+    // ---- acc += w . V over token quads (transposed reads give token pairs)
 #pragma unroll
     for (int q8 = 0; q8 < kStageTok / 8; ++q8) {
       u32x4_t pp[kHpw];                            // pairs of tokens 8 q8 .. 8 q8 + 7 (uniform)
@@ -362,11 +493,12 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   for (int h = 0; h < kHpw; ++h) {
     const float L = wave_sum(l_run[h]);
     const float inv = 1.0f / L;
+    const float off = Q8 ? 128.f * wave_sum(ps_run[h]) : 0.f;
     const int64_t row = (int64_t)b * n_h + h0 + h;
 #pragma unroll
     for (int e = 0; e < R::kHalves; ++e) {
       const int d = 16 * (4 * e + vg) + vi;
-      const float o = acc[h][e] * inv;
+      const float o = (acc[h][e] - off) * inv;
       if (nsp == 1) {
         reinterpret_cast<uint16_t*>(p.out)[row * D + d] = f32_to_bf16_rne(o);
       } else {
@@ -381,19 +513,29 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
 }  // namespace
 
 bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
-  return kv == KV::BF16 && q_bf16 && d_k == d_v && (d_k == 64 || d_k == 128) && (g == 4 || g == 8);
+  return (kv == KV::BF16 || kv == KV::INT8) && q_bf16 && d_k == d_v && (d_k == 64 || d_k == 128) &&
+         (g == 4 || g == 8);
 }
 
 hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.num_splits, (unsigned)p.n_kv, (unsigned)p.B);
+  const dim3 grid((unsigned)p.n_kv, (unsigned)p.B, (unsigned)p.num_splits);
   const int g = p.n_h / p.n_kv;
-#define PKV_RING(D_, G_, NW_, RING_) \
-  hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_>), grid, dim3(64 * NW_), 0, stream, p)
-  if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_G8_NW, PKV_G8_RING);
-  else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_G4_RING);
-  else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_G8_NW, PKV_G8_RING);
-  else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_G4_RING);
-  else return hipErrorInvalidValue;
+  const bool q8 = p.kv == KV::INT8;
+#define PKV_RING(D_, G_, NW_, RING_, Q8_) \
+  hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_>), grid, dim3(64 * NW_), 0, stream, p)
+  if (!q8) {
+    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_G8_NW, PKV_G8_RING, false);
+    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_G4_RING, false);
+    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_G8_NW, PKV_G8_RING, false);
+    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_G4_RING, false);
+    else return hipErrorInvalidValue;
+  } else {
+    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, 8, PKV_Q8_G8_RING, true);
+    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_Q8_G4_RING, true);
+    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, 8, PKV_Q8_G8_RING, true);
+    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_Q8_G4_RING, true);
+    else return hipErrorInvalidValue;
+  }
 #undef PKV_RING
   return hipGetLastError();
 }

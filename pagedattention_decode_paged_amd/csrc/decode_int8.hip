@@ -50,9 +50,12 @@ __global__ __launch_bounds__(kThreads) void decode_int8_kernel(const DecodeParam
   __shared__ float s_l[kWaves][G];
   __shared__ __align__(16) float s_acc[kWaves][G * D];
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // grid (KV head, sequence, split), KV head fastest: workgroups are dealt
+  // to the 8 XCDs round-robin by linear index, so each XCD serves whole KV
+  // heads (identical work) whatever the context lengths and split count
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int split = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void decode_int8_kernel(const DecodeParam
 
 template <int D, int G>
 hipError_t launch8(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)p.num_splits, (unsigned)p.n_kv, (unsigned)p.B);
+  dim3 grid((unsigned)p.n_kv, (unsigned)p.B, (unsigned)p.num_splits);
   hipLaunchKernelGGL((decode_int8_kernel<D, G>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -313,9 +313,13 @@ MlaWorkspace mla_workspace(const kvp_decode_desc* d) {
 }
 
 // Context split size: aim for about kTargetUnits workgroups doing real work
-// (two 4-wave workgroups per compute unit on 256 CUs), in multiples of the
+// (two resident workgroups per compute unit on 256 CUs), in multiples of the
 // kernel's granule; longer splits amortise each workgroup's set-up and merge.
+// Ragged batches (the sum of the contexts well below B times the longest)
+// take about four times as many, shorter splits: their workgroups differ in
+// size, and more of them even out the compute units' loads.
 constexpr int64_t kTargetUnits = 512;
+constexpr int64_t kTargetUnitsRagged = 2048;
 constexpr int32_t kMaxSplit = 8192;
 
 // A split stages at most kBtSlots block-table entries in LDS.
@@ -333,7 +337,9 @@ int32_t plan_split(const kvp_decode_desc* d, Variant v) {
                                                  : (int64_t)d->B * d->max_context_len;
   const int64_t heads = v == Variant::Mla ? 1 : d->n_kv;
   const int64_t work = total * heads;
-  int64_t split = (work + kTargetUnits - 1) / kTargetUnits;
+  const bool ragged = 4 * total < 3 * (int64_t)d->B * d->max_context_len;
+  const int64_t units = ragged ? kTargetUnitsRagged : kTargetUnits;
+  int64_t split = (work + units - 1) / units;
   split = (split + g - 1) / g * g;
   if (split < g) split = g;
   if (split > max_split(d)) split = max_split(d);

@@ -72,13 +72,17 @@ def test_int8_70b_full_size():
     assert float((out.float() - out2.float()).abs().max()) <= TOL_BF16
 
 
-@pytest.mark.parametrize("d,g", [(128, 8), (128, 1), (64, 4), (64, 2)])
-def test_int8_ragged(d, g):
+@pytest.mark.parametrize("d,g,bs", [(128, 8, 16), (128, 1, 16), (64, 4, 16), (64, 2, 16),
+                                    (128, 4, 16), (128, 8, 1), (128, 4, 64), (64, 8, 1), (64, 4, 64)])
+def test_int8_ragged(d, g, bs):
     ctxs = [1, 15, 16, 17, 64, 65, 255, 257, 600]
-    s = custom_structure(ctxs, 16, seed=d + g, pad_blocks=1)
+    s = custom_structure(ctxs, bs, seed=d + g + bs, pad_blocks=1)
+    s.extra["bs"] = bs
     n_kv = 2
     pool, q, bt, ctx = _int8_case(s, n_kv * g, n_kv, d, 100 + d + g)
     _check_attention(pool, q, bt, ctx, s, 1.0 / math.sqrt(d))
+    # several context splits: the partial merge over the INT8 path
+    _check_attention(pool, q, bt, ctx, s, 1.0 / math.sqrt(d), split_tokens=256)
 
 
 def test_int8_from_fp32_rows():
