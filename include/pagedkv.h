@@ -228,7 +228,8 @@ kvp_status paged_decode_attention_int8(const void* q, const int8_t* k_codes,
  * persistent workgroups share in equal contiguous ranges; a sequence cut
  * between workgroups is merged by log-sum-exp in a second kernel.  The
  * workspace (always needed for MLA) holds a per-sequence record and, when
- * more than one workgroup runs, the fp32 partials of the cut sequences. */
+ * more than one workgroup runs, the partials of the cut sequences: fp32
+ * (max, sum) per head and a bf16 unnormalised output per head. */
 kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
                                       const int32_t* block_table, const int32_t* context_lens,
                                       float scale, void* out, const kvp_decode_desc* desc,

@@ -37,6 +37,10 @@
 #include "device_common.h"
 #include "internal.h"
 
+#ifndef PKV_MLA_KAHEAD
+#define PKV_MLA_KAHEAD 1
+#endif
+
 namespace pkv {
 namespace {
 
@@ -59,9 +63,14 @@ constexpr int kWavesM = 8;
 constexpr int kThreadsM = 64 * kWavesM;
 constexpr int kHeadsPerWave = 16;
 constexpr int kHeadsPerGroup = kHeadsPerWave * kWavesM;
+static_assert(kHeadsPerGroup == kMlaHeadsPerGroup, "workspace sizing assumes 128 heads per group");
 constexpr int kDmaMax = (kDmaPerTile + kWavesM - 1) / kWavesM;      // 5 (waves 0-3), 4 (waves 4-7)
 constexpr int kKSteps = kDk / 32;                     // 18 score k-steps per token block
 constexpr int kDvBlocks = kDv / 16;                   // 32 value column blocks
+constexpr int kColBlocksPerWave = kDvBlocks / kWavesM;   // 4: a wave's 64 value columns
+constexpr int kAccBlocks = kWavesM * kColBlocksPerWave;  // 8 head blocks x 4 column blocks
+constexpr int kKAhead = PKV_MLA_KAHEAD;               // k-steps of K operands read ahead
+constexpr int kPAhead = 2;                            // head blocks of P operands read ahead
 constexpr int kTileCap = 256;                         // tiles whose block ids sit in LDS at once
 constexpr float kRescaleSlack = 8.f;                  // log2 units a stale max may lag by
 
@@ -75,7 +84,7 @@ struct MlaParams {
   const int32_t* block_table;
   const int32_t* context_lens;
   uint16_t* out;            // [B, n_h, 512] bf16
-  float* part_o;            // [W + B, n_h, 512] unnormalised
+  uint16_t* part_o;         // [W + B, head groups, 8 waves, 32 blocks, 64 lanes, 4] bf16, unnormalised
   float* part_ml;           // [W + B, n_h, 2]   (running max in log2 units, sum)
   int32_t* seq_meta;        // [B, 2] first and last workgroup holding the sequence
   float scale_log2;         // scale * log2(e)
@@ -96,6 +105,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Every LDS access of this wave has completed, then the workgroup barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// A copy of v the compiler cannot see through: values derived from it are
+// recomputed where they are used instead of being kept live across the tile
+// loop (the accumulators and query fragments leave few registers free).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // One tile's block ids and fill, staged in LDS for the DMA issue.
 struct TileInfo {
@@ -157,12 +174,18 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
   __shared__ int32_t s_pref[kMlaMaxBatch + 1];
   __shared__ TileInfo s_tile[kTileCap + NS];
   __shared__ int32_t s_scan[kThreadsM];
+  // probabilities of the tile, one 16-byte B fragment per (head block, lane)
+  __shared__ bf16x8_t s_p[kWavesM * 64];
+  __shared__ float s_alpha[kHeadsPerGroup];   // rescale factor per head
+  __shared__ float s_linv[kHeadsPerGroup];    // 1 / softmax sum per head
+  __shared__ __attribute__((aligned(8))) uint8_t s_flag[kWavesM];    // head block rescaled
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = blockIdx.x;
-  const int hbase = blockIdx.y * kHeadsPerGroup + wave * kHeadsPerWave;
-  const bool wave_active = hbase < p.n_h;
+  const int hgroup = blockIdx.y * kHeadsPerGroup;
+  const int hbase = hgroup + wave * kHeadsPerWave;   // this wave's heads for the scores
+  const bool score_active = hbase < p.n_h;
   const int B = p.B;
 
   // ---- tile prefix over the batch (every workgroup computes it) ----
@@ -196,12 +219,11 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
   const int end = (int)((int64_t)(w + 1) * T / W);
   const int n = end - start;
 
-  // ---- per-lane roles: lane group g (k / token groups), index l16 ----
-  const int g = lane >> 4, l16 = lane & 15;
-  // K operand of block mt, k-step ks: row 16 mt + l16, chunk 4 ks + g; V^T
-  // operand of column block m: rows 4 g + (l16 >> 2) (and + 16), 8-byte
-  // piece l16 & 3 of columns 16 m .. 16 m + 15 (offsets formed per tile)
-  const int tk = l16, tv = 4 * g + (l16 >> 2), cp = l16 & 3;
+  // Per-lane roles (formed per phase from an opaque lane index): lane group
+  // g = lane >> 4 (k / token groups), index l16 = lane & 15.  K operand of
+  // block mt, k-step ks: row 16 mt + l16, chunk 4 ks + g.  V^T operand of
+  // column block m: rows 4 g + (l16 >> 2) (and + 16), 8-byte piece l16 & 3
+  // of columns 16 m .. 16 m + 15.
   const uint32_t stage0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)s_stage;
 
   // ---- block ids of the next tiles, staged in LDS ----
@@ -230,11 +252,13 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
     if (s < n) issue_tile(p, stage0 + s * kStageBytes, s_tile[s], wave, lane);
 
   bf16x8_t qf[kKSteps];
-  f32x4_t acc[kDvBlocks];
-  float m_run = -INFINITY, l_run = 0.f;
+  // value accumulators: head block hb, column block cb of this wave's 64
+  // columns -> acc[hb * 4 + cb]; lane holds head 16 hb + l16, columns
+  // 64 wave + 16 cb + 4 g .. + 3
+  f32x4_t acc[kAccBlocks];
+  float m_run = -INFINITY, l_run = 0.f;   // scores side: this lane's head (partial sum over g)
   int piece_first = 0;        // tile index in the sequence where this piece began
   int cur_b = -1;
-  const int h = hbase + l16;  // this lane's head
 
   for (int i = 0; i < n; ++i) {
     const int x = start + i;
@@ -272,9 +296,10 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
       m_run = -INFINITY;
       l_run = 0.f;
 #pragma unroll
-      for (int m = 0; m < kDvBlocks; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (h < p.n_h) {
-        const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(p.q + ((int64_t)b * p.n_h + h) * kDk + 8 * g);
+      for (int m = 0; m < kAccBlocks; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int ln = opaque(lane), h = hbase + (ln & 15);
+      if (score_active && h < p.n_h) {
+        const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(p.q + ((int64_t)b * p.n_h + h) * kDk + 8 * (ln >> 4));
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = qp[4 * ks];
       } else {
@@ -283,27 +308,31 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
       }
     }
 
-    if (wave_active) {
-      // ---- S^T = K Q^T: two 16-token blocks ----
+    // ---- scores of this wave's 16 heads: S^T = K Q^T, two 16-token blocks ----
+    bf16x8_t pb = {};
+    int rescaled = 0;
+    if (score_active) {
+      const int ln = opaque(lane), g = ln >> 4, l16 = ln & 15, tk = l16;
       f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       const uint32_t kb0 = stage + (uint32_t)(tk * kRowBytes), kb1 = kb0 + 16 * kRowBytes;
       const uint32_t ke = 16 * (g ^ swz(tk)), ko = 16 * ((4 + g) ^ swz(tk));   // swz(tk + 16) = swz(tk)
       auto kc = [&](int ks) { return 128 * (ks >> 1) + ((ks & 1) ? ko : ke); };
-      // one k-step of operands in flight ahead of the matrix instructions
-      bf16x8_t ka0 = *(const lds_bf16x8_t*)(uintptr_t)(kb0 + kc(0));
-      bf16x8_t ka1 = *(const lds_bf16x8_t*)(uintptr_t)(kb1 + kc(0));
+      // kKAhead k-steps of operands in flight ahead of the matrix instructions
+      bf16x8_t ka0[kKSteps], ka1[kKSteps];
+#pragma unroll
+      for (int ks = 0; ks < kKAhead; ++ks) {
+        ka0[ks] = *(const lds_bf16x8_t*)(uintptr_t)(kb0 + kc(ks));
+        ka1[ks] = *(const lds_bf16x8_t*)(uintptr_t)(kb1 + kc(ks));
+      }
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        bf16x8_t kn0 = ka0, kn1 = ka1;
-        if (ks + 1 < kKSteps) {
-          kn0 = *(const lds_bf16x8_t*)(uintptr_t)(kb0 + kc(ks + 1));
-          kn1 = *(const lds_bf16x8_t*)(uintptr_t)(kb1 + kc(ks + 1));
+        if (ks + kKAhead < kKSteps) {
+          ka0[ks + kKAhead] = *(const lds_bf16x8_t*)(uintptr_t)(kb0 + kc(ks + kKAhead));
+          ka1[ks + kKAhead] = *(const lds_bf16x8_t*)(uintptr_t)(kb1 + kc(ks + kKAhead));
         }
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[ks], s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[ks], qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[ks], qf[ks], s1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        ka0 = kn0;
-        ka1 = kn1;
       }
 
       // ---- online softmax (base 2) for head l16: tokens 4g + e, 16 + 4g + e
@@ -323,12 +352,11 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
       } else if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int m = 0; m < kDvBlocks; ++m) acc[m] *= alpha;
         l_run *= alpha;
         m_run = m_new;
+        rescaled = 1;
+        if (g == 0) s_alpha[wave * kHeadsPerWave + l16] = alpha;
       }
-      bf16x8_t pb;
       float lsum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -337,24 +365,46 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
         lsum += (float)pr;
       }
       l_run += lsum;
+    }
+    // heads past n_h (inactive waves) contribute zero probabilities
+    s_p[wave * 64 + opaque(lane)] = pb;
+    if (lane == 0) s_flag[wave] = (uint8_t)rescaled;
+    lds_barrier();
 
-      // ---- O^T += V^T P^T over the 32 column blocks ----
+    // ---- O^T += V^T P^T for this wave's 64 columns and all 128 heads ----
+    {
+      const uint2 fw = *reinterpret_cast<const uint2*>(s_flag);
+      const uint64_t flags = ((uint64_t)__builtin_amdgcn_readfirstlane(fw.y) << 32) |
+                             (uint32_t)__builtin_amdgcn_readfirstlane(fw.x);
+      const int ln = opaque(lane), g = ln >> 4, l16 = ln & 15;
+      const int tv = 4 * g + (l16 >> 2), cp = l16 & 3;
       const uint32_t vb = stage + (uint32_t)(tv * kRowBytes) + 8 * (cp & 1);
       const int sv = swz(tv);
-      auto vread = [&](int m) {
+      bf16x8_t va[kColBlocksPerWave];
+#pragma unroll
+      for (int cb = 0; cb < kColBlocksPerWave; ++cb) {
+        const int m = kColBlocksPerWave * wave + cb;
         const uint32_t a = vb + 128 * (m >> 2) + 16 * ((2 * (m & 3) + (cp >> 1)) ^ sv);
         const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a);
         const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(a + 16 * kRowBytes));
-        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8_t va = vread(0);
+        va[cb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      bf16x8_t pv[kWavesM];
 #pragma unroll
-      for (int m = 0; m < kDvBlocks; ++m) {
-        bf16x8_t vn = va;
-        if (m + 1 < kDvBlocks) vn = vread(m + 1);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[m], 0, 0, 0);
+      for (int hb = 0; hb < kPAhead; ++hb) pv[hb] = s_p[hb * 64 + lane];
+#pragma unroll
+      for (int hb = 0; hb < kWavesM; ++hb) {
+        if (hb + kPAhead < kWavesM) pv[hb + kPAhead] = s_p[(hb + kPAhead) * 64 + lane];
+        if ((flags >> (8 * hb)) & 1) {
+          const float alpha = s_alpha[hb * kHeadsPerWave + l16];
+#pragma unroll
+          for (int cb = 0; cb < kColBlocksPerWave; ++cb) acc[hb * kColBlocksPerWave + cb] *= alpha;
+        }
+#pragma unroll
+        for (int cb = 0; cb < kColBlocksPerWave; ++cb)
+          acc[hb * kColBlocksPerWave + cb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[cb], pv[hb], acc[hb * kColBlocksPerWave + cb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        va = vn;
       }
     }
 
@@ -369,27 +419,47 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
         p.seq_meta[2 * b] = w;
         p.seq_meta[2 * b + 1] = last;
       }
-      float l_tot = l_run + __shfl_xor(l_run, 16);
-      l_tot += __shfl_xor(l_tot, 32);
-      if (wave_active && h < p.n_h) {
-        if (whole) {
-          const float inv = 1.f / l_tot;
-          uint16_t* orow = p.out + ((int64_t)b * p.n_h + h) * kDv + 4 * g;
+      const int ln = opaque(lane), g = ln >> 4, l16 = ln & 15;
+      if (score_active) {
+        const int h = hbase + l16;
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (g == 0) {
+          s_linv[wave * kHeadsPerWave + l16] = 1.f / l_tot;
+          if (!whole && h < p.n_h)
+            *reinterpret_cast<float2*>(p.part_ml + 2 * ((int64_t)(w + b) * p.n_h + h)) = float2{m_run, l_tot};
+        }
+      }
+      lds_barrier();
+      const int col0 = kColBlocksPerWave * 16 * wave + 4 * g;
+      if (whole) {
 #pragma unroll
-          for (int m = 0; m < kDvBlocks; ++m) {
-            const uint32_t lo = (uint32_t)dev::f32_to_bf16_rne(acc[m][0] * inv) |
-                                ((uint32_t)dev::f32_to_bf16_rne(acc[m][1] * inv) << 16);
-            const uint32_t hi = (uint32_t)dev::f32_to_bf16_rne(acc[m][2] * inv) |
-                                ((uint32_t)dev::f32_to_bf16_rne(acc[m][3] * inv) << 16);
-            *reinterpret_cast<dev::u32x2_t*>(orow + 16 * m) = dev::u32x2_t{lo, hi};
+        for (int hb = 0; hb < kWavesM; ++hb) {
+          const int ho = hgroup + hb * kHeadsPerWave + l16;
+          if (ho < p.n_h) {
+            const float inv = s_linv[hb * kHeadsPerWave + l16];
+            uint16_t* orow = p.out + ((int64_t)b * p.n_h + ho) * kDv + col0;
+#pragma unroll
+            for (int cb = 0; cb < kColBlocksPerWave; ++cb) {
+              const f32x4_t a = acc[hb * kColBlocksPerWave + cb];
+              const uint32_t lo = (uint32_t)dev::f32_to_bf16_rne(a[0] * inv) |
+                                  ((uint32_t)dev::f32_to_bf16_rne(a[1] * inv) << 16);
+              const uint32_t hi = (uint32_t)dev::f32_to_bf16_rne(a[2] * inv) |
+                                  ((uint32_t)dev::f32_to_bf16_rne(a[3] * inv) << 16);
+              *reinterpret_cast<dev::u32x2_t*>(orow + 16 * cb) = dev::u32x2_t{lo, hi};
+            }
           }
-        } else {
-          const int64_t prow = (int64_t)(w + b) * p.n_h + h;
-          float* po = p.part_o + prow * kDv + 4 * g;
+        }
+      } else {
+        // unnormalised partial, rounded to bf16, in the accumulator layout:
+        // one contiguous 512-byte run per (wave, block)
+        uint16_t* po = p.part_o + ((((int64_t)(w + b) * gridDim.y + blockIdx.y) * kWavesM + wave) *
+                                   kAccBlocks * 64 + ln) * 4;
 #pragma unroll
-          for (int m = 0; m < kDvBlocks; ++m)
-            *reinterpret_cast<float4*>(po + 16 * m) = float4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
-          if (g == 0) *reinterpret_cast<float2*>(p.part_ml + 2 * prow) = float2{m_run, l_tot};
+        for (int a = 0; a < kAccBlocks; ++a) {
+          const uint32_t lo = (uint32_t)dev::f32_to_bf16_rne(acc[a][0]) | ((uint32_t)dev::f32_to_bf16_rne(acc[a][1]) << 16);
+          const uint32_t hi = (uint32_t)dev::f32_to_bf16_rne(acc[a][2]) | ((uint32_t)dev::f32_to_bf16_rne(acc[a][3]) << 16);
+          *reinterpret_cast<dev::u32x2_t*>(po + a * 64 * 4) = dev::u32x2_t{lo, hi};
         }
       }
       cur_b = -1;
@@ -398,11 +468,24 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
 }
 
 // Merge the pieces of the sequences that were cut across workgroups, and
-// zero the output of empty sequences.  One 128-thread workgroup per (b, h);
-// thread t owns output columns 4t .. 4t+3.
-__global__ void __launch_bounds__(128) mla_combine_kernel(MlaParams p) {
-  const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  uint16_t* orow = p.out + ((int64_t)b * p.n_h + h) * kDv + 4 * t;
+// zero the output of empty sequences.  The partials are read in the layout
+// the decode kernel leaves them: workgroup (b, y) with y = (head group,
+// wave, 4 accumulator blocks) has thread t handle accumulator block
+// 4 (y % 8) + t / 64 of lane t % 64, i.e. four output columns of one head.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineSlices = kAccBlocks * 64 / kCombineThreads;   // 8 workgroups per (group, wave)
+constexpr int kCombineBatch = 8;
+
+__global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(MlaParams p) {
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int slice = blockIdx.y % kCombineSlices;
+  const int wave = (blockIdx.y / kCombineSlices) % kWavesM;
+  const int hg = blockIdx.y / (kCombineSlices * kWavesM);
+  const int a = slice * (kCombineThreads / 64) + t / 64, ln = t % 64;
+  const int h = hg * kHeadsPerGroup + (a / kColBlocksPerWave) * kHeadsPerWave + (ln & 15);
+  if (h >= p.n_h) return;
+  const int col = 16 * (kColBlocksPerWave * wave + a % kColBlocksPerWave) + 4 * (ln >> 4);
+  uint16_t* orow = p.out + ((int64_t)b * p.n_h + h) * kDv + col;
   const int ctx = p.context_lens[b];
   if (ctx <= 0) {
     *reinterpret_cast<dev::u32x2_t*>(orow) = dev::u32x2_t{0u, 0u};
@@ -410,24 +493,48 @@ __global__ void __launch_bounds__(128) mla_combine_kernel(MlaParams p) {
   }
   const int wf = p.seq_meta[2 * b], wl = p.seq_meta[2 * b + 1];
   if (wf == wl) return;   // finished in place
-  float M = -INFINITY;
-  for (int s = wf; s <= wl; ++s) M = fmaxf(M, p.part_ml[2 * ((int64_t)(s + b) * p.n_h + h)]);
-  float L = 0.f;
-  float4 O = {0.f, 0.f, 0.f, 0.f};
-  for (int s = wf; s <= wl; ++s) {
-    const int64_t prow = (int64_t)(s + b) * p.n_h + h;
-    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + 2 * prow);
-    const float f = __builtin_amdgcn_exp2f(ml.x - M);
-    L = fmaf(ml.y, f, L);
-    const float4 o = *reinterpret_cast<const float4*>(p.part_o + prow * kDv + 4 * t);
-    O.x = fmaf(o.x, f, O.x);
-    O.y = fmaf(o.y, f, O.y);
-    O.z = fmaf(o.z, f, O.z);
-    O.w = fmaf(o.w, f, O.w);
+  const int groups = gridDim.y / (kCombineSlices * kWavesM);
+  // pieces in batches of kCombineBatch with every load of a batch issued
+  // before any is used; the running max M is raised batch by batch
+  float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  for (int s0 = wf; s0 <= wl; s0 += kCombineBatch) {
+    float2 ml[kCombineBatch];
+    dev::u32x2_t v[kCombineBatch];
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const int s = s0 + k;
+      if (s <= wl) {
+        ml[k] = *reinterpret_cast<const float2*>(p.part_ml + 2 * ((int64_t)(s + b) * p.n_h + h));
+        v[k] = *reinterpret_cast<const dev::u32x2_t*>(
+            p.part_o + ((((int64_t)(s + b) * groups + hg) * kWavesM + wave) * kAccBlocks * 64 + a * 64 + ln) * 4);
+      } else {
+        ml[k] = float2{-INFINITY, 0.f};
+        v[k] = dev::u32x2_t{0u, 0u};
+      }
+    }
+    float mc = M;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) mc = fmaxf(mc, ml[k].x);
+    const float r = __builtin_amdgcn_exp2f(M - mc);   // 0 on the first batch (M = -inf, mc finite)
+    L *= r;
+    o0 *= r;
+    o1 *= r;
+    o2 *= r;
+    o3 *= r;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const float f = __builtin_amdgcn_exp2f(ml[k].x - mc);   // 0 for the padding
+      L = fmaf(ml[k].y, f, L);
+      o0 = fmaf(__uint_as_float(v[k][0] << 16), f, o0);
+      o1 = fmaf(__uint_as_float(v[k][0] & 0xffff0000u), f, o1);
+      o2 = fmaf(__uint_as_float(v[k][1] << 16), f, o2);
+      o3 = fmaf(__uint_as_float(v[k][1] & 0xffff0000u), f, o3);
+    }
+    M = mc;
   }
   const float inv = 1.f / L;
-  const uint32_t lo = (uint32_t)dev::f32_to_bf16_rne(O.x * inv) | ((uint32_t)dev::f32_to_bf16_rne(O.y * inv) << 16);
-  const uint32_t hi = (uint32_t)dev::f32_to_bf16_rne(O.z * inv) | ((uint32_t)dev::f32_to_bf16_rne(O.w * inv) << 16);
+  const uint32_t lo = (uint32_t)dev::f32_to_bf16_rne(o0 * inv) | ((uint32_t)dev::f32_to_bf16_rne(o1 * inv) << 16);
+  const uint32_t hi = (uint32_t)dev::f32_to_bf16_rne(o2 * inv) | ((uint32_t)dev::f32_to_bf16_rne(o3 * inv) << 16);
   *reinterpret_cast<dev::u32x2_t*>(orow) = dev::u32x2_t{lo, hi};
 }
 
@@ -448,7 +555,7 @@ hipError_t launch_decode_mla(const DecodeParams& d, hipStream_t stream) {
   p.block_table = d.block_table;
   p.context_lens = d.context_lens;
   p.out = static_cast<uint16_t*>(d.out);
-  p.part_o = d.part_o;
+  p.part_o = reinterpret_cast<uint16_t*>(d.part_o);
   p.part_ml = d.part_ml;
   p.seq_meta = d.seq_meta;
   p.scale_log2 = d.scale * kLog2e;
@@ -461,7 +568,8 @@ hipError_t launch_decode_mla(const DecodeParams& d, hipStream_t stream) {
   hipLaunchKernelGGL((decode_mla_kernel<kMlaStages>), grid, dim3(kThreadsM), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)p.B, (unsigned)p.n_h), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)p.B, grid.y * kWavesM * kCombineSlices),
+                     dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();
 }
 

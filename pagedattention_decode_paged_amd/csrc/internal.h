@@ -89,6 +89,7 @@ constexpr int kGqaSplitGranule = 256;
 // MLA: context tiles of 32 tokens; every workgroup stages the batch's tile
 // prefix in LDS, which bounds the batch.
 constexpr int kMlaTileTokens = 32;
+constexpr int kMlaHeadsPerGroup = 128;   // heads per MLA workgroup (one head group)
 constexpr int kMlaMaxBatch = 4096;
 
 }  // namespace pkv

@@ -305,9 +305,12 @@ MlaWorkspace mla_workspace(const kvp_decode_desc* d) {
   const int32_t W = mla_workgroups(d);
   m.meta = round_up((size_t)d->B * 2 * sizeof(int32_t), 256);
   if (W > 1) {
+    // per piece: (max, sum) per head in fp32; the unnormalised output of
+    // every head of the launched head groups in bf16
     const size_t rows = (size_t)(W + d->B) * d->n_h;
+    const size_t o_rows = (size_t)(W + d->B) * pkv::mla_head_groups(d->n_h) * pkv::kMlaHeadsPerGroup;
     m.ml = round_up(rows * 2 * sizeof(float), 256);
-    m.o = round_up(rows * d->d_v * sizeof(float), 256);
+    m.o = round_up(o_rows * d->d_v * sizeof(uint16_t), 256);
   }
   return m;
 }

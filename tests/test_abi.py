@@ -85,7 +85,14 @@ def test_split_planning_and_workspace():
     W = pk.decode_mla_workgroups(dm)
     assert 1 <= W <= 64 * 256
     rows = (W + 64) * 128
-    assert pk.decode_workspace_size(dm) >= 64 * 2 * 4 + rows * 2 * 4 + rows * 512 * 4
+    # fp32 (max, sum) per head and a bf16 unnormalised output per head
+    assert pk.decode_workspace_size(dm) >= 64 * 2 * 4 + rows * 2 * 4 + rows * 512 * 2
+    # n_h = 160 launches two groups of 128 heads: the outputs cover both
+    dm160 = _desc(B=64, n_h=160, n_kv=1, d_k=576, d_v=512, block_size=64, max_blocks_per_seq=128,
+                  max_context_len=8192)
+    W160 = pk.decode_mla_workgroups(dm160)
+    assert pk.decode_workspace_size(dm160) >= (64 * 2 * 4 + (W160 + 64) * 160 * 2 * 4
+                                               + (W160 + 64) * 256 * 512 * 2)
     dm1 = _desc(B=2, n_h=128, n_kv=1, d_k=576, d_v=512, block_size=64, max_blocks_per_seq=1,
                 max_context_len=20, workgroups=0)
     assert pk.decode_mla_workgroups(dm1) == 2          # two tiles in the whole batch
