@@ -98,6 +98,10 @@ struct MlaParams {
 // (rows 4g..4g+3, chunk pairs); rows t and t + 16 share the permutation.
 __device__ __forceinline__ int swz(int t) { return t & 7; }
 
+// s_waitcnt immediate with vmcnt = 0 and the other counters at their
+// maximum (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -122,9 +126,9 @@ struct TileInfo {
 };
 
 // Issue this wave's share of the LDS DMA for one tile: stage position P
-// (16-byte units, 64 per instruction) holds logical chunk c of row t.  Rows
-// at or beyond the context re-read the last valid row (finite data for the
-// masked tokens).
+// (16-byte units, 64 per instruction) holds logical chunk c of row t, i.e.
+// P = 72 t + (c ^ swz(t)).  Rows at or beyond the context re-read the last
+// valid row (finite data for the masked tokens).
 __device__ __forceinline__ void issue_tile(const MlaParams& p, uint32_t stage_lds, const TileInfo ti,
                                            int wave, int lane) {
   const int nvalid = ti.nvalid_row0 & 0xff;
@@ -134,6 +138,26 @@ __device__ __forceinline__ void issue_tile(const MlaParams& p, uint32_t stage_ld
   // at every tile rather than kept live across the loop (registers are full)
   int ln = lane;
   asm volatile("" : "+v"(ln));
+  if (nvalid == kTileTok && p.block_shift >= 5) {
+    // A whole tile inside one block (block size >= 32, tiles start at
+    // multiples of 32): its 32 rows are one contiguous 36 KB run, and since
+    // a row holds a whole number of 8-chunk groups, stage position P reads
+    // source chunk P ^ swz(P / 72) of the run.  One scalar base per tile.
+    const uint32_t slot0 = __builtin_amdgcn_readfirstlane(((uint32_t)ti.blk0 << p.block_shift) | (uint32_t)row0);
+    const uint8_t* base = p.pool + (uint64_t)slot0 * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < kDmaMax; ++i) {
+      const int j = wave + kWavesM * i;
+      if (j < kDmaPerTile) {
+        const uint32_t P = (uint32_t)(j * 64 + ln);
+        const uint32_t off = 16u * (P ^ (uint32_t)swz((int)(P / (uint32_t)kRowChunks)));
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage_lds + (uint32_t)(j * 1024));
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(m0), "v"(off), "s"(base) : "memory", "m0");
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kDmaMax; ++i) {
     const int j = wave + kWavesM * i;              // instruction index in the tile
@@ -306,6 +330,10 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = bf16x8_t{};
       }
+      // The query loads complete here, in a wait the compiler sees: otherwise
+      // it spreads waits for them over the score loop on every tile's path,
+      // ending in vmcnt(0), which also waits for the DMA of the next tiles.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
     // ---- scores of this wave's 16 heads: S^T = K Q^T, two 16-token blocks ----
@@ -314,39 +342,57 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
     if (score_active) {
       const int ln = opaque(lane), g = ln >> 4, l16 = ln & 15, tk = l16;
       f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      const uint32_t kb0 = stage + (uint32_t)(tk * kRowBytes), kb1 = kb0 + 16 * kRowBytes;
-      const uint32_t ke = 16 * (g ^ swz(tk)), ko = 16 * ((4 + g) ^ swz(tk));   // swz(tk + 16) = swz(tk)
-      auto kc = [&](int ks) { return 128 * (ks >> 1) + ((ks & 1) ? ko : ke); };
+      // k-step ks of row tk: chunk 4 ks + g at position 8 (ks >> 1) + ((4 (ks & 1) + g) ^ swz(tk));
+      // two base pointers (even / odd k-steps) and constant offsets, row tk + 16
+      // 16 rows further (swz(tk + 16) = swz(tk))
+      const lds_bf16x8_t* kpe =
+          (const lds_bf16x8_t*)(uintptr_t)(stage + (uint32_t)(tk * kRowBytes + 16 * (g ^ swz(tk))));
+      const lds_bf16x8_t* kpo =
+          (const lds_bf16x8_t*)(uintptr_t)(stage + (uint32_t)(tk * kRowBytes + 16 * ((4 + g) ^ swz(tk))));
+      auto kread = [&](int ks, int blk) { return ((ks & 1) ? kpo : kpe)[8 * (ks >> 1) + blk * 16 * kRowChunks]; };
       // kKAhead k-steps of operands in flight ahead of the matrix instructions
       bf16x8_t ka0[kKSteps], ka1[kKSteps];
 #pragma unroll
       for (int ks = 0; ks < kKAhead; ++ks) {
-        ka0[ks] = *(const lds_bf16x8_t*)(uintptr_t)(kb0 + kc(ks));
-        ka1[ks] = *(const lds_bf16x8_t*)(uintptr_t)(kb1 + kc(ks));
+        ka0[ks] = kread(ks, 0);
+        ka1[ks] = kread(ks, 1);
       }
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         if (ks + kKAhead < kKSteps) {
-          ka0[ks + kKAhead] = *(const lds_bf16x8_t*)(uintptr_t)(kb0 + kc(ks + kKAhead));
-          ka1[ks + kKAhead] = *(const lds_bf16x8_t*)(uintptr_t)(kb1 + kc(ks + kKAhead));
+          ka0[ks + kKAhead] = kread(ks + kKAhead, 0);
+          ka1[ks + kKAhead] = kread(ks + kKAhead, 1);
         }
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[ks], qf[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[ks], qf[ks], s1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- online softmax (base 2) for head l16: tokens 4g + e, 16 + 4g + e
-      float xv[8];
-      float mx = -INFINITY;
+      // ---- online softmax (base 2) for head l16: tokens 4g + e, 16 + 4g + e.
+      // With c = |scale log2 e| and the scores negated when the scale is
+      // negative, x = c s' and, c being non-negative, max x = c max s'
+      // exactly (rounding is monotonic); p = 2^(c s' - m) by one fma.
+      float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      const float c = fabsf(p.scale_log2);
+      if (p.scale_log2 < 0.f) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t0 = 4 * g + e, t1 = 16 + 4 * g + e;
-        xv[e] = t0 < nvalid ? s0[e] * p.scale_log2 : -INFINITY;
-        xv[4 + e] = t1 < nvalid ? s1[e] * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, fmaxf(xv[e], xv[4 + e]));
+        for (int e = 0; e < 8; ++e) sv[e] = -sv[e];
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (nvalid < kTileTok) {   // the last tile of a sequence: mask the tokens past its end
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((e & 4) * 4 + 4 * g + (e & 3) >= nvalid) sv[e] = -INFINITY;
+      }
+      float smax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      // the same head sits in lanes l16, l16 + 16, l16 + 32, l16 + 48
+      {
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+        smax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+        smax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      }
+      const float mx = c * smax;
       if (m_run == -INFINITY) {
         m_run = mx;             // first tile of the piece: nothing accumulated yet
       } else if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
@@ -357,14 +403,23 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
         rescaled = 1;
         if (g == 0) s_alpha[wave * kHeadsPerWave + l16] = alpha;
       }
-      float lsum = 0.f;
+      // probabilities rounded to bf16; the running sum adds the rounded values
+      // (dot2 with ones: exact products, fp32 sums)
+      const float nm = -m_run;
+      if (nvalid < kTileTok) {   // masked tokens get 0 (c may be 0, and 0 * -inf is NaN)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 pr = (__bf16)__builtin_amdgcn_exp2f(xv[e] - m_run);
-        pb[e] = pr;
-        lsum += (float)pr;
+        for (int e = 0; e < 8; ++e)
+          pb[e] = (__bf16)(sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(sv[e], c, nm)));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[e], c, nm));
       }
-      l_run += lsum;
+      const dev::u32x4_t pw = __builtin_bit_cast(dev::u32x4_t, pb);
+      constexpr uint32_t kOnes = 0x3f803f80u;   // bf16 (1, 1)
+      l_run = dev::dot2_bf16(pw[0], kOnes, l_run);
+      l_run = dev::dot2_bf16(pw[1], kOnes, l_run);
+      l_run = dev::dot2_bf16(pw[2], kOnes, l_run);
+      l_run = dev::dot2_bf16(pw[3], kOnes, l_run);
     }
     // heads past n_h (inactive waves) contribute zero probabilities
     s_p[wave * 64 + opaque(lane)] = pb;

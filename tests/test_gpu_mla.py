@@ -72,6 +72,18 @@ def test_mla_ragged_against_oracle(bs, n_h, workgroups):
     assert torch.count_nonzero(out[4]) == 0
 
 
+@pytest.mark.parametrize("scale", [-1.0 / math.sqrt(192.0), 0.0])
+def test_mla_negative_and_zero_scale(scale):
+    """The softmax takes scale * q.k for any finite scale: a negative scale
+    favours the lowest scores, a zero scale averages the context."""
+    s = custom_structure([1, 31, 32, 33, 100, 257], 64, seed=23)
+    pool, q = _latent_case(s, 64, 128, seed=24)
+    bt, ctx = tables_to_device(s)
+    out = _mla(pool, q, bt, ctx, s, scale, workgroups=3)
+    torch.cuda.synchronize()
+    assert max_err(out, _oracle(q, pool, s, scale)) <= TOL_BF16
+
+
 def test_mla_single_token_returns_latent_values_exactly():
     """One context token: its weight is exactly 1, so the output is the
     first 512 columns of its latent row, bit for bit."""
