@@ -71,6 +71,8 @@ constexpr int kColBlocksPerWave = kDvBlocks / kWavesM;   // 4: a wave's 64 value
 constexpr int kAccBlocks = kWavesM * kColBlocksPerWave;  // 8 head blocks x 4 column blocks
 constexpr int kKAhead = PKV_MLA_KAHEAD;               // k-steps of K operands read ahead
 constexpr int kPAhead = 2;                            // head blocks of P operands read ahead
+constexpr int kDmaEvery = 3;                          // k-steps between a wave's DMA instructions
+static_assert((kDmaMax - 1) * kDmaEvery < kKSteps, "every DMA instruction issues inside the score loop");
 constexpr int kTileCap = 256;                         // tiles whose block ids sit in LDS at once
 constexpr float kRescaleSlack = 8.f;                  // log2 units a stale max may lag by
 
@@ -98,6 +100,14 @@ struct MlaParams {
 // (rows 4g..4g+3, chunk pairs); rows t and t + 16 share the permutation.
 __device__ __forceinline__ int swz(int t) { return t & 7; }
 
+// Two floats to a packed bf16 pair (low half = a), round to nearest even:
+// one v_cvt_pk_bf16_f32.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // s_waitcnt immediate with vmcnt = 0 and the other counters at their
 // maximum (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -123,41 +133,47 @@ struct TileInfo {
   int32_t blk0, blk1;       // physical blocks of rows [0, 16) and [16, 32) when block_size is 16
   int32_t nvalid_row0;      // valid rows | first row inside blk0 << 8
   int32_t seq;
+  int32_t j_last;           // tile index in the sequence << 1 | (last tile of the sequence)
 };
 
-// Issue this wave's share of the LDS DMA for one tile: stage position P
-// (16-byte units, 64 per instruction) holds logical chunk c of row t, i.e.
-// P = 72 t + (c ^ swz(t)).  Rows at or beyond the context re-read the last
-// valid row (finite data for the masked tokens).
+// LDS DMA of one tile: stage position P (16-byte units, 64 per
+// instruction, instruction j = wave + 8 i of the workgroup) holds logical
+// chunk c of row t, i.e. P = 72 t + (c ^ swz(t)).
+//
+// A whole tile inside one block (block size >= 32, tiles start at multiples
+// of 32) is one contiguous 36 KB run of 32 rows; since a row holds a whole
+// number of 8-chunk groups, position P reads chunk P ^ swz(P / 72) of the
+// run: one scalar base per tile and a lane offset.  tile_run returns that
+// base, or null for the other tiles.
+__device__ __forceinline__ const uint8_t* tile_run(const MlaParams& p, const TileInfo ti) {
+  const int nvalid = ti.nvalid_row0 & 0xff;
+  const int row0 = ti.nvalid_row0 >> 8;
+  if (nvalid != kTileTok || p.block_shift < 5) return nullptr;
+  const uint32_t slot0 = __builtin_amdgcn_readfirstlane(((uint32_t)ti.blk0 << p.block_shift) | (uint32_t)row0);
+  return p.pool + (uint64_t)slot0 * kRowBytes;
+}
+
+// Instruction i of this wave for a whole tile (ln: lane index).
+__device__ __forceinline__ void dma_run(const uint8_t* run, uint32_t stage_lds, int wave, int i, int ln) {
+  const int j = wave + kWavesM * i;
+  if (j < kDmaPerTile) {
+    const uint32_t P = (uint32_t)(j * 64 + ln);
+    const uint32_t off = 16u * (P ^ (uint32_t)swz((int)(P / (uint32_t)kRowChunks)));
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage_lds + (uint32_t)(j * 1024));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0), "v"(off), "s"(run) : "memory", "m0");
+  }
+}
+
+// All of this wave's instructions for any tile: rows at or beyond the
+// context re-read the last valid row (finite data for the masked tokens);
+// rows [16, 32) may sit in a second block when the block size is 16.
 __device__ __forceinline__ void issue_tile(const MlaParams& p, uint32_t stage_lds, const TileInfo ti,
                                            int wave, int lane) {
   const int nvalid = ti.nvalid_row0 & 0xff;
   const int row0 = ti.nvalid_row0 >> 8;
   const int bs_mask = (1 << p.block_shift) - 1;
-  // opaque copy of the lane index: the per-lane offsets below are recomputed
-  // at every tile rather than kept live across the loop (registers are full)
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
-  if (nvalid == kTileTok && p.block_shift >= 5) {
-    // A whole tile inside one block (block size >= 32, tiles start at
-    // multiples of 32): its 32 rows are one contiguous 36 KB run, and since
-    // a row holds a whole number of 8-chunk groups, stage position P reads
-    // source chunk P ^ swz(P / 72) of the run.  One scalar base per tile.
-    const uint32_t slot0 = __builtin_amdgcn_readfirstlane(((uint32_t)ti.blk0 << p.block_shift) | (uint32_t)row0);
-    const uint8_t* base = p.pool + (uint64_t)slot0 * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < kDmaMax; ++i) {
-      const int j = wave + kWavesM * i;
-      if (j < kDmaPerTile) {
-        const uint32_t P = (uint32_t)(j * 64 + ln);
-        const uint32_t off = 16u * (P ^ (uint32_t)swz((int)(P / (uint32_t)kRowChunks)));
-        const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage_lds + (uint32_t)(j * 1024));
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                     :: "s"(m0), "v"(off), "s"(base) : "memory", "m0");
-      }
-    }
-    return;
-  }
+  const int ln = opaque(lane);
 #pragma unroll
   for (int i = 0; i < kDmaMax; ++i) {
     const int j = wave + kWavesM * i;              // instruction index in the tile
@@ -264,16 +280,12 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
       const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks_per_seq;
       const int32_t b0 = bt[kb];
       const int32_t b1 = (row0 + nvalid > (1 << p.block_shift)) ? bt[kb + 1] : b0;
-      s_tile[k] = TileInfo{b0, b1, nvalid | (row0 << 8), b};
+      const int jt = x - s_pref[b];
+      s_tile[k] = TileInfo{b0, b1, nvalid | (row0 << 8), b, (jt << 1) | (int)(x + 1 == s_pref[b + 1])};
     }
   };
   fill_tiles(c0);
   __syncthreads();
-
-  // ---- prologue: first NS - 1 tiles in flight ----
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < n) issue_tile(p, stage0 + s * kStageBytes, s_tile[s], wave, lane);
 
   bf16x8_t qf[kKSteps];
   // value accumulators: head block hb, column block cb of this wave's 64
@@ -283,6 +295,38 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
   float m_run = -INFINITY, l_run = 0.f;   // scores side: this lane's head (partial sum over g)
   int piece_first = 0;        // tile index in the sequence where this piece began
   int cur_b = -1;
+
+  // A new piece (sequence b from its tile j on): reset the softmax state and
+  // the accumulators and load the sequence's queries.  The loads complete
+  // in a wait the compiler sees: otherwise it spreads waits for them over
+  // the score loop on every tile's path, ending in vmcnt(0), which would
+  // also wait for the DMA in flight for the next tiles.
+  auto start_piece = [&](int b, int j) {
+    cur_b = b;
+    piece_first = j;
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int m = 0; m < kAccBlocks; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int ln = opaque(lane), h = hbase + (ln & 15);
+    if (score_active && h < p.n_h) {
+      const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(p.q + ((int64_t)b * p.n_h + h) * kDk + 8 * (ln >> 4));
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = qp[4 * ks];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = bf16x8_t{};
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  };
+
+  // ---- prologue: first NS - 1 tiles in flight ----
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < n) issue_tile(p, stage0 + s * kStageBytes, s_tile[s], wave, lane);
+
+  // the first piece's queries load with the first tiles' DMA: one wait for all
+  if (n > 0) start_piece(s_tile[0].seq, s_tile[0].j_last >> 1);
 
   for (int i = 0; i < n; ++i) {
     const int x = start + i;
@@ -307,33 +351,29 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
     const TileInfo ti = s_tile[x - c0];
     const int b = ti.seq;
     const int nvalid = ti.nvalid_row0 & 0xff;
-    const int j = x - s_pref[b];
+    const int j = ti.j_last >> 1;
+    const bool last_of_seq = ti.j_last & 1;
     const uint32_t stage = stage0 + (uint32_t)((i % NS) * kStageBytes);
-    // stage (i - 1) % NS is free: every wave passed this tile's barrier
-    if (i + NS - 1 < n)
-      issue_tile(p, stage0 + (uint32_t)(((i + NS - 1) % NS) * kStageBytes),
-                 s_tile[x + NS - 1 - c0], wave, lane);
+    if (b != cur_b) start_piece(b, j);   // a new piece
 
-    if (b != cur_b) {           // a new piece: load this sequence's queries
-      cur_b = b;
-      piece_first = j;
-      m_run = -INFINITY;
-      l_run = 0.f;
+    // Tile i + NS - 1 goes to stage (i - 1) % NS, free now: every wave has
+    // passed this tile's barrier.  A whole contiguous tile is issued one
+    // instruction every kDmaEvery k-steps of the score loop, so that the
+    // workgroup's 36 instructions do not all queue at the same moment;
+    // other tiles (and waves without score work) issue theirs here.
+    const uint32_t stage_next = stage0 + (uint32_t)(((i + NS - 1) % NS) * kStageBytes);
+    const uint8_t* run = nullptr;
+    if (i + NS - 1 < n) {
+      const TileInfo tn = s_tile[x + NS - 1 - c0];
+      run = tile_run(p, tn);
+      if (!run) {
+        issue_tile(p, stage_next, tn, wave, lane);
+      } else if (!score_active) {
+        const int ln = opaque(lane);
 #pragma unroll
-      for (int m = 0; m < kAccBlocks; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int ln = opaque(lane), h = hbase + (ln & 15);
-      if (score_active && h < p.n_h) {
-        const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(p.q + ((int64_t)b * p.n_h + h) * kDk + 8 * (ln >> 4));
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = qp[4 * ks];
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = bf16x8_t{};
+        for (int d = 0; d < kDmaMax; ++d) dma_run(run, stage_next, wave, d, ln);
+        run = nullptr;
       }
-      // The query loads complete here, in a wait the compiler sees: otherwise
-      // it spreads waits for them over the score loop on every tile's path,
-      // ending in vmcnt(0), which also waits for the DMA of the next tiles.
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
     // ---- scores of this wave's 16 heads: S^T = K Q^T, two 16-token blocks ----
@@ -359,6 +399,8 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
       }
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
+        if (ks % kDmaEvery == 0 && ks / kDmaEvery < kDmaMax && run)
+          dma_run(run, stage_next, wave, ks / kDmaEvery, ln);
         if (ks + kKAhead < kKSteps) {
           ka0[ks + kKAhead] = kread(ks + kKAhead, 0);
           ka1[ks + kKAhead] = kread(ks + kKAhead, 1);
@@ -464,9 +506,8 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
     }
 
     // ---- end of a piece: finish the sequence or leave a partial ----
-    const int nt = s_pref[b + 1] - s_pref[b];
-    if (j == nt - 1 || i == n - 1) {
-      const bool whole = piece_first == 0 && j == nt - 1;
+    if (last_of_seq || i == n - 1) {
+      const bool whole = piece_first == 0 && last_of_seq;
       if (piece_first == 0 && tid == 0) {
         // the workgroup holding the first tile records which workgroups
         // hold the sequence (for the combine step)
@@ -497,11 +538,8 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
 #pragma unroll
             for (int cb = 0; cb < kColBlocksPerWave; ++cb) {
               const f32x4_t a = acc[hb * kColBlocksPerWave + cb];
-              const uint32_t lo = (uint32_t)dev::f32_to_bf16_rne(a[0] * inv) |
-                                  ((uint32_t)dev::f32_to_bf16_rne(a[1] * inv) << 16);
-              const uint32_t hi = (uint32_t)dev::f32_to_bf16_rne(a[2] * inv) |
-                                  ((uint32_t)dev::f32_to_bf16_rne(a[3] * inv) << 16);
-              *reinterpret_cast<dev::u32x2_t*>(orow + 16 * cb) = dev::u32x2_t{lo, hi};
+              *reinterpret_cast<dev::u32x2_t*>(orow + 16 * cb) =
+                  dev::u32x2_t{pack_bf16(a[0] * inv, a[1] * inv), pack_bf16(a[2] * inv, a[3] * inv)};
             }
           }
         }
@@ -512,9 +550,8 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
                                    kAccBlocks * 64 + ln) * 4;
 #pragma unroll
         for (int a = 0; a < kAccBlocks; ++a) {
-          const uint32_t lo = (uint32_t)dev::f32_to_bf16_rne(acc[a][0]) | ((uint32_t)dev::f32_to_bf16_rne(acc[a][1]) << 16);
-          const uint32_t hi = (uint32_t)dev::f32_to_bf16_rne(acc[a][2]) | ((uint32_t)dev::f32_to_bf16_rne(acc[a][3]) << 16);
-          *reinterpret_cast<dev::u32x2_t*>(po + a * 64 * 4) = dev::u32x2_t{lo, hi};
+          *reinterpret_cast<dev::u32x2_t*>(po + a * 64 * 4) =
+              dev::u32x2_t{pack_bf16(acc[a][0], acc[a][1]), pack_bf16(acc[a][2], acc[a][3])};
         }
       }
       cur_b = -1;
@@ -588,9 +625,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(MlaParams 
     M = mc;
   }
   const float inv = 1.f / L;
-  const uint32_t lo = (uint32_t)dev::f32_to_bf16_rne(o0 * inv) | ((uint32_t)dev::f32_to_bf16_rne(o1 * inv) << 16);
-  const uint32_t hi = (uint32_t)dev::f32_to_bf16_rne(o2 * inv) | ((uint32_t)dev::f32_to_bf16_rne(o3 * inv) << 16);
-  *reinterpret_cast<dev::u32x2_t*>(orow) = dev::u32x2_t{lo, hi};
+  *reinterpret_cast<dev::u32x2_t*>(orow) = dev::u32x2_t{pack_bf16(o0 * inv, o1 * inv), pack_bf16(o2 * inv, o3 * inv)};
 }
 
 constexpr int kMlaStages = 3;
