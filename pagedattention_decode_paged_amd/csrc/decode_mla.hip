@@ -405,6 +405,9 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
           ka0[ks + kKAhead] = kread(ks + kKAhead, 0);
           ka1[ks + kKAhead] = kread(ks + kKAhead, 1);
         }
+        // the reads for the coming k-steps are issued before this step's
+        // matrix instructions, which then cover their latency
+        __builtin_amdgcn_sched_barrier(0);
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[ks], qf[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[ks], qf[ks], s1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
