@@ -5,10 +5,11 @@ Default workload: 70B-shaped decode, bf16, B=16, n_h=64, n_kv=8, d_h=128,
 every context 8192 tokens, block 16, 80 layers, each layer its own pool of
 8192 randomly permuted physical blocks (40 GiB of K+V in HBM).  One step is
 the whole decode step of the path over the 80 layers: for each layer the new
-token's K/V is written through reshape_and_cache (position 8191 of every
-sequence, overwritten each step) and paged_decode_attention runs over the
-layer's cache.  Inputs are seeded N(0,1) synthetic data resident in HBM
-before timing starts.
+token's K/V is written at position 8191 of every sequence (overwritten each
+step) and the attention runs over the layer's cache, both in one
+paged_decode_attention_append call (--separate-calls: reshape_and_cache,
+then paged_decode_attention).  Inputs are seeded N(0,1) synthetic data
+resident in HBM before timing starts.
 
 Prints one JSON line:  KV GB/s (value), % of the 8 TB/s HBM peak, tokens/s,
 token*heads/s, a roofline record of the dominant kernel (timed with HIP
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=80, help="layers of the 70B-shaped model (80)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library's automatic split")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="step = reshape_and_cache + paged_decode_attention per layer (not the one-call append)")
     ap.add_argument("--kernel-reps", type=int, default=3,
                     help="passes over the layers when timing the attention kernel alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -110,7 +113,7 @@ def main():
         layers.append(dict(pool=pool, q=q, k_new=kv_new[0], v_new=kv_new[1], bt=bt, ctx=ctx,
                            slots=slots, out=out, s=s))
     ws_bytes = 0
-    calls_rc, calls_dec = [], []
+    calls_rc, calls_dec, calls_app = [], [], []
     workspace = None
     for ly in layers:
         desc = pk.make_desc(B=B, n_h=n_h, n_kv=n_kv, d_k=d, d_v=d, block_size=bs,
@@ -120,6 +123,9 @@ def main():
         if workspace is None and ws_bytes:
             workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
         calls_rc.append(pk.prepare_reshape_and_cache(ly["pool"], ly["k_new"], ly["v_new"], ly["slots"]))
+        calls_app.append(pk.prepare_decode_append(ly["pool"], ly["q"], ly["k_new"], ly["v_new"], ly["bt"],
+                                                  ly["ctx"], cfg.scale, ly["out"], max_context_len=8192,
+                                                  split_tokens=args.split_tokens, workspace=workspace))
         calls_dec.append(pk.prepare_decode(ly["q"], ly["pool"].k, ly["pool"].v, ly["bt"], ly["ctx"],
                                            cfg.scale, ly["out"], max_context_len=8192,
                                            split_tokens=args.split_tokens, workspace=workspace))
@@ -129,9 +135,14 @@ def main():
     torch.cuda.synchronize()
 
     def step():
-        for rc, dec in zip(calls_rc, calls_dec):
-            rc()
-            dec()
+        if args.separate_calls:
+            for rc, dec in zip(calls_rc, calls_dec):
+                rc()
+                dec()
+        else:
+            for app in calls_app:
+                app()
+    calls_attn = calls_dec if args.separate_calls else calls_app
 
     stream = torch.cuda.current_stream(dev)
     run = step
@@ -168,8 +179,8 @@ def main():
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
     for _ in range(reps):
-        for dec in calls_dec:
-            dec()
+        for c in calls_attn:
+            c()
     k1.record(stream)
     torch.cuda.synchronize()
     us_launch = 1e3 * k0.elapsed_time(k1) / (reps * L)
@@ -197,20 +208,25 @@ def main():
         "config": {"workload": "70B-shaped paged decode attention, 80 layers",
                    "B": B, "n_h": n_h, "n_kv": n_kv, "d_h": d, "context": 8192, "block_size": bs,
                    "layers": L, "kv_bytes_per_step": kv_bytes_step, "split_tokens": split,
-                   "graph": bool(args.graph), "parallelism": "single GPU"},
+                   "graph": bool(args.graph),
+                   "step": ("reshape_and_cache + paged_decode_attention" if args.separate_calls
+                            else "paged_decode_attention_append"),
+                   "parallelism": "single GPU"},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_per_s, 1),
         "token_heads_per_s": float(f"{tok_heads:.4g}"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "paged_decode_attention: decode_gqa_ring_kernel<128,8,8,2> + decode_reduce_kernel",
+                     "kernel": ("paged_decode_attention" if args.separate_calls else
+                                "paged_decode_attention_append (the ring kernel writes the new rows)") +
+                               ": decode_gqa_ring_kernel<128,8,8,2> + decode_reduce_kernel",
                      "avg_launch_us": round(us_launch, 2),
                      "bytes_per_launch": kv_bytes_layer},
     }
 
     if not args.headline_only:
-        del layers, calls_rc, calls_dec
+        del layers, calls_rc, calls_dec, calls_app, calls_attn
         torch.cuda.empty_cache()
         result["secondary"] = [bench_llama8b(dev), bench_int8(dev), bench_mla(dev)]
     if not args.no_cpu_baseline:

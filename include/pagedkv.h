@@ -235,6 +235,33 @@ kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
                                       float scale, void* out, const kvp_decode_desc* desc,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step in one call (qwbw 1.2: each step appends the new token's
+ * K/V, then attends over the whole cache; talentme chapter 3, write_kv
+ * followed by the paged attention): writes the new row of every sequence b
+ * at position context_lens[b] - 1 (its slot read from block_table), then
+ * computes exactly what paged_decode_attention (or _int8 / _mla, chosen by
+ * the pool) computes.  Same result, bit for bit, as paged_slot_mapping +
+ * reshape_and_cache + the decode call.
+ *   pool:  the pool both reads and writes (its n_kv, d_k, d_v, block_size
+ *          and dtype must equal desc's; a latent pool goes with an MLA desc)
+ *   k_new: device [B, n_kv, d_k] rows in desc->q_dtype (quantized on write
+ *          for an INT8 pool), 16-byte aligned; v_new: [B, n_kv, d_v], NULL
+ *          for a latent pool
+ *   q, block_table, context_lens, scale, out, workspace: as for the decode
+ *          call of the pool's kind.
+ * Precondition (the usual decode step): no other sequence of the call reads
+ * the slot a sequence appends to.  For bf16 pools with g in {4, 8} the rows
+ * are written by the attention kernel itself (one launch); otherwise by the
+ * cache kernel just before it.  A sequence with context_lens[b] = 0, or
+ * whose last position maps to no block, appends nothing.  Errors as for
+ * the decode calls, plus KVP_ERR_INVALID_ARG for a NULL pool or rows, a
+ * pool that does not match desc, or misaligned rows. */
+kvp_status paged_decode_attention_append(kvp_pool* pool, const void* q, const void* k_new,
+                                         const void* v_new, const int32_t* block_table,
+                                         const int32_t* context_lens, float scale, void* out,
+                                         const kvp_decode_desc* desc, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Gather (qwbw 3.4: read each physical block through the table): copies
  * rows 0 .. context_lens[b]-1 of every sequence, bit for bit, into

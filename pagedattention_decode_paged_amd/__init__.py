@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
         "paged_decode_attention_int8": (ctypes.c_int, [P, P, P, P, P, P, P, F, P,
                                                        ctypes.POINTER(_DecodeDesc), P, SZ, P]),
         "paged_decode_attention_mla": (ctypes.c_int, [P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc), P, SZ, P]),
+        "paged_decode_attention_append": (ctypes.c_int, [P, P, P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc),
+                                                         P, SZ, P]),
         "paged_gather": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P]),
         "paged_decode_validate": (ctypes.c_int, [P, P, ctypes.POINTER(_DecodeDesc), I64, P]),
     }
@@ -92,7 +94,7 @@ EXPORTED_SYMBOLS = (
     "kv_pool_view_get", "paged_slot_mapping", "reshape_and_cache", "paged_decode_workspace_size",
     "paged_decode_split_tokens", "paged_decode_mla_workgroups", "paged_decode_attention",
     "paged_decode_attention_int8",
-    "paged_decode_attention_mla", "paged_gather", "paged_decode_validate",
+    "paged_decode_attention_mla", "paged_decode_attention_append", "paged_gather", "paged_decode_validate",
 )
 
 
@@ -338,6 +340,31 @@ def paged_decode_attention_mla(q, latent_pool, block_table, context_lens, scale,
     return out
 
 
+def _append_desc(pool: KVPool, q, block_table, context_lens, max_context_len, split_tokens,
+                 total_context_len, workgroups) -> _DecodeDesc:
+    kv = KVP_INT8 if pool.dtype == torch.int8 else _TORCH_TO_KVP[pool.dtype]
+    return _desc(q, block_table, context_lens, pool.n_kv, pool.d_k, pool.d_v, pool.block_size, kv,
+                 max_context_len, split_tokens, total_context_len, workgroups)
+
+
+def paged_decode_attention_append(pool: KVPool, q, k_new, v_new, block_table, context_lens, scale,
+                                  out=None, *, max_context_len, split_tokens=0, total_context_len=0,
+                                  workgroups=0, workspace=None):
+    """One decode step: write each sequence's new K/V row (``k_new``/``v_new``
+    ``[B, n_kv, d]`` in q's dtype; ``v_new`` None for a latent pool) at position
+    ``context_lens[b] - 1``, then attend (the decode call of the pool's kind)."""
+    dev = _need_cuda(q, k_new, block_table, context_lens)
+    desc = _append_desc(pool, q, block_table, context_lens, max_context_len, split_tokens,
+                        total_context_len, workgroups)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], pool.d_v), dtype=q.dtype, device=dev)
+    ws, wsb = _workspace(desc, workspace, dev)
+    _check(_lib.paged_decode_attention_append(pool.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                              _ptr(block_table), _ptr(context_lens), float(scale),
+                                              _ptr(out), ctypes.byref(desc), _ptr(ws), wsb, _stream(dev)))
+    return out
+
+
 def make_desc(*, B, n_h, n_kv, d_k, d_v, block_size, max_blocks_per_seq, max_context_len,
               q_dtype, kv_dtype, split_tokens=0, total_context_len=0, workgroups=0) -> _DecodeDesc:
     """A decode description from plain values (dtype codes KVP_F32/BF16/INT8)."""
@@ -387,3 +414,16 @@ def prepare_reshape_and_cache(pool: KVPool, k_new, v_new, slot_mapping) -> Prepa
     n = slot_mapping.numel()
     args = (pool.handle, _ptr(k_new), _ptr(v_new), _TORCH_TO_KVP[k_new.dtype], _ptr(slot_mapping), n, None)
     return PreparedCall(_lib.reshape_and_cache, args, dev, (pool, k_new, v_new, slot_mapping))
+
+
+def prepare_decode_append(pool: KVPool, q, k_new, v_new, block_table, context_lens, scale, out, *,
+                          max_context_len, split_tokens=0, total_context_len=0,
+                          workspace=None) -> PreparedCall:
+    dev = _need_cuda(q, k_new, block_table, context_lens, out)
+    desc = _append_desc(pool, q, block_table, context_lens, max_context_len, split_tokens,
+                        total_context_len, 0)
+    ws, wsb = _workspace(desc, workspace, dev)
+    args = (pool.handle, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(context_lens),
+            ctypes.c_float(scale), _ptr(out), ctypes.byref(desc), _ptr(ws), wsb, None)
+    return PreparedCall(_lib.paged_decode_attention_append, args, dev,
+                        (pool, q, k_new, v_new, block_table, context_lens, out, ws, desc))

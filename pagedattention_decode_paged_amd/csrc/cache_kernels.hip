@@ -37,10 +37,10 @@ struct CopyJob {
 };
 
 template <typename V>
-__global__ void cache_copy_kernel(CopyJob k, CopyJob v, const int64_t* __restrict__ slots) {
+__global__ void cache_copy_kernel(CopyJob k, CopyJob v, SlotSource slots) {
   const CopyJob j = blockIdx.y == 0 ? k : v;
   const int64_t t = blockIdx.x;
-  const int64_t s = slots[t];
+  const int64_t s = slot_of(slots, t);
   if (s < 0) return;
   const V* in = reinterpret_cast<const V*>(j.src + t * j.row_bytes);
   V* out = reinterpret_cast<V*>(j.pool + s * j.row_bytes);
@@ -67,9 +67,8 @@ struct QuantJob {
   int32_t d;
 };
 
-__global__ void cache_quant_int8_kernel(QuantJob kj, QuantJob vj, int bf16,
-                                        const int64_t* __restrict__ slots, int64_t num_rows,
-                                        int32_t n_kv) {
+__global__ void cache_quant_int8_kernel(QuantJob kj, QuantJob vj, int bf16, SlotSource slots,
+                                        int64_t num_rows, int32_t n_kv) {
   const QuantJob j = blockIdx.y == 0 ? kj : vj;
   const int32_t d = j.d;
   int8_t* __restrict__ codes = j.codes;
@@ -80,7 +79,7 @@ __global__ void cache_quant_int8_kernel(QuantJob kj, QuantJob vj, int bf16,
   if (row >= num_rows) return;
   const int64_t t = row / n_kv;
   const int32_t h = (int32_t)(row - t * n_kv);
-  const int64_t s = slots[t];
+  const int64_t s = slot_of(slots, t);
   if (s < 0) return;
   const int64_t in_base = row * d;
   float amax = 0.f;
@@ -132,7 +131,7 @@ hipError_t launch_slot_mapping(const int32_t* block_table, int32_t mb, int32_t s
 }
 
 hipError_t launch_cache_copy(void* k_pool, const void* k_src, int64_t k_row_bytes, void* v_pool,
-                             const void* v_src, int64_t v_row_bytes, const int64_t* slots,
+                             const void* v_src, int64_t v_row_bytes, const SlotSource& slots,
                              int64_t num_tokens, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const bool two = v_pool != nullptr;
@@ -154,7 +153,7 @@ hipError_t launch_cache_copy(void* k_pool, const void* k_src, int64_t k_row_byte
 
 hipError_t launch_cache_quant_int8(int8_t* k_codes, float* k_scales, const void* k_src, int32_t d_k,
                                    int8_t* v_codes, float* v_scales, const void* v_src, int32_t d_v,
-                                   bool src_bf16, const int64_t* slots, int64_t num_tokens,
+                                   bool src_bf16, const SlotSource& slots, int64_t num_tokens,
                                    int32_t n_kv, hipStream_t stream) {
   const int64_t rows = num_tokens * n_kv;
   if (rows == 0) return hipSuccess;

@@ -543,6 +543,9 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
       (p.split_tokens >> p.block_shift) > kBtSlots)
     return hipErrorInvalidValue;
   const int g = p.n_h / p.n_kv;
+  // only the bf16 LDS-ring kernel writes appended rows itself
+  if (p.k_new && !(p.kv == KV::BF16 && gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)))
+    return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
   if (gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)) {
     e = launch_decode_gqa_ring(p, stream);

@@ -61,6 +61,9 @@
 #ifndef PKV_G4_RING
 #define PKV_G4_RING 2
 #endif
+#ifndef PKV_Q8_G8_NW
+#define PKV_Q8_G8_NW 8
+#endif
 #ifndef PKV_Q8_G8_RING
 #define PKV_Q8_G8_RING 2
 #endif
@@ -126,6 +129,10 @@ __device__ __forceinline__ void wait_vm(int n) {
   if (n >= 32) n = 0;                             // stricter than needed, never looser
   wait_vm_sel(n, std::make_integer_sequence<int, 32>{});
 }
+
+// s_waitcnt immediate with vmcnt = 0 and the other counters at their
+// maximum (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // LDS DMA, 16 (or 4) bytes per lane to LDS m0 + 16 (or 4) * lane.  The
 // address is either a per-lane 64-bit pointer or a wave-uniform 64-bit base
@@ -213,6 +220,29 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   __syncthreads();
 
   const int64_t slot_stride = (int64_t)p.n_kv * R::kSrcRow;
+  if constexpr (!Q8) {
+    if (p.k_new != nullptr && t_end == ctx) {
+      // Append: the workgroup holding the sequence's last token writes that
+      // token's new K and V rows (this KV head) into its slot, and the store
+      // completes before any of the workgroup's DMA can read the slot.
+      if (wave == 0) {
+        constexpr int kLanesPerRow = R::kSrcRow / 16;       // 16-byte pieces per row
+        const int m = lane / kLanesPerRow, piece = lane % kLanesPerRow;
+        const int32_t phys = s_bt[(t_last >> shift) - lb0];
+        if (m < 2 && phys >= 0) {                            // an unmapped block is skipped
+          const int64_t sl = ((int64_t)phys << shift) + (t_last & bmask);
+          const int64_t off = (int64_t)kvh * R::kSrcRow + piece * 16;
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(m ? p.v_new : p.k_new) +
+                               ((int64_t)b * p.n_kv) * R::kSrcRow + off;
+          uint8_t* dst = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(m ? p.v : p.k)) +
+                         sl * slot_stride + off;
+          *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
+      __syncthreads();
+    }
+  }
   const int n_stages = (t_end - t_begin + kStageTok - 1) / kStageTok;
 
   // ---- this wave's DMA share: instructions j0 .. j0 + kDmaPerWave - 1 of a
@@ -530,9 +560,9 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
     else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_G4_RING, false);
     else return hipErrorInvalidValue;
   } else {
-    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, 8, PKV_Q8_G8_RING, true);
+    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true);
     else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_Q8_G4_RING, true);
-    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, 8, PKV_Q8_G8_RING, true);
+    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true);
     else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_Q8_G4_RING, true);
     else return hipErrorInvalidValue;
   }

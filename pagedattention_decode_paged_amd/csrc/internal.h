@@ -14,17 +14,40 @@ hipError_t launch_slot_mapping(const int32_t* block_table, int32_t max_blocks_pe
                                const int32_t* positions, int64_t num_tokens,
                                int64_t* slots, hipStream_t stream);
 
+// Where the rows of the new tokens go: an explicit slot per token, or (slots
+// null) one token per sequence t at position context_lens[t] - 1, its slot
+// read from the block table.  A negative slot (or a position or block the
+// table does not map) skips the token.
+struct SlotSource {
+  const int64_t* slots;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int32_t max_blocks_per_seq;
+  int32_t block_shift;
+};
+
+__device__ __forceinline__ int64_t slot_of(const SlotSource& s, int64_t t) {
+  if (s.slots) return s.slots[t];
+  const int32_t pos = s.context_lens[t] - 1;
+  if (pos < 0) return -1;
+  const int32_t lb = pos >> s.block_shift;
+  if (lb >= s.max_blocks_per_seq) return -1;
+  const int32_t phys = s.block_table[t * s.max_blocks_per_seq + lb];
+  if (phys < 0) return -1;
+  return ((int64_t)phys << s.block_shift) + (pos & ((1 << s.block_shift) - 1));
+}
+
 // Bit copy of the K rows (and V rows when v_pool is not null) of num_tokens
 // tokens into their slots, one launch (row bytes % 4 == 0).
 hipError_t launch_cache_copy(void* k_pool, const void* k_src, int64_t k_row_bytes, void* v_pool,
-                             const void* v_src, int64_t v_row_bytes, const int64_t* slots,
+                             const void* v_src, int64_t v_row_bytes, const SlotSource& slots,
                              int64_t num_tokens, hipStream_t stream);
 
 // Quantize-on-write of K and V, one launch: src rows [num_tokens, n_kv, d]
 // (f32 or bf16 bits), codes [slots, n_kv, d] int8, scales [slots, n_kv] f32.
 hipError_t launch_cache_quant_int8(int8_t* k_codes, float* k_scales, const void* k_src, int32_t d_k,
                                    int8_t* v_codes, float* v_scales, const void* v_src, int32_t d_v,
-                                   bool src_bf16, const int64_t* slots, int64_t num_tokens,
+                                   bool src_bf16, const SlotSource& slots, int64_t num_tokens,
                                    int32_t n_kv, hipStream_t stream);
 
 hipError_t launch_gather(const void* pool, int64_t row_bytes, int32_t block_shift,
@@ -58,6 +81,11 @@ struct DecodeParams {
   // record of which workgroups hold a sequence ([B, 2], in the workspace).
   int32_t workgroups;
   int32_t* seq_meta;
+  // Append (bf16 LDS-ring kernel only; null otherwise): the new token's K and
+  // V rows [B, n_kv, d], written by the kernel to position context_lens[b] - 1
+  // of each sequence (k and v above then point at writable pools).
+  const void* k_new;
+  const void* v_new;
 };
 
 // GQA/MQA/MHA over float or INT8 pools (VALU kernels).  Returns

@@ -190,37 +190,6 @@ kvp_status paged_slot_mapping(const int32_t* block_table, int32_t max_blocks_per
                     "paged_slot_mapping");
 }
 
-kvp_status reshape_and_cache(kvp_pool* pool, const void* k_new, const void* v_new,
-                             kvp_dtype in_dtype, const int64_t* slot_mapping, int64_t num_tokens,
-                             void* stream) {
-  if (!pool) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: pool is NULL");
-  if (num_tokens < 0) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: num_tokens < 0");
-  if (num_tokens == 0) return ok();
-  const kvp_pool_desc& d = pool->desc;
-  if (!k_new || !slot_mapping) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: NULL pointer");
-  if (!d.latent && !v_new) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: v_new is NULL");
-  if (!dtype_valid(in_dtype)) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: unknown in_dtype");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  kvp_pool_view v;
-  kv_pool_view_get(pool, &v);
-  if (d.dtype == KVP_INT8) {
-    if (in_dtype == KVP_INT8) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: INT8 pools take F32 or BF16 rows");
-    const bool bf = in_dtype == KVP_BF16;
-    return hip_status(pkv::launch_cache_quant_int8(static_cast<int8_t*>(v.k), v.k_scale, k_new, d.d_k,
-                                                  static_cast<int8_t*>(v.v), v.v_scale, v_new, d.d_v,
-                                                  bf, slot_mapping, num_tokens, d.n_kv, st),
-                      "reshape_and_cache");
-  }
-  if (in_dtype != d.dtype)
-    return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: rows must have the pool's dtype");
-  const size_t eb = dtype_bytes(d.dtype);
-  // K and V rows in one launch (a latent pool has no V region)
-  return hip_status(pkv::launch_cache_copy(v.k, k_new, (int64_t)d.n_kv * d.d_k * eb,
-                                           d.latent ? nullptr : v.v, v_new,
-                                           (int64_t)d.n_kv * d.d_v * eb, slot_mapping, num_tokens, st),
-                    "reshape_and_cache");
-}
-
 }  // extern "C"
 
 // ---------------------------------------------------------------- decode
@@ -411,11 +380,47 @@ kvp_status launch_mla(const char* fn, const void* q, const void* pool, const int
   return hip_status(pkv::launch_decode_mla(p, static_cast<hipStream_t>(stream)), fn);
 }
 
+// Rows of new tokens into a pool (reshape_and_cache, and the append path
+// of paged_decode_attention_append when the decode kernel does not write
+// them itself): bit copy for float pools, quantize-on-write for INT8.
+kvp_status write_rows(kvp_pool* pool, const void* k_new, const void* v_new, kvp_dtype in_dtype,
+                      const pkv::SlotSource& slots, int64_t num_tokens, void* stream, const char* fn) {
+  const kvp_pool_desc& d = pool->desc;
+  if (!k_new) return fail(KVP_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!d.latent && !v_new) return fail(KVP_ERR_INVALID_ARG, "%s: v_new is NULL", fn);
+  if (!dtype_valid(in_dtype)) return fail(KVP_ERR_INVALID_ARG, "%s: unknown in_dtype", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  kvp_pool_view v;
+  kv_pool_view_get(pool, &v);
+  if (d.dtype == KVP_INT8) {
+    if (in_dtype == KVP_INT8) return fail(KVP_ERR_INVALID_ARG, "%s: INT8 pools take F32 or BF16 rows", fn);
+    const bool bf = in_dtype == KVP_BF16;
+    return hip_status(pkv::launch_cache_quant_int8(static_cast<int8_t*>(v.k), v.k_scale, k_new, d.d_k,
+                                                  static_cast<int8_t*>(v.v), v.v_scale, v_new, d.d_v,
+                                                  bf, slots, num_tokens, d.n_kv, st),
+                      fn);
+  }
+  if (in_dtype != d.dtype) return fail(KVP_ERR_INVALID_ARG, "%s: rows must have the pool's dtype", fn);
+  const size_t eb = dtype_bytes(d.dtype);
+  // K and V rows in one launch (a latent pool has no V region)
+  return hip_status(pkv::launch_cache_copy(v.k, k_new, (int64_t)d.n_kv * d.d_k * eb,
+                                           d.latent ? nullptr : v.v, v_new,
+                                           (int64_t)d.n_kv * d.d_v * eb, slots, num_tokens, st),
+                    fn);
+}
+
+// The append request of paged_decode_attention_append (null for a plain decode).
+struct AppendRows {
+  kvp_pool* pool;
+  const void* k_new;
+  const void* v_new;
+};
+
 kvp_status decode_common(Variant var, const char* fn, const void* q, const void* k,
                          const void* v, const float* ks, const float* vs,
                          const int32_t* block_table, const int32_t* context_lens, float scale,
                          void* out, const kvp_decode_desc* d, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream, const AppendRows* app = nullptr) {
   if (const char* e = decode_desc_error(d)) return fail(KVP_ERR_INVALID_ARG, "%s: %s", fn, e);
   if (variant_of(d) != var) {
     if (var == Variant::Int8) return fail(KVP_ERR_INVALID_ARG, "%s: desc->kv_dtype must be KVP_INT8", fn);
@@ -452,6 +457,22 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
     if (d->kv_dtype != KVP_BF16 || !q_bf16 || !pkv::mla_supported(d->d_k, d->d_v, d->n_h, d->block_size))
       return fail(KVP_ERR_UNSUPPORTED, "%s: no MLA kernel for n_h %d, d_k %d, d_v %d, block %d", fn,
                   d->n_h, d->d_k, d->d_v, d->block_size);
+  }
+
+  // Append: the bf16 LDS-ring kernel writes the new rows itself (one launch);
+  // every other kernel gets them from the cache kernel first.
+  const bool fused_append = app && var == Variant::Float && d->kv_dtype == KVP_BF16 && q_bf16 &&
+                            pkv::gqa_ring_supported(pkv::KV::BF16, true, d->d_k, d->d_v, g);
+  if (app && !fused_append) {
+    if (!aligned(app->k_new, 4) || (app->v_new && !aligned(app->v_new, 4)))
+      return fail(KVP_ERR_INVALID_ARG, "%s: k_new and v_new must be 4-byte aligned", fn);
+    pkv::SlotSource src{};
+    src.block_table = block_table;
+    src.context_lens = context_lens;
+    src.max_blocks_per_seq = d->max_blocks_per_seq;
+    src.block_shift = log2i(d->block_size);
+    const kvp_status rc = write_rows(app->pool, app->k_new, app->v_new, d->q_dtype, src, d->B, stream, fn);
+    if (rc != KVP_OK) return rc;
   }
 
   if (var == Variant::Mla) return launch_mla(fn, q, k, block_table, context_lens, scale, out, d,
@@ -499,6 +520,10 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   p.num_splits = ns;
   p.q_bf16 = q_bf16;
   p.kv = var == Variant::Int8 ? pkv::KV::INT8 : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
+  if (fused_append) {
+    p.k_new = app->k_new;
+    p.v_new = app->v_new;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(pkv::launch_decode_gqa(p, st), fn);
 }
@@ -506,6 +531,18 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
 }  // namespace
 
 extern "C" {
+
+kvp_status reshape_and_cache(kvp_pool* pool, const void* k_new, const void* v_new,
+                             kvp_dtype in_dtype, const int64_t* slot_mapping, int64_t num_tokens,
+                             void* stream) {
+  if (!pool) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: pool is NULL");
+  if (num_tokens < 0) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: num_tokens < 0");
+  if (num_tokens == 0) return ok();
+  if (!slot_mapping) return fail(KVP_ERR_INVALID_ARG, "reshape_and_cache: NULL pointer");
+  pkv::SlotSource src{};
+  src.slots = slot_mapping;
+  return write_rows(pool, k_new, v_new, in_dtype, src, num_tokens, stream, "reshape_and_cache");
+}
 
 size_t paged_decode_workspace_size(const kvp_decode_desc* desc) {
   if (decode_desc_error(desc)) return 0;
@@ -549,6 +586,38 @@ kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
   return decode_common(Variant::Mla, "paged_decode_attention_mla", q, latent_pool, latent_pool,
                        nullptr, nullptr, block_table, context_lens, scale, out, desc, workspace,
                        workspace_bytes, stream);
+}
+
+kvp_status paged_decode_attention_append(kvp_pool* pool, const void* q, const void* k_new,
+                                         const void* v_new, const int32_t* block_table,
+                                         const int32_t* context_lens, float scale, void* out,
+                                         const kvp_decode_desc* desc, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  const char* fn = "paged_decode_attention_append";
+  if (!pool) return fail(KVP_ERR_INVALID_ARG, "%s: pool is NULL", fn);
+  if (const char* e = decode_desc_error(desc)) return fail(KVP_ERR_INVALID_ARG, "%s: %s", fn, e);
+  const kvp_pool_desc& pd = pool->desc;
+  if (pd.n_kv != desc->n_kv || pd.d_k != desc->d_k || pd.d_v != desc->d_v ||
+      pd.block_size != desc->block_size || pd.dtype != desc->kv_dtype)
+    return fail(KVP_ERR_INVALID_ARG, "%s: the pool's n_kv, d_k, d_v, block_size or dtype differs from desc", fn);
+  const Variant var = variant_of(desc);
+  if (pd.latent != (var == Variant::Mla))
+    return fail(KVP_ERR_INVALID_ARG, "%s: a latent pool goes with an MLA description and only with one", fn);
+  if (desc->B == 0) return ok();
+  if (!k_new || (!pd.latent && !v_new)) return fail(KVP_ERR_INVALID_ARG, "%s: NULL k_new or v_new", fn);
+  if (!aligned(k_new, 16) || (!pd.latent && !aligned(v_new, 16)))
+    return fail(KVP_ERR_INVALID_ARG, "%s: k_new and v_new must be 16-byte aligned", fn);
+  kvp_pool_view v;
+  kv_pool_view_get(pool, &v);
+  const AppendRows app{pool, k_new, pd.latent ? nullptr : v_new};
+  if (var == Variant::Int8)
+    return decode_common(var, fn, q, v.k, v.v, v.k_scale, v.v_scale, block_table, context_lens, scale,
+                         out, desc, workspace, workspace_bytes, stream, &app);
+  if (var == Variant::Mla)
+    return decode_common(var, fn, q, v.k, v.k, nullptr, nullptr, block_table, context_lens, scale, out,
+                         desc, workspace, workspace_bytes, stream, &app);
+  return decode_common(var, fn, q, v.k, v.v, nullptr, nullptr, block_table, context_lens, scale, out,
+                       desc, workspace, workspace_bytes, stream, &app);
 }
 
 kvp_status paged_gather(const void* pool, int32_t elem_bytes, int32_t block_size, int32_t n_kv,

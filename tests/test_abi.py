@@ -146,3 +146,33 @@ def test_cache_ops_reject_bad_arguments_on_host():
     assert lib.paged_gather(P(16), 3, 16, 2, 64, P(16), 4, P(16), 2, 50, P(16), None) == pk.KVP_ERR_INVALID_ARG
     assert lib.paged_gather(P(16), 4, 16, 2, 64, P(16), 4, P(16), 2, 65, P(16), None) == pk.KVP_ERR_INVALID_ARG
     assert lib.kv_pool_create(None, None, 0, ctypes.byref(P())) == pk.KVP_ERR_INVALID_ARG
+
+
+def test_append_rejects_bad_arguments_on_host():
+    """paged_decode_attention_append checks the pool against the description
+    and its row pointers before any device work (a pool handle over
+    caller-given storage touches no device memory)."""
+    lib = pk.lib()
+    P = ctypes.c_void_p
+    pd = pk._PoolDesc(64, 16, 8, 128, 128, pk.KVP_BF16, 0)
+    need = lib.kv_pool_required_bytes(ctypes.byref(pd))
+    handle = P()
+    assert lib.kv_pool_create(ctypes.byref(pd), P(1 << 20), need, ctypes.byref(handle)) == pk.KVP_OK
+
+    def call(desc, pool=handle, k_new=P(4096), v_new=P(4096)):
+        return lib.paged_decode_attention_append(pool, P(4096), k_new, v_new, P(4096), P(4096),
+                                                 ctypes.c_float(0.1), P(4096), ctypes.byref(desc),
+                                                 None, 0, None)
+    try:
+        good = _desc(max_context_len=200)
+        assert call(good, pool=None) == pk.KVP_ERR_INVALID_ARG
+        assert b"pool is NULL" in lib.kvp_last_error()
+        assert call(_desc(max_context_len=200, d_k=64, d_v=64)) == pk.KVP_ERR_INVALID_ARG
+        assert b"differs from desc" in lib.kvp_last_error()
+        assert call(good, k_new=None) == pk.KVP_ERR_INVALID_ARG
+        assert call(good, v_new=P(4100)) == pk.KVP_ERR_INVALID_ARG
+        assert b"16-byte aligned" in lib.kvp_last_error()
+        latent = _desc(n_h=16, n_kv=1, d_k=576, d_v=512, max_context_len=200)
+        assert call(latent) == pk.KVP_ERR_INVALID_ARG
+    finally:
+        lib.kv_pool_destroy(handle)
