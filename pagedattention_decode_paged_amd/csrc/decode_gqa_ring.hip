@@ -171,7 +171,7 @@ __device__ __forceinline__ void widen_codes(const u32x4_t c, u32x4_t& lo, u32x4_
   hi = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
-template <int D, int G, int NW, int RING, bool Q8>
+template <int D, int G, int NW, int RING, bool Q8, bool COMPACT>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodeParams p) {
   using R = Ring<D, NW, Q8>;
   constexpr int kThr = 64 * NW;
@@ -185,17 +185,24 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   __shared__ __align__(16) float s_scl[2][Q8 ? RING : 1][Q8 ? kStageTok : 1];
   __shared__ __align__(16) int32_t s_bt[kBtSlots];
   __shared__ __align__(16) uint32_t s_pp[NW][kHpw][kStageTok / 2];
+  // compact grid only: units before each sequence, and the context lengths
+  __shared__ int32_t s_upre[COMPACT ? kCompactMaxB + 1 : 1];
+  __shared__ int32_t s_ctx[COMPACT ? kCompactMaxB : 1];
 
-  // grid (KV head, sequence, split), KV head fastest: workgroups are dealt
-  // to the 8 XCDs round-robin by linear index, so each XCD serves whole KV
-  // heads (identical work) whatever the context lengths and split count
+  // KV head fastest in the grid: workgroups are dealt to the 8 XCDs
+  // round-robin by linear index, so each XCD serves whole KV heads
+  // (identical work) whatever the context lengths and split count
   const int kvh = blockIdx.x;
-  const int b = blockIdx.y;
-  const int split = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+
+  // ---- one unit of work: split `split` of sequence b (ctx tokens).  In the
+  // compact grid the thread index is an opaque copy, so that the
+  // lane-dependent offsets below are formed per unit rather than hoisted out
+  // of the loop over units and kept live across it.
+  auto unit = [&](const int b, const int split, const int ctx) {
+  int tid = threadIdx.x;
+  if constexpr (COMPACT) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
-  const int ctx = p.context_lens[b];
   const int t_begin = split * p.split_tokens;
   const int n_h = p.n_h;
   const int h0 = kvh * G + wave * kHpw;            // first query head of this wave
@@ -538,6 +545,59 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       }
     }
   }
+  };
+
+  if constexpr (!COMPACT) {
+    // grid (KV head, sequence, split)
+    unit(blockIdx.y, blockIdx.z, p.context_lens[blockIdx.y]);
+  } else {
+    // Grid (KV head, unit) for ragged batches, a unit being one split of one
+    // sequence; an empty sequence has one unit, which zeros its output.
+    // Only units with work are launched, instead of every sequence times the
+    // largest split count.  Wave 0 forms the prefix of the units per
+    // sequence (B <= kCompactMaxB, 8 sequences per lane), and the workgroup
+    // takes units blockIdx.y, blockIdx.y + gridDim.y, ..., so that every
+    // unit is covered whatever grid size the host chose.
+    if (wave == 0) {
+      const int lane = threadIdx.x & 63;
+      int cnt[8];
+      int sum = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sb = 8 * lane + k;
+        const int c = sb < p.B ? p.context_lens[sb] : 0;
+        if (sb < p.B) s_ctx[sb] = c;
+        cnt[k] = sb < p.B ? max(1, (c + p.split_tokens - 1) / p.split_tokens) : 0;
+        sum += cnt[k];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      int run = incl - sum;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        s_upre[8 * lane + k] = run;
+        run += cnt[k];
+      }
+      if (lane == kWave - 1) s_upre[kCompactMaxB] = incl;
+    }
+    __syncthreads();
+    const int n_units = __builtin_amdgcn_readfirstlane(s_upre[p.B]);
+    for (int u = blockIdx.y; u < n_units; u += gridDim.y) {
+      // the sequence whose units hold u: the largest b with s_upre[b] <= u
+      int lo = 0, hi = p.B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_upre[mid] <= u) lo = mid; else hi = mid;
+      }
+      const int b = __builtin_amdgcn_readfirstlane(lo);
+      unit(b, __builtin_amdgcn_readfirstlane(u - s_upre[b]), __builtin_amdgcn_readfirstlane(s_ctx[b]));
+      __syncthreads();                              // the unit's LDS is free again
+    }
+  }
 }
 
 }  // namespace
@@ -548,11 +608,20 @@ bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
 }
 
 hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.n_kv, (unsigned)p.B, (unsigned)p.num_splits);
+  if (p.compact_units != 0 && (p.B > kCompactMaxB || p.compact_units < 0)) return hipErrorInvalidValue;
+  const dim3 grid = p.compact_units != 0 ? dim3((unsigned)p.n_kv, (unsigned)p.compact_units, 1u)
+                                          : dim3((unsigned)p.n_kv, (unsigned)p.B, (unsigned)p.num_splits);
   const int g = p.n_h / p.n_kv;
   const bool q8 = p.kv == KV::INT8;
-#define PKV_RING(D_, G_, NW_, RING_, Q8_) \
-  hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_>), grid, dim3(64 * NW_), 0, stream, p)
+#define PKV_RING(D_, G_, NW_, RING_, Q8_)                                                            \
+  do {                                                                                              \
+    if (p.compact_units != 0)                                                                      \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, true>), grid, dim3(64 * NW_), \
+                         0, stream, p);                                                            \
+    else                                                                                           \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, false>), grid,              \
+                         dim3(64 * NW_), 0, stream, p);                                            \
+  } while (0)
   if (!q8) {
     if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_G8_NW, PKV_G8_RING, false);
     else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_G4_RING, false);

@@ -86,7 +86,14 @@ struct DecodeParams {
   // of each sequence (k and v above then point at writable pools).
   const void* k_new;
   const void* v_new;
+  // LDS-ring kernel: 0 = grid (KV head, sequence, split); > 0 = grid (KV
+  // head, compact_units) over the splits that exist (ragged batches,
+  // B <= kCompactMaxB), each workgroup looping over units blockIdx.y + k *
+  // compact_units until all are done.
+  int32_t compact_units;
 };
+
+constexpr int kCompactMaxB = 512;
 
 // GQA/MQA/MHA over float or INT8 pools (VALU kernels).  Returns
 // hipErrorInvalidValue for a (d, g, dtype) combination with no instance.

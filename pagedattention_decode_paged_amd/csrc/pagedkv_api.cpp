@@ -524,6 +524,17 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
     p.k_new = app->k_new;
     p.v_new = app->v_new;
   }
+  // Ragged batches on the LDS-ring kernel: launch only the splits that exist
+  // (grid from the host's total, which only sizes it: the kernel covers
+  // every unit whatever that total says).
+  const int64_t total = d->total_context_len;
+  if (total > 0 && ns > 1 && d->B <= pkv::kCompactMaxB && 4 * total < 3 * (int64_t)d->B * d->max_context_len &&
+      pkv::gqa_ring_supported(p.kv, q_bf16, d->d_k, d->d_v, g)) {
+    int64_t units = total / split + d->B;
+    if (units > (int64_t)d->B * ns) units = (int64_t)d->B * ns;
+    if (units > 65535) units = 65535;
+    p.compact_units = (int32_t)units;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(pkv::launch_decode_gqa(p, st), fn);
 }

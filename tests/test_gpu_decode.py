@@ -236,3 +236,43 @@ def test_one_workspace_serves_calls_of_different_shapes():
                                         split_tokens=split, workspace=ws)
         torch.cuda.synchronize()
         assert max_err(out, ref[rows]) <= TOL_BF16, split
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8"])
+@pytest.mark.parametrize("g,d", [(8, 128), (4, 64)])
+def test_compact_grid_for_ragged_batches_is_bit_exact(kind, g, d):
+    """Ragged batch with a total-context hint: the LDS-ring kernel launches
+    only the splits that exist (grid (KV head, unit)) instead of every
+    sequence times the largest split count.  Bit-exact against the full
+    grid (no hint), and with a hint far too small (a grid of B units per KV
+    head, each workgroup looping over many units): the hint only sizes the
+    grid.  Empty sequences are zeroed through their one unit."""
+    ctxs = [50, 3000, 0, 700, 9000, 64, 1, 2049, 128, 4500]
+    n_kv = 2
+    s = custom_structure(ctxs, 16, seed=g + d, pad_blocks=1)
+    bt, ctx = tables_to_device(s)
+    B = len(ctxs)
+    q = device_normal_(torch.empty((B, g * n_kv, d), dtype=torch.bfloat16, device="cuda"), 90 + g)
+    total = int(sum(ctxs))
+    outs = []
+    if kind == "bf16":
+        pool = pk.kv_pool_create(s.num_blocks, 16, n_kv, d, d, torch.bfloat16)
+        device_normal_(pool.storage.view(torch.bfloat16), 91 + g)
+        for hint in (0, total, 1):
+            outs.append(pk.paged_decode_attention(q, pool.k, pool.v, bt, ctx, 0.1, max_context_len=9000,
+                                                  split_tokens=256, total_context_len=hint))
+    else:
+        pool = pk.kv_pool_create(s.num_blocks, 16, n_kv, d, d, torch.int8)
+        seq, pos = prefill_tokens(s.context_lens)
+        slots = pk.paged_slot_mapping(bt, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), 16)
+        rows = device_normal_(torch.empty((2, len(seq), n_kv, d), dtype=torch.bfloat16, device="cuda"), 92)
+        pk.reshape_and_cache(pool, rows[0], rows[1], slots)
+        for hint in (0, total, 1):
+            outs.append(pk.paged_decode_attention_int8(q, pool.k, pool.k_scale, pool.v, pool.v_scale, bt, ctx,
+                                                       0.1, max_context_len=9000, split_tokens=256,
+                                                       total_context_len=hint))
+    torch.cuda.synchronize()
+    ref = outs[0].view(torch.int16)
+    assert torch.equal(outs[1].view(torch.int16), ref)
+    assert torch.equal(outs[2].view(torch.int16), ref)
+    assert torch.count_nonzero(outs[0][2]) == 0
