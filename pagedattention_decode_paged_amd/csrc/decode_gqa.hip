@@ -434,46 +434,62 @@ __global__ __launch_bounds__(kThreads, 2) void decode_gqa_kernel(const DecodePar
 // Log-sum-exp merge of split partials (the split-context reduction that
 // qwbw 8 Q2/Q3 name FlashDecoding): with M the largest split maximum (scores
 // in base 2), out = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.
-// One wavefront per (sequence, query head).  The split (m, l) pairs are
-// uniform and come through the scalar cache; the partial outputs do not
-// depend on them, so all the loads of a batch are in flight at once and the
-// kernel costs about one memory round trip.
+// One wavefront per (sequence, query head), kReduceWaves of them per
+// workgroup.  The first batch of partials is loaded before the context
+// length arrives (every split the launch has is inside the workspace, and
+// splits past the sequence's own count are discarded by selects, never
+// multiplied), so the kernel costs about one memory round trip.
 constexpr int kReduceThreads = 64;
+constexpr int kReduceWaves = 4;
 constexpr int kMaxSplits = 1024;
 constexpr int kFewSplits = 8;       // splits whose loads are issued together (d_v <= 128)
 
-__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(
+__global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ context_lens, void* __restrict__ out, int n_h, int d_v,
+    const int32_t* __restrict__ context_lens, void* __restrict__ out, int rows, int n_h, int d_v,
     int num_splits, int split_tokens, int out_bf16) {
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x * kReduceWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kReduceThreads);
+  if (bh >= rows) return;
   const int b = bh / n_h;
-  const int lane = threadIdx.x;
-  const int ctx = context_lens[b];
-  const int nsp = min(num_splits, (ctx + split_tokens - 1) / split_tokens);
-  if (nsp <= 1) return;                 // written by the decode kernel itself
+  const int lane = threadIdx.x % kReduceThreads;
   const int64_t base = (int64_t)bh * num_splits;
   const float* ml = part_ml + 2 * base;
   const float* po = part_o + base * d_v + lane;
   const bool c0 = lane < d_v, c1 = lane + kReduceThreads < d_v;
-  // batches of kFewSplits splits, all loads of a batch issued before their
-  // first use; batches merged online (running max M, sum L, outputs o)
+  // split s of this row into slot k of the batch (defaults past lim)
+#define PKV_REDUCE_LOAD(s, k, lim)                                    \
+  do {                                                                \
+    if ((s) < (lim)) {                                                \
+      m[k] = ml[2 * (s)];                                             \
+      l[k] = ml[2 * (s) + 1];                                         \
+      v0[k] = c0 ? po[(int64_t)(s) * d_v] : 0.f;                      \
+      v1[k] = c1 ? po[(int64_t)(s) * d_v + kReduceThreads] : 0.f;     \
+    } else {                                                          \
+      m[k] = -INFINITY;                                               \
+      l[k] = 0.f;                                                     \
+      v0[k] = v1[k] = 0.f;                                            \
+    }                                                                 \
+  } while (0)
+  float m[kFewSplits], l[kFewSplits], v0[kFewSplits], v1[kFewSplits];
+#pragma unroll
+  for (int k = 0; k < kFewSplits; ++k) PKV_REDUCE_LOAD(k, k, num_splits);   // in flight with ctx
+  const int ctx = context_lens[b];
+  const int nsp = min(num_splits, (ctx + split_tokens - 1) / split_tokens);
+  if (nsp <= 1) return;                 // written by the decode kernel itself
+  // batches of kFewSplits splits merged online (running max M, sum L, outputs o)
   float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
   for (int s0 = 0; s0 < nsp; s0 += kFewSplits) {
-    float m[kFewSplits], l[kFewSplits], v0[kFewSplits], v1[kFewSplits];
+    if (s0 > 0) {
+#pragma unroll
+      for (int k = 0; k < kFewSplits; ++k) PKV_REDUCE_LOAD(s0 + k, k, nsp);
+    }
 #pragma unroll
     for (int k = 0; k < kFewSplits; ++k) {
-      const int s = s0 + k;
-      if (s < nsp) {
-        m[k] = ml[2 * s];
-        l[k] = ml[2 * s + 1];
-        v0[k] = c0 ? po[(int64_t)s * d_v] : 0.f;
-        v1[k] = c1 ? po[(int64_t)s * d_v + kReduceThreads] : 0.f;
-      } else {
-        m[k] = -INFINITY;
-        l[k] = 0.f;
-        v0[k] = v1[k] = 0.f;
-      }
+      const bool in = s0 + k < nsp;
+      m[k] = in ? m[k] : -INFINITY;
+      l[k] = in ? l[k] : 0.f;
+      v0[k] = in ? v0[k] : 0.f;
+      v1[k] = in ? v1[k] : 0.f;
     }
     float Mb = M;
 #pragma unroll
@@ -491,6 +507,7 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(
       o1 = fmaf(v1[k], w, o1);
     }
   }
+#undef PKV_REDUCE_LOAD
   const float inv = 1.0f / L;
   const int64_t o = (int64_t)bh * d_v + lane;
   if (out_bf16) {
@@ -562,9 +579,11 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
   }
   if (e != hipSuccess || p.num_splits == 1) return e;
   if (p.num_splits > kMaxSplits) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(p.B * p.n_h)), dim3(kReduceThreads), 0,
-                     stream, (const float*)p.part_o, (const float*)p.part_ml, p.context_lens, p.out,
-                     p.n_h, p.d_v, p.num_splits, p.split_tokens, p.q_bf16 ? 1 : 0);
+  const int rows = p.B * p.n_h;
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((rows + kReduceWaves - 1) / kReduceWaves)),
+                     dim3(kReduceThreads * kReduceWaves), 0, stream, (const float*)p.part_o,
+                     (const float*)p.part_ml, p.context_lens, p.out, rows, p.n_h, p.d_v, p.num_splits,
+                     p.split_tokens, p.q_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 
