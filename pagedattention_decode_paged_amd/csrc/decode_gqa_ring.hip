@@ -50,10 +50,11 @@
 #include "device_common.h"
 
 // Launch shapes (measured on the 70B-shaped layer): two 64 KiB rings per
-// compute unit (two workgroups resident) beat one 128 KiB ring; g = 8 runs
-// 8 waves (one head each), g = 4 runs 4 waves.
+// compute unit (two workgroups resident) beat one 128 KiB ring; bf16 runs
+// 4 waves for g = 8 (two heads each: each K/V row read from LDS serves two
+// heads; 1 % faster than 8 waves of one head) and for g = 4 (one head each).
 #ifndef PKV_G8_NW
-#define PKV_G8_NW 8
+#define PKV_G8_NW 4
 #endif
 #ifndef PKV_G8_RING
 #define PKV_G8_RING 2
