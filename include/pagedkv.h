@@ -61,8 +61,11 @@ typedef enum {
  * Layout, row-major (talentme chapter 3, the NumPy pool class):
  *   K codes/values  [num_blocks, block_size, n_kv, d_k]
  *   V codes/values  [num_blocks, block_size, n_kv, d_v]
- *   K, V scales     [num_blocks, block_size, n_kv] float   (KVP_INT8 only)
- * Slot s is block s / block_size, offset s % block_size.  A latent pool
+ *   K, V scales     [num_blocks, n_kv, block_size] float   (KVP_INT8 only)
+ * Slot s is block s / block_size, offset s % block_size.  The scales are
+ * paged like the codes (one per slot and KV head); inside a block, one
+ * head's scales are adjacent so that a kernel working on one KV head reads
+ * them as contiguous runs.  A latent pool
  * (latent = 1, absorbed MLA; faulkner, matrix absorption section) has
  * n_kv = 1 and no V array: the value of a token is the first d_v columns
  * of its K row.  Each region starts 256-byte aligned.
@@ -208,7 +211,7 @@ kvp_status paged_decode_attention(const void* q, const void* k_pool, const void*
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* INT8 pools: codes as in the pool layout plus fp32 scales
- * [num_blocks, block_size, n_kv]; dequantization (code * scale,
+ * [num_blocks, n_kv, block_size]; dequantization (code * scale,
  * guijiagi 4.2) happens inside the kernel.  desc->kv_dtype == KVP_INT8. */
 kvp_status paged_decode_attention_int8(const void* q, const int8_t* k_codes,
                                        const float* k_scale, const int8_t* v_codes,

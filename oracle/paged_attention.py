@@ -243,13 +243,14 @@ def paged_decode_attention_int8(q, k_codes, k_scales, v_codes, v_scales,
                                 block_table, context_lens, scale: float) -> np.ndarray:
     """Decode attention over an INT8 paged cache with per-(slot, head) scales.
 
-    Pools: codes ``int8 [NB, bs, n_kv, d]``, scales ``float32 [NB, bs, n_kv]``
-    (one scale per token per KV head, paged exactly like the codes).  The
-    cache is dequantized (guijiagi section 4.2) and then attended exactly as
+    Pools: codes ``int8 [NB, bs, n_kv, d]``, scales ``float32 [NB, n_kv, bs]``
+    (one scale per token per KV head, paged like the codes: the block is the
+    page, and inside it one head's scales are adjacent).  The cache is
+    dequantized (guijiagi section 4.2) and then attended exactly as
     :func:`paged_decode_attention`.
     """
-    k = dequantize_int8(k_codes, k_scales)
-    v = dequantize_int8(v_codes, v_scales)
+    k = dequantize_int8(k_codes, np.swapaxes(np.asarray(k_scales), 1, 2))
+    v = dequantize_int8(v_codes, np.swapaxes(np.asarray(v_scales), 1, 2))
     return paged_decode_attention(q, k, v, block_table, context_lens, scale)
 
 

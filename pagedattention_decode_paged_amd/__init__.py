@@ -192,8 +192,8 @@ def kv_pool_create(num_blocks: int, block_size: int, n_kv: int, d_k: int, d_v: i
     slots = num_blocks * block_size
     k = sub(view.k, slots * n_kv * d_k, dtype, (num_blocks, block_size, n_kv, d_k))
     v = k if latent else sub(view.v, slots * n_kv * d_v, dtype, (num_blocks, block_size, n_kv, d_v))
-    ks = sub(view.k_scale, slots * n_kv, torch.float32, (num_blocks, block_size, n_kv))
-    vs = sub(view.v_scale, slots * n_kv, torch.float32, (num_blocks, block_size, n_kv))
+    ks = sub(view.k_scale, slots * n_kv, torch.float32, (num_blocks, n_kv, block_size))
+    vs = sub(view.v_scale, slots * n_kv, torch.float32, (num_blocks, n_kv, block_size))
     return KVPool(h, storage, k, v, ks, vs, num_blocks, block_size, n_kv, d_k, d_v, dtype, latent)
 
 

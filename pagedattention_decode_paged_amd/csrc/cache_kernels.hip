@@ -68,7 +68,7 @@ struct QuantJob {
 };
 
 __global__ void cache_quant_int8_kernel(QuantJob kj, QuantJob vj, int bf16, SlotSource slots,
-                                        int64_t num_rows, int32_t n_kv) {
+                                        int64_t num_rows, int32_t n_kv, int32_t bshift) {
   const QuantJob j = blockIdx.y == 0 ? kj : vj;
   const int32_t d = j.d;
   int8_t* __restrict__ codes = j.codes;
@@ -88,6 +88,8 @@ __global__ void cache_quant_int8_kernel(QuantJob kj, QuantJob vj, int bf16, Slot
   const float scale = amax / 127.0f;
   const int64_t out_row = s * n_kv + h;
   int8_t* crow = codes + out_row * d;
+  // scales [num_blocks, n_kv, block_size]: one block's tokens of a head are adjacent
+  const int64_t out_scale = (((s >> bshift) * n_kv + h) << bshift) + (s & ((1 << bshift) - 1));
   for (int i = lane; i < d; i += 64) {
     int c = 0;
     if (scale > 0.f) {
@@ -97,7 +99,7 @@ __global__ void cache_quant_int8_kernel(QuantJob kj, QuantJob vj, int bf16, Slot
     }
     crow[i] = (int8_t)c;
   }
-  if (lane == 0) scales[out_row] = scale;
+  if (lane == 0) scales[out_scale] = scale;
 }
 
 // qwbw 3.4: walk each sequence's table and copy its rows in logical order.
@@ -154,14 +156,14 @@ hipError_t launch_cache_copy(void* k_pool, const void* k_src, int64_t k_row_byte
 hipError_t launch_cache_quant_int8(int8_t* k_codes, float* k_scales, const void* k_src, int32_t d_k,
                                    int8_t* v_codes, float* v_scales, const void* v_src, int32_t d_v,
                                    bool src_bf16, const SlotSource& slots, int64_t num_tokens,
-                                   int32_t n_kv, hipStream_t stream) {
+                                   int32_t n_kv, int32_t block_shift, hipStream_t stream) {
   const int64_t rows = num_tokens * n_kv;
   if (rows == 0) return hipSuccess;
   const int waves = 4;
   dim3 grid((unsigned)((rows + waves - 1) / waves), 2u);
   hipLaunchKernelGGL(cache_quant_int8_kernel, grid, dim3(64 * waves), 0, stream,
                      QuantJob{k_codes, k_scales, k_src, d_k}, QuantJob{v_codes, v_scales, v_src, d_v},
-                     src_bf16 ? 1 : 0, slots, rows, n_kv);
+                     src_bf16 ? 1 : 0, slots, rows, n_kv, block_shift);
   return hipGetLastError();
 }
 

@@ -317,9 +317,11 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
     }
     if constexpr (Q8) {
       if (wave < R::kScaleWaves) {
+        // scales [num_blocks, n_kv, block_size]: a block's scales of this
+        // head are adjacent, so the 64 tokens' scales are whole 64-byte runs
         const int t = min(tile0 + lane, t_last);
-        const int64_t sl = ((int64_t)s_bt[(t >> shift) - lb0] << shift) + (t & bmask);
-        dma4(scl_src + sl * p.n_kv + kvh, lds_scl + (uint32_t)(slot * kStageTok * 4));
+        const int64_t si = (((int64_t)s_bt[(t >> shift) - lb0] * p.n_kv + kvh) << shift) + (t & bmask);
+        dma4(scl_src + si, lds_scl + (uint32_t)(slot * kStageTok * 4));
       }
     }
   };

@@ -82,10 +82,15 @@ __global__ __launch_bounds__(kThreads) void decode_int8_kernel(const DecodeParam
   const int8_t* kcodes = reinterpret_cast<const int8_t*>(p.k);
   const int8_t* vcodes = reinterpret_cast<const int8_t*>(p.v);
   const float qscale = p.scale * kLog2e;
-  // slot * n_kv + kvh: row index into codes (x D bytes) and scales
+  // slot * n_kv + kvh: row index into the codes (x D bytes); the scales are
+  // [num_blocks, n_kv, block_size]
   auto row_of = [&](int t) -> int64_t {
     const int32_t phys = s_bt[(t >> shift) - lb0];
     return (((int64_t)phys << shift) + (t & bmask)) * n_kv + kvh;
+  };
+  auto scale_of = [&](int t) -> int64_t {
+    const int32_t phys = s_bt[(t >> shift) - lb0];
+    return (((int64_t)phys * n_kv + kvh) << shift) + (t & bmask);
   };
   const int64_t q_dw0 = ((int64_t)b * n_h + (int64_t)kvh * G) * Gm::kQdw;
 
@@ -120,8 +125,9 @@ __global__ __launch_bounds__(kThreads) void decode_int8_kernel(const DecodeParam
       const uint4* src = reinterpret_cast<const uint4*>(kcodes + r * D);
 #pragma unroll
       for (int i = 0; i < Gm::kRowQ; ++i) kreg[i] = src[i];
-      ks = p.k_scale[r];
-      vs = p.v_scale[r];
+      const int64_t si = scale_of(my_t);
+      ks = p.k_scale[si];
+      vs = p.v_scale[si];
     } else {
 #pragma unroll
       for (int i = 0; i < Gm::kRowQ; ++i) kreg[i] = make_uint4(0, 0, 0, 0);

@@ -44,11 +44,12 @@ hipError_t launch_cache_copy(void* k_pool, const void* k_src, int64_t k_row_byte
                              int64_t num_tokens, hipStream_t stream);
 
 // Quantize-on-write of K and V, one launch: src rows [num_tokens, n_kv, d]
-// (f32 or bf16 bits), codes [slots, n_kv, d] int8, scales [slots, n_kv] f32.
+// (f32 or bf16 bits), codes [slots, n_kv, d] int8, scales
+// [num_blocks, n_kv, block_size] f32 (block_size = 1 << block_shift).
 hipError_t launch_cache_quant_int8(int8_t* k_codes, float* k_scales, const void* k_src, int32_t d_k,
                                    int8_t* v_codes, float* v_scales, const void* v_src, int32_t d_v,
                                    bool src_bf16, const SlotSource& slots, int64_t num_tokens,
-                                   int32_t n_kv, hipStream_t stream);
+                                   int32_t n_kv, int32_t block_shift, hipStream_t stream);
 
 hipError_t launch_gather(const void* pool, int64_t row_bytes, int32_t block_shift,
                          const int32_t* block_table, int32_t max_blocks_per_seq,

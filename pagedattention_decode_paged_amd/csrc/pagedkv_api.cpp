@@ -397,7 +397,8 @@ kvp_status write_rows(kvp_pool* pool, const void* k_new, const void* v_new, kvp_
     const bool bf = in_dtype == KVP_BF16;
     return hip_status(pkv::launch_cache_quant_int8(static_cast<int8_t*>(v.k), v.k_scale, k_new, d.d_k,
                                                   static_cast<int8_t*>(v.v), v.v_scale, v_new, d.d_v,
-                                                  bf, slots, num_tokens, d.n_kv, st),
+                                                  bf, slots, num_tokens, d.n_kv,
+                                                  __builtin_ctz((unsigned)d.block_size), st),
                       fn);
   }
   if (in_dtype != d.dtype) return fail(KVP_ERR_INVALID_ARG, "%s: rows must have the pool's dtype", fn);

@@ -103,7 +103,7 @@ def test_int8_quantize_on_write_bit_exact(src):
     for new, codes_t, scales_t in [(k_new, pool.k, pool.k_scale), (v_new, pool.v, pool.v_scale)]:
         c_ref, s_ref = oracle.quantize_int8_rows(new)
         codes = host(codes_t).reshape(-1, n_kv, d)
-        scales = host(scales_t).reshape(-1, n_kv)
+        scales = host(scales_t).transpose(0, 2, 1).reshape(-1, n_kv)   # [NB, n_kv, bs] -> per slot
         assert np.array_equal(codes[ref_slots], c_ref)
         assert np.array_equal(scales[ref_slots].view(np.uint32), s_ref.view(np.uint32))
 

@@ -101,8 +101,9 @@ def test_int8_attention_is_attention_over_the_dequantized_cache():
     kc, ks = oracle.quantize_int8_rows(kx)
     vc, vs = oracle.quantize_int8_rows(vx)
     q = rng.standard_normal((2, 4, d))
-    got = oracle.paged_decode_attention_int8(q, kc, ks, vc, vs, s.block_table,
-                                             s.context_lens, 0.25)
+    # the pool keeps a block's scales head by head: [NB, n_kv, bs]
+    got = oracle.paged_decode_attention_int8(q, kc, ks.transpose(0, 2, 1), vc, vs.transpose(0, 2, 1),
+                                             s.block_table, s.context_lens, 0.25)
     # explicit dequantization, then the contiguous definition per sequence
     for b, c in enumerate(ctxs):
         K = np.stack([kc[s.block_table[b, j // bs], j % bs].astype(np.float64)
