@@ -25,9 +25,17 @@
 //   out exactly afterwards: q . code = q . u - 128 sum(q) for the scores and
 //   sum_t p'_t code_t = sum_t p'_t u_t - 128 sum_t p'_t for the values, with
 //   p'_t = p_t * sV_t.
-// * The waves split the g heads (g / NW each) and every wave walks all
-//   tokens of the stage, so a K/V byte crosses HBM once and feeds all g
-//   heads, and each wave's softmax state is final at the end.
+// * Matrix-core path (the default): four waves, each taking 16 tokens of a
+//   stage for all g heads (padded to 16).  Per KV head the work is a dense
+//   [g x d] . [d x tokens] contraction: S^T = K Q^T and O^T += V^T P^T on
+//   v_mfma_f32_16x16x32_bf16 / 16x16x16bf16_1k, with lane l holding head
+//   l % 16 and tokens 4 (l / 16) .. + 3 in both, so the weights feed the
+//   second product from the lane's own registers.  Each wave keeps its own
+//   softmax state; the four are merged through LDS at the end.
+// * Lane-per-token path (PKV_GQA_MFMA=0): the waves split the g heads
+//   (g / NW each) and every wave walks all tokens of the stage, so each
+//   wave's softmax state is final at the end; described below.  On both
+//   paths a K/V byte crosses HBM once and feeds all g heads.
 // * Scores: lane i owns token i of the stage and reads its K row from LDS
 //   (rows are stored with their 16-byte pieces permuted by the row index, so
 //   the 16 lanes of a read phase hit distinct banks of the 64-bank LDS); q
@@ -71,6 +79,10 @@
 #ifndef PKV_Q8_G4_RING
 #define PKV_Q8_G4_RING 2
 #endif
+// matrix-core path (four waves, 16 tokens of each stage per wave)
+#ifndef PKV_GQA_MFMA
+#define PKV_GQA_MFMA 1
+#endif
 
 namespace pkv {
 namespace {
@@ -80,6 +92,8 @@ using namespace dev;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kStageTok = 64;    // tokens per stage (one per lane in the score phase)
 
@@ -108,6 +122,12 @@ struct Ring {
   static __device__ __forceinline__ int swz_k(int r) { return (r / kRows256) % kPieces; }
   static __device__ __forceinline__ int swz_v(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  }
+  // matrix-core path: V is read transposed, 4 rows of 2 pieces per 16
+  // lanes, the two 16-lane groups of a phase on rows 4 apart, so the 8 rows
+  // of a phase need distinct piece positions
+  static __device__ __forceinline__ int swz_vm(int r) {
+    return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
   }
 };
 
@@ -172,12 +192,17 @@ __device__ __forceinline__ void widen_codes(const u32x4_t c, u32x4_t& lo, u32x4_
   hi = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
-template <int D, int G, int NW, int RING, bool Q8, bool COMPACT>
+template <int D, int G, int NW, int RING, bool Q8, bool COMPACT, bool MF>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodeParams p) {
   using R = Ring<D, NW, Q8>;
   constexpr int kThr = 64 * NW;
-  constexpr int kHpw = G / NW;                     // heads per wave
-  static_assert(G % NW == 0, "g must be a multiple of the wave count");
+  constexpr int kHpw = MF ? 1 : G / NW;            // heads per wave (lane-per-token path)
+  static_assert(MF || G % NW == 0, "g must be a multiple of the wave count");
+  static_assert(!MF || (NW == 4 && G <= 16), "matrix-core path: four waves of 16 tokens, g <= 16");
+  // matrix-core path: k-steps of the score product (32 dims each) and
+  // 16-column blocks of the value product
+  constexpr int kKs = D / 32;
+  constexpr int kCb = D / 16;
   // bf16: the DMA ring holds the K and V tiles themselves.  INT8: it holds
   // codes and scales, and one pair of bf16 tiles receives each stage.
   constexpr int kRingBytes = Q8 ? R::kSrcBytes : R::kMatBytes;
@@ -185,7 +210,10 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[Q8 ? 2 : 1][Q8 ? R::kMatBytes : 16];
   __shared__ __align__(16) float s_scl[2][Q8 ? RING : 1][Q8 ? kStageTok : 1];
   __shared__ __align__(16) int32_t s_bt[kBtSlots];
-  __shared__ __align__(16) uint32_t s_pp[NW][kHpw][kStageTok / 2];
+  __shared__ __align__(16) uint32_t s_pp[MF ? 1 : NW][kHpw][kStageTok / 2];
+  // matrix-core path: per wave and head the running maximum, sum (and the
+  // INT8 weight sum) for the final merge of the four waves
+  __shared__ float s_mml[MF ? 3 * NW * G : 1];
   // compact grid only: units before each sequence, and the context lengths
   __shared__ int32_t s_upre[COMPACT ? kCompactMaxB + 1 : 1];
   __shared__ int32_t s_ctx[COMPACT ? kCompactMaxB : 1];
@@ -267,7 +295,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   // (permuted); INT8 codes go to the staging ring in order
   auto src_piece = [&](int r) {
     if constexpr (Q8) return lpiece;
-    else return lpiece ^ (dma_v ? R::swz_v(r) : R::swz_k(r));
+    else return lpiece ^ (dma_v ? (MF ? R::swz_vm(r) : R::swz_v(r)) : R::swz_k(r));
   };
   // per-lane offsets inside a block for the fast path; the permutation
   // depends on the row only through jm mod kSwzPeriod
@@ -342,13 +370,48 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   float qsum[kHpw];
 #pragma unroll
   for (int h = 0; h < kHpw; ++h) qsum[h] = 0.f;
-  if constexpr (Q8) {
+  if constexpr (Q8 && !MF) {
 #pragma unroll
     for (int h = 0; h < kHpw; ++h) {
       float t = 0.f;
       const uint32_t* qh = reinterpret_cast<const uint32_t*>(p.q) + q_dw0 + h * (D / 2);
       for (int i = lane; i < D / 2; i += kWave) t += bf_lo(qh[i]) + bf_hi(qh[i]);
       qsum[h] = wave_sum(t);
+    }
+  }
+
+  // ---- matrix-core path.  Per stage each wave takes 16 tokens (rows
+  // 16 wave .. + 15): S^T = K Q^T (A: K rows from LDS, B: Q^T fragments
+  // kept in registers, zero for the padding heads g .. 15), then
+  // O^T += V^T P^T (A: V^T by transposed LDS reads, B: the lane's own
+  // weights).  In both products lane l holds head l % 16 and tokens
+  // 4 (l / 16) .. + 3 of the wave's block, so the weights need no shuffle
+  // and a head's rescale factor is in the lanes that hold its outputs.  Each
+  // wave keeps its own softmax state; the four are merged at the end.
+  const int ml16 = lane & 15, mg = lane >> 4;
+  u32x4_t qf[MF ? kKs : 1];
+  f32x4_t macc[MF ? kCb : 1];
+  float mm_run = -INFINITY, ml_run = 0.f, mps_run = 0.f, mqsum = 0.f;
+  if constexpr (MF) {
+#pragma unroll
+    for (int c = 0; c < kCb; ++c) macc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) +
+                          ((int64_t)b * n_h + (int64_t)kvh * G + min(ml16, G - 1)) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + (32 * ks + 8 * mg) * 2);
+      qf[ks] = ml16 < G ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if constexpr (Q8) {
+      // sum of the head's q (it multiplies the +128 offset of the codes)
+      float t = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t += bf_lo(qf[ks][j]) + bf_hi(qf[ks][j]);
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+      mqsum = t;
     }
   }
 
@@ -398,7 +461,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
         const u32x4_t c = *reinterpret_cast<const u32x4_t*>(&s_dma[m][slot][(r * R::kSrcPieces + e) * 16]);
         u32x4_t lo, hi;
         widen_codes(c, lo, hi);
-        const int sw = m ? R::swz_v(r) : R::swz_k(r);
+        const int sw = m ? (MF ? R::swz_vm(r) : R::swz_v(r)) : R::swz_k(r);
         uint8_t* row = &s_tile[m][r * R::kRowBytes];
         *reinterpret_cast<u32x4_t*>(row + ((2 * e) ^ sw) * 16) = lo;
         *reinterpret_cast<u32x4_t*>(row + ((2 * e + 1) ^ sw) * 16) = hi;
@@ -412,6 +475,84 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
     }
     const int tile0 = t_begin + s * kStageTok;
     const bool valid = tile0 + lane < t_end;
+
+    if constexpr (MF) {
+      const int row = 16 * wave + ml16;              // K row of this lane (A operand)
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
+            kst + row * R::kRowBytes + (((4 * ks + mg) ^ R::swz_k(row)) * 16));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
+                                                       __builtin_bit_cast(bf16x8_t, qf[ks]), sacc, 0, 0, 0);
+      }
+      const int tl0 = 16 * wave + 4 * mg;            // this lane's first token in the stage
+      float sk[4] = {1.f, 1.f, 1.f, 1.f}, svv[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (Q8) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&s_scl[0][slot][tl0]);
+        const f32x4_t c = *reinterpret_cast<const f32x4_t*>(&s_scl[1][slot][tl0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sk[i] = a[i]; svv[i] = c[i]; }
+      }
+      float sc4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float raw = Q8 ? fmaf(-128.f, mqsum, sacc[i]) * sk[i] : sacc[i];
+        sc4[i] = tile0 + tl0 + i < t_end ? raw * qscale : -INFINITY;
+      }
+      // maximum of the head over the wave's 16 tokens (lanes l16 + 16 j)
+      float smax = fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3]));
+      {
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+        smax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+        smax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      }
+      // lazy rescale: the running maximum moves only when a score exceeds it
+      // by more than 2^8 (weights stay below 2^8, well inside bf16)
+      constexpr float kSlack = 8.f;
+      if (mm_run == -INFINITY) {
+        mm_run = smax;                               // still -inf if no token was valid yet
+      } else if (__builtin_amdgcn_ballot_w64(smax > mm_run + kSlack)) {
+        const float m_new = fmaxf(mm_run, smax);
+        const float alpha = __builtin_amdgcn_exp2f(mm_run - m_new);
+        ml_run *= alpha;
+        mps_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < kCb; ++c) macc[c] *= alpha;
+        mm_run = m_new;
+      }
+      float pw[4], pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = sc4[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc4[i] - mm_run);
+        pw[i] = Q8 ? pr[i] * svv[i] : pr[i];
+      }
+      const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{pw[0], pw[1]}), bf16x2_t));
+      const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{pw[2], pw[3]}), bf16x2_t));
+      const float rsum = bf_lo(p01) + bf_hi(p01) + bf_lo(p23) + bf_hi(p23);
+      if constexpr (Q8) {
+        ml_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        mps_run += rsum;
+      } else {
+        ml_run += rsum;
+      }
+      const i16x4_t pb = __builtin_bit_cast(i16x4_t, (u32x2_t{p01, p23}));
+      // V^T fragments: lane (mg, ml16) addresses row tl0 + ml16 / 4 and 8
+      // bytes of the block's columns; the transposed read hands lane ml16
+      // column ml16 of rows tl0 .. tl0 + 3
+      const int tv = tl0 + (ml16 >> 2), cp = ml16 & 3;
+      const uint32_t vrow = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)vst +
+                            (uint32_t)(tv * R::kRowBytes + 8 * (cp & 1));
+      const int svz = R::swz_vm(tv);
+#pragma unroll
+      for (int c = 0; c < kCb; ++c) {
+        const uint32_t a = vrow + (uint32_t)((((2 * c + (cp >> 1)) ^ svz)) * 16);
+        const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a);
+        macc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, macc[c], 0, 0, 0);
+      }
+      return;
+    }
 
     // ---- scores: this lane's token row against the wave's heads
     u32x4_t kreg[R::kPieces];
@@ -527,8 +668,59 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       if (s0 + u < n_stages) stage(s0 + u, u);
   }
 
-  // ---- finish: each wave owns whole heads; lane owns columns 16 k + vi
   const int nsp = (ctx + p.split_tokens - 1) / p.split_tokens;
+  if constexpr (MF) {
+    // ---- finish (matrix-core path): per wave and head, the sums over the
+    // four lane groups; then the four waves' states are merged through LDS
+    // (the ring is free once every wave is past the last stage)
+    float L = ml_run;
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    float PS = mps_run;
+    if constexpr (Q8) {
+      PS += __shfl_xor(PS, 16);
+      PS += __shfl_xor(PS, 32);
+    }
+    __syncthreads();
+    float* s_mo = reinterpret_cast<float*>(Q8 ? &s_tile[0][0] : &s_dma[0][0][0]);   // [NW][G][D]
+    if (ml16 < G) {
+#pragma unroll
+      for (int c = 0; c < kCb; ++c)
+        *reinterpret_cast<f32x4_t*>(&s_mo[(wave * G + ml16) * D + 16 * c + 4 * mg]) = macc[c];
+      if (mg == 0) {
+        s_mml[wave * G + ml16] = mm_run;
+        s_mml[NW * G + wave * G + ml16] = L;
+        s_mml[2 * NW * G + wave * G + ml16] = PS;
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += kThr) {
+      const int h = idx / D, d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_mml[w * G + h]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_mml[w * G + h];
+        const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        const float ow = s_mo[(w * G + h) * D + d] - (Q8 ? 128.f * s_mml[2 * NW * G + w * G + h] : 0.f);
+        num = fmaf(f, ow, num);
+        den = fmaf(f, s_mml[NW * G + w * G + h], den);
+      }
+      const float o = den > 0.f ? num / den : 0.f;
+      const int64_t row = (int64_t)b * n_h + (int64_t)kvh * G + h;
+      if (nsp == 1) {
+        reinterpret_cast<uint16_t*>(p.out)[row * D + d] = f32_to_bf16_rne(o);
+      } else {
+        const int64_t pi = row * p.num_splits + split;
+        p.part_o[pi * D + d] = o;
+        if (d == 0) { p.part_ml[2 * pi] = M; p.part_ml[2 * pi + 1] = den; }
+      }
+    }
+    return;
+  }
+  // ---- finish: each wave owns whole heads; lane owns columns 16 k + vi
 #pragma unroll
   for (int h = 0; h < kHpw; ++h) {
     const float L = wave_sum(l_run[h]);
@@ -616,26 +808,32 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
                                           : dim3((unsigned)p.n_kv, (unsigned)p.B, (unsigned)p.num_splits);
   const int g = p.n_h / p.n_kv;
   const bool q8 = p.kv == KV::INT8;
-#define PKV_RING(D_, G_, NW_, RING_, Q8_)                                                            \
+#define PKV_RING(D_, G_, NW_, RING_, Q8_, MF_)                                                      \
   do {                                                                                              \
     if (p.compact_units != 0)                                                                      \
-      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, true>), grid, dim3(64 * NW_), \
-                         0, stream, p);                                                            \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, true, MF_>), grid,          \
+                         dim3(64 * NW_), 0, stream, p);                                            \
     else                                                                                           \
-      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, false>), grid,              \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, false, MF_>), grid,         \
                          dim3(64 * NW_), 0, stream, p);                                            \
   } while (0)
-  if (!q8) {
-    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_G8_NW, PKV_G8_RING, false);
-    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_G4_RING, false);
-    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_G8_NW, PKV_G8_RING, false);
-    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_G4_RING, false);
+  if (PKV_GQA_MFMA) {
+    if (p.d_k == 128 && g == 8) { if (q8) PKV_RING(128, 8, 4, 2, true, true); else PKV_RING(128, 8, 4, 2, false, true); }
+    else if (p.d_k == 128 && g == 4) { if (q8) PKV_RING(128, 4, 4, 2, true, true); else PKV_RING(128, 4, 4, 2, false, true); }
+    else if (p.d_k == 64 && g == 8) { if (q8) PKV_RING(64, 8, 4, 2, true, true); else PKV_RING(64, 8, 4, 2, false, true); }
+    else if (p.d_k == 64 && g == 4) { if (q8) PKV_RING(64, 4, 4, 2, true, true); else PKV_RING(64, 4, 4, 2, false, true); }
+    else return hipErrorInvalidValue;
+  } else if (!q8) {
+    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_G8_NW, PKV_G8_RING, false, false);
+    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_G4_RING, false, false);
+    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_G8_NW, PKV_G8_RING, false, false);
+    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_G4_RING, false, false);
     else return hipErrorInvalidValue;
   } else {
-    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true);
-    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_Q8_G4_RING, true);
-    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true);
-    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_Q8_G4_RING, true);
+    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true, false);
+    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_Q8_G4_RING, true, false);
+    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true, false);
+    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_Q8_G4_RING, true, false);
     else return hipErrorInvalidValue;
   }
 #undef PKV_RING
