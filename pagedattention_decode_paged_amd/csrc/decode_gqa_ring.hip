@@ -694,29 +694,38 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += kThr) {
-      const int h = idx / D, d = idx % D;
-      float M = -INFINITY;
+    // thread -> head h, columns d0 .. d0 + kCpt - 1: the merge factors once
+    // per thread, the waves' outputs as vector reads
+    constexpr int kCpt = G * D / kThr;
+    static_assert(G * D % kThr == 0 && (kCpt == 1 || kCpt == 2 || kCpt == 4), "merge split");
+    const int h = tid / (D / kCpt), d0 = (tid % (D / kCpt)) * kCpt;
+    float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_mml[w * G + h]);
-      float num = 0.f, den = 0.f;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_mml[w * G + h]);
+    float num[kCpt], den = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = s_mml[w * G + h];
-        const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        const float ow = s_mo[(w * G + h) * D + d] - (Q8 ? 128.f * s_mml[2 * NW * G + w * G + h] : 0.f);
-        num = fmaf(f, ow, num);
-        den = fmaf(f, s_mml[NW * G + w * G + h], den);
-      }
-      const float o = den > 0.f ? num / den : 0.f;
-      const int64_t row = (int64_t)b * n_h + (int64_t)kvh * G + h;
-      if (nsp == 1) {
-        reinterpret_cast<uint16_t*>(p.out)[row * D + d] = f32_to_bf16_rne(o);
-      } else {
-        const int64_t pi = row * p.num_splits + split;
-        p.part_o[pi * D + d] = o;
-        if (d == 0) { p.part_ml[2 * pi] = M; p.part_ml[2 * pi + 1] = den; }
-      }
+    for (int c = 0; c < kCpt; ++c) num[c] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = s_mml[w * G + h];
+      const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      den = fmaf(f, s_mml[NW * G + w * G + h], den);
+      const float off = Q8 ? 128.f * s_mml[2 * NW * G + w * G + h] : 0.f;
+      const float* ow = &s_mo[(w * G + h) * D + d0];
+#pragma unroll
+      for (int c = 0; c < kCpt; ++c) num[c] = fmaf(f, ow[c] - off, num[c]);
+    }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    const int64_t row = (int64_t)b * n_h + (int64_t)kvh * G + h;
+    if (nsp == 1) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * D + d0;
+#pragma unroll
+      for (int c = 0; c < kCpt; ++c) o[c] = f32_to_bf16_rne(num[c] * inv);
+    } else {
+      const int64_t pi = row * p.num_splits + split;
+#pragma unroll
+      for (int c = 0; c < kCpt; ++c) p.part_o[pi * D + d0 + c] = num[c] * inv;
+      if (d0 == 0) { p.part_ml[2 * pi] = M; p.part_ml[2 * pi + 1] = den; }
     }
     return;
   }
