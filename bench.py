@@ -220,7 +220,7 @@ def main():
                      "traffic": measured_traffic(),
                      "kernel": ("paged_decode_attention" if args.separate_calls else
                                 "paged_decode_attention_append (the ring kernel writes the new rows)") +
-                               ": decode_gqa_ring_kernel<128,8,4,2,MFMA> + decode_reduce_kernel",
+                               ": decode_gqa_ring_kernel<128,8,4,2,MFMA,2 KV heads> + decode_reduce_kernel",
                      "avg_launch_us": round(us_launch, 2),
                      "bytes_per_launch": kv_bytes_layer},
     }

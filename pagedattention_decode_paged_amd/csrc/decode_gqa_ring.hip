@@ -83,6 +83,11 @@
 #ifndef PKV_GQA_MFMA
 #define PKV_GQA_MFMA 1
 #endif
+// bf16 matrix-core path with d = 128: two adjacent KV heads per workgroup
+// (512 contiguous bytes per token per DMA row), when n_kv is even
+#ifndef PKV_GQA_PAIR
+#define PKV_GQA_PAIR 1
+#endif
 
 namespace pkv {
 namespace {
@@ -95,13 +100,17 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kStageTok = 64;    // tokens per stage (one per lane in the score phase)
-
-template <int D, int NW, bool Q8>
+// A workgroup serves KH adjacent KV heads (1, or 2 on the bf16 matrix-core
+// path): a token's rows of those heads are adjacent in the pool, so the DMA
+// moves KH * 256 contiguous bytes per token.  A stage holds 64 / KH tokens
+// (32 KiB of K and V either way).
+template <int D, int NW, bool Q8, int KH = 1>
 struct Ring {
-  static constexpr int kRowBytes = D * 2;                     // bf16 row (the LDS tiles)
-  static constexpr int kPieces = kRowBytes / 16;              // 16-byte pieces per bf16 row
-  static constexpr int kSrcRow = Q8 ? D : D * 2;              // bytes per row in the pool
+  static constexpr int kStageTok = 64 / KH;                   // tokens per stage
+  static constexpr int kHeadRow = Q8 ? D : D * 2;             // bytes of one head's row in the pool
+  static constexpr int kRowBytes = KH * D * 2;                // bf16 row of the LDS tiles (KH heads)
+  static constexpr int kPieces = D * 2 / 16;                  // 16-byte pieces per head row (bf16)
+  static constexpr int kSrcRow = KH * kHeadRow;               // bytes per token moved by the DMA
   static constexpr int kSrcPieces = kSrcRow / 16;
   static constexpr int kRowsPerDma = kWave / kSrcPieces;      // rows per DMA instruction
   static constexpr int kDmaPerMat = kStageTok / kRowsPerDma;  // per stage, per matrix
@@ -114,12 +123,14 @@ struct Ring {
   // waves 0 and 1
   static constexpr int kScaleWaves = Q8 ? 2 : 0;
   static_assert(D == 64 || D == 128, "row must be 64 or 128 elements");
+  static_assert(KH == 1 || (KH == 2 && !Q8 && D == 128), "two KV heads per workgroup: bf16, d = 128");
   static_assert(kDmaPerMat % kDmaPerWave == 0, "a wave issues K or V instructions only");
-  // Piece permutations of the bf16 tiles (row r's logical piece p sits at
-  // position p ^ swz(r)): K rows are read one row per lane, 16 lanes per LDS
-  // phase; V is read transposed, 4 rows x 2 pieces per 16 lanes, 32 lanes
-  // per phase.
-  static __device__ __forceinline__ int swz_k(int r) { return (r / kRows256) % kPieces; }
+  // Piece permutations of the bf16 tiles (row r's logical piece p of a head
+  // sits at position p ^ swz(r) of that head's pieces; every swz is below
+  // the pieces per head row): K rows are read one row per lane, 16 lanes
+  // per LDS phase; V is read transposed, 4 rows x 2 pieces per 16 lanes, 32
+  // lanes per phase.
+  static __device__ __forceinline__ int swz_k(int r) { return KH == 2 ? (r & 15) : (r / kRows256) % kPieces; }
   static __device__ __forceinline__ int swz_v(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
   }
@@ -192,10 +203,12 @@ __device__ __forceinline__ void widen_codes(const u32x4_t c, u32x4_t& lo, u32x4_
   hi = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
-template <int D, int G, int NW, int RING, bool Q8, bool COMPACT, bool MF>
+template <int D, int G, int NW, int RING, bool Q8, bool COMPACT, bool MF, int KH>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodeParams p) {
-  using R = Ring<D, NW, Q8>;
+  using R = Ring<D, NW, Q8, KH>;
+  constexpr int kStageTok = R::kStageTok;
   constexpr int kThr = 64 * NW;
+  static_assert(KH == 1 || MF, "two KV heads per workgroup only on the matrix-core path");
   constexpr int kHpw = MF ? 1 : G / NW;            // heads per wave (lane-per-token path)
   static_assert(MF || G % NW == 0, "g must be a multiple of the wave count");
   static_assert(!MF || (NW == 4 && G <= 16), "matrix-core path: four waves of 16 tokens, g <= 16");
@@ -218,9 +231,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   __shared__ int32_t s_upre[COMPACT ? kCompactMaxB + 1 : 1];
   __shared__ int32_t s_ctx[COMPACT ? kCompactMaxB : 1];
 
-  // KV head fastest in the grid: workgroups are dealt to the 8 XCDs
-  // round-robin by linear index, so each XCD serves whole KV heads
-  // (identical work) whatever the context lengths and split count
+  // KV head (group of KH heads) fastest in the grid: workgroups are dealt to
+  // the 8 XCDs round-robin by linear index, so each XCD serves whole KV
+  // heads (identical work) whatever the context lengths and split count
   const int kvh = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 
@@ -238,8 +251,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
 
   if (t_begin >= ctx) {
     if (split == 0) {                               // empty sequence: zero output
-      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)b * n_h + (int64_t)kvh * G) * D;
-      for (int i = tid; i < G * D; i += kThr) o[i] = 0;
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)b * n_h + (int64_t)kvh * KH * G) * D;
+      for (int i = tid; i < KH * G * D; i += kThr) o[i] = 0;
     }
     return;
   }
@@ -255,11 +268,11 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   }
   __syncthreads();
 
-  const int64_t slot_stride = (int64_t)p.n_kv * R::kSrcRow;
+  const int64_t slot_stride = (int64_t)p.n_kv * R::kHeadRow;   // bytes per token slot
   if constexpr (!Q8) {
     if (p.k_new != nullptr && t_end == ctx) {
       // Append: the workgroup holding the sequence's last token writes that
-      // token's new K and V rows (this KV head) into its slot, and the store
+      // token's new K and V rows (its KV heads) into its slot, and the store
       // completes before any of the workgroup's DMA can read the slot.
       if (wave == 0) {
         constexpr int kLanesPerRow = R::kSrcRow / 16;       // 16-byte pieces per row
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
           const int64_t sl = ((int64_t)phys << shift) + (t_last & bmask);
           const int64_t off = (int64_t)kvh * R::kSrcRow + piece * 16;
           const uint8_t* src = reinterpret_cast<const uint8_t*>(m ? p.v_new : p.k_new) +
-                               ((int64_t)b * p.n_kv) * R::kSrcRow + off;
+                               ((int64_t)b * p.n_kv) * R::kHeadRow + off;
           uint8_t* dst = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(m ? p.v : p.k)) +
                          sl * slot_stride + off;
           *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
@@ -299,7 +312,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   };
   // per-lane offsets inside a block for the fast path; the permutation
   // depends on the row only through jm mod kSwzPeriod
-  constexpr int kSwzPeriod = Q8 ? 1 : (D == 128 ? 4 : 2);
+  constexpr int kSwzPeriod = Q8 ? 1 : (KH == 2 ? 8 : (D == 128 ? 4 : 2));
   uint32_t voff[kSwzPeriod];
 #pragma unroll
   for (int i = 0; i < kSwzPeriod; ++i)
@@ -395,8 +408,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   if constexpr (MF) {
 #pragma unroll
     for (int c = 0; c < kCb; ++c) macc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int kv_w = kvh * KH + (KH == 2 ? (wave >> 1) : 0);   // this wave's KV head
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) +
-                          ((int64_t)b * n_h + (int64_t)kvh * G + min(ml16, G - 1)) * D * 2;
+                          ((int64_t)b * n_h + (int64_t)kv_w * G + min(ml16, G - 1)) * D * 2;
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + (32 * ks + 8 * mg) * 2);
@@ -477,16 +491,19 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
     const bool valid = tile0 + lane < t_end;
 
     if constexpr (MF) {
-      const int row = 16 * wave + ml16;              // K row of this lane (A operand)
+      // wave -> (KV head of the group, 16-token block of the stage)
+      const int tb = KH == 2 ? 16 * (wave & 1) : 16 * wave;
+      const int hoff = KH == 2 ? (wave >> 1) * (D * 2) : 0;
+      const int row = tb + ml16;                     // K row of this lane (A operand)
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks) {
         const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
-            kst + row * R::kRowBytes + (((4 * ks + mg) ^ R::swz_k(row)) * 16));
+            kst + row * R::kRowBytes + hoff + (((4 * ks + mg) ^ R::swz_k(row)) * 16));
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
                                                        __builtin_bit_cast(bf16x8_t, qf[ks]), sacc, 0, 0, 0);
       }
-      const int tl0 = 16 * wave + 4 * mg;            // this lane's first token in the stage
+      const int tl0 = tb + 4 * mg;                   // this lane's first token in the stage
       float sk[4] = {1.f, 1.f, 1.f, 1.f}, svv[4] = {1.f, 1.f, 1.f, 1.f};
       if constexpr (Q8) {
         const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&s_scl[0][slot][tl0]);
@@ -543,7 +560,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       // column ml16 of rows tl0 .. tl0 + 3
       const int tv = tl0 + (ml16 >> 2), cp = ml16 & 3;
       const uint32_t vrow = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)vst +
-                            (uint32_t)(tv * R::kRowBytes + 8 * (cp & 1));
+                            (uint32_t)(tv * R::kRowBytes + hoff + 8 * (cp & 1));
       const int svz = R::swz_vm(tv);
 #pragma unroll
       for (int c = 0; c < kCb; ++c) {
@@ -694,19 +711,23 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       }
     }
     __syncthreads();
-    // thread -> head h, columns d0 .. d0 + kCpt - 1: the merge factors once
-    // per thread, the waves' outputs as vector reads
-    constexpr int kCpt = G * D / kThr;
-    static_assert(G * D % kThr == 0 && (kCpt == 1 || kCpt == 2 || kCpt == 4), "merge split");
-    const int h = tid / (D / kCpt), d0 = (tid % (D / kCpt)) * kCpt;
+    // thread -> head h of KV head kh of the group, columns d0 .. d0 + kCpt - 1:
+    // the merge factors once per thread, the waves' outputs as vector reads;
+    // waves kh * kWph .. + kWph - 1 hold that KV head
+    constexpr int kWph = NW / KH;
+    constexpr int kCpt = KH * G * D / kThr;
+    static_assert(KH * G * D % kThr == 0 && kCpt >= 1 && kCpt <= 8 && (kCpt & (kCpt - 1)) == 0, "merge split");
+    const int hh = tid / (D / kCpt), d0 = (tid % (D / kCpt)) * kCpt;
+    const int kh = hh / G, h = hh % G;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_mml[w * G + h]);
+    for (int j = 0; j < kWph; ++j) M = fmaxf(M, s_mml[(kh * kWph + j) * G + h]);
     float num[kCpt], den = 0.f;
 #pragma unroll
     for (int c = 0; c < kCpt; ++c) num[c] = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int j = 0; j < kWph; ++j) {
+      const int w = kh * kWph + j;
       const float mw = s_mml[w * G + h];
       const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       den = fmaf(f, s_mml[NW * G + w * G + h], den);
@@ -716,7 +737,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       for (int c = 0; c < kCpt; ++c) num[c] = fmaf(f, ow[c] - off, num[c]);
     }
     const float inv = den > 0.f ? 1.0f / den : 0.f;
-    const int64_t row = (int64_t)b * n_h + (int64_t)kvh * G + h;
+    const int64_t row = (int64_t)b * n_h + (int64_t)(kvh * KH + kh) * G + h;
     if (nsp == 1) {
       uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * D + d0;
 #pragma unroll
@@ -811,38 +832,53 @@ bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
          (g == 4 || g == 8);
 }
 
+int gqa_ring_kv_group(KV kv, bool q_bf16, int d_k, int d_v, int g, int n_kv) {
+  return (PKV_GQA_MFMA && PKV_GQA_PAIR && kv == KV::BF16 && q_bf16 && d_k == 128 && d_v == 128 &&
+          (g == 4 || g == 8) && n_kv % 2 == 0)
+             ? 2
+             : 1;
+}
+
 hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
   if (p.compact_units != 0 && (p.B > kCompactMaxB || p.compact_units < 0)) return hipErrorInvalidValue;
-  const dim3 grid = p.compact_units != 0 ? dim3((unsigned)p.n_kv, (unsigned)p.compact_units, 1u)
-                                          : dim3((unsigned)p.n_kv, (unsigned)p.B, (unsigned)p.num_splits);
   const int g = p.n_h / p.n_kv;
+  const int kh = gqa_ring_kv_group(p.kv, p.q_bf16, p.d_k, p.d_v, g, p.n_kv);
+  const unsigned groups = (unsigned)(p.n_kv / kh);
+  const dim3 grid = p.compact_units != 0 ? dim3(groups, (unsigned)p.compact_units, 1u)
+                                          : dim3(groups, (unsigned)p.B, (unsigned)p.num_splits);
   const bool q8 = p.kv == KV::INT8;
-#define PKV_RING(D_, G_, NW_, RING_, Q8_, MF_)                                                      \
+#define PKV_RING(D_, G_, NW_, RING_, Q8_, MF_, KH_)                                                 \
   do {                                                                                              \
     if (p.compact_units != 0)                                                                      \
-      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, true, MF_>), grid,          \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, true, MF_, KH_>), grid,     \
                          dim3(64 * NW_), 0, stream, p);                                            \
     else                                                                                           \
-      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, false, MF_>), grid,         \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, false, MF_, KH_>), grid,    \
                          dim3(64 * NW_), 0, stream, p);                                            \
   } while (0)
   if (PKV_GQA_MFMA) {
-    if (p.d_k == 128 && g == 8) { if (q8) PKV_RING(128, 8, 4, 2, true, true); else PKV_RING(128, 8, 4, 2, false, true); }
-    else if (p.d_k == 128 && g == 4) { if (q8) PKV_RING(128, 4, 4, 2, true, true); else PKV_RING(128, 4, 4, 2, false, true); }
-    else if (p.d_k == 64 && g == 8) { if (q8) PKV_RING(64, 8, 4, 2, true, true); else PKV_RING(64, 8, 4, 2, false, true); }
-    else if (p.d_k == 64 && g == 4) { if (q8) PKV_RING(64, 4, 4, 2, true, true); else PKV_RING(64, 4, 4, 2, false, true); }
+    if (p.d_k == 128 && g == 8) {
+      if (q8) PKV_RING(128, 8, 4, 2, true, true, 1);
+      else if (kh == 2) PKV_RING(128, 8, 4, 2, false, true, 2);
+      else PKV_RING(128, 8, 4, 2, false, true, 1);
+    } else if (p.d_k == 128 && g == 4) {
+      if (q8) PKV_RING(128, 4, 4, 2, true, true, 1);
+      else if (kh == 2) PKV_RING(128, 4, 4, 2, false, true, 2);
+      else PKV_RING(128, 4, 4, 2, false, true, 1);
+    } else if (p.d_k == 64 && g == 8) { if (q8) PKV_RING(64, 8, 4, 2, true, true, 1); else PKV_RING(64, 8, 4, 2, false, true, 1); }
+    else if (p.d_k == 64 && g == 4) { if (q8) PKV_RING(64, 4, 4, 2, true, true, 1); else PKV_RING(64, 4, 4, 2, false, true, 1); }
     else return hipErrorInvalidValue;
   } else if (!q8) {
-    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_G8_NW, PKV_G8_RING, false, false);
-    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_G4_RING, false, false);
-    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_G8_NW, PKV_G8_RING, false, false);
-    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_G4_RING, false, false);
+    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_G8_NW, PKV_G8_RING, false, false, 1);
+    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_G4_RING, false, false, 1);
+    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_G8_NW, PKV_G8_RING, false, false, 1);
+    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_G4_RING, false, false, 1);
     else return hipErrorInvalidValue;
   } else {
-    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true, false);
-    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_Q8_G4_RING, true, false);
-    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true, false);
-    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_Q8_G4_RING, true, false);
+    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true, false, 1);
+    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_Q8_G4_RING, true, false, 1);
+    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true, false, 1);
+    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_Q8_G4_RING, true, false, 1);
     else return hipErrorInvalidValue;
   }
 #undef PKV_RING

@@ -112,6 +112,10 @@ int mla_head_groups(int n_h);
 // bf16 GQA with g in {4, 8}: the LDS-ring kernel (decode_gqa_ring.hip);
 // launch_decode_gqa routes the shapes it covers there.
 bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g);
+// KV heads served by one workgroup of that kernel (1, or 2 when a token's
+// rows of two adjacent KV heads are moved together); the split planning
+// counts work units per group.
+int gqa_ring_kv_group(KV kv, bool q_bf16, int d_k, int d_v, int g, int n_kv);
 hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream);
 
 // Whether an instance exists (host-side check before launch).
