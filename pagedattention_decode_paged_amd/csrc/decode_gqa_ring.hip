@@ -88,6 +88,12 @@
 #ifndef PKV_GQA_PAIR
 #define PKV_GQA_PAIR 1
 #endif
+// INT8 matrix-core path with d = 128: up to this many adjacent KV heads per
+// workgroup (128-byte code rows moved KH at a time; on the skewed 70B-shaped
+// INT8 batch 1, 2, 4 heads: 113.4, 112.5, 123.5 us)
+#ifndef PKV_Q8_KH
+#define PKV_Q8_KH 2
+#endif
 
 namespace pkv {
 namespace {
@@ -100,10 +106,10 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-// A workgroup serves KH adjacent KV heads (1, or 2 on the bf16 matrix-core
+// A workgroup serves KH adjacent KV heads (1, or 2 / 4 on the matrix-core
 // path): a token's rows of those heads are adjacent in the pool, so the DMA
-// moves KH * 256 contiguous bytes per token.  A stage holds 64 / KH tokens
-// (32 KiB of K and V either way).
+// moves KH rows of 256 (bf16) or 128 (INT8) contiguous bytes per token.  A
+// stage holds 64 / KH tokens.
 template <int D, int NW, bool Q8, int KH = 1>
 struct Ring {
   static constexpr int kStageTok = 64 / KH;                   // tokens per stage
@@ -118,19 +124,20 @@ struct Ring {
   static constexpr int kMatBytes = kStageTok * kRowBytes;     // one bf16 tile
   static constexpr int kSrcBytes = kStageTok * kSrcRow;       // one matrix of a staged stage
   static constexpr int kHalves = D / 64;                      // 64-column passes of the value phase
-  static constexpr int kRows256 = 256 / kRowBytes;            // bf16 rows per 256 bytes
+  static constexpr int kRows256 = kRowBytes >= 256 ? 1 : 256 / kRowBytes;   // bf16 rows per 256 bytes (>= 1)
   // INT8 scales: one 4-byte DMA instruction per matrix per stage, issued by
   // waves 0 and 1
   static constexpr int kScaleWaves = Q8 ? 2 : 0;
   static_assert(D == 64 || D == 128, "row must be 64 or 128 elements");
-  static_assert(KH == 1 || (KH == 2 && !Q8 && D == 128), "two KV heads per workgroup: bf16, d = 128");
+  static_assert(KH == 1 || (D == 128 && (KH == 2 || (Q8 && KH == 4))),
+                "KV-head groups: d = 128, two heads (bf16, INT8) or four (INT8)");
   static_assert(kDmaPerMat % kDmaPerWave == 0, "a wave issues K or V instructions only");
   // Piece permutations of the bf16 tiles (row r's logical piece p of a head
   // sits at position p ^ swz(r) of that head's pieces; every swz is below
   // the pieces per head row): K rows are read one row per lane, 16 lanes
   // per LDS phase; V is read transposed, 4 rows x 2 pieces per 16 lanes, 32
   // lanes per phase.
-  static __device__ __forceinline__ int swz_k(int r) { return KH == 2 ? (r & 15) : (r / kRows256) % kPieces; }
+  static __device__ __forceinline__ int swz_k(int r) { return (r / kRows256) % kPieces; }
   static __device__ __forceinline__ int swz_v(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
   }
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   constexpr int kRingBytes = Q8 ? R::kSrcBytes : R::kMatBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t s_dma[2][RING][kRingBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[Q8 ? 2 : 1][Q8 ? R::kMatBytes : 16];
-  __shared__ __align__(16) float s_scl[2][Q8 ? RING : 1][Q8 ? kStageTok : 1];
+  __shared__ __align__(16) float s_scl[2][Q8 ? RING : 1][Q8 ? KH * kStageTok : 1];   // [head][token]
   __shared__ __align__(16) int32_t s_bt[kBtSlots];
   __shared__ __align__(16) uint32_t s_pp[MF ? 1 : NW][kHpw][kStageTok / 2];
   // matrix-core path: per wave and head the running maximum, sum (and the
@@ -323,6 +330,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   const float* scl_src = wave == 0 ? p.k_scale : p.v_scale;
   const uint32_t lds_scl =
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&s_scl[wave == 0 ? 0 : 1][0][0];
+  const int scl_h = lane / kStageTok, scl_t = lane % kStageTok;   // lane -> (head of the group, token)
   const int dma_per_wave = R::kDmaPerWave + (wave < R::kScaleWaves ? 1 : 0);
 
   auto issue = [&](int s, int slot) {
@@ -358,11 +366,12 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
     }
     if constexpr (Q8) {
       if (wave < R::kScaleWaves) {
-        // scales [num_blocks, n_kv, block_size]: a block's scales of this
-        // head are adjacent, so the 64 tokens' scales are whole 64-byte runs
-        const int t = min(tile0 + lane, t_last);
-        const int64_t si = (((int64_t)s_bt[(t >> shift) - lb0] * p.n_kv + kvh) << shift) + (t & bmask);
-        dma4(scl_src + si, lds_scl + (uint32_t)(slot * kStageTok * 4));
+        // scales [num_blocks, n_kv, block_size]: a block's scales of the
+        // group's heads are adjacent, so the stage's scales are whole runs
+        const int t = min(tile0 + scl_t, t_last);
+        const int64_t si =
+            (((int64_t)s_bt[(t >> shift) - lb0] * p.n_kv + kvh * KH + scl_h) << shift) + (t & bmask);
+        dma4(scl_src + si, lds_scl + (uint32_t)(slot * KH * kStageTok * 4));
       }
     }
   };
@@ -408,7 +417,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   if constexpr (MF) {
 #pragma unroll
     for (int c = 0; c < kCb; ++c) macc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int kv_w = kvh * KH + (KH == 2 ? (wave >> 1) : 0);   // this wave's KV head
+    const int kv_w = kvh * KH + wave / (NW / KH);             // this wave's KV head
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) +
                           ((int64_t)b * n_h + (int64_t)kv_w * G + min(ml16, G - 1)) * D * 2;
 #pragma unroll
@@ -473,12 +482,15 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
         const int r = (q / R::kSrcPieces) % kStageTok;
         const int e = q % R::kSrcPieces;
         const u32x4_t c = *reinterpret_cast<const u32x4_t*>(&s_dma[m][slot][(r * R::kSrcPieces + e) * 16]);
+        constexpr int kCodePiecesPerHead = D / 16;              // 16-byte code pieces per head row
+        const int eh = e % kCodePiecesPerHead;
+        const int ehead = e / kCodePiecesPerHead;
         u32x4_t lo, hi;
         widen_codes(c, lo, hi);
         const int sw = m ? (MF ? R::swz_vm(r) : R::swz_v(r)) : R::swz_k(r);
-        uint8_t* row = &s_tile[m][r * R::kRowBytes];
-        *reinterpret_cast<u32x4_t*>(row + ((2 * e) ^ sw) * 16) = lo;
-        *reinterpret_cast<u32x4_t*>(row + ((2 * e + 1) ^ sw) * 16) = hi;
+        uint8_t* row = &s_tile[m][r * R::kRowBytes + ehead * (D * 2)];
+        *reinterpret_cast<u32x4_t*>(row + ((2 * eh) ^ sw) * 16) = lo;
+        *reinterpret_cast<u32x4_t*>(row + ((2 * eh + 1) ^ sw) * 16) = hi;
       }
       lds_barrier();
       kst = &s_tile[0][0];
@@ -492,8 +504,10 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
 
     if constexpr (MF) {
       // wave -> (KV head of the group, 16-token block of the stage)
-      const int tb = KH == 2 ? 16 * (wave & 1) : 16 * wave;
-      const int hoff = KH == 2 ? (wave >> 1) * (D * 2) : 0;
+      constexpr int kWphS = NW / KH;
+      const int khw = wave / kWphS;
+      const int tb = 16 * (wave % kWphS);
+      const int hoff = khw * (D * 2);
       const int row = tb + ml16;                     // K row of this lane (A operand)
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -506,8 +520,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       const int tl0 = tb + 4 * mg;                   // this lane's first token in the stage
       float sk[4] = {1.f, 1.f, 1.f, 1.f}, svv[4] = {1.f, 1.f, 1.f, 1.f};
       if constexpr (Q8) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&s_scl[0][slot][tl0]);
-        const f32x4_t c = *reinterpret_cast<const f32x4_t*>(&s_scl[1][slot][tl0]);
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&s_scl[0][slot][khw * kStageTok + tl0]);
+        const f32x4_t c = *reinterpret_cast<const f32x4_t*>(&s_scl[1][slot][khw * kStageTok + tl0]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) { sk[i] = a[i]; svv[i] = c[i]; }
       }
@@ -716,7 +730,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
     // waves kh * kWph .. + kWph - 1 hold that KV head
     constexpr int kWph = NW / KH;
     constexpr int kCpt = KH * G * D / kThr;
-    static_assert(KH * G * D % kThr == 0 && kCpt >= 1 && kCpt <= 8 && (kCpt & (kCpt - 1)) == 0, "merge split");
+    static_assert(KH * G * D % kThr == 0 && kCpt >= 1 && kCpt <= 16 && (kCpt & (kCpt - 1)) == 0, "merge split");
     const int hh = tid / (D / kCpt), d0 = (tid % (D / kCpt)) * kCpt;
     const int kh = hh / G, h = hh % G;
     float M = -INFINITY;
@@ -833,10 +847,13 @@ bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
 }
 
 int gqa_ring_kv_group(KV kv, bool q_bf16, int d_k, int d_v, int g, int n_kv) {
-  return (PKV_GQA_MFMA && PKV_GQA_PAIR && kv == KV::BF16 && q_bf16 && d_k == 128 && d_v == 128 &&
-          (g == 4 || g == 8) && n_kv % 2 == 0)
-             ? 2
-             : 1;
+  if (!PKV_GQA_MFMA || !q_bf16 || d_k != 128 || d_v != 128 || !(g == 4 || g == 8)) return 1;
+  if (kv == KV::BF16) return PKV_GQA_PAIR && n_kv % 2 == 0 ? 2 : 1;
+  if (kv == KV::INT8) {
+    if (PKV_Q8_KH >= 4 && n_kv % 4 == 0) return 4;
+    if (PKV_Q8_KH >= 2 && n_kv % 2 == 0) return 2;
+  }
+  return 1;
 }
 
 hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
@@ -858,11 +875,15 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
   } while (0)
   if (PKV_GQA_MFMA) {
     if (p.d_k == 128 && g == 8) {
-      if (q8) PKV_RING(128, 8, 4, 2, true, true, 1);
+      if (q8 && kh == 4) PKV_RING(128, 8, 4, 2, true, true, 4);
+      else if (q8 && kh == 2) PKV_RING(128, 8, 4, 2, true, true, 2);
+      else if (q8) PKV_RING(128, 8, 4, 2, true, true, 1);
       else if (kh == 2) PKV_RING(128, 8, 4, 2, false, true, 2);
       else PKV_RING(128, 8, 4, 2, false, true, 1);
     } else if (p.d_k == 128 && g == 4) {
-      if (q8) PKV_RING(128, 4, 4, 2, true, true, 1);
+      if (q8 && kh == 4) PKV_RING(128, 4, 4, 2, true, true, 4);
+      else if (q8 && kh == 2) PKV_RING(128, 4, 4, 2, true, true, 2);
+      else if (q8) PKV_RING(128, 4, 4, 2, true, true, 1);
       else if (kh == 2) PKV_RING(128, 4, 4, 2, false, true, 2);
       else PKV_RING(128, 4, 4, 2, false, true, 1);
     } else if (p.d_k == 64 && g == 8) { if (q8) PKV_RING(64, 8, 4, 2, true, true, 1); else PKV_RING(64, 8, 4, 2, false, true, 1); }

@@ -308,11 +308,12 @@ int32_t plan_split(const kvp_decode_desc* d, Variant v) {
   const int64_t total = d->total_context_len > 0 ? d->total_context_len
                                                  : (int64_t)d->B * d->max_context_len;
   int64_t heads = v == Variant::Mla ? 1 : d->n_kv;
-  if (v == Variant::Float && d->n_kv > 0) {
-    // the ring kernel may serve two KV heads per workgroup
+  if ((v == Variant::Float || v == Variant::Int8) && d->n_kv > 0) {
+    // the ring kernel may serve a group of adjacent KV heads per workgroup
     const int gq = d->n_h / d->n_kv;
     const bool qb = d->q_dtype == KVP_BF16;
-    const pkv::KV kv = d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32;
+    const pkv::KV kv = v == Variant::Int8 ? pkv::KV::INT8
+                                          : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
     if (pkv::gqa_ring_supported(kv, qb, d->d_k, d->d_v, gq))
       heads /= pkv::gqa_ring_kv_group(kv, qb, d->d_k, d->d_v, gq, d->n_kv);
   }

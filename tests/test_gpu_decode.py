@@ -85,6 +85,24 @@ def test_ragged_contexts(kind, d, g, bs):
     assert max_err(out, ref) <= tol
 
 
+@pytest.mark.parametrize("n_kv,g", [(1, 8), (2, 8), (3, 8), (4, 4), (6, 4), (8, 8)])
+def test_kv_head_groups_bf16(n_kv, g):
+    """bf16 with d = 128 runs two adjacent KV heads per workgroup when n_kv
+    is even and one otherwise; both against the oracle on the plain grid,
+    with several context splits and on the compact grid."""
+    ctxs = [1, 17, 40, 300, 1025, 0, 64]
+    d, bs = 128, 16
+    cfg = type("C", (), dict(block_size=bs, n_kv=n_kv, d_k=d, d_v=d, n_h=n_kv * g))
+    s = custom_structure(ctxs, bs, seed=n_kv * 10 + g, pad_blocks=1)
+    pool, bt, ctx, q, (_, _, qh, _) = _prefilled_case(cfg, s, 300 + n_kv + g, "bf16")
+    scale = 1.0 / math.sqrt(d)
+    ref = oracle.paged_decode_attention(qh, host(pool.k), host(pool.v), s.block_table, s.context_lens, scale)
+    for kw in (dict(), dict(split_tokens=256), dict(total_context_len=int(s.context_lens.sum()))):
+        out = _run(pool, q, bt, ctx, s, scale, **kw)
+        torch.cuda.synchronize()
+        assert max_err(out, ref) <= TOL_BF16, kw
+
+
 def test_single_token_context_returns_v_exactly_and_empty_context_gives_zero():
     cfg = CONFIGS["tiny"]
     s = custom_structure([1, 0, 1], 16, seed=2)

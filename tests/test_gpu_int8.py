@@ -85,6 +85,20 @@ def test_int8_ragged(d, g, bs):
     _check_attention(pool, q, bt, ctx, s, 1.0 / math.sqrt(d), split_tokens=256)
 
 
+@pytest.mark.parametrize("n_kv,g", [(1, 8), (2, 8), (4, 8), (6, 4), (8, 4), (12, 8)])
+def test_int8_kv_head_groups(n_kv, g):
+    """INT8 with d = 128 runs four adjacent KV heads per workgroup when n_kv
+    is a multiple of 4, two when it is even, else one: all against the oracle
+    on the plain grid, with several context splits and on the compact grid."""
+    ctxs = [1, 17, 40, 300, 1025, 0, 64]
+    s = custom_structure(ctxs, 16, seed=n_kv * 10 + g, pad_blocks=1)
+    pool, q, bt, ctx = _int8_case(s, n_kv * g, n_kv, 128, 300 + n_kv + g)
+    scale = 1.0 / math.sqrt(128)
+    _check_attention(pool, q, bt, ctx, s, scale)
+    _check_attention(pool, q, bt, ctx, s, scale, split_tokens=256)
+    _check_attention(pool, q, bt, ctx, s, scale, total_context_len=int(s.context_lens.sum()))
+
+
 def test_int8_from_fp32_rows():
     s = custom_structure([40, 300], 16, seed=4)
     pool, q, bt, ctx = _int8_case(s, 16, 2, 128, 9, src_dtype=torch.float32)
