@@ -25,30 +25,20 @@
 //   out exactly afterwards: q . code = q . u - 128 sum(q) for the scores and
 //   sum_t p'_t code_t = sum_t p'_t u_t - 128 sum_t p'_t for the values, with
 //   p'_t = p_t * sV_t.
-// * Matrix-core path (the default): four waves, each taking 16 tokens of a
-//   stage for all g heads (padded to 16).  Per KV head the work is a dense
-//   [g x d] . [d x tokens] contraction: S^T = K Q^T and O^T += V^T P^T on
-//   v_mfma_f32_16x16x32_bf16 / 16x16x16bf16_1k, with lane l holding head
-//   l % 16 and tokens 4 (l / 16) .. + 3 in both, so the weights feed the
-//   second product from the lane's own registers.  Each wave keeps its own
-//   softmax state; the four are merged through LDS at the end.
-// * Lane-per-token path (PKV_GQA_MFMA=0): the waves split the g heads
-//   (g / NW each) and every wave walks all tokens of the stage, so each
-//   wave's softmax state is final at the end; described below.  On both
-//   paths a K/V byte crosses HBM once and feeds all g heads.
-// * Scores: lane i owns token i of the stage and reads its K row from LDS
-//   (rows are stored with their 16-byte pieces permuted by the row index, so
-//   the 16 lanes of a read phase hit distinct banks of the 64-bank LDS); q
-//   is uniform per wave and streamed through scalar registers; v_dot2 on
-//   bf16 pairs, fp32 sums.
-// * Online softmax per stage in base 2 (scale * log2 e folded into q.K);
-//   the stage maximum comes from DPP; the value-phase weights are rounded to
-//   bf16 by v_cvt_pk_bf16_f32 in token pairs into a per-wave LDS slice.
-// * Values: lane (group j, index i) owns output column 16 k + i of every
-//   head of the wave, k = j (+ 4 for the upper half of d = 128); one
-//   transposed LDS read (ds_read_b64_tr_b16) returns that column for four
-//   consecutive tokens, i.e. two bf16 token pairs that v_dot2 multiplies
-//   with the matching weight pairs.  Each lane accumulates whole columns.
+// * Four waves; each takes 16 tokens of a stage for all g heads (padded to
+//   16).  Per KV head the work is a dense [g x d] . [d x tokens]
+//   contraction: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16
+//   / 16x16x16bf16_1k, with lane l holding head l % 16 and tokens
+//   4 (l / 16) .. + 3 in both, so the weights feed the second product from
+//   the lane's own registers and a head's rescale factor sits in the lanes
+//   that hold its outputs.  Online softmax in base 2 (scale * log2 e folded
+//   in), with a lazy rescale.  Each wave keeps its own softmax state; the
+//   four are merged through LDS at the end.  A K/V byte crosses HBM once and
+//   feeds all g heads.
+// * K rows are read one per lane (16 lanes per LDS phase) and V transposed
+//   (ds_read_b64_tr_b16, 4 rows of 2 pieces per 16 lanes); both tiles are
+//   stored with their 16-byte pieces permuted by row so that every read
+//   phase hits distinct banks of the 64-bank LDS.
 // * Tokens at or past the context length re-read the last valid row (finite
 //   data): their scores are -inf and weights 0, so unused slots (NaN in the
 //   tests) are never read.
@@ -57,38 +47,16 @@
 #include "internal.h"
 #include "device_common.h"
 
-// Launch shapes (measured on the 70B-shaped layer): two 64 KiB rings per
-// compute unit (two workgroups resident) beat one 128 KiB ring; bf16 runs
-// 4 waves for g = 8 (two heads each: each K/V row read from LDS serves two
-// heads; 1 % faster than 8 waves of one head) and for g = 4 (one head each).
-#ifndef PKV_G8_NW
-#define PKV_G8_NW 4
-#endif
-#ifndef PKV_G8_RING
-#define PKV_G8_RING 2
-#endif
-#ifndef PKV_G4_RING
-#define PKV_G4_RING 2
-#endif
-#ifndef PKV_Q8_G8_NW
-#define PKV_Q8_G8_NW 8
-#endif
-#ifndef PKV_Q8_G8_RING
-#define PKV_Q8_G8_RING 2
-#endif
-#ifndef PKV_Q8_G4_RING
-#define PKV_Q8_G4_RING 2
-#endif
-// matrix-core path (four waves, 16 tokens of each stage per wave)
-#ifndef PKV_GQA_MFMA
-#define PKV_GQA_MFMA 1
-#endif
-// bf16 matrix-core path with d = 128: two adjacent KV heads per workgroup
+// Launch shape (measured on the 70B-shaped layer): four waves, two 32 KiB
+// stages (two workgroups resident per compute unit).
+constexpr int kWaves = 4;
+constexpr int kRing = 2;
+// bf16 with d = 128: two adjacent KV heads per workgroup
 // (512 contiguous bytes per token per DMA row), when n_kv is even
 #ifndef PKV_GQA_PAIR
 #define PKV_GQA_PAIR 1
 #endif
-// INT8 matrix-core path with d = 128: up to this many adjacent KV heads per
+// INT8 with d = 128: up to this many adjacent KV heads per
 // workgroup (128-byte code rows moved KH at a time; on the skewed 70B-shaped
 // INT8 batch 1, 2, 4 heads: 113.4, 112.5, 123.5 us)
 #ifndef PKV_Q8_KH
@@ -123,7 +91,6 @@ struct Ring {
   static constexpr int kDmaPerWave = 2 * kDmaPerMat / NW;     // each wave's row share (K or V)
   static constexpr int kMatBytes = kStageTok * kRowBytes;     // one bf16 tile
   static constexpr int kSrcBytes = kStageTok * kSrcRow;       // one matrix of a staged stage
-  static constexpr int kHalves = D / 64;                      // 64-column passes of the value phase
   static constexpr int kRows256 = kRowBytes >= 256 ? 1 : 256 / kRowBytes;   // bf16 rows per 256 bytes (>= 1)
   // INT8 scales: one 4-byte DMA instruction per matrix per stage, issued by
   // waves 0 and 1
@@ -138,13 +105,9 @@ struct Ring {
   // per LDS phase; V is read transposed, 4 rows x 2 pieces per 16 lanes, 32
   // lanes per phase.
   static __device__ __forceinline__ int swz_k(int r) { return (r / kRows256) % kPieces; }
+  // V: the two 16-lane groups of a transposed read phase are on rows 4
+  // apart, so the 8 rows of a phase need distinct piece positions
   static __device__ __forceinline__ int swz_v(int r) {
-    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-  }
-  // matrix-core path: V is read transposed, 4 rows of 2 pieces per 16
-  // lanes, the two 16-lane groups of a phase on rows 4 apart, so the 8 rows
-  // of a phase need distinct piece positions
-  static __device__ __forceinline__ int swz_vm(int r) {
     return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
   }
 };
@@ -210,17 +173,14 @@ __device__ __forceinline__ void widen_codes(const u32x4_t c, u32x4_t& lo, u32x4_
   hi = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
-template <int D, int G, int NW, int RING, bool Q8, bool COMPACT, bool MF, int KH>
+template <int D, int G, int NW, int RING, bool Q8, bool COMPACT, int KH>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodeParams p) {
   using R = Ring<D, NW, Q8, KH>;
   constexpr int kStageTok = R::kStageTok;
   constexpr int kThr = 64 * NW;
-  static_assert(KH == 1 || MF, "two KV heads per workgroup only on the matrix-core path");
-  constexpr int kHpw = MF ? 1 : G / NW;            // heads per wave (lane-per-token path)
-  static_assert(MF || G % NW == 0, "g must be a multiple of the wave count");
-  static_assert(!MF || (NW == 4 && G <= 16), "matrix-core path: four waves of 16 tokens, g <= 16");
-  // matrix-core path: k-steps of the score product (32 dims each) and
-  // 16-column blocks of the value product
+  static_assert(NW == 4 && G <= 16, "four waves of 16 tokens per stage, g <= 16");
+  // k-steps of the score product (32 dims each) and 16-column blocks of
+  // the value product
   constexpr int kKs = D / 32;
   constexpr int kCb = D / 16;
   // bf16: the DMA ring holds the K and V tiles themselves.  INT8: it holds
@@ -230,10 +190,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[Q8 ? 2 : 1][Q8 ? R::kMatBytes : 16];
   __shared__ __align__(16) float s_scl[2][Q8 ? RING : 1][Q8 ? KH * kStageTok : 1];   // [head][token]
   __shared__ __align__(16) int32_t s_bt[kBtSlots];
-  __shared__ __align__(16) uint32_t s_pp[MF ? 1 : NW][kHpw][kStageTok / 2];
-  // matrix-core path: per wave and head the running maximum, sum (and the
-  // INT8 weight sum) for the final merge of the four waves
-  __shared__ float s_mml[MF ? 3 * NW * G : 1];
+  // per wave and head the running maximum, sum (and the INT8 weight sum)
+  // for the final merge of the four waves
+  __shared__ float s_mml[3 * NW * G];
   // compact grid only: units before each sequence, and the context lengths
   __shared__ int32_t s_upre[COMPACT ? kCompactMaxB + 1 : 1];
   __shared__ int32_t s_ctx[COMPACT ? kCompactMaxB : 1];
@@ -254,7 +213,6 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   const int lane = tid & 63;
   const int t_begin = split * p.split_tokens;
   const int n_h = p.n_h;
-  const int h0 = kvh * G + wave * kHpw;            // first query head of this wave
 
   if (t_begin >= ctx) {
     if (split == 0) {                               // empty sequence: zero output
@@ -315,7 +273,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   // (permuted); INT8 codes go to the staging ring in order
   auto src_piece = [&](int r) {
     if constexpr (Q8) return lpiece;
-    else return lpiece ^ (dma_v ? (MF ? R::swz_vm(r) : R::swz_v(r)) : R::swz_k(r));
+    else return lpiece ^ (dma_v ? R::swz_v(r) : R::swz_k(r));
   };
   // per-lane offsets inside a block for the fast path; the permutation
   // depends on the row only through jm mod kSwzPeriod
@@ -376,33 +334,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
     }
   };
 
-  float m_run[kHpw], l_run[kHpw], ps_run[kHpw];
-  float acc[kHpw][R::kHalves];
-#pragma unroll
-  for (int h = 0; h < kHpw; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-    ps_run[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < R::kHalves; ++e) acc[h][e] = 0.f;
-  }
   const float qscale = p.scale * kLog2e;
-  const int64_t q_dw0 = ((int64_t)b * n_h + h0) * (D / 2);   // this wave's q rows (contiguous)
-  // INT8: sum of each head's q (it multiplies the +128 offset of the codes)
-  float qsum[kHpw];
-#pragma unroll
-  for (int h = 0; h < kHpw; ++h) qsum[h] = 0.f;
-  if constexpr (Q8 && !MF) {
-#pragma unroll
-    for (int h = 0; h < kHpw; ++h) {
-      float t = 0.f;
-      const uint32_t* qh = reinterpret_cast<const uint32_t*>(p.q) + q_dw0 + h * (D / 2);
-      for (int i = lane; i < D / 2; i += kWave) t += bf_lo(qh[i]) + bf_hi(qh[i]);
-      qsum[h] = wave_sum(t);
-    }
-  }
-
-  // ---- matrix-core path.  Per stage each wave takes 16 tokens (rows
+  // ---- per stage each wave takes 16 tokens (rows
   // 16 wave .. + 15): S^T = K Q^T (A: K rows from LDS, B: Q^T fragments
   // kept in registers, zero for the padding heads g .. 15), then
   // O^T += V^T P^T (A: V^T by transposed LDS reads, B: the lane's own
@@ -411,10 +344,10 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   // and a head's rescale factor is in the lanes that hold its outputs.  Each
   // wave keeps its own softmax state; the four are merged at the end.
   const int ml16 = lane & 15, mg = lane >> 4;
-  u32x4_t qf[MF ? kKs : 1];
-  f32x4_t macc[MF ? kCb : 1];
+  u32x4_t qf[kKs];
+  f32x4_t macc[kCb];
   float mm_run = -INFINITY, ml_run = 0.f, mps_run = 0.f, mqsum = 0.f;
-  if constexpr (MF) {
+  {
 #pragma unroll
     for (int c = 0; c < kCb; ++c) macc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int kv_w = kvh * KH + wave / (NW / KH);             // this wave's KV head
@@ -436,25 +369,6 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       t += __shfl_xor(t, 32);
       mqsum = t;
     }
-  }
-
-  // loop-invariant LDS offsets: K row pieces of this lane's token, and the
-  // transposed V reads (lane = 16-lane group vg, index vi: token vt of a
-  // quad, 4-column chunk vc; output column 16 k + vi, k = 4 e + vg)
-  const int vg = lane >> 4, vi = lane & 15;
-  const int vt = vi >> 2, vc = vi & 3;
-  uint32_t koff[R::kPieces];
-  {
-    const int sw = R::swz_k(lane);
-#pragma unroll
-    for (int i = 0; i < R::kPieces; ++i) koff[i] = (uint32_t)(lane * R::kRowBytes + ((i ^ sw) * 16));
-  }
-  uint32_t vofs[R::kHalves];
-#pragma unroll
-  for (int e = 0; e < R::kHalves; ++e) {
-    const int k = 4 * e + vg;
-    const int piece = (2 * k + (vc >> 1)) ^ R::swz_v(vt);   // swz_v of rows 4 m + vt depends on vt only
-    vofs[e] = (uint32_t)(vt * R::kRowBytes + piece * 16 + 8 * (vc & 1));
   }
 
 #pragma unroll
@@ -487,7 +401,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
         const int ehead = e / kCodePiecesPerHead;
         u32x4_t lo, hi;
         widen_codes(c, lo, hi);
-        const int sw = m ? (MF ? R::swz_vm(r) : R::swz_v(r)) : R::swz_k(r);
+        const int sw = m ? R::swz_v(r) : R::swz_k(r);
         uint8_t* row = &s_tile[m][r * R::kRowBytes + ehead * (D * 2)];
         *reinterpret_cast<u32x4_t*>(row + ((2 * eh) ^ sw) * 16) = lo;
         *reinterpret_cast<u32x4_t*>(row + ((2 * eh + 1) ^ sw) * 16) = hi;
@@ -500,9 +414,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       vst = &s_dma[1][slot][0];
     }
     const int tile0 = t_begin + s * kStageTok;
-    const bool valid = tile0 + lane < t_end;
-
-    if constexpr (MF) {
+    {
       // wave -> (KV head of the group, 16-token block of the stage)
       constexpr int kWphS = NW / KH;
       const int khw = wave / kWphS;
@@ -575,120 +487,12 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       const int tv = tl0 + (ml16 >> 2), cp = ml16 & 3;
       const uint32_t vrow = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)vst +
                             (uint32_t)(tv * R::kRowBytes + hoff + 8 * (cp & 1));
-      const int svz = R::swz_vm(tv);
+      const int svz = R::swz_v(tv);
 #pragma unroll
       for (int c = 0; c < kCb; ++c) {
         const uint32_t a = vrow + (uint32_t)((((2 * c + (cp >> 1)) ^ svz)) * 16);
         const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a);
         macc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, macc[c], 0, 0, 0);
-      }
-      return;
-    }
-
-    // ---- scores: this lane's token row against the wave's heads
-    u32x4_t kreg[R::kPieces];
-#pragma unroll
-    for (int i = 0; i < R::kPieces; ++i) kreg[i] = *reinterpret_cast<const u32x4_t*>(kst + koff[i]);
-    float sc[kHpw];
-    {
-      // q is uniform and read with scalar loads in 16-dword chunks, one chunk
-      // ahead of its use; the opaque base (tied to the finished sums) keeps
-      // the compiler from hoisting every q dword into scalar registers.
-      using QPtr = const __attribute__((address_space(4))) uint32_t*;
-      constexpr int kQch = 16;
-      constexpr int kCph = (D / 2) / kQch;           // chunks per head
-      constexpr int kNch = kHpw * kCph;
-      float ax[kHpw], ay[kHpw];
-#pragma unroll
-      for (int h = 0; h < kHpw; ++h) { ax[h] = 0.f; ay[h] = 0.f; }
-      uintptr_t qaddr = (uintptr_t)p.q + (uintptr_t)q_dw0 * 4u;
-      asm volatile("" : "+s"(qaddr));
-      uint32_t qa[kQch], qb[kQch];
-      auto load_chunk = [&](uint32_t (&dst)[kQch], int c) {
-        const QPtr qp = (QPtr)qaddr;
-        const int off = c * kQch;
-#pragma unroll
-        for (int i = 0; i < kQch; ++i) dst[i] = qp[off + i];
-      };
-      load_chunk(qa, 0);
-#pragma unroll
-      for (int c = 0; c < kNch; ++c) {
-        if (c > 0) {
-          const int hp = (c - 1) / kCph;
-          asm volatile("" : "+s"(qaddr) : "v"(ax[hp]), "v"(ay[hp]));
-        }
-        if (c + 1 < kNch) load_chunk(qb, c + 1);
-        const int h = c / kCph;
-        const int w0 = (c % kCph) * kQch;
-#pragma unroll
-        for (int i = 0; i < kQch; i += 2) {
-          ax[h] = dot2_bf16(qa[i], kdw(kreg, w0 + i), ax[h]);
-          ay[h] = dot2_bf16(qa[i + 1], kdw(kreg, w0 + i + 1), ay[h]);
-        }
-#pragma unroll
-        for (int i = 0; i < kQch; ++i) qa[i] = qb[i];
-      }
-      if constexpr (Q8) {
-        const float sk = s_scl[0][slot][lane] * qscale;
-#pragma unroll
-        for (int h = 0; h < kHpw; ++h)
-          sc[h] = valid ? fmaf(-128.f, qsum[h], ax[h] + ay[h]) * sk : -INFINITY;
-      } else {
-#pragma unroll
-        for (int h = 0; h < kHpw; ++h) sc[h] = valid ? (ax[h] + ay[h]) * qscale : -INFINITY;
-      }
-    }
-
-    // ---- online softmax; value weights as bf16 token pairs in LDS (bf16:
-    // p, whose rounded value also feeds the running sum; INT8: p * sV)
-    float sv = 1.f;
-    if constexpr (Q8) sv = s_scl[1][slot][lane];
-#pragma unroll
-    for (int h = 0; h < kHpw; ++h) {
-      const float tmax = wave_max(sc[h]);          // finite: the stage's first token is valid
-      if (tmax > m_run[h]) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[h] - tmax);
-        l_run[h] *= alpha;
-        ps_run[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < R::kHalves; ++e) acc[h][e] *= alpha;
-        m_run[h] = tmax;
-      }
-      const float pr = __builtin_amdgcn_exp2f(sc[h] - m_run[h]);
-      const float pw = Q8 ? pr * sv : pr;
-      const float pn = dpp<0xB1>(pw);              // token lane ^ 1
-      const f32x2_t two = {pw, pn};
-      const uint32_t pair = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_t));
-      if constexpr (Q8) {
-        l_run[h] += pr;
-        ps_run[h] += __uint_as_float(pair << 16);
-      } else {
-        l_run[h] += __uint_as_float(pair << 16);
-      }
-      if ((lane & 1) == 0) s_pp[wave][h][lane >> 1] = pair;
-    }
-    wave_sync_lds();
-
-    // ---- acc += w . V over token quads (transposed reads give token pairs)
-#pragma unroll
-    for (int q8 = 0; q8 < kStageTok / 8; ++q8) {
-      u32x4_t pp[kHpw];                            // pairs of tokens 8 q8 .. 8 q8 + 7 (uniform)
-#pragma unroll
-      for (int h = 0; h < kHpw; ++h) pp[h] = *reinterpret_cast<const u32x4_t*>(&s_pp[wave][h][4 * q8]);
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int e = 0; e < R::kHalves; ++e) {
-          const uint8_t* a = vst + (8 * q8 + 4 * half) * R::kRowBytes + vofs[e];
-          const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_t*)(uintptr_t)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)a);
-          const u32x2_t w = __builtin_bit_cast(u32x2_t, v);
-#pragma unroll
-          for (int h = 0; h < kHpw; ++h) {
-            acc[h][e] = dot2_bf16(pp[h][2 * half], w[0], acc[h][e]);
-            acc[h][e] = dot2_bf16(pp[h][2 * half + 1], w[1], acc[h][e]);
-          }
-        }
       }
     }
   };
@@ -700,8 +504,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   }
 
   const int nsp = (ctx + p.split_tokens - 1) / p.split_tokens;
-  if constexpr (MF) {
-    // ---- finish (matrix-core path): per wave and head, the sums over the
+  {
+    // ---- finish: per wave and head, the sums over the
     // four lane groups; then the four waves' states are merged through LDS
     // (the ring is free once every wave is past the last stage)
     float L = ml_run;
@@ -761,27 +565,6 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
 #pragma unroll
       for (int c = 0; c < kCpt; ++c) p.part_o[pi * D + d0 + c] = num[c] * inv;
       if (d0 == 0) { p.part_ml[2 * pi] = M; p.part_ml[2 * pi + 1] = den; }
-    }
-    return;
-  }
-  // ---- finish: each wave owns whole heads; lane owns columns 16 k + vi
-#pragma unroll
-  for (int h = 0; h < kHpw; ++h) {
-    const float L = wave_sum(l_run[h]);
-    const float inv = 1.0f / L;
-    const float off = Q8 ? 128.f * wave_sum(ps_run[h]) : 0.f;
-    const int64_t row = (int64_t)b * n_h + h0 + h;
-#pragma unroll
-    for (int e = 0; e < R::kHalves; ++e) {
-      const int d = 16 * (4 * e + vg) + vi;
-      const float o = (acc[h][e] - off) * inv;
-      if (nsp == 1) {
-        reinterpret_cast<uint16_t*>(p.out)[row * D + d] = f32_to_bf16_rne(o);
-      } else {
-        const int64_t pi = row * p.num_splits + split;
-        p.part_o[pi * D + d] = o;
-        if (lane == 0 && e == 0) { p.part_ml[2 * pi] = m_run[h]; p.part_ml[2 * pi + 1] = L; }
-      }
     }
   }
   };
@@ -847,7 +630,7 @@ bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
 }
 
 int gqa_ring_kv_group(KV kv, bool q_bf16, int d_k, int d_v, int g, int n_kv) {
-  if (!PKV_GQA_MFMA || !q_bf16 || d_k != 128 || d_v != 128 || !(g == 4 || g == 8)) return 1;
+  if (!q_bf16 || d_k != 128 || d_v != 128 || !(g == 4 || g == 8)) return 1;
   if (kv == KV::BF16) return PKV_GQA_PAIR && n_kv % 2 == 0 ? 2 : 1;
   if (kv == KV::INT8) {
     if (PKV_Q8_KH >= 4 && n_kv % 4 == 0) return 4;
@@ -864,43 +647,35 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid = p.compact_units != 0 ? dim3(groups, (unsigned)p.compact_units, 1u)
                                           : dim3(groups, (unsigned)p.B, (unsigned)p.num_splits);
   const bool q8 = p.kv == KV::INT8;
-#define PKV_RING(D_, G_, NW_, RING_, Q8_, MF_, KH_)                                                 \
+#define PKV_RING(D_, G_, Q8_, KH_)                                                                 \
   do {                                                                                              \
     if (p.compact_units != 0)                                                                      \
-      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, true, MF_, KH_>), grid,     \
-                         dim3(64 * NW_), 0, stream, p);                                            \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, true, KH_>), grid,       \
+                         dim3(64 * kWaves), 0, stream, p);                                         \
     else                                                                                           \
-      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, NW_, RING_, Q8_, false, MF_, KH_>), grid,    \
-                         dim3(64 * NW_), 0, stream, p);                                            \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, false, KH_>), grid,      \
+                         dim3(64 * kWaves), 0, stream, p);                                         \
   } while (0)
-  if (PKV_GQA_MFMA) {
-    if (p.d_k == 128 && g == 8) {
-      if (q8 && kh == 4) PKV_RING(128, 8, 4, 2, true, true, 4);
-      else if (q8 && kh == 2) PKV_RING(128, 8, 4, 2, true, true, 2);
-      else if (q8) PKV_RING(128, 8, 4, 2, true, true, 1);
-      else if (kh == 2) PKV_RING(128, 8, 4, 2, false, true, 2);
-      else PKV_RING(128, 8, 4, 2, false, true, 1);
-    } else if (p.d_k == 128 && g == 4) {
-      if (q8 && kh == 4) PKV_RING(128, 4, 4, 2, true, true, 4);
-      else if (q8 && kh == 2) PKV_RING(128, 4, 4, 2, true, true, 2);
-      else if (q8) PKV_RING(128, 4, 4, 2, true, true, 1);
-      else if (kh == 2) PKV_RING(128, 4, 4, 2, false, true, 2);
-      else PKV_RING(128, 4, 4, 2, false, true, 1);
-    } else if (p.d_k == 64 && g == 8) { if (q8) PKV_RING(64, 8, 4, 2, true, true, 1); else PKV_RING(64, 8, 4, 2, false, true, 1); }
-    else if (p.d_k == 64 && g == 4) { if (q8) PKV_RING(64, 4, 4, 2, true, true, 1); else PKV_RING(64, 4, 4, 2, false, true, 1); }
-    else return hipErrorInvalidValue;
-  } else if (!q8) {
-    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_G8_NW, PKV_G8_RING, false, false, 1);
-    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_G4_RING, false, false, 1);
-    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_G8_NW, PKV_G8_RING, false, false, 1);
-    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_G4_RING, false, false, 1);
-    else return hipErrorInvalidValue;
+  if (p.d_k == 128 && g == 8) {
+    if (q8 && kh == 4) PKV_RING(128, 8, true, 4);
+    else if (q8 && kh == 2) PKV_RING(128, 8, true, 2);
+    else if (q8) PKV_RING(128, 8, true, 1);
+    else if (kh == 2) PKV_RING(128, 8, false, 2);
+    else PKV_RING(128, 8, false, 1);
+  } else if (p.d_k == 128 && g == 4) {
+    if (q8 && kh == 4) PKV_RING(128, 4, true, 4);
+    else if (q8 && kh == 2) PKV_RING(128, 4, true, 2);
+    else if (q8) PKV_RING(128, 4, true, 1);
+    else if (kh == 2) PKV_RING(128, 4, false, 2);
+    else PKV_RING(128, 4, false, 1);
+  } else if (p.d_k == 64 && g == 8) {
+    if (q8) PKV_RING(64, 8, true, 1);
+    else PKV_RING(64, 8, false, 1);
+  } else if (p.d_k == 64 && g == 4) {
+    if (q8) PKV_RING(64, 4, true, 1);
+    else PKV_RING(64, 4, false, 1);
   } else {
-    if (p.d_k == 128 && g == 8) PKV_RING(128, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true, false, 1);
-    else if (p.d_k == 128 && g == 4) PKV_RING(128, 4, 4, PKV_Q8_G4_RING, true, false, 1);
-    else if (p.d_k == 64 && g == 8) PKV_RING(64, 8, PKV_Q8_G8_NW, PKV_Q8_G8_RING, true, false, 1);
-    else if (p.d_k == 64 && g == 4) PKV_RING(64, 4, 4, PKV_Q8_G4_RING, true, false, 1);
-    else return hipErrorInvalidValue;
+    return hipErrorInvalidValue;
   }
 #undef PKV_RING
   return hipGetLastError();
