@@ -96,8 +96,10 @@ struct DecodeParams {
 
 constexpr int kCompactMaxB = 512;
 
-// GQA/MQA/MHA over float or INT8 pools (VALU kernels).  Returns
-// hipErrorInvalidValue for a (d, g, dtype) combination with no instance.
+// GQA/MQA/MHA over float, bf16 or INT8 pools: routes the shapes the
+// LDS-ring kernel covers there and the others to the general kernels, then
+// launches the split reduce.  Returns hipErrorInvalidValue for a
+// (d, g, dtype) combination with no instance.
 hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream);
 
 // INT8 pools (fused dequant); called by launch_decode_gqa.
@@ -109,11 +111,11 @@ hipError_t launch_decode_int8(const DecodeParams& p, int g, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
 int mla_head_groups(int n_h);
 
-// bf16 GQA with g in {4, 8}: the LDS-ring kernel (decode_gqa_ring.hip);
-// launch_decode_gqa routes the shapes it covers there.
+// bf16 and INT8 GQA with g in {4, 8}, d in {64, 128}: the LDS-ring kernel
+// on the matrix cores (decode_gqa_ring.hip).
 bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g);
-// KV heads served by one workgroup of that kernel (1, or 2 when a token's
-// rows of two adjacent KV heads are moved together); the split planning
+// KV heads served by one workgroup of that kernel (1, or 2 / 4 when a
+// token's rows of adjacent KV heads are moved together); the split planning
 // counts work units per group.
 int gqa_ring_kv_group(KV kv, bool q_bf16, int d_k, int d_v, int g, int n_kv);
 hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream);
