@@ -284,12 +284,18 @@ MlaWorkspace mla_workspace(const kvp_decode_desc* d) {
   return m;
 }
 
-// Context split size: aim for about kTargetUnits workgroups doing real work
-// (two resident workgroups per compute unit on 256 CUs), in multiples of the
-// kernel's granule; longer splits amortise each workgroup's set-up and merge.
-// Ragged batches (the sum of the contexts well below B times the longest)
-// take about four times as many, shorter splits: their workgroups differ in
-// size, and more of them even out the compute units' loads.
+// Context split size, in multiples of the kernel's granule.  Uniform
+// batches: about kTargetUnits workgroups doing real work (two resident per
+// compute unit on 256 CUs: exactly one round); longer splits amortise each
+// workgroup's set-up and merge.  Ragged batches (the sum of the contexts
+// well below B times the longest) on the LDS-ring kernel (compact grid: only
+// the splits that exist are launched): the shortest split whose workgroups
+// still fit one round of two per compute unit, counting about half a
+// partial split per sequence and KV-head group (skewed INT8 batch: 1536,
+// 97.9 us against 113.0 us at 512 and 141 us at 1280, where a few
+// workgroups spill into a second round; 8B-shaped bf16 batch: 768, 46.9 us
+// against 56.2 us at 512).  Other ragged cases take about four times
+// kTargetUnits shorter splits, which even out the loads.
 constexpr int64_t kTargetUnits = 512;
 constexpr int64_t kTargetUnitsRagged = 2048;
 constexpr int32_t kMaxSplit = 8192;
@@ -308,19 +314,29 @@ int32_t plan_split(const kvp_decode_desc* d, Variant v) {
   const int64_t total = d->total_context_len > 0 ? d->total_context_len
                                                  : (int64_t)d->B * d->max_context_len;
   int64_t heads = v == Variant::Mla ? 1 : d->n_kv;
+  bool ring = false;
   if ((v == Variant::Float || v == Variant::Int8) && d->n_kv > 0) {
     // the ring kernel may serve a group of adjacent KV heads per workgroup
     const int gq = d->n_h / d->n_kv;
     const bool qb = d->q_dtype == KVP_BF16;
     const pkv::KV kv = v == Variant::Int8 ? pkv::KV::INT8
                                           : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
-    if (pkv::gqa_ring_supported(kv, qb, d->d_k, d->d_v, gq))
+    if (pkv::gqa_ring_supported(kv, qb, d->d_k, d->d_v, gq)) {
+      ring = true;
       heads /= pkv::gqa_ring_kv_group(kv, qb, d->d_k, d->d_v, gq, d->n_kv);
+    }
   }
   const int64_t work = total * heads;
   const bool ragged = 4 * total < 3 * (int64_t)d->B * d->max_context_len;
-  const int64_t units = ragged ? kTargetUnitsRagged : kTargetUnits;
-  int64_t split = (work + units - 1) / units;
+  int64_t split;
+  const int64_t slots = 2 * (int64_t)device_cus();
+  const int64_t avail = slots - (((int64_t)d->B + 1) / 2) * heads;
+  if (ragged && ring && d->total_context_len > 0 && d->B <= pkv::kCompactMaxB && 4 * avail >= slots) {
+    split = (work + avail - 1) / avail;
+  } else {
+    const int64_t units = ragged ? kTargetUnitsRagged : kTargetUnits;
+    split = (work + units - 1) / units;
+  }
   split = (split + g - 1) / g * g;
   if (split < g) split = g;
   if (split > max_split(d)) split = max_split(d);
