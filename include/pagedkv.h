@@ -184,7 +184,11 @@ typedef struct {
   int32_t split_tokens;        /* tokens per context split; 0 = automatic */
   int64_t total_context_len;   /* optional host hint: sum of context_lens
                                   (0 = unknown; then B * max_context_len is
-                                  assumed when sizing splits) */
+                                  assumed when sizing splits).  For a ragged
+                                  batch it lets the bf16/INT8 GQA path launch
+                                  only the context splits that exist and size
+                                  them to one round of workgroups; a wrong
+                                  value costs time, never results. */
   int32_t workgroups;          /* MLA only: persistent workgroups per group
                                   of 128 heads; 0 = one per compute unit of
                                   the current device (at most the number of
