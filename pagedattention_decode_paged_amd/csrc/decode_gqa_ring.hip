@@ -19,26 +19,30 @@
 //   and each lane adds a loop-invariant 32-bit offset (rows of an
 //   instruction share a block); the last, partial stage (and blocks smaller
 //   than an instruction's rows) use per-lane addresses.
-// * INT8: codes and the per-token scales land in a staging ring; the waves
-//   then widen each stage's codes to bf16 tiles in LDS as u = code + 128
-//   (exact: every integer in [0, 255] is a bf16), and the offset is taken
-//   out exactly afterwards: q . code = q . u - 128 sum(q) for the scores and
-//   sum_t p'_t code_t = sum_t p'_t u_t - 128 sum_t p'_t for the values, with
-//   p'_t = p_t * sV_t.
+// * INT8: codes and the per-token scales land in a staging ring, and each
+//   wave takes the codes of its own rows from there (no other wave waits for
+//   them).  Scores: the K codes go as they are into the 8-bit matrix-core
+//   product against the query held as two int8 parts with one scale per
+//   head, q ~ s_q (q1 + q2 / 256) (error at most s_q / 256 per element,
+//   about 2^-15 of the head's largest |q|).  Values: the wave widens its V
+//   codes to a bf16 tile in LDS as u = code + 128 (exact: every integer in
+//   [0, 255] is a bf16), read back transposed, and the offset is taken out
+//   exactly afterwards: sum_t p'_t code_t = sum_t p'_t u_t - 128 sum_t p'_t
+//   with p'_t = p_t * sV_t.
 // * Four waves; each takes 16 tokens of a stage for all g heads (padded to
 //   16).  Per KV head the work is a dense [g x d] . [d x tokens]
 //   contraction: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16
-//   / 16x16x16bf16_1k, with lane l holding head l % 16 and tokens
-//   4 (l / 16) .. + 3 in both, so the weights feed the second product from
-//   the lane's own registers and a head's rescale factor sits in the lanes
-//   that hold its outputs.  Online softmax in base 2 (scale * log2 e folded
+//   (INT8: v_mfma_i32_16x16x64_i8) / 16x16x16bf16_1k, with lane l holding
+//   head l % 16 and tokens 4 (l / 16) .. + 3 in both, so the weights feed
+//   the second product from the lane's own registers and a head's rescale
+//   factor sits in the lanes that hold its outputs.  Online softmax in base 2 (scale * log2 e folded
 //   in), with a lazy rescale.  Each wave keeps its own softmax state; the
 //   four are merged through LDS at the end.  A K/V byte crosses HBM once and
 //   feeds all g heads.
-// * K rows are read one per lane (16 lanes per LDS phase) and V transposed
-//   (ds_read_b64_tr_b16, 4 rows of 2 pieces per 16 lanes); both tiles are
-//   stored with their 16-byte pieces permuted by row so that every read
-//   phase hits distinct banks of the 64-bank LDS.
+// * K rows (or code rows) are read one per lane (16 lanes per LDS phase) and
+//   V transposed (ds_read_b64_tr_b16, 4 rows of 2 pieces per 16 lanes); the
+//   tiles and the code ring are stored with their 16-byte pieces permuted by
+//   row so that every read phase hits distinct banks of the 64-bank LDS.
 // * Tokens at or past the context length re-read the last valid row (finite
 //   data): their scores are -inf and weights 0, so unused slots (NaN in the
 //   tests) are never read.
@@ -58,7 +62,7 @@ constexpr int kRing = 2;
 #endif
 // INT8 with d = 128: up to this many adjacent KV heads per
 // workgroup (128-byte code rows moved KH at a time; on the skewed 70B-shaped
-// INT8 batch 1, 2, 4 heads: 113.4, 112.5, 123.5 us)
+// INT8 batch 1, 2, 4 heads: 108.5, 88.5, 90.6 us)
 #ifndef PKV_Q8_KH
 #define PKV_Q8_KH 2
 #endif
@@ -72,6 +76,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // A workgroup serves KH adjacent KV heads (1, or 2 / 4 on the matrix-core
@@ -106,10 +111,19 @@ struct Ring {
   // lanes per phase.
   static __device__ __forceinline__ int swz_k(int r) { return (r / kRows256) % kPieces; }
   // V: the two 16-lane groups of a transposed read phase are on rows 4
-  // apart, so the 8 rows of a phase need distinct piece positions
+  // apart, so the 8 rows of a phase need distinct piece positions.  INT8
+  // (d = 128): the waves write their widened rows 16 rows at a time, so rows
+  // 8 apart also differ (in the lowest bit, constant over a read phase's 8
+  // rows).
   static __device__ __forceinline__ int swz_v(int r) {
-    return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+    return D == 128 ? (2 * (r & 7) | (Q8 ? (r >> 3) & 1 : 0)) : 2 * ((r >> 1) & 3);
   }
+  // INT8 code rows in the staging ring: 16-byte piece p of row r sits at
+  // position p ^ swz_c(r).  A wave reads one piece of 16 consecutive rows
+  // per phase, which then fall on the 16 distinct 16-byte bank groups.
+  static constexpr int kCodeRows256 = kSrcPieces >= 16 ? 1 : 16 / kSrcPieces;   // code rows per 256 bytes
+  static constexpr int kCodeSwzMask = (kSrcPieces >= 16 ? 16 : kSrcPieces) - 1;
+  static __device__ __forceinline__ int swz_c(int r) { return (r / kCodeRows256) & kCodeSwzMask; }
 };
 
 // Every LDS access of this wave has completed, then the workgroup barrier.
@@ -173,8 +187,11 @@ __device__ __forceinline__ void widen_codes(const u32x4_t c, u32x4_t& lo, u32x4_
   hi = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
+// INT8: registers for three waves per SIMD (at most 168, no AGPR copies;
+// on the skewed INT8 batch 81.4 against 84.7 us with 136 + 40 AGPRs)
 template <int D, int G, int NW, int RING, bool Q8, bool COMPACT, int KH>
-__global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Q8 ? 3 : 1)))
+void decode_gqa_ring_kernel(const DecodeParams p) {
   using R = Ring<D, NW, Q8, KH>;
   constexpr int kStageTok = R::kStageTok;
   constexpr int kThr = 64 * NW;
@@ -187,15 +204,12 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   // codes and scales, and one pair of bf16 tiles receives each stage.
   constexpr int kRingBytes = Q8 ? R::kSrcBytes : R::kMatBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t s_dma[2][RING][kRingBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_tile[Q8 ? 2 : 1][Q8 ? R::kMatBytes : 16];
+  // INT8: the bf16 V tile (each wave widens its own rows into it)
+  __shared__ __attribute__((aligned(1024))) uint8_t s_tile[Q8 ? R::kMatBytes : 16];
   __shared__ __align__(16) float s_scl[2][Q8 ? RING : 1][Q8 ? KH * kStageTok : 1];   // [head][token]
-  __shared__ __align__(16) int32_t s_bt[kBtSlots];
-  // per wave and head the running maximum, sum (and the INT8 weight sum)
-  // for the final merge of the four waves
-  __shared__ float s_mml[3 * NW * G];
-  // compact grid only: units before each sequence, and the context lengths
+  __shared__ __align__(16) int32_t s_bt[Q8 ? kBtSlotsInt8 : kBtSlots];
+  // compact grid only: units before each sequence
   __shared__ int32_t s_upre[COMPACT ? kCompactMaxB + 1 : 1];
-  __shared__ int32_t s_ctx[COMPACT ? kCompactMaxB : 1];
 
   // KV head (group of KH heads) fastest in the grid: workgroups are dealt to
   // the 8 XCDs round-robin by linear index, so each XCD serves whole KV
@@ -269,19 +283,22 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   const uint32_t lds_mat =
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&s_dma[dma_v ? 1 : 0][0][0];
   const int lrow = lane / R::kSrcPieces, lpiece = lane % R::kSrcPieces;
-  // source piece a lane moves for row r: bf16 rows go straight to the tile
-  // (permuted); INT8 codes go to the staging ring in order
+  // source piece a lane moves for row r: bf16 rows go straight to the tile,
+  // INT8 codes to the staging ring, both permuted by row
   auto src_piece = [&](int r) {
-    if constexpr (Q8) return lpiece;
+    if constexpr (Q8) return lpiece ^ R::swz_c(r);
     else return lpiece ^ (dma_v ? R::swz_v(r) : R::swz_k(r));
   };
-  // per-lane offsets inside a block for the fast path; the permutation
-  // depends on the row only through jm mod kSwzPeriod
-  constexpr int kSwzPeriod = Q8 ? 1 : (KH == 2 ? 8 : (D == 128 ? 4 : 2));
-  uint32_t voff[kSwzPeriod];
+  // per-lane offsets inside a block for the fast path, for instructions
+  // jbase + i; the permutation depends on the row only through the
+  // instruction index mod kSwzPeriod
+  constexpr int kSwzPeriod = Q8 ? 16 / R::kRowsPerDma : (KH == 2 ? 8 : (D == 128 ? 4 : 2));
+  constexpr int kVoffN = kSwzPeriod < R::kDmaPerWave ? kSwzPeriod : R::kDmaPerWave;
+  static_assert(kVoffN == R::kDmaPerWave || R::kDmaPerWave % kSwzPeriod == 0, "offset table period");
+  uint32_t voff[kVoffN];
 #pragma unroll
-  for (int i = 0; i < kSwzPeriod; ++i)
-    voff[i] = (uint32_t)(lrow * slot_stride) + (uint32_t)src_piece(i * R::kRowsPerDma + lrow) * 16u;
+  for (int i = 0; i < kVoffN; ++i)
+    voff[i] = (uint32_t)(lrow * slot_stride) + (uint32_t)src_piece((jbase + i) * R::kRowsPerDma + lrow) * 16u;
   const bool fast_ok = (1 << shift) >= R::kRowsPerDma;
   // INT8 scales: wave 0 moves the K scales, wave 1 the V scales, one fp32
   // per lane and token
@@ -302,7 +319,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
         const int t0 = tile0 + jm * R::kRowsPerDma;
         const int32_t phys = __builtin_amdgcn_readfirstlane(s_bt[(t0 >> shift) - lb0]);
         const uint8_t* sb = mat + (((int64_t)phys << shift) + (t0 & bmask)) * slot_stride;
-        dma16(sb, voff[jm % kSwzPeriod], dst0 + (uint32_t)(jm * 1024));
+        dma16(sb, voff[jj % kVoffN], dst0 + (uint32_t)(jm * 1024));
       }
     } else {
       // last (partial) stage or tiny blocks: per-lane rows, clamped to the
@@ -345,29 +362,72 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
   // wave keeps its own softmax state; the four are merged at the end.
   const int ml16 = lane & 15, mg = lane >> 4;
   u32x4_t qf[kKs];
+  // INT8: the query of the lane's head as three int8 parts with one scale
+  // per head, q ~ s_q (q1 + q2 / 254 + q3 / 254^2) with s_q = max |q| / 127:
+  // each part is the rounded remainder of the one before times 254, so
+  // every part is within [-127, 127] and |q - s_q (...)| <= s_q / (2 254^2),
+  // about 6e-8 of max |q| (the rounding of fp32 itself).  The scores then
+  // run on the 8-bit matrix cores straight from the codes, each part's
+  // q_i . code in exact int32.
+  constexpr int kLp = D / 64;                      // 16-byte code pieces per lane and row
+  constexpr float kQb = 254.f;
+  i32x4_t q1f[kLp], q2f[kLp], q3f[kLp];
+  float qk = 0.f;                                  // s_q * scale * log2(e)
   f32x4_t macc[kCb];
-  float mm_run = -INFINITY, ml_run = 0.f, mps_run = 0.f, mqsum = 0.f;
+  float mm_run = -INFINITY, ml_run = 0.f, mps_run = 0.f;
   {
 #pragma unroll
     for (int c = 0; c < kCb; ++c) macc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int kv_w = kvh * KH + wave / (NW / KH);             // this wave's KV head
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) +
                           ((int64_t)b * n_h + (int64_t)kv_w * G + min(ml16, G - 1)) * D * 2;
+    // k-step ks of lane group mg covers elements 32 ks + 8 mg .. + 7 (bf16:
+    // the K tile's order), or (D / 4) mg + 8 ks .. + 7 (INT8: each lane
+    // group takes one contiguous quarter of a code row)
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + (32 * ks + 8 * mg) * 2);
+      const int e0 = Q8 ? (D / 4) * mg + 8 * ks : 32 * ks + 8 * mg;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + e0 * 2);
       qf[ks] = ml16 < G ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
     if constexpr (Q8) {
-      // sum of the head's q (it multiplies the +128 offset of the codes)
-      float t = 0.f;
+      float amax = 0.f;
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t += bf_lo(qf[ks][j]) + bf_hi(qf[ks][j]);
-      t += __shfl_xor(t, 16);
-      t += __shfl_xor(t, 32);
-      mqsum = t;
+        for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(qf[ks][j])), fabsf(bf_hi(qf[ks][j]))));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const float inv = amax > 0.f ? 127.f / amax : 0.f;
+      qk = amax * (1.f / 127.f) * qscale;
+      // byte m of piece j pairs with code 16 j + m of the lane's quarter
+      // row: element (D / 4) mg + 16 j + m, i.e. k-step 2 j + m / 8
+#pragma unroll
+      for (int j = 0; j < kLp; ++j) {
+        uint32_t w1[4], w2[4], w3[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t bits = qf[2 * j + d / 2][2 * (d % 2)], bits2 = qf[2 * j + d / 2][2 * (d % 2) + 1];
+          const float x[4] = {bf_lo(bits) * inv, bf_hi(bits) * inv, bf_lo(bits2) * inv, bf_hi(bits2) * inv};
+          uint32_t a = 0u, c = 0u, e = 0u;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float p1 = rintf(x[m]);                          // |x| <= 127
+            const float x2 = (x[m] - p1) * kQb;                    // |x2| <= 127
+            const float p2 = rintf(x2);
+            const float p3 = rintf((x2 - p2) * kQb);               // |.| <= 127
+            a |= ((uint32_t)(int)p1 & 0xffu) << (8 * m);
+            c |= ((uint32_t)(int)p2 & 0xffu) << (8 * m);
+            e |= ((uint32_t)(int)p3 & 0xffu) << (8 * m);
+          }
+          w1[d] = a;
+          w2[d] = c;
+          w3[d] = e;
+        }
+        q1f[j] = i32x4_t{(int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+        q2f[j] = i32x4_t{(int)w2[0], (int)w2[1], (int)w2[2], (int)w2[3]};
+        q3f[j] = i32x4_t{(int)w3[0], (int)w3[1], (int)w3[2], (int)w3[3]};
+      }
     }
   }
 
@@ -382,37 +442,11 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
     lds_barrier();
     if (s + RING - 1 < n_stages) issue(s + RING - 1, (slot + RING - 1) % RING);
 
-    const uint8_t* kst;
-    const uint8_t* vst;
-    if constexpr (Q8) {
-      // widen the stage's codes into the bf16 tiles (each thread its share
-      // of the 16-byte code pieces), then make them visible to every wave
-      constexpr int kCodePieces = 2 * kStageTok * R::kSrcPieces;
-      static_assert(kCodePieces % kThr == 0, "code pieces must split evenly over the threads");
-#pragma unroll
-      for (int i = 0; i < kCodePieces / kThr; ++i) {
-        const int q = i * kThr + tid;
-        const int m = q / (kStageTok * R::kSrcPieces);          // 0: K, 1: V
-        const int r = (q / R::kSrcPieces) % kStageTok;
-        const int e = q % R::kSrcPieces;
-        const u32x4_t c = *reinterpret_cast<const u32x4_t*>(&s_dma[m][slot][(r * R::kSrcPieces + e) * 16]);
-        constexpr int kCodePiecesPerHead = D / 16;              // 16-byte code pieces per head row
-        const int eh = e % kCodePiecesPerHead;
-        const int ehead = e / kCodePiecesPerHead;
-        u32x4_t lo, hi;
-        widen_codes(c, lo, hi);
-        const int sw = m ? R::swz_v(r) : R::swz_k(r);
-        uint8_t* row = &s_tile[m][r * R::kRowBytes + ehead * (D * 2)];
-        *reinterpret_cast<u32x4_t*>(row + ((2 * eh) ^ sw) * 16) = lo;
-        *reinterpret_cast<u32x4_t*>(row + ((2 * eh + 1) ^ sw) * 16) = hi;
-      }
-      lds_barrier();
-      kst = &s_tile[0][0];
-      vst = &s_tile[1][0];
-    } else {
-      kst = &s_dma[0][slot][0];
-      vst = &s_dma[1][slot][0];
-    }
+    // bf16: the K and V tiles are the ring slot itself.  INT8: the slot
+    // holds codes; each wave widens those of its own rows (below), so no
+    // other wave waits for them.
+    const uint8_t* kst = &s_dma[0][slot][0];
+    const uint8_t* vst = Q8 ? &s_tile[0] : &s_dma[1][slot][0];
     const int tile0 = t_begin + s * kStageTok;
     {
       // wave -> (KV head of the group, 16-token block of the stage)
@@ -422,12 +456,56 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       const int hoff = khw * (D * 2);
       const int row = tb + ml16;                     // K row of this lane (A operand)
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (Q8) {
+        // The lane's codes: elements (D / 4) mg .. + D / 4 - 1 of row `row`
+        // of its KV head, for K and V (kLp 16-byte pieces each; the k index
+        // of the score product is permuted the same way in qf).
+        constexpr int kLp = D / 64;
+        constexpr int kHeadPieces = D / 16;                 // 16-byte code pieces per head row
+        const int cz = R::swz_c(row);
+        const uint8_t* ck = &s_dma[0][slot][row * R::kSrcRow];
+        const uint8_t* cv = &s_dma[1][slot][row * R::kSrcRow];
+        u32x4_t kc[kLp], vc[kLp];
 #pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) {
-        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
-            kst + row * R::kRowBytes + hoff + (((4 * ks + mg) ^ R::swz_k(row)) * 16));
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
-                                                       __builtin_bit_cast(bf16x8_t, qf[ks]), sacc, 0, 0, 0);
+        for (int j = 0; j < kLp; ++j) {
+          const int pc = (khw * kHeadPieces + kLp * mg + j) ^ cz;
+          kc[j] = *reinterpret_cast<const u32x4_t*>(ck + pc * 16);
+          vc[j] = *reinterpret_cast<const u32x4_t*>(cv + pc * 16);
+        }
+        // V codes -> this wave's rows of the bf16 V tile (read back below,
+        // transposed, by this wave only: LDS keeps a wave's accesses in order)
+        uint8_t* vrow_w = &s_tile[row * R::kRowBytes + hoff];
+        const int sv = R::swz_v(row);
+#pragma unroll
+        for (int j = 0; j < kLp; ++j) {
+          u32x4_t lo, hi;
+          widen_codes(vc[j], lo, hi);
+          const int pb = 2 * (kLp * mg + j);
+          *reinterpret_cast<u32x4_t*>(vrow_w + (pb ^ sv) * 16) = lo;
+          *reinterpret_cast<u32x4_t*>(vrow_w + ((pb + 1) ^ sv) * 16) = hi;
+        }
+        // K codes straight into the 8-bit products (no widening)
+        i32x4_t a1 = {0, 0, 0, 0}, a2 = {0, 0, 0, 0}, a3 = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < kLp; ++j) {
+          const i32x4_t kci = __builtin_bit_cast(i32x4_t, kc[j]);
+          a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kci, q1f[j], a1, 0, 0, 0);
+          a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kci, q2f[j], a2, 0, 0, 0);
+          a3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kci, q3f[j], a3, 0, 0, 0);
+        }
+        // each |a_i| <= 128 * 127 * 127 < 2^24: exact in fp32
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sacc[i] = fmaf((float)a3[i], 1.f / (kQb * kQb), fmaf((float)a2[i], 1.f / kQb, (float)a1[i]));
+        asm volatile("" ::: "memory");               // the V tile stores stay before its reads
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) {
+          const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
+              kst + row * R::kRowBytes + hoff + (((4 * ks + mg) ^ R::swz_k(row)) * 16));
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
+                                                         __builtin_bit_cast(bf16x8_t, qf[ks]), sacc, 0, 0, 0);
+        }
       }
       const int tl0 = tb + 4 * mg;                   // this lane's first token in the stage
       float sk[4] = {1.f, 1.f, 1.f, 1.f}, svv[4] = {1.f, 1.f, 1.f, 1.f};
@@ -440,8 +518,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       float sc4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float raw = Q8 ? fmaf(-128.f, mqsum, sacc[i]) * sk[i] : sacc[i];
-        sc4[i] = tile0 + tl0 + i < t_end ? raw * qscale : -INFINITY;
+        const float raw = Q8 ? sacc[i] * (sk[i] * qk) : sacc[i] * qscale;
+        sc4[i] = tile0 + tl0 + i < t_end ? raw : -INFINITY;
       }
       // maximum of the head over the wave's 16 tokens (lanes l16 + 16 j)
       float smax = fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3]));
@@ -517,7 +595,11 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       PS += __shfl_xor(PS, 32);
     }
     __syncthreads();
-    float* s_mo = reinterpret_cast<float*>(Q8 ? &s_tile[0][0] : &s_dma[0][0][0]);   // [NW][G][D]
+    // the merge buffers in the ring: the waves' outputs [NW][G][D], then per
+    // wave and head the running maximum, sum (and the INT8 weight sum)
+    static_assert(sizeof(s_dma) >= (NW * G * D + 3 * NW * G) * sizeof(float), "the merge buffers fit the ring");
+    float* s_mo = reinterpret_cast<float*>(&s_dma[0][0][0]);
+    float* s_mml = s_mo + NW * G * D;
     if (ml16 < G) {
 #pragma unroll
       for (int c = 0; c < kCb; ++c)
@@ -588,7 +670,6 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
       for (int k = 0; k < 8; ++k) {
         const int sb = 8 * lane + k;
         const int c = sb < p.B ? p.context_lens[sb] : 0;
-        if (sb < p.B) s_ctx[sb] = c;
         cnt[k] = sb < p.B ? max(1, (c + p.split_tokens - 1) / p.split_tokens) : 0;
         sum += cnt[k];
       }
@@ -616,7 +697,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_ring_kernel(const DecodePa
         if (s_upre[mid] <= u) lo = mid; else hi = mid;
       }
       const int b = __builtin_amdgcn_readfirstlane(lo);
-      unit(b, __builtin_amdgcn_readfirstlane(u - s_upre[b]), __builtin_amdgcn_readfirstlane(s_ctx[b]));
+      unit(b, __builtin_amdgcn_readfirstlane(u - s_upre[b]), p.context_lens[b]);
       __syncthreads();                              // the unit's LDS is free again
     }
   }
@@ -647,6 +728,7 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid = p.compact_units != 0 ? dim3(groups, (unsigned)p.compact_units, 1u)
                                           : dim3(groups, (unsigned)p.B, (unsigned)p.num_splits);
   const bool q8 = p.kv == KV::INT8;
+  if (q8 && (p.split_tokens >> p.block_shift) > kBtSlotsInt8) return hipErrorInvalidValue;
 #define PKV_RING(D_, G_, Q8_, KH_)                                                                 \
   do {                                                                                              \
     if (p.compact_units != 0)                                                                      \

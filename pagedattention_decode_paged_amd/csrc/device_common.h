@@ -14,6 +14,7 @@ static constexpr int kThreads = kWave * kWaves;
 static constexpr int kTile = 64;                   // tokens per wave tile
 static constexpr int kMaxSplitTokens = 8192;       // longest context split
 static constexpr int kBtSlots = 512;               // block-table entries staged per split
+static constexpr int kBtSlotsInt8 = 256;           // the same, INT8 caches (smaller LDS footprint)
 static constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

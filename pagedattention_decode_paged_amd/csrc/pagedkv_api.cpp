@@ -292,19 +292,21 @@ MlaWorkspace mla_workspace(const kvp_decode_desc* d) {
 // the splits that exist are launched): the shortest split whose workgroups
 // still fit one round of two per compute unit, counting about half a
 // partial split per sequence and KV-head group (skewed INT8 batch: 1536,
-// 97.9 us against 113.0 us at 512 and 141 us at 1280, where a few
-// workgroups spill into a second round; 8B-shaped bf16 batch: 768, 46.9 us
-// against 56.2 us at 512).  Other ragged cases take about four times
+// 81.0 us against 82.4 us at 1024, 87.6 us at 1280, where a few
+// workgroups spill into a second round, and 97 us at 2048; 8B-shaped bf16
+// batch: 768, 46.9 us against 56.2 us at 512).  Other ragged cases take about four times
 // kTargetUnits shorter splits, which even out the loads.
 constexpr int64_t kTargetUnits = 512;
 constexpr int64_t kTargetUnitsRagged = 2048;
 constexpr int32_t kMaxSplit = 8192;
 
-// A split stages at most kBtSlots block-table entries in LDS.
+// A split stages at most kBtSlots block-table entries in LDS (INT8 caches:
+// kBtSlotsInt8, part of the INT8 ring kernel's smaller LDS footprint).
 constexpr int32_t kBtSlots = 512;
+constexpr int32_t kBtSlotsInt8 = 256;
 
-int32_t max_split(const kvp_decode_desc* d) {
-  const int64_t cap = (int64_t)kBtSlots * d->block_size;
+int32_t max_split(const kvp_decode_desc* d, Variant v) {
+  const int64_t cap = (int64_t)(v == Variant::Int8 ? kBtSlotsInt8 : kBtSlots) * d->block_size;
   return (int32_t)(cap < kMaxSplit ? cap : kMaxSplit);
 }
 
@@ -339,7 +341,7 @@ int32_t plan_split(const kvp_decode_desc* d, Variant v) {
   }
   split = (split + g - 1) / g * g;
   if (split < g) split = g;
-  if (split > max_split(d)) split = max_split(d);
+  if (split > max_split(d, v)) split = max_split(d, v);
   return (int32_t)split;
 }
 
@@ -504,8 +506,9 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   if (var == Variant::Mla) return launch_mla(fn, q, k, block_table, context_lens, scale, out, d,
                                              workspace, workspace_bytes, stream);
   const int gr = granule(var);
-  if (d->split_tokens > 0 && (d->split_tokens % gr || d->split_tokens > max_split(d)))
-    return fail(KVP_ERR_INVALID_ARG, "%s: split_tokens must be a multiple of %d and <= %d", fn, gr, max_split(d));
+  if (d->split_tokens > 0 && (d->split_tokens % gr || d->split_tokens > max_split(d, var)))
+    return fail(KVP_ERR_INVALID_ARG, "%s: split_tokens must be a multiple of %d and <= %d", fn, gr,
+                max_split(d, var));
   const int32_t split = plan_split(d, var);
   const int32_t ns = num_splits_of(d, split);
   const size_t need = workspace_for(d, var);

@@ -103,3 +103,24 @@ def test_int8_from_fp32_rows():
     s = custom_structure([40, 300], 16, seed=4)
     pool, q, bt, ctx = _int8_case(s, 16, 2, 128, 9, src_dtype=torch.float32)
     _check_attention(pool, q, bt, ctx, s, 0.0883)
+
+
+@pytest.mark.parametrize("d,g", [(128, 8), (128, 4), (64, 8)])
+def test_int8_query_outliers(d, g):
+    """Queries with outlier channels (every 37th channel 30 times the rest)
+    and one head all zero.  The matrix-core INT8 path holds each head's
+    query as 8-bit parts under one scale set by its largest channel, so the
+    small channels must survive that scale; the outliers also make the
+    softmax steep, where a score error shows in the output.  Against the
+    oracle on the plain grid and with several context splits."""
+    ctxs = [300, 1025, 64, 1]
+    s = custom_structure(ctxs, 16, seed=d + g + 5, pad_blocks=1)
+    n_kv = 2
+    pool, q, bt, ctx = _int8_case(s, n_kv * g, n_kv, d, 500 + d + g)
+    qf = q.float()
+    qf[:, :, ::37] *= 30.0
+    qf[0, 1, :] = 0.0                            # uniform weights for this head
+    q = qf.to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    _check_attention(pool, q, bt, ctx, s, scale)
+    _check_attention(pool, q, bt, ctx, s, scale, split_tokens=256)
