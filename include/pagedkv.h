@@ -185,10 +185,14 @@ typedef struct {
   int64_t total_context_len;   /* optional host hint: sum of context_lens
                                   (0 = unknown; then B * max_context_len is
                                   assumed when sizing splits).  For a ragged
-                                  batch it lets the bf16/INT8 GQA path launch
-                                  only the context splits that exist and size
-                                  them to one round of workgroups; a wrong
-                                  value costs time, never results. */
+                                  batch (B <= 512) on the GQA path with
+                                  g in {4, 8}: bf16 pools cut the batch's
+                                  tokens into equal ranges, one per
+                                  workgroup (one round of workgroups on the
+                                  current device); INT8 pools launch only
+                                  the context splits that exist, sized to
+                                  one round.  A wrong value costs time,
+                                  never results. */
   int32_t workgroups;          /* MLA only: persistent workgroups per group
                                   of 128 heads; 0 = one per compute unit of
                                   the current device (at most the number of
@@ -196,11 +200,16 @@ typedef struct {
                                   other entry points. */
 } kvp_decode_desc;
 
-/* Workspace bytes the call needs for this description (split partials). */
+/* Workspace bytes the call needs for this description (split partials).
+ * For MLA and for ragged bf16 batches with a total_context_len hint it
+ * depends on the current device's compute units: query it with the device
+ * current that runs the call. */
 size_t paged_decode_workspace_size(const kvp_decode_desc* desc);
 
 /* Tokens per context split the automatic policy picks (for reporting);
- * for an MLA description, the 32-token tile the work is divided in. */
+ * for an MLA description, the 32-token tile the work is divided in; for a
+ * ragged bf16 batch with a total_context_len hint, the tokens of one
+ * workgroup's range by that hint. */
 int32_t paged_decode_split_tokens(const kvp_decode_desc* desc);
 
 /* MLA: persistent workgroups per head group the call launches (0 for a

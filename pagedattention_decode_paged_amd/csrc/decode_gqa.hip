@@ -519,6 +519,60 @@ __global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_k
   }
 }
 
+// The same merge for the LDS-ring kernel's stream grid: row (b, h) takes the
+// pieces j + b of workgroups j = jf .. jl, [jf, jl] = seq_meta[b] (nothing
+// when jf == jl: the sequence was written whole, or is empty).  Piece p's
+// partials sit at row p * n_h + h.
+__global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_stream_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ seq_meta, void* __restrict__ out, int rows, int n_h, int d_v,
+    int out_bf16) {
+  const int bh = blockIdx.x * kReduceWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kReduceThreads);
+  if (bh >= rows) return;
+  const int b = bh / n_h, h = bh % n_h;
+  const int lane = threadIdx.x % kReduceThreads;
+  const int jf = seq_meta[2 * b], jl = seq_meta[2 * b + 1];
+  if (jl <= jf) return;
+  const bool c0 = lane < d_v, c1 = lane + kReduceThreads < d_v;
+  float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int j0 = jf; j0 <= jl; j0 += kFewSplits) {
+    float m[kFewSplits], l[kFewSplits], v0[kFewSplits], v1[kFewSplits];
+#pragma unroll
+    for (int k = 0; k < kFewSplits; ++k) {
+      const bool in = j0 + k <= jl;
+      const int64_t pi = (int64_t)(j0 + k + b) * n_h + h;
+      m[k] = in ? part_ml[2 * pi] : -INFINITY;
+      l[k] = in ? part_ml[2 * pi + 1] : 0.f;
+      v0[k] = in && c0 ? part_o[pi * d_v + lane] : 0.f;
+      v1[k] = in && c1 ? part_o[pi * d_v + lane + kReduceThreads] : 0.f;
+    }
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < kFewSplits; ++k) Mb = fmaxf(Mb, m[k]);
+    const float f = __builtin_amdgcn_exp2f(M - Mb);   // 0 for the first batch
+    L *= f;
+    o0 *= f;
+    o1 *= f;
+    M = Mb;
+#pragma unroll
+    for (int k = 0; k < kFewSplits; ++k) {
+      const float w = l[k] * __builtin_amdgcn_exp2f(m[k] - M);   // 0 past the last piece
+      L += w;
+      o0 = fmaf(v0[k], w, o0);
+      o1 = fmaf(v1[k], w, o1);
+    }
+  }
+  const float inv = 1.0f / L;
+  const int64_t o = (int64_t)bh * d_v + lane;
+  if (out_bf16) {
+    if (c0) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(o0 * inv);
+    if (c1) reinterpret_cast<uint16_t*>(out)[o + kReduceThreads] = f32_to_bf16_rne(o1 * inv);
+  } else {
+    if (c0) reinterpret_cast<float*>(out)[o] = o0 * inv;
+    if (c1) reinterpret_cast<float*>(out)[o + kReduceThreads] = o1 * inv;
+  }
+}
+
 template <int D, int G, bool BF16, bool PAIR>
 hipError_t launch_inst(const DecodeParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.n_kv, (unsigned)p.B, (unsigned)p.num_splits);
@@ -563,6 +617,8 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
   // only the bf16 LDS-ring kernel writes appended rows itself
   if (p.k_new && !(p.kv == KV::BF16 && gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)))
     return hipErrorInvalidValue;
+  // the stream grid exists on the LDS-ring kernel only
+  if (p.stream_wgs != 0 && !gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)) return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
   if (gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)) {
     e = launch_decode_gqa_ring(p, stream);
@@ -577,9 +633,16 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
   } else if (p.kv == KV::INT8) {
     e = launch_decode_int8(p, g, stream);
   }
+  const int rows = p.B * p.n_h;
+  if (e == hipSuccess && p.stream_wgs != 0) {
+    hipLaunchKernelGGL(decode_reduce_stream_kernel, dim3((unsigned)((rows + kReduceWaves - 1) / kReduceWaves)),
+                       dim3(kReduceThreads * kReduceWaves), 0, stream, (const float*)p.part_o,
+                       (const float*)p.part_ml, (const int32_t*)p.seq_meta, p.out, rows, p.n_h, p.d_v,
+                       p.q_bf16 ? 1 : 0);
+    return hipGetLastError();
+  }
   if (e != hipSuccess || p.num_splits == 1) return e;
   if (p.num_splits > kMaxSplits) return hipErrorInvalidValue;
-  const int rows = p.B * p.n_h;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((rows + kReduceWaves - 1) / kReduceWaves)),
                      dim3(kReduceThreads * kReduceWaves), 0, stream, (const float*)p.part_o,
                      (const float*)p.part_ml, p.context_lens, p.out, rows, p.n_h, p.d_v, p.num_splits,

@@ -55,6 +55,7 @@
 // stages (two workgroups resident per compute unit).
 constexpr int kWaves = 4;
 constexpr int kRing = 2;
+constexpr int kGridSplit = 0, kGridCompact = 1, kGridStream = 2;
 // bf16 with d = 128: two adjacent KV heads per workgroup
 // (512 contiguous bytes per token per DMA row), when n_kv is even
 #ifndef PKV_GQA_PAIR
@@ -189,7 +190,10 @@ __device__ __forceinline__ void widen_codes(const u32x4_t c, u32x4_t& lo, u32x4_
 
 // INT8: registers for three waves per SIMD (at most 168, no AGPR copies;
 // on the skewed INT8 batch 81.4 against 84.7 us with 136 + 40 AGPRs)
-template <int D, int G, int NW, int RING, bool Q8, bool COMPACT, int KH>
+// GRID: kGridSplit (KV head group, sequence, split), kGridCompact (KV head
+// group, unit: the splits that exist) or kGridStream (KV head group, equal
+// token ranges).
+template <int D, int G, int NW, int RING, bool Q8, int GRID, int KH>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Q8 ? 3 : 1)))
 void decode_gqa_ring_kernel(const DecodeParams p) {
   using R = Ring<D, NW, Q8, KH>;
@@ -208,8 +212,9 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[Q8 ? R::kMatBytes : 16];
   __shared__ __align__(16) float s_scl[2][Q8 ? RING : 1][Q8 ? KH * kStageTok : 1];   // [head][token]
   __shared__ __align__(16) int32_t s_bt[Q8 ? kBtSlotsInt8 : kBtSlots];
-  // compact grid only: units before each sequence
-  __shared__ int32_t s_upre[COMPACT ? kCompactMaxB + 1 : 1];
+  // compact grid: units before each sequence; stream grid: padded tokens
+  // before each sequence; then the total
+  __shared__ int32_t s_upre[GRID != kGridSplit ? kCompactMaxB + 1 : 1];
 
   // KV head (group of KH heads) fastest in the grid: workgroups are dealt to
   // the 8 XCDs round-robin by linear index, so each XCD serves whole KV
@@ -217,61 +222,76 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
   const int kvh = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 
-  // ---- one unit of work: split `split` of sequence b (ctx tokens).  In the
-  // compact grid the thread index is an opaque copy, so that the
-  // lane-dependent offsets below are formed per unit rather than hoisted out
-  // of the loop over units and kept live across it.
-  auto unit = [&](const int b, const int split, const int ctx) {
-  int tid = threadIdx.x;
-  if constexpr (COMPACT) asm volatile("" : "+v"(tid));
-  const int lane = tid & 63;
-  const int t_begin = split * p.split_tokens;
-  const int n_h = p.n_h;
+  // Zero output for an empty sequence (this workgroup's heads).
+  auto zero_out = [&](const int b) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)b * p.n_h + (int64_t)kvh * KH * G) * D;
+    for (int i = threadIdx.x; i < KH * G * D; i += kThr) o[i] = 0;
+  };
 
-  if (t_begin >= ctx) {
-    if (split == 0) {                               // empty sequence: zero output
-      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)b * n_h + (int64_t)kvh * KH * G) * D;
-      for (int i = tid; i < KH * G * D; i += kThr) o[i] = 0;
-    }
-    return;
-  }
-  const int t_end = min(ctx, t_begin + p.split_tokens);
-  const int t_last = t_end - 1;
+  // ---- one unit of work: tokens [t_begin, t_end) of sequence b (ctx > 0
+  // tokens).  Its per-head result is the output itself when the unit is the
+  // whole sequence, else a partial at row pmul * row + padd of the
+  // workspace (row = b * n_h + head).  In the compact and stream grids the
+  // thread index is an opaque copy, so that the lane-dependent offsets below
+  // are formed per unit rather than hoisted out of the loop over units and
+  // kept live across it.
+  auto unit = [&](const int b, const int t_begin, const int t_end, const int ctx, const int64_t pmul,
+                  const int64_t padd) {
+  int tid = threadIdx.x;
+  if constexpr (GRID != kGridSplit) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int n_h = p.n_h;
   const int shift = p.block_shift;
   const int bmask = (1 << shift) - 1;
-  const int lb0 = t_begin >> shift;
-  {
-    const int nblk = (t_last >> shift) - lb0 + 1;
-    const int32_t* row = p.block_table + (int64_t)b * p.max_blocks_per_seq + lb0;
-    for (int i = tid; i < nblk; i += kThr) s_bt[i] = row[i];
-  }
-  __syncthreads();
-
+  // The tokens go in chunks [cb, ce) whose blocks fit the staged block table
+  // (one chunk unless the unit is longer than that); the softmax state runs
+  // on across chunks.
+  int cb = t_begin, ce = t_end, lb0 = 0, n_stages = 0;
   const int64_t slot_stride = (int64_t)p.n_kv * R::kHeadRow;   // bytes per token slot
-  if constexpr (!Q8) {
-    if (p.k_new != nullptr && t_end == ctx) {
-      // Append: the workgroup holding the sequence's last token writes that
-      // token's new K and V rows (its KV heads) into its slot, and the store
-      // completes before any of the workgroup's DMA can read the slot.
-      if (wave == 0) {
-        constexpr int kLanesPerRow = R::kSrcRow / 16;       // 16-byte pieces per row
-        const int m = lane / kLanesPerRow, piece = lane % kLanesPerRow;
-        const int32_t phys = s_bt[(t_last >> shift) - lb0];
-        if (m < 2 && phys >= 0) {                            // an unmapped block is skipped
-          const int64_t sl = ((int64_t)phys << shift) + (t_last & bmask);
-          const int64_t off = (int64_t)kvh * R::kSrcRow + piece * 16;
-          const uint8_t* src = reinterpret_cast<const uint8_t*>(m ? p.v_new : p.k_new) +
-                               ((int64_t)b * p.n_kv) * R::kHeadRow + off;
-          uint8_t* dst = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(m ? p.v : p.k)) +
-                         sl * slot_stride + off;
-          *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      }
-      __syncthreads();
+
+  // tokens per chunk: every chunk spans at most kBtN blocks, and chunk
+  // starts stay at multiples of 16 tokens (the DMA's whole-stage path takes
+  // rows of one instruction from one block).  On the split and compact grids
+  // the launch bounds a split to kBtN blocks, so a split is a single chunk.
+  constexpr int kBtN = Q8 ? kBtSlotsInt8 : kBtSlots;
+  const int chunk = (int)min((int64_t)(kBtN - 1) << shift, (int64_t)1 << 30) & ~(kStageTok - 1);
+  // a chunk's block-table entries into LDS (and, for the chunk that holds
+  // the sequence's last token, the appended rows), ready for its DMA
+  auto begin_chunk = [&]() {
+    ce = GRID != kGridStream ? t_end : min(t_end, cb + chunk);   // a split is one chunk
+    lb0 = cb >> shift;
+    {
+      const int nblk = ((ce - 1) >> shift) - lb0 + 1;
+      const int32_t* row = p.block_table + (int64_t)b * p.max_blocks_per_seq + lb0;
+      for (int i = tid; i < nblk; i += kThr) s_bt[i] = row[i];
     }
-  }
-  const int n_stages = (t_end - t_begin + kStageTok - 1) / kStageTok;
+    __syncthreads();
+    if constexpr (!Q8) {
+      if (p.k_new != nullptr && ce == ctx) {
+        // Append: the workgroup holding the sequence's last token writes that
+        // token's new K and V rows (its KV heads) into its slot, and the store
+        // completes before any of the workgroup's DMA can read the slot.
+        if (wave == 0) {
+          const int t_last = ce - 1;
+          constexpr int kLanesPerRow = R::kSrcRow / 16;     // 16-byte pieces per row
+          const int m = lane / kLanesPerRow, piece = lane % kLanesPerRow;
+          const int32_t phys = s_bt[(t_last >> shift) - lb0];
+          if (m < 2 && phys >= 0) {                          // an unmapped block is skipped
+            const int64_t sl = ((int64_t)phys << shift) + (t_last & bmask);
+            const int64_t off = (int64_t)kvh * R::kSrcRow + piece * 16;
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(m ? p.v_new : p.k_new) +
+                                 ((int64_t)b * p.n_kv) * R::kHeadRow + off;
+            uint8_t* dst = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(m ? p.v : p.k)) +
+                           sl * slot_stride + off;
+            *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+          }
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        }
+        __syncthreads();
+      }
+    }
+  };
+  begin_chunk();                                    // the first chunk (cb = t_begin)
 
   // ---- this wave's DMA share: instructions j0 .. j0 + kDmaPerWave - 1 of a
   // stage, all on K (first half of the waves) or all on V.  Lane l moves
@@ -309,9 +329,10 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
   const int dma_per_wave = R::kDmaPerWave + (wave < R::kScaleWaves ? 1 : 0);
 
   auto issue = [&](int s, int slot) {
-    const int tile0 = t_begin + s * kStageTok;
+    const int tile0 = cb + s * kStageTok;
+    const int t_last = ce - 1;
     const uint32_t dst0 = lds_mat + (uint32_t)(slot * kRingBytes);
-    if (fast_ok && tile0 + kStageTok <= t_end) {
+    if (fast_ok && tile0 + kStageTok <= ce) {
       // whole stage: one block per instruction, address base on the scalar unit
 #pragma unroll
       for (int jj = 0; jj < R::kDmaPerWave; ++jj) {
@@ -431,10 +452,6 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
     }
   }
 
-#pragma unroll
-  for (int s = 0; s < RING - 1; ++s)
-    if (s < n_stages) issue(s, s);
-
   auto stage = [&](int s, int slot) {
     // this wave's DMA for stage s has landed (later stages may still fly),
     // then every wave's has, and every wave is done with stage s - 1
@@ -447,7 +464,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
     // other wave waits for them.
     const uint8_t* kst = &s_dma[0][slot][0];
     const uint8_t* vst = Q8 ? &s_tile[0] : &s_dma[1][slot][0];
-    const int tile0 = t_begin + s * kStageTok;
+    const int tile0 = cb + s * kStageTok;
     {
       // wave -> (KV head of the group, 16-token block of the stage)
       constexpr int kWphS = NW / KH;
@@ -519,7 +536,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float raw = Q8 ? sacc[i] * (sk[i] * qk) : sacc[i] * qscale;
-        sc4[i] = tile0 + tl0 + i < t_end ? raw : -INFINITY;
+        sc4[i] = tile0 + tl0 + i < ce ? raw : -INFINITY;
       }
       // maximum of the head over the wave's 16 tokens (lanes l16 + 16 j)
       float smax = fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3]));
@@ -575,13 +592,27 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
     }
   };
 
-  for (int s0 = 0; s0 < n_stages; s0 += RING) {
+  // the chunk [cb, ce): prologue DMA, then its stages
+  auto run_chunk = [&]() {
+    n_stages = (ce - cb + kStageTok - 1) / kStageTok;
 #pragma unroll
-    for (int u = 0; u < RING; ++u)
-      if (s0 + u < n_stages) stage(s0 + u, u);
+    for (int s = 0; s < RING - 1; ++s)
+      if (s < n_stages) issue(s, s);
+    for (int s0 = 0; s0 < n_stages; s0 += RING) {
+#pragma unroll
+      for (int u = 0; u < RING; ++u)
+        if (s0 + u < n_stages) stage(s0 + u, u);
+    }
+  };
+  if constexpr (GRID != kGridStream) {
+    run_chunk();
+  } else {
+    for (cb = t_begin; cb < t_end; cb += chunk) {
+      if (cb != t_begin) begin_chunk();
+      run_chunk();
+      if (cb + chunk < t_end) __syncthreads();      // ring and block table free for the next chunk
+    }
   }
-
-  const int nsp = (ctx + p.split_tokens - 1) / p.split_tokens;
   {
     // ---- finish: per wave and head, the sums over the
     // four lane groups; then the four waves' states are merged through LDS
@@ -638,12 +669,12 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
     }
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     const int64_t row = (int64_t)b * n_h + (int64_t)(kvh * KH + kh) * G + h;
-    if (nsp == 1) {
+    if (t_begin == 0 && t_end == ctx) {
       uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * D + d0;
 #pragma unroll
       for (int c = 0; c < kCpt; ++c) o[c] = f32_to_bf16_rne(num[c] * inv);
     } else {
-      const int64_t pi = row * p.num_splits + split;
+      const int64_t pi = row * pmul + padd;
 #pragma unroll
       for (int c = 0; c < kCpt; ++c) p.part_o[pi * D + d0 + c] = num[c] * inv;
       if (d0 == 0) { p.part_ml[2 * pi] = M; p.part_ml[2 * pi + 1] = den; }
@@ -651,10 +682,16 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
   }
   };
 
-  if constexpr (!COMPACT) {
+  if constexpr (GRID == kGridSplit) {
     // grid (KV head, sequence, split)
-    unit(blockIdx.y, blockIdx.z, p.context_lens[blockIdx.y]);
-  } else {
+    const int b = blockIdx.y, split = blockIdx.z, ctx = p.context_lens[b];
+    const int t_begin = split * p.split_tokens;
+    if (t_begin >= ctx) {
+      if (split == 0) zero_out(b);
+    } else {
+      unit(b, t_begin, min(ctx, t_begin + p.split_tokens), ctx, p.num_splits, split);
+    }
+  } else if constexpr (GRID == kGridCompact) {
     // Grid (KV head, unit) for ragged batches, a unit being one split of one
     // sequence; an empty sequence has one unit, which zeros its output.
     // Only units with work are launched, instead of every sequence times the
@@ -697,7 +734,82 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
         if (s_upre[mid] <= u) lo = mid; else hi = mid;
       }
       const int b = __builtin_amdgcn_readfirstlane(lo);
-      unit(b, __builtin_amdgcn_readfirstlane(u - s_upre[b]), p.context_lens[b]);
+      const int split = __builtin_amdgcn_readfirstlane(u - s_upre[b]);
+      const int ctx = p.context_lens[b];
+      const int t_begin = split * p.split_tokens;
+      if (t_begin >= ctx) {
+        if (split == 0) zero_out(b);
+      } else {
+        unit(b, t_begin, min(ctx, t_begin + p.split_tokens), ctx, p.num_splits, split);
+      }
+      __syncthreads();                              // the unit's LDS is free again
+    }
+  } else {
+    // Stream grid (KV head, workgroup j of gridDim.y) for ragged batches
+    // (B <= kCompactMaxB).  The batch's tokens, each sequence padded to a
+    // multiple of 16, are laid end to end and cut into gridDim.y equal ranges
+    // of T tokens (a multiple of 16); workgroup j takes range j, i.e. its
+    // share of every sequence the range overlaps.  Each share is a unit whose
+    // partial goes to piece j + b (distinct for every (j, b) that has a
+    // share: the ranges and the sequences are both in order), and the
+    // workgroup holding a sequence's first share records its first and last
+    // workgroup for the merge.  Wave 0 forms the padded prefix (8 sequences
+    // per lane).
+    if (wave == 0) {
+      const int lane = threadIdx.x & 63;
+      int len[8];
+      int sum = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sb = 8 * lane + k;
+        const int c = sb < p.B ? p.context_lens[sb] : 0;
+        len[k] = (max(c, 0) + 15) & ~15;
+        sum += len[k];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      int run = incl - sum;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        s_upre[8 * lane + k] = run;
+        run += len[k];
+      }
+      if (lane == kWave - 1) s_upre[kCompactMaxB] = incl;
+    }
+    __syncthreads();
+    const int nwg = gridDim.y, j = blockIdx.y;
+    const int total = __builtin_amdgcn_readfirstlane(s_upre[p.B]);
+    const int T = max(16, ((total + nwg - 1) / nwg + 15) & ~15);
+    const int64_t r0 = (int64_t)j * T, r1 = r0 + T;
+    // empty sequences: zeroed by workgroup b mod gridDim.y (one piece, done)
+    for (int b = j; b < p.B; b += nwg) {
+      if (p.context_lens[b] <= 0) {
+        zero_out(b);
+        if (kvh == 0 && threadIdx.x == 0) { p.seq_meta[2 * b] = 0; p.seq_meta[2 * b + 1] = 0; }
+      }
+    }
+    // the first sequence that can overlap the range: the largest b with
+    // s_upre[b] <= r0
+    int lo = 0, hi = p.B;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_upre[mid] <= r0) lo = mid; else hi = mid - 1;
+    }
+    for (int b = __builtin_amdgcn_readfirstlane(lo); b < p.B; ++b) {
+      const int st = __builtin_amdgcn_readfirstlane(s_upre[b]);
+      if (st >= r1) break;
+      const int ctx = p.context_lens[b];
+      const int a = (int)max(r0 - st, (int64_t)0), e = (int)min(r1 - st, (int64_t)ctx);
+      if (ctx <= 0 || a >= e) continue;
+      if (a == 0 && kvh == 0 && threadIdx.x == 0) {
+        p.seq_meta[2 * b] = j;
+        p.seq_meta[2 * b + 1] = (st + ctx - 1) / T;
+      }
+      unit(b, a, e, ctx, 1, (int64_t)j * p.n_h);
       __syncthreads();                              // the unit's LDS is free again
     }
   }
@@ -721,21 +833,33 @@ int gqa_ring_kv_group(KV kv, bool q_bf16, int d_k, int d_v, int g, int n_kv) {
 }
 
 hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
-  if (p.compact_units != 0 && (p.B > kCompactMaxB || p.compact_units < 0)) return hipErrorInvalidValue;
+  if (p.compact_units != 0 && p.stream_wgs != 0) return hipErrorInvalidValue;
+  if (p.compact_units != 0 && (p.B > kCompactMaxB || p.compact_units < 0 || p.compact_units > 65535))
+    return hipErrorInvalidValue;
+  if (p.stream_wgs != 0 && (p.B > kCompactMaxB || p.stream_wgs < 0 || p.stream_wgs > 65535 ||
+                            p.seq_meta == nullptr))
+    return hipErrorInvalidValue;
   const int g = p.n_h / p.n_kv;
   const int kh = gqa_ring_kv_group(p.kv, p.q_bf16, p.d_k, p.d_v, g, p.n_kv);
   const unsigned groups = (unsigned)(p.n_kv / kh);
-  const dim3 grid = p.compact_units != 0 ? dim3(groups, (unsigned)p.compact_units, 1u)
-                                          : dim3(groups, (unsigned)p.B, (unsigned)p.num_splits);
   const bool q8 = p.kv == KV::INT8;
-  if (q8 && (p.split_tokens >> p.block_shift) > kBtSlotsInt8) return hipErrorInvalidValue;
+  // ragged batches: the compact grid on INT8 pools, the stream grid on bf16
+  // ones (each measured the faster there)
+  if ((q8 && p.stream_wgs != 0) || (!q8 && p.compact_units != 0)) return hipErrorInvalidValue;
+  // a split's blocks must fit the staged block table (one chunk)
+  if ((p.split_tokens >> p.block_shift) > (q8 ? kBtSlotsInt8 : kBtSlots)) return hipErrorInvalidValue;
+  const dim3 grid = p.stream_wgs != 0     ? dim3(groups, (unsigned)p.stream_wgs, 1u)
+                    : p.compact_units != 0 ? dim3(groups, (unsigned)p.compact_units, 1u)
+                                           : dim3(groups, (unsigned)p.B, (unsigned)p.num_splits);
+  const int mode = p.stream_wgs != 0 ? kGridStream : (p.compact_units != 0 ? kGridCompact : kGridSplit);
 #define PKV_RING(D_, G_, Q8_, KH_)                                                                 \
   do {                                                                                              \
-    if (p.compact_units != 0)                                                                      \
-      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, true, KH_>), grid,       \
+    constexpr int kRagged = Q8_ ? kGridCompact : kGridStream;                                       \
+    if (mode != kGridSplit)                                                                         \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, kRagged, KH_>), grid,    \
                          dim3(64 * kWaves), 0, stream, p);                                         \
     else                                                                                           \
-      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, false, KH_>), grid,      \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, kGridSplit, KH_>), grid, \
                          dim3(64 * kWaves), 0, stream, p);                                         \
   } while (0)
   if (p.d_k == 128 && g == 8) {

@@ -78,8 +78,9 @@ struct DecodeParams {
   int32_t num_splits;
   bool q_bf16;
   KV kv;
-  // MLA only: persistent workgroups per head group, and the per-sequence
-  // record of which workgroups hold a sequence ([B, 2], in the workspace).
+  // MLA, and the LDS-ring kernel's stream grid: persistent workgroups per
+  // head group (MLA), and the per-sequence record of which workgroups hold a
+  // sequence ([B, 2], in the workspace).
   int32_t workgroups;
   int32_t* seq_meta;
   // Append (bf16 LDS-ring kernel only; null otherwise): the new token's K and
@@ -87,11 +88,18 @@ struct DecodeParams {
   // of each sequence (k and v above then point at writable pools).
   const void* k_new;
   const void* v_new;
-  // LDS-ring kernel: 0 = grid (KV head, sequence, split); > 0 = grid (KV
-  // head, compact_units) over the splits that exist (ragged batches,
-  // B <= kCompactMaxB), each workgroup looping over units blockIdx.y + k *
-  // compact_units until all are done.
+  // LDS-ring kernel, ragged batches (B <= kCompactMaxB; at most one of the
+  // two is set).  Both 0: grid (KV head group, sequence, split).
+  // compact_units > 0 (INT8 pools): grid (KV head group, compact_units) over
+  // the splits that exist, each workgroup looping over units blockIdx.y +
+  // k * compact_units until all are done.  stream_wgs > 0 (bf16 pools): grid
+  // (KV head group, stream_wgs), the batch's tokens (each sequence padded to
+  // a multiple of 16) cut into stream_wgs equal ranges, one per workgroup;
+  // partials go to piece j + b (part_o [stream_wgs + B, n_h, d_v], part_ml
+  // [stream_wgs + B, n_h, 2]) and seq_meta [B, 2] receives each sequence's
+  // first and last workgroup.
   int32_t compact_units;
+  int32_t stream_wgs;
 };
 
 constexpr int kCompactMaxB = 512;

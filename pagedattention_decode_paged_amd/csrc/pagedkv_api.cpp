@@ -284,18 +284,18 @@ MlaWorkspace mla_workspace(const kvp_decode_desc* d) {
   return m;
 }
 
-// Context split size, in multiples of the kernel's granule.  Uniform
-// batches: about kTargetUnits workgroups doing real work (two resident per
-// compute unit on 256 CUs: exactly one round); longer splits amortise each
-// workgroup's set-up and merge.  Ragged batches (the sum of the contexts
-// well below B times the longest) on the LDS-ring kernel (compact grid: only
-// the splits that exist are launched): the shortest split whose workgroups
-// still fit one round of two per compute unit, counting about half a
-// partial split per sequence and KV-head group (skewed INT8 batch: 1536,
-// 81.0 us against 82.4 us at 1024, 87.6 us at 1280, where a few
-// workgroups spill into a second round, and 97 us at 2048; 8B-shaped bf16
-// batch: 768, 46.9 us against 56.2 us at 512).  Other ragged cases take about four times
-// kTargetUnits shorter splits, which even out the loads.
+// Context split size, in multiples of the kernel's granule (split grids).
+// Uniform batches: about kTargetUnits workgroups doing real work (two
+// resident per compute unit on 256 CUs: exactly one round); longer splits
+// amortise each workgroup's set-up and merge.  Ragged INT8 batches with a
+// total hint on the LDS-ring kernel (the compact grid below): the shortest
+// split whose workgroups still fit one round of two per compute unit,
+// counting about half a partial split per sequence and KV-head group
+// (skewed INT8 batch: 1536, 81.0 us against 82.4 us at 1024, 87.6 us at
+// 1280, where a few workgroups spill into a second round, and 97 us at
+// 2048).  (Ragged bf16 batches with a hint take the stream grid instead.)
+// Other ragged cases take about four times kTargetUnits shorter splits,
+// which even out the loads.
 constexpr int64_t kTargetUnits = 512;
 constexpr int64_t kTargetUnitsRagged = 2048;
 constexpr int32_t kMaxSplit = 8192;
@@ -310,30 +310,69 @@ int32_t max_split(const kvp_decode_desc* d, Variant v) {
   return (int32_t)(cap < kMaxSplit ? cap : kMaxSplit);
 }
 
+// KV heads per workgroup of the LDS-ring kernel for this description, 0 when
+// the description does not run on it.
+int ring_kv_group(const kvp_decode_desc* d, Variant v) {
+  if (!(v == Variant::Float || v == Variant::Int8) || d->n_kv <= 0) return 0;
+  const int gq = d->n_h / d->n_kv;
+  const bool qb = d->q_dtype == KVP_BF16;
+  const pkv::KV kv = v == Variant::Int8 ? pkv::KV::INT8
+                                        : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
+  if (!pkv::gqa_ring_supported(kv, qb, d->d_k, d->d_v, gq)) return 0;
+  return pkv::gqa_ring_kv_group(kv, qb, d->d_k, d->d_v, gq, d->n_kv);
+}
+
+// Ragged bf16 batches with a total hint on the LDS-ring kernel (no split
+// forced, B <= kCompactMaxB): the stream grid, which cuts the batch's tokens
+// into equal ranges, one per workgroup, so that no workgroup waits on a long
+// sequence's last split (8B-shaped batch: 43.5 against 47.5 us on the
+// compact grid; three workgroups per compute unit 55.4 us).  Workgroups per
+// KV-head group: one round of two per compute unit, each range at least
+// kStreamMinTokens tokens by the hint.  0 = a split grid.  INT8 pools keep
+// the compact split grid: there the stream grid ran 89.5 against 81.6 us
+// (with one, two or three workgroups per compute unit: 116.5, 89.5, 89.2),
+// the equal ranges all streaming at once drawing less bandwidth from their
+// 256-byte code runs than the uneven units, whose short ones finish early.
+constexpr int64_t kStreamMinTokens = 256;
+
+int32_t stream_wgs(const kvp_decode_desc* d, Variant v) {
+  if (d->split_tokens > 0 || d->total_context_len <= 0 || d->B <= 0 || d->B > pkv::kCompactMaxB) return 0;
+  if (4 * d->total_context_len >= 3 * (int64_t)d->B * d->max_context_len) return 0;   // not ragged
+  if ((int64_t)d->B * ((int64_t)d->max_context_len + 15) >= ((int64_t)1 << 31)) return 0;
+  if (v != Variant::Float) return 0;
+  const int kh = ring_kv_group(d, v);
+  if (kh == 0) return 0;
+  const int64_t groups = d->n_kv / kh;
+  int64_t w = 2 * (int64_t)device_cus() / groups;
+  const int64_t by_len = (d->total_context_len + kStreamMinTokens - 1) / kStreamMinTokens;
+  if (w > by_len) w = by_len;
+  if (w > 65535) w = 65535;
+  return (int32_t)(w < 1 ? 1 : w);
+}
+
+// Ragged INT8 batches with a total hint on the LDS-ring kernel (no split
+// forced, B <= kCompactMaxB): the compact grid, which launches only the
+// splits that exist.
+bool compact_ok(const kvp_decode_desc* d, Variant v) {
+  return v == Variant::Int8 && d->split_tokens == 0 && d->total_context_len > 0 && d->B > 0 &&
+         d->B <= pkv::kCompactMaxB && 4 * d->total_context_len < 3 * (int64_t)d->B * d->max_context_len &&
+         ring_kv_group(d, v) > 0;
+}
+
 int32_t plan_split(const kvp_decode_desc* d, Variant v) {
   const int g = granule(v);
   if (d->split_tokens > 0) return d->split_tokens;
   const int64_t total = d->total_context_len > 0 ? d->total_context_len
                                                  : (int64_t)d->B * d->max_context_len;
   int64_t heads = v == Variant::Mla ? 1 : d->n_kv;
-  bool ring = false;
-  if ((v == Variant::Float || v == Variant::Int8) && d->n_kv > 0) {
-    // the ring kernel may serve a group of adjacent KV heads per workgroup
-    const int gq = d->n_h / d->n_kv;
-    const bool qb = d->q_dtype == KVP_BF16;
-    const pkv::KV kv = v == Variant::Int8 ? pkv::KV::INT8
-                                          : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
-    if (pkv::gqa_ring_supported(kv, qb, d->d_k, d->d_v, gq)) {
-      ring = true;
-      heads /= pkv::gqa_ring_kv_group(kv, qb, d->d_k, d->d_v, gq, d->n_kv);
-    }
-  }
+  const int kh = ring_kv_group(d, v);
+  if (kh > 0) heads /= kh;                      // the ring kernel's KV-head groups
   const int64_t work = total * heads;
   const bool ragged = 4 * total < 3 * (int64_t)d->B * d->max_context_len;
   int64_t split;
   const int64_t slots = 2 * (int64_t)device_cus();
   const int64_t avail = slots - (((int64_t)d->B + 1) / 2) * heads;
-  if (ragged && ring && d->total_context_len > 0 && d->B <= pkv::kCompactMaxB && 4 * avail >= slots) {
+  if (compact_ok(d, v) && 4 * avail >= slots) {
     split = (work + avail - 1) / avail;
   } else {
     const int64_t units = ragged ? kTargetUnitsRagged : kTargetUnits;
@@ -350,8 +389,22 @@ int32_t num_splits_of(const kvp_decode_desc* d, int32_t split) {
   return (d->max_context_len + split - 1) / split;
 }
 
+// Stream grid workspace: [part_o (wgs + B) x n_h x d_v][part_ml (wgs + B) x
+// n_h x 2][seq_meta B x 2 int32], each region 256-byte aligned.
+struct StreamWorkspace {
+  size_t o_bytes, ml_bytes, meta_bytes;
+  size_t total() const { return o_bytes + ml_bytes + meta_bytes; }
+};
+StreamWorkspace stream_workspace(const kvp_decode_desc* d, int32_t wgs) {
+  const size_t rows = ((size_t)wgs + d->B) * d->n_h;
+  return {round_up(rows * d->d_v * sizeof(float), 256), round_up(rows * 2 * sizeof(float), 256),
+          round_up((size_t)d->B * 2 * sizeof(int32_t), 256)};
+}
+
 size_t workspace_for(const kvp_decode_desc* d, Variant v) {
   if (v == Variant::Mla) return d->B > 0 ? mla_workspace(d).total() : 0;
+  const int32_t sw = stream_wgs(d, v);
+  if (sw > 0) return stream_workspace(d, sw).total();
   const int32_t split = plan_split(d, v);
   const int32_t ns = num_splits_of(d, split);
   if (ns <= 1) return 0;
@@ -518,7 +571,9 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
       return fail(KVP_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
     if (!aligned(workspace, 256)) return fail(KVP_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   }
-  if (ns > 1024) return fail(KVP_ERR_UNSUPPORTED, "%s: more than 1024 context splits (raise split_tokens)", fn);
+  const int32_t sw = stream_wgs(d, var);
+  if (sw == 0 && ns > 1024)
+    return fail(KVP_ERR_UNSUPPORTED, "%s: more than 1024 context splits (raise split_tokens)", fn);
 
   pkv::DecodeParams p{};
   p.q = q;
@@ -529,7 +584,14 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   p.block_table = block_table;
   p.context_lens = context_lens;
   p.out = out;
-  if (need > 0) {
+  if (sw > 0) {
+    const StreamWorkspace sws = stream_workspace(d, sw);
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    p.part_o = reinterpret_cast<float*>(w);
+    p.part_ml = reinterpret_cast<float*>(w + sws.o_bytes);
+    p.seq_meta = reinterpret_cast<int32_t*>(w + sws.o_bytes + sws.ml_bytes);
+    p.stream_wgs = sw;
+  } else if (need > 0) {
     const size_t rows = (size_t)d->B * d->n_h * ns;
     // [part_o][part_ml]
     uint8_t* w = static_cast<uint8_t*>(workspace);
@@ -553,13 +615,11 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
     p.k_new = app->k_new;
     p.v_new = app->v_new;
   }
-  // Ragged batches on the LDS-ring kernel: launch only the splits that exist
-  // (grid from the host's total, which only sizes it: the kernel covers
-  // every unit whatever that total says).
-  const int64_t total = d->total_context_len;
-  if (total > 0 && ns > 1 && d->B <= pkv::kCompactMaxB && 4 * total < 3 * (int64_t)d->B * d->max_context_len &&
-      pkv::gqa_ring_supported(p.kv, q_bf16, d->d_k, d->d_v, g)) {
-    int64_t units = total / split + d->B;
+  // Ragged INT8 batches: launch only the splits that exist (grid from the
+  // host's total, which only sizes it: the kernel covers every unit whatever
+  // that total says).
+  if (sw == 0 && ns > 1 && compact_ok(d, var)) {
+    int64_t units = d->total_context_len / split + d->B;
     if (units > (int64_t)d->B * ns) units = (int64_t)d->B * ns;
     if (units > 65535) units = 65535;
     p.compact_units = (int32_t)units;
@@ -592,6 +652,12 @@ size_t paged_decode_workspace_size(const kvp_decode_desc* desc) {
 int32_t paged_decode_split_tokens(const kvp_decode_desc* desc) {
   if (decode_desc_error(desc)) return 0;
   if (variant_of(desc) == Variant::Mla) return pkv::kMlaTileTokens;
+  const int32_t sw = stream_wgs(desc, variant_of(desc));
+  if (sw > 0) {
+    // stream grid: the tokens of one workgroup's range, by the hint
+    const int64_t t = (desc->total_context_len + 15 * (int64_t)desc->B + sw - 1) / sw;
+    return (int32_t)(t < 16 ? 16 : (t + 15) / 16 * 16);
+  }
   return plan_split(desc, variant_of(desc));
 }
 

@@ -153,3 +153,31 @@ def test_append_row_enters_the_attention():
     assert max_err(out, ref) <= TOL_BF16
     o = host(out)
     assert np.array_equal(o[0].reshape(2, 8, 128), np.broadcast_to(host(v_new)[0][:, None, :], (2, 8, 128)))
+
+
+def test_append_on_the_stream_grid():
+    """Ragged batch with a total-context hint (the stream grid): the
+    workgroup holding a sequence's last token writes the new rows, even when
+    the sequence is cut across workgroups.  Bit for bit against the same
+    step in separate calls with the same hint."""
+    ctxs = [1, 700, 4000, 0, 65, 2500, 33]
+    s = custom_structure(ctxs, 16, seed=12, pad_blocks=1)
+    pa, pb, _ = _two_pools("bf16", s, 16, 2, 128, 128, False, 61)
+    B = len(ctxs)
+    q = device_normal_(torch.empty((B, 16, 128), dtype=torch.bfloat16, device="cuda"), 62)
+    k_new = device_normal_(torch.empty((B, 2, 128), dtype=torch.bfloat16, device="cuda"), 63)
+    v_new = device_normal_(torch.empty((B, 2, 128), dtype=torch.bfloat16, device="cuda"), 64)
+    bt, ctx = tables_to_device(s)
+    hint = int(sum(ctxs))
+    seq = torch.arange(B, dtype=torch.int32, device="cuda")
+    slots = pk.paged_slot_mapping(bt, seq, (ctx - 1).to(torch.int32), 16)
+    pk.reshape_and_cache(pa, k_new, v_new, slots)
+    out_a = pk.paged_decode_attention(q, pa.k, pa.v, bt, ctx, 0.0884, max_context_len=4000,
+                                      total_context_len=hint)
+    out_b = pk.paged_decode_attention_append(pb, q, k_new, v_new, bt, ctx, 0.0884, max_context_len=4000,
+                                             total_context_len=hint)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out_a), _bits(out_b))
+    assert torch.equal(pa.storage, pb.storage)
+    ref = oracle.paged_decode_attention(host(q), host(pb.k), host(pb.v), s.block_table, s.context_lens, 0.0884)
+    assert max_err(out_b, ref) <= TOL_BF16

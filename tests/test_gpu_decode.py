@@ -89,7 +89,7 @@ def test_ragged_contexts(kind, d, g, bs):
 def test_kv_head_groups_bf16(n_kv, g):
     """bf16 with d = 128 runs two adjacent KV heads per workgroup when n_kv
     is even and one otherwise; both against the oracle on the plain grid,
-    with several context splits and on the compact grid."""
+    with several context splits and on the stream grid."""
     ctxs = [1, 17, 40, 300, 1025, 0, 64]
     d, bs = 128, 16
     cfg = type("C", (), dict(block_size=bs, n_kv=n_kv, d_k=d, d_v=d, n_h=n_kv * g))
@@ -257,40 +257,46 @@ def test_one_workspace_serves_calls_of_different_shapes():
 
 
 @pytest.mark.parametrize("kind", ["bf16", "int8"])
-@pytest.mark.parametrize("g,d", [(8, 128), (4, 64)])
-def test_compact_grid_for_ragged_batches_is_bit_exact(kind, g, d):
-    """Ragged batch with a total-context hint: the LDS-ring kernel launches
-    only the splits that exist (grid (KV head, unit)) instead of every
-    sequence times the largest split count.  Bit-exact against the full
-    grid (no hint), and with a hint far too small (a grid of B units per KV
-    head, each workgroup looping over many units): the hint only sizes the
-    grid.  Empty sequences are zeroed through their one unit."""
-    ctxs = [50, 3000, 0, 700, 9000, 64, 1, 2049, 128, 4500]
+@pytest.mark.parametrize("g,d,bs", [(8, 128, 16), (4, 64, 16), (8, 128, 1)])
+def test_ragged_grids_with_total_hint(kind, g, d, bs):
+    """Ragged batch with a total-context hint and no split forced.  bf16: the
+    LDS-ring kernel's stream grid (the batch's tokens cut into equal ranges,
+    one per workgroup; a sequence cut across workgroups is merged from its
+    pieces), against the oracle with the true total, with a hint of 1 (one
+    workgroup per KV-head group takes the whole batch, so the long sequences
+    run in several block-table chunks) and with a hint 50 times too large
+    (every workgroup of a full round, short ranges).  INT8: the compact grid
+    (only the splits that exist), whose grid size the hint sets (a hint of 1
+    leaves each workgroup looping over many splits).  Empty sequences are
+    zeroed."""
+    ctxs = [50, 3000, 0, 700, 9000, 64, 1, 2049, 128, 4500, 0]
     n_kv = 2
-    s = custom_structure(ctxs, 16, seed=g + d, pad_blocks=1)
+    s = custom_structure(ctxs, bs, seed=g + d + bs, pad_blocks=1)
     bt, ctx = tables_to_device(s)
     B = len(ctxs)
     q = device_normal_(torch.empty((B, g * n_kv, d), dtype=torch.bfloat16, device="cuda"), 90 + g)
     total = int(sum(ctxs))
-    outs = []
+    scale = 1.0 / math.sqrt(d)
     if kind == "bf16":
-        pool = pk.kv_pool_create(s.num_blocks, 16, n_kv, d, d, torch.bfloat16)
+        pool = pk.kv_pool_create(s.num_blocks, bs, n_kv, d, d, torch.bfloat16)
         device_normal_(pool.storage.view(torch.bfloat16), 91 + g)
-        for hint in (0, total, 1):
-            outs.append(pk.paged_decode_attention(q, pool.k, pool.v, bt, ctx, 0.1, max_context_len=9000,
-                                                  split_tokens=256, total_context_len=hint))
+        call = lambda hint: pk.paged_decode_attention(q, pool.k, pool.v, bt, ctx, scale, max_context_len=9000,
+                                                      total_context_len=hint)
+        ref = oracle.paged_decode_attention(host(q), host(pool.k), host(pool.v), s.block_table,
+                                            s.context_lens, scale)
     else:
-        pool = pk.kv_pool_create(s.num_blocks, 16, n_kv, d, d, torch.int8)
+        pool = pk.kv_pool_create(s.num_blocks, bs, n_kv, d, d, torch.int8)
         seq, pos = prefill_tokens(s.context_lens)
-        slots = pk.paged_slot_mapping(bt, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), 16)
+        slots = pk.paged_slot_mapping(bt, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), bs)
         rows = device_normal_(torch.empty((2, len(seq), n_kv, d), dtype=torch.bfloat16, device="cuda"), 92)
         pk.reshape_and_cache(pool, rows[0], rows[1], slots)
-        for hint in (0, total, 1):
-            outs.append(pk.paged_decode_attention_int8(q, pool.k, pool.k_scale, pool.v, pool.v_scale, bt, ctx,
-                                                       0.1, max_context_len=9000, split_tokens=256,
-                                                       total_context_len=hint))
-    torch.cuda.synchronize()
-    ref = outs[0].view(torch.int16)
-    assert torch.equal(outs[1].view(torch.int16), ref)
-    assert torch.equal(outs[2].view(torch.int16), ref)
-    assert torch.count_nonzero(outs[0][2]) == 0
+        call = lambda hint: pk.paged_decode_attention_int8(q, pool.k, pool.k_scale, pool.v, pool.v_scale, bt,
+                                                           ctx, scale, max_context_len=9000,
+                                                           total_context_len=hint)
+        ref = oracle.paged_decode_attention_int8(host(q), host(pool.k), host(pool.k_scale), host(pool.v),
+                                                 host(pool.v_scale), s.block_table, s.context_lens, scale)
+    for hint in (total, 1, 50 * total):
+        out = call(hint)
+        torch.cuda.synchronize()
+        assert max_err(out, ref) <= TOL_BF16, hint
+        assert torch.count_nonzero(out[2]) == 0 and torch.count_nonzero(out[10]) == 0
