@@ -22,23 +22,23 @@
 // * INT8: codes and the per-token scales land in a staging ring, and each
 //   wave takes the codes of its own rows from there (no other wave waits for
 //   them).  Scores: the K codes go as they are into the 8-bit matrix-core
-//   product against the query held as two int8 parts with one scale per
-//   head, q ~ s_q (q1 + q2 / 256) (error at most s_q / 256 per element,
-//   about 2^-15 of the head's largest |q|).  Values: the wave widens its V
-//   codes to a bf16 tile in LDS as u = code + 128 (exact: every integer in
-//   [0, 255] is a bf16), read back transposed, and the offset is taken out
-//   exactly afterwards: sum_t p'_t code_t = sum_t p'_t u_t - 128 sum_t p'_t
-//   with p'_t = p_t * sV_t.
+//   product against the query held as three int8 parts with one scale per
+//   head, q ~ s_q (q1 + q2 / 254 + q3 / 254^2) (error at most
+//   s_q / (2 * 254^2) per element, about 6e-8 of the head's largest |q|).
+//   Values: the wave widens its V codes to a bf16 tile in LDS as
+//   u = code + 128 (exact: every integer in [0, 255] is a bf16), read back
+//   transposed, and the offset is taken out exactly afterwards:
+//   sum_t p'_t code_t = sum_t p'_t u_t - 128 sum_t p'_t with p'_t = p_t * sV_t.
 // * Four waves; each takes 16 tokens of a stage for all g heads (padded to
 //   16).  Per KV head the work is a dense [g x d] . [d x tokens]
 //   contraction: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16
 //   (INT8: v_mfma_i32_16x16x64_i8) / 16x16x16bf16_1k, with lane l holding
 //   head l % 16 and tokens 4 (l / 16) .. + 3 in both, so the weights feed
 //   the second product from the lane's own registers and a head's rescale
-//   factor sits in the lanes that hold its outputs.  Online softmax in base 2 (scale * log2 e folded
-//   in), with a lazy rescale.  Each wave keeps its own softmax state; the
-//   four are merged through LDS at the end.  A K/V byte crosses HBM once and
-//   feeds all g heads.
+//   factor sits in the lanes that hold its outputs.  Online softmax in
+//   base 2 (scale * log2 e folded in), with a lazy rescale.  Each wave keeps
+//   its own softmax state; the four are merged through LDS at the end.  A
+//   K/V byte crosses HBM once and feeds all g heads.
 // * K rows (or code rows) are read one per lane (16 lanes per LDS phase) and
 //   V transposed (ds_read_b64_tr_b16, 4 rows of 2 pieces per 16 lanes); the
 //   tiles and the code ring are stored with their 16-byte pieces permuted by

@@ -300,3 +300,41 @@ def test_ragged_grids_with_total_hint(kind, g, d, bs):
         torch.cuda.synchronize()
         assert max_err(out, ref) <= TOL_BF16, hint
         assert torch.count_nonzero(out[2]) == 0 and torch.count_nonzero(out[10]) == 0
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8"])
+def test_ragged_grids_at_the_batch_limit(kind):
+    """B = 512, the most sequences the ragged grids take (wave 0 forms the
+    per-sequence prefix 8 sequences per lane): contexts 0 .. 300 with a
+    total hint, bf16 on the stream grid and INT8 on the compact grid,
+    against the oracle."""
+    rng = np.random.default_rng(77)
+    ctxs = [int(c) for c in rng.integers(0, 301, size=512)]
+    ctxs[0], ctxs[511] = 0, 300
+    n_kv, g, d, bs = 2, 8, 128, 16
+    s = custom_structure(ctxs, bs, seed=78, pad_blocks=1)
+    bt, ctx = tables_to_device(s)
+    B = len(ctxs)
+    q = device_normal_(torch.empty((B, g * n_kv, d), dtype=torch.bfloat16, device="cuda"), 79)
+    scale = 1.0 / math.sqrt(d)
+    hint = int(sum(ctxs))
+    if kind == "bf16":
+        pool = pk.kv_pool_create(s.num_blocks, bs, n_kv, d, d, torch.bfloat16)
+        device_normal_(pool.storage.view(torch.bfloat16), 80)
+        out = pk.paged_decode_attention(q, pool.k, pool.v, bt, ctx, scale, max_context_len=300,
+                                        total_context_len=hint)
+        ref = oracle.paged_decode_attention(host(q), host(pool.k), host(pool.v), s.block_table,
+                                            s.context_lens, scale)
+    else:
+        pool = pk.kv_pool_create(s.num_blocks, bs, n_kv, d, d, torch.int8)
+        seq, pos = prefill_tokens(s.context_lens)
+        slots = pk.paged_slot_mapping(bt, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), bs)
+        rows = device_normal_(torch.empty((2, len(seq), n_kv, d), dtype=torch.bfloat16, device="cuda"), 81)
+        pk.reshape_and_cache(pool, rows[0], rows[1], slots)
+        out = pk.paged_decode_attention_int8(q, pool.k, pool.k_scale, pool.v, pool.v_scale, bt, ctx, scale,
+                                             max_context_len=300, total_context_len=hint)
+        ref = oracle.paged_decode_attention_int8(host(q), host(pool.k), host(pool.k_scale), host(pool.v),
+                                                 host(pool.v_scale), s.block_table, s.context_lens, scale)
+    torch.cuda.synchronize()
+    assert max_err(out, ref) <= TOL_BF16
+    assert torch.count_nonzero(out[0]) == 0
