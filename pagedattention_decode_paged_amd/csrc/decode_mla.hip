@@ -568,7 +568,8 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
 // wave, 4 accumulator blocks) has thread t handle accumulator block
 // 4 (y % 8) + t / 64 of lane t % 64, i.e. four output columns of one head.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineSlices = kAccBlocks * 64 / kCombineThreads;   // 8 workgroups per (group, wave)
+// a thread takes two adjacent accumulator lanes (two heads, 4 columns each)
+constexpr int kCombineSlices = kAccBlocks * 32 / kCombineThreads;   // 4 workgroups per (group, wave)
 constexpr int kCombineBatch = 8;
 
 __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(MlaParams p) {
@@ -576,59 +577,75 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(MlaParams 
   const int slice = blockIdx.y % kCombineSlices;
   const int wave = (blockIdx.y / kCombineSlices) % kWavesM;
   const int hg = blockIdx.y / (kCombineSlices * kWavesM);
-  const int a = slice * (kCombineThreads / 64) + t / 64, ln = t % 64;
+  // accumulator block a, lanes ln and ln + 1: heads h and h + 1 (ln even, so
+  // both in one 16-head block), the same 4 columns
+  const int a = slice * (kCombineThreads / 32) + t / 32, ln = 2 * (t % 32);
   const int h = hg * kHeadsPerGroup + (a / kColBlocksPerWave) * kHeadsPerWave + (ln & 15);
   if (h >= p.n_h) return;
+  const bool two = h + 1 < p.n_h;
   const int col = 16 * (kColBlocksPerWave * wave + a % kColBlocksPerWave) + 4 * (ln >> 4);
   uint16_t* orow = p.out + ((int64_t)b * p.n_h + h) * kDv + col;
   const int ctx = p.context_lens[b];
   if (ctx <= 0) {
     *reinterpret_cast<dev::u32x2_t*>(orow) = dev::u32x2_t{0u, 0u};
+    if (two) *reinterpret_cast<dev::u32x2_t*>(orow + kDv) = dev::u32x2_t{0u, 0u};
     return;
   }
   const int wf = p.seq_meta[2 * b], wl = p.seq_meta[2 * b + 1];
   if (wf == wl) return;   // finished in place
   const int groups = gridDim.y / (kCombineSlices * kWavesM);
   // pieces in batches of kCombineBatch with every load of a batch issued
-  // before any is used; the running max M is raised batch by batch
-  float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  // before any is used; the running maxima are raised batch by batch
+  float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
+  float o[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   for (int s0 = wf; s0 <= wl; s0 += kCombineBatch) {
-    float2 ml[kCombineBatch];
-    dev::u32x2_t v[kCombineBatch];
+    float2 ml[kCombineBatch][2];
+    dev::u32x4_t v[kCombineBatch];
 #pragma unroll
     for (int k = 0; k < kCombineBatch; ++k) {
       const int s = s0 + k;
       if (s <= wl) {
-        ml[k] = *reinterpret_cast<const float2*>(p.part_ml + 2 * ((int64_t)(s + b) * p.n_h + h));
-        v[k] = *reinterpret_cast<const dev::u32x2_t*>(
+        const float* mlp = p.part_ml + 2 * ((int64_t)(s + b) * p.n_h + h);
+        ml[k][0] = *reinterpret_cast<const float2*>(mlp);
+        ml[k][1] = two ? *reinterpret_cast<const float2*>(mlp + 2) : float2{-INFINITY, 0.f};
+        v[k] = *reinterpret_cast<const dev::u32x4_t*>(
             p.part_o + ((((int64_t)(s + b) * groups + hg) * kWavesM + wave) * kAccBlocks * 64 + a * 64 + ln) * 4);
       } else {
-        ml[k] = float2{-INFINITY, 0.f};
-        v[k] = dev::u32x2_t{0u, 0u};
+        ml[k][0] = ml[k][1] = float2{-INFINITY, 0.f};
+        v[k] = dev::u32x4_t{0u, 0u, 0u, 0u};
       }
     }
-    float mc = M;
 #pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k) mc = fmaxf(mc, ml[k].x);
-    const float r = __builtin_amdgcn_exp2f(M - mc);   // 0 on the first batch (M = -inf, mc finite)
-    L *= r;
-    o0 *= r;
-    o1 *= r;
-    o2 *= r;
-    o3 *= r;
+    for (int e = 0; e < 2; ++e) {
+      float mc = M[e];
 #pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k) {
-      const float f = __builtin_amdgcn_exp2f(ml[k].x - mc);   // 0 for the padding
-      L = fmaf(ml[k].y, f, L);
-      o0 = fmaf(__uint_as_float(v[k][0] << 16), f, o0);
-      o1 = fmaf(__uint_as_float(v[k][0] & 0xffff0000u), f, o1);
-      o2 = fmaf(__uint_as_float(v[k][1] << 16), f, o2);
-      o3 = fmaf(__uint_as_float(v[k][1] & 0xffff0000u), f, o3);
+      for (int k = 0; k < kCombineBatch; ++k) mc = fmaxf(mc, ml[k][e].x);
+      // 0 on the first batch (M = -inf); a second head that does not exist
+      // stays at -inf throughout and is never stored
+      const float r = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[e] - mc);
+      L[e] *= r;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[e][c] *= r;
+#pragma unroll
+      for (int k = 0; k < kCombineBatch; ++k) {
+        const float f = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[k][e].x - mc);   // 0 for the padding
+        L[e] = fmaf(ml[k][e].y, f, L[e]);
+        const uint32_t w0 = v[k][2 * e], w1 = v[k][2 * e + 1];
+        o[e][0] = fmaf(__uint_as_float(w0 << 16), f, o[e][0]);
+        o[e][1] = fmaf(__uint_as_float(w0 & 0xffff0000u), f, o[e][1]);
+        o[e][2] = fmaf(__uint_as_float(w1 << 16), f, o[e][2]);
+        o[e][3] = fmaf(__uint_as_float(w1 & 0xffff0000u), f, o[e][3]);
+      }
+      M[e] = mc;
     }
-    M = mc;
   }
-  const float inv = 1.f / L;
-  *reinterpret_cast<dev::u32x2_t*>(orow) = dev::u32x2_t{pack_bf16(o0 * inv, o1 * inv), pack_bf16(o2 * inv, o3 * inv)};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if (e == 1 && !two) break;
+    const float inv = 1.f / L[e];
+    *reinterpret_cast<dev::u32x2_t*>(orow + e * kDv) =
+        dev::u32x2_t{pack_bf16(o[e][0] * inv, o[e][1] * inv), pack_bf16(o[e][2] * inv, o[e][3] * inv)};
+  }
 }
 
 constexpr int kMlaStages = 3;

@@ -56,7 +56,7 @@ RAGGED = [1, 31, 32, 33, 0, 64, 65, 100, 257, 2]
 
 
 @pytest.mark.parametrize("bs", [16, 64])
-@pytest.mark.parametrize("n_h", [128, 16, 160])
+@pytest.mark.parametrize("n_h", [128, 16, 160, 19])
 @pytest.mark.parametrize("workgroups", [0, 1, 3, 7])
 def test_mla_ragged_against_oracle(bs, n_h, workgroups):
     s = custom_structure(RAGGED, bs, seed=bs + n_h + workgroups, pad_blocks=1)
