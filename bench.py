@@ -288,6 +288,7 @@ def bench_llama8b(dev, instances=16, cycles=20):
             "kv_gbs_logical": round(logical / (us * 1e-6) / 1e9, 1),
             "kv_gbs_unique": round(unique / (us * 1e-6) / 1e9, 1),
             "pct_hbm_peak_logical": round(100 * logical / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "pct_hbm_peak_unique": round(100 * unique / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "token_heads_per_s": float(f"{total * cfg.n_h / (us * 1e-6):.4g}"),
             "logical_kv_bytes": logical, "unique_kv_bytes": unique,
             "note": "logical bytes count every sequence's view of the shared prefix; the prefix "

@@ -176,3 +176,39 @@ def test_append_rejects_bad_arguments_on_host():
         assert call(latent) == pk.KVP_ERR_INVALID_ARG
     finally:
         lib.kv_pool_destroy(handle)
+
+
+def _r256(n):
+    return -(-n // 256) * 256
+
+
+def test_ragged_planning_with_total_hint():
+    """Host planning for ragged batches with a total-context hint (no GPU: the
+    library plans for 256 compute units).  bf16, g = 4: the stream grid, two
+    workgroups per compute unit over the 4 KV-head pairs (at most one per 256
+    tokens of the hint), workspace = pieces (workgroups + B) x heads x
+    (d_v + 2) fp32 plus a [B, 2] record.  A forced split leaves the split
+    grid.  INT8: the compact split grid, split = the shortest that fits one
+    round of two workgroups per compute unit, counting half a partial split
+    per sequence and KV-head pair."""
+    B, n_h, n_kv, d, mc, total = 32, 32, 8, 128, 4096, 73728
+    kw = dict(B=B, n_h=n_h, n_kv=n_kv, max_blocks_per_seq=256, max_context_len=mc)
+    d_bf = _desc(total_context_len=total, **kw)
+    w = min(2 * 256 // 4, -(-total // 256))
+    assert pk.decode_workspace_size(d_bf) == (_r256((w + B) * n_h * d * 4) + _r256((w + B) * n_h * 2 * 4)
+                                            + _r256(B * 2 * 4))
+    t = (total + 15 * B + w - 1) // w
+    assert pk.decode_split_tokens(d_bf) == -(-t // 16) * 16
+    d_one = _desc(total_context_len=1, **kw)                   # one workgroup per KV-head pair
+    assert pk.decode_workspace_size(d_one) == (_r256((1 + B) * n_h * d * 4) + _r256((1 + B) * n_h * 2 * 4)
+                                             + _r256(B * 2 * 4))
+    d_forced = _desc(total_context_len=total, split_tokens=512, **kw)
+    ns = mc // 512
+    assert pk.decode_workspace_size(d_forced) == _r256(B * n_h * ns * d * 4) + _r256(B * n_h * ns * 2 * 4)
+    d_q8 = _desc(total_context_len=total, kv_dtype=pk.KVP_INT8, **kw)
+    avail = 2 * 256 - ((B + 1) // 2) * (n_kv // 2)
+    split = -(-(total * (n_kv // 2)) // avail)
+    split = -(-split // 256) * 256
+    assert pk.decode_split_tokens(d_q8) == split
+    ns = -(-mc // split)
+    assert pk.decode_workspace_size(d_q8) == _r256(B * n_h * ns * d * 4) + _r256(B * n_h * ns * 2 * 4)
