@@ -257,7 +257,7 @@ def test_one_workspace_serves_calls_of_different_shapes():
 
 
 @pytest.mark.parametrize("kind", ["bf16", "int8"])
-@pytest.mark.parametrize("g,d,bs", [(8, 128, 16), (4, 64, 16), (8, 128, 1)])
+@pytest.mark.parametrize("g,d,bs", [(8, 128, 16), (4, 64, 16), (8, 128, 1), (4, 128, 64)])
 def test_ragged_grids_with_total_hint(kind, g, d, bs):
     """Ragged batch with a total-context hint and no split forced.  bf16: the
     LDS-ring kernel's stream grid (the batch's tokens cut into equal ranges,
