@@ -27,6 +27,14 @@
  *   Device data that breaks a documented precondition (a block id out of
  *   range, a context longer than the block table covers) is not checked in
  *   the fast path; paged_decode_validate() checks it on request.
+ * - Debug mode: with the environment variable PAGEDKV_VALIDATE set to a
+ *   value other than "0" (read at every call), each decode entry point
+ *   first runs the checks of paged_decode_validate() on its block table
+ *   and context lengths (synchronising the stream) and returns their
+ *   status without launching anything when they fail.  The pool's block
+ *   count is the pool's own (append; any pointer into a pool made by
+ *   kv_pool_create) or, for other memory, the blocks that fit between the
+ *   pool pointer and the end of its device allocation.
  * - No C++ exception crosses this interface.
  */
 #ifndef PAGEDKV_H
@@ -265,13 +273,15 @@ kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
  *          for a latent pool
  *   q, block_table, context_lens, scale, out, workspace: as for the decode
  *          call of the pool's kind.
- * Precondition (the usual decode step): no other sequence of the call reads
- * the slot a sequence appends to.  For bf16 pools with g in {4, 8} the rows
- * are written by the attention kernel itself (one launch); otherwise by the
- * cache kernel just before it.  A sequence with context_lens[b] = 0, or
- * whose last position maps to no block, appends nothing.  Errors as for
- * the decode calls, plus KVP_ERR_INVALID_ARG for a NULL pool or rows, a
- * pool that does not match desc, or misaligned rows. */
+ * Preconditions (the usual decode step): block_table maps every position
+ * below context_lens[b] to a block of the pool, the new token's position
+ * included (paged_decode_validate checks this), and no other sequence of
+ * the call reads the slot a sequence appends to.  A sequence with
+ * context_lens[b] = 0 appends nothing and gets a zero output.  For bf16
+ * pools with g in {4, 8} the rows are written by the attention kernel
+ * itself (one launch); otherwise by the cache kernel just before it.
+ * Errors as for the decode calls, plus KVP_ERR_INVALID_ARG for a NULL pool
+ * or rows, a pool that does not match desc, or misaligned rows. */
 kvp_status paged_decode_attention_append(kvp_pool* pool, const void* q, const void* k_new,
                                          const void* v_new, const int32_t* block_table,
                                          const int32_t* context_lens, float scale, void* out,
@@ -291,8 +301,9 @@ kvp_status paged_gather(const void* pool, int32_t elem_bytes, int32_t block_size
 
 /* Debug check (synchronises the stream, copies the tables to the host):
  * every context length within [0, max_context_len] and every table entry
- * a sequence uses within [0, num_blocks).  KVP_ERR_INVALID_ARG names the
- * first violation. */
+ * a sequence uses (logical blocks 0 .. ceil(context_lens[b] / block_size)
+ * - 1) within [0, num_blocks).  KVP_ERR_INVALID_ARG names the first
+ * violation (sequence, logical block and value); KVP_OK otherwise. */
 kvp_status paged_decode_validate(const int32_t* block_table, const int32_t* context_lens,
                                  const kvp_decode_desc* desc, int64_t num_blocks,
                                  void* stream);

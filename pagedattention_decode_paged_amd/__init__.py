@@ -16,7 +16,9 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+# PAGEDKV_LIBRARY names another build of the same library (the host-sanitizer
+# build of sanitize_check.py); the default is the in-tree libpagedkv.so.
+LIB_PATH = os.environ.get("PAGEDKV_LIBRARY") or os.path.join(_HERE, "libpagedkv.so")
 
 KVP_OK, KVP_ERR_INVALID_ARG, KVP_ERR_OUT_OF_MEMORY, KVP_ERR_UNSUPPORTED, KVP_ERR_HIP = 0, -1, -2, -3, -4
 KVP_F32, KVP_BF16, KVP_INT8 = 0, 1, 2

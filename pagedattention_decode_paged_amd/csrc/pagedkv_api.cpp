@@ -6,7 +6,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -78,6 +80,9 @@ const char* pool_desc_error(const kvp_pool_desc* d) {
   if (d->latent && d->dtype == KVP_INT8) return "INT8 latent pools are not supported";
   const size_t eb = dtype_bytes(d->dtype);
   if ((d->d_k * eb) % 4 || (d->d_v * eb) % 4) return "row bytes must be a multiple of 4";
+  // K + V + scales per slot, times the slots, must stay far from size_t's end
+  const double per_slot = (double)d->n_kv * ((double)(d->d_k + d->d_v) * eb + 8.0);
+  if ((double)d->num_blocks * d->block_size * per_slot > 1.0e18) return "pool larger than 1e18 bytes";
   return nullptr;
 }
 
@@ -105,6 +110,35 @@ struct kvp_pool {
   uint8_t* base = nullptr;
   bool owned = false;
 };
+
+namespace {
+
+// Live pools, so that the debug mode can find the block count of a pool
+// passed to a decode call as a raw pointer.
+std::mutex g_pools_mu;
+std::vector<const kvp_pool*> g_pools;
+
+void register_pool(const kvp_pool* p) {
+  std::lock_guard<std::mutex> lk(g_pools_mu);
+  g_pools.push_back(p);
+}
+
+void unregister_pool(const kvp_pool* p) {
+  std::lock_guard<std::mutex> lk(g_pools_mu);
+  for (size_t i = 0; i < g_pools.size(); ++i)
+    if (g_pools[i] == p) { g_pools[i] = g_pools.back(); g_pools.pop_back(); break; }
+}
+
+// Block count of the live pool whose memory holds ptr (-1 if none does).
+int64_t registered_blocks(const void* ptr) {
+  std::lock_guard<std::mutex> lk(g_pools_mu);
+  const uint8_t* a = static_cast<const uint8_t*>(ptr);
+  for (const kvp_pool* p : g_pools)
+    if (a >= p->base && a < p->base + p->layout.total) return p->desc.num_blocks;
+  return -1;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -151,12 +185,14 @@ kvp_status kv_pool_create(const kvp_pool_desc* desc, void* storage, size_t stora
   pool->layout = L;
   pool->base = base;
   pool->owned = owned;
+  register_pool(pool);
   *out = pool;
   return ok();
 }
 
 void kv_pool_destroy(kvp_pool* pool) {
   if (!pool) return;
+  unregister_pool(pool);
   if (pool->owned && pool->base) (void)hipFree(pool->base);
   delete pool;
 }
@@ -490,6 +526,58 @@ kvp_status write_rows(kvp_pool* pool, const void* k_new, const void* v_new, kvp_
                     fn);
 }
 
+// The checks of paged_decode_validate (synchronises the stream): context
+// lengths within [0, max_context_len], table entries a sequence uses within
+// [0, num_blocks).
+kvp_status check_tables(const char* fn, const int32_t* block_table, const int32_t* context_lens,
+                        const kvp_decode_desc* desc, int64_t num_blocks, void* stream) {
+  if (desc->B == 0) return ok();
+  if (!block_table || !context_lens) return fail(KVP_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> ctx(desc->B);
+  std::vector<int32_t> bt((size_t)desc->B * desc->max_blocks_per_seq);
+  hipError_t e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(bt.data(), block_table, bt.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  for (int32_t b = 0; b < desc->B; ++b) {
+    const int32_t c = ctx[b];
+    if (c < 0 || c > desc->max_context_len)
+      return fail(KVP_ERR_INVALID_ARG, "%s: context_lens[%d] = %d outside [0, %d]", fn, b, c,
+                  desc->max_context_len);
+    const int32_t nb = (int32_t)(((int64_t)c + desc->block_size - 1) / desc->block_size);
+    for (int32_t j = 0; j < nb; ++j) {
+      const int32_t p = bt[(size_t)b * desc->max_blocks_per_seq + j];
+      if (p < 0 || p >= num_blocks)
+        return fail(KVP_ERR_INVALID_ARG, "%s: block_table[%d][%d] = %d outside [0, %lld)", fn, b, j, p,
+                    (long long)num_blocks);
+    }
+  }
+  return ok();
+}
+
+// Debug mode: PAGEDKV_VALIDATE set to anything but "0" (read at every call).
+bool validate_mode() {
+  const char* v = std::getenv("PAGEDKV_VALIDATE");
+  return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
+// Blocks of block_bytes each that fit in the memory a pool pointer reaches:
+// the pool's own count for a pool made by kv_pool_create, else what fits
+// between ptr and the end of its device allocation.
+int64_t blocks_reachable(const void* ptr, size_t block_bytes) {
+  const int64_t reg = registered_blocks(ptr);
+  if (reg >= 0) return reg;
+  void* base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(ptr)) != hipSuccess || !base) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const size_t used = static_cast<const uint8_t*>(ptr) - static_cast<const uint8_t*>(base);
+  return used >= size ? 0 : (int64_t)((size - used) / block_bytes);
+}
+
 // The append request of paged_decode_attention_append (null for a plain decode).
 struct AppendRows {
   kvp_pool* pool;
@@ -538,6 +626,27 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
     if (d->kv_dtype != KVP_BF16 || !q_bf16 || !pkv::mla_supported(d->d_k, d->d_v, d->n_h, d->block_size))
       return fail(KVP_ERR_UNSUPPORTED, "%s: no MLA kernel for n_h %d, d_k %d, d_v %d, block %d", fn,
                   d->n_h, d->d_k, d->d_v, d->block_size);
+  }
+
+  if (validate_mode()) {
+    int64_t nb;
+    if (app) {
+      nb = app->pool->desc.num_blocks;
+    } else {
+      const size_t eb = dtype_bytes(d->kv_dtype);
+      const size_t bsz = (size_t)d->block_size * d->n_kv;
+      nb = blocks_reachable(k, bsz * d->d_k * eb);
+      if (var != Variant::Mla) {
+        const int64_t nv = blocks_reachable(v, bsz * d->d_v * eb);
+        if (nv < nb) nb = nv;
+      }
+      if (var == Variant::Int8) {
+        const int64_t ns = std::min(blocks_reachable(ks, bsz * 4), blocks_reachable(vs, bsz * 4));
+        if (ns < nb) nb = ns;
+      }
+    }
+    const kvp_status vs_rc = check_tables(fn, block_table, context_lens, d, nb, stream);
+    if (vs_rc != KVP_OK) return vs_rc;
   }
 
   // Append: the bf16 LDS-ring kernel writes the new rows itself (one launch);
@@ -752,29 +861,7 @@ kvp_status paged_gather(const void* pool, int32_t elem_bytes, int32_t block_size
 kvp_status paged_decode_validate(const int32_t* block_table, const int32_t* context_lens,
                                  const kvp_decode_desc* desc, int64_t num_blocks, void* stream) {
   if (const char* e = decode_desc_error(desc)) return fail(KVP_ERR_INVALID_ARG, "paged_decode_validate: %s", e);
-  if (desc->B == 0) return ok();
-  if (!block_table || !context_lens) return fail(KVP_ERR_INVALID_ARG, "paged_decode_validate: NULL pointer");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  std::vector<int32_t> ctx(desc->B);
-  std::vector<int32_t> bt((size_t)desc->B * desc->max_blocks_per_seq);
-  hipError_t e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * 4, hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipMemcpyAsync(bt.data(), block_table, bt.size() * 4, hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return hip_status(e, "paged_decode_validate");
-  for (int32_t b = 0; b < desc->B; ++b) {
-    const int32_t c = ctx[b];
-    if (c < 0 || c > desc->max_context_len)
-      return fail(KVP_ERR_INVALID_ARG, "paged_decode_validate: context_lens[%d] = %d outside [0, %d]", b, c,
-                  desc->max_context_len);
-    const int32_t nb = (c + desc->block_size - 1) / desc->block_size;
-    for (int32_t j = 0; j < nb; ++j) {
-      const int32_t p = bt[(size_t)b * desc->max_blocks_per_seq + j];
-      if (p < 0 || p >= num_blocks)
-        return fail(KVP_ERR_INVALID_ARG, "paged_decode_validate: block_table[%d][%d] = %d outside [0, %lld)", b, j,
-                    p, (long long)num_blocks);
-    }
-  }
-  return ok();
+  return check_tables("paged_decode_validate", block_table, context_lens, desc, num_blocks, stream);
 }
 
 }  // extern "C"

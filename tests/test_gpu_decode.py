@@ -197,23 +197,40 @@ def test_llama8b_shared_prefix_full_size(split):
     assert max_err(out, ref) <= TOL_BF16
 
 
-def test_llama70b_layers_full_shape_sampled():
+def test_llama70b_layers_full_shape_append_every_sequence():
     """The 70B-shaped layer at full size (B=16, ctx 8192, 8192 permuted
-    blocks) in the launch configuration the bench times (automatic split);
-    two layers, every head of four sampled sequences per layer."""
+    blocks) through paged_decode_attention_append in the launch
+    configuration the bench times (automatic split; the attention kernel
+    writes the new K/V rows at position 8191 itself); two layers, every
+    output element of all 16 sequences against the oracle over the pool as
+    the call left it, and the pool bit-exact against the oracle's write."""
     cfg = CONFIGS["llama70b"]
     for layer in (0, 79):
         s = structure(cfg, layer=layer)
         k, v, q = _big_case(cfg, s, cfg.seed * 100 + layer, poison=False)
         bt, ctx = tables_to_device(s)
-        out = pk.paged_decode_attention(q, k, v, bt, ctx, cfg.scale, max_context_len=8192)
-        torch.cuda.synchronize()
-        kh, vh, qh, oh = host(k), host(v), host(q), out
-        for b in (0, 5, 10, 15):
-            ref = oracle.paged_decode_attention(qh[b:b + 1], kh, vh, s.block_table[b:b + 1],
-                                                s.context_lens[b:b + 1], cfg.scale)
-            assert max_err(oh[b:b + 1], ref) <= TOL_BF16, (layer, b)
+        pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v, torch.bfloat16)
+        pool.k.copy_(k)
+        pool.v.copy_(v)
         del k, v
+        kv_new = device_normal_(torch.empty((2, cfg.B, cfg.n_kv, cfg.d_k), dtype=torch.bfloat16,
+                                            device="cuda"), cfg.seed * 100 + layer + 7)
+        k0, v0 = host(pool.k), host(pool.v)
+        out = pk.paged_decode_attention_append(pool, q, kv_new[0], kv_new[1], bt, ctx, cfg.scale,
+                                               max_context_len=8192)
+        torch.cuda.synchronize()
+        seq, pos = decode_positions(s.context_lens)
+        slots = oracle.slot_mapping(s.block_table, seq, pos, cfg.block_size)
+        k1 = oracle.reshape_and_cache(k0, host(kv_new[0]), slots)
+        v1 = oracle.reshape_and_cache(v0, host(kv_new[1]), slots)
+        del k0, v0
+        kh, vh = host(pool.k), host(pool.v)
+        assert np.array_equal(kh, k1) and np.array_equal(vh, v1), layer
+        del k1, v1
+        ref = oracle.paged_decode_attention(host(q), kh, vh, s.block_table, s.context_lens, cfg.scale)
+        assert ref.shape == (cfg.B, cfg.n_h, cfg.d_v)
+        assert max_err(out, ref) <= TOL_BF16, layer
+        del pool, kh, vh
 
 
 def test_split_count_invariance():
@@ -265,7 +282,7 @@ def test_ragged_grids_with_total_hint(kind, g, d, bs):
     pieces), against the oracle with the true total, with a hint of 1 (one
     workgroup per KV-head group takes the whole batch, so the long sequences
     run in several block-table chunks) and with a hint 50 times too large
-    (every workgroup of a full round, short ranges).  INT8: the compact grid
+    (which makes the batch look uniform: the plain split grid).  INT8: the compact grid
     (only the splits that exist), whose grid size the hint sets (a hint of 1
     leaves each workgroup looping over many splits).  Empty sequences are
     zeroed."""
@@ -300,6 +317,62 @@ def test_ragged_grids_with_total_hint(kind, g, d, bs):
         torch.cuda.synchronize()
         assert max_err(out, ref) <= TOL_BF16, hint
         assert torch.count_nonzero(out[2]) == 0 and torch.count_nonzero(out[10]) == 0
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8"])
+@pytest.mark.parametrize("factor", [1.3, 10.0])
+def test_ragged_grids_with_an_oversized_hint(kind, factor):
+    """A hint too large but still ragged (max_context_len well above every
+    context): more workgroups are launched than the real tokens fill.
+    bf16: the stream grid (asserted through its workspace size), whose
+    trailing workgroups get empty ranges; INT8: the compact grid (asserted
+    through its split size), whose extra workgroups find no unit.  Against
+    the oracle; empty sequences are zeroed."""
+    ctxs = [5, 90, 0, 33, 200, 16, 1, 47, 0, 128, 64]
+    n_kv, g, d, bs = 2, 8, 128, 16
+    max_ctx = 2048
+    s = custom_structure(ctxs, bs, seed=31, pad_blocks=max_ctx // bs)
+    bt, ctx = tables_to_device(s)
+    B = len(ctxs)
+    total = int(sum(ctxs))
+    hint = int(factor * total)
+    assert 4 * hint < 3 * B * max_ctx                      # still ragged by the hint
+    q = device_normal_(torch.empty((B, g * n_kv, d), dtype=torch.bfloat16, device="cuda"), 32)
+    scale = 1.0 / math.sqrt(d)
+    desc = pk.make_desc(B=B, n_h=g * n_kv, n_kv=n_kv, d_k=d, d_v=d, block_size=bs,
+                        max_blocks_per_seq=s.max_blocks_per_seq, max_context_len=max_ctx,
+                        q_dtype=pk.KVP_BF16, kv_dtype=pk.KVP_BF16 if kind == "bf16" else pk.KVP_INT8,
+                        total_context_len=hint)
+    if kind == "bf16":
+        w = min(2 * 256 // (n_kv // 2), -(-hint // 256))      # stream workgroups per KV-head pair
+        r = lambda n: -(-n // 256) * 256
+        if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+            assert pk.decode_workspace_size(desc) == (r((w + B) * g * n_kv * d * 4) + r((w + B) * g * n_kv * 8)
+                                                      + r(B * 8))
+        pool = pk.kv_pool_create(s.num_blocks, bs, n_kv, d, d, torch.bfloat16)
+        device_normal_(pool.storage.view(torch.bfloat16), 33)
+        out = pk.paged_decode_attention(q, pool.k, pool.v, bt, ctx, scale, max_context_len=max_ctx,
+                                        total_context_len=hint)
+        ref = oracle.paged_decode_attention(host(q), host(pool.k), host(pool.v), s.block_table,
+                                            s.context_lens, scale)
+    else:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        avail = 2 * cus - ((B + 1) // 2) * (n_kv // 2)
+        split = -(-(hint * (n_kv // 2)) // avail)
+        split = max(256, -(-split // 256) * 256)
+        assert pk.decode_split_tokens(desc) == split           # the compact grid's rule
+        pool = pk.kv_pool_create(s.num_blocks, bs, n_kv, d, d, torch.int8)
+        seq, pos = prefill_tokens(s.context_lens)
+        slots = pk.paged_slot_mapping(bt, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), bs)
+        rows = device_normal_(torch.empty((2, len(seq), n_kv, d), dtype=torch.bfloat16, device="cuda"), 34)
+        pk.reshape_and_cache(pool, rows[0], rows[1], slots)
+        out = pk.paged_decode_attention_int8(q, pool.k, pool.k_scale, pool.v, pool.v_scale, bt, ctx, scale,
+                                             max_context_len=max_ctx, total_context_len=hint)
+        ref = oracle.paged_decode_attention_int8(host(q), host(pool.k), host(pool.k_scale), host(pool.v),
+                                                 host(pool.v_scale), s.block_table, s.context_lens, scale)
+    torch.cuda.synchronize()
+    assert max_err(out, ref) <= TOL_BF16
+    assert torch.count_nonzero(out[2]) == 0 and torch.count_nonzero(out[8]) == 0
 
 
 @pytest.mark.parametrize("kind", ["bf16", "int8"])

@@ -116,18 +116,17 @@ def test_mla_workgroup_count_invariance():
     assert max_err(outs[3].to(torch.bfloat16), ref) <= TOL_BF16
 
 
-def test_mla_full_size_sampled():
+def test_mla_full_size_every_sequence():
     """The MLA workload at full size (B=64, n_h=128, contexts uniform in
     [1024, 8192], block 64, permuted blocks) in the launch configuration the
-    bench times (one persistent workgroup per compute unit); every head of
-    six sampled sequences, including the first and the last."""
+    bench times (one persistent workgroup per compute unit); every output
+    element of all 64 sequences against the oracle."""
     cfg = CONFIGS["mla"]
     s = structure(cfg)
     pool, q = _latent_case(s, cfg.block_size, cfg.n_h, seed=cfg.seed)
     bt, ctx = tables_to_device(s)
     out = _mla(pool, q, bt, ctx, s, cfg.scale, total_context_len=int(s.context_lens.sum()))
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(out.float()).all())
-    rows = [0, 1, 17, 32, 50, cfg.B - 1]
-    ref = _oracle(q, pool, s, cfg.scale, rows=rows)
-    assert max_err(out[rows], ref) <= TOL_BF16
+    ref = _oracle(q, pool, s, cfg.scale)
+    assert ref.shape == (cfg.B, cfg.n_h, D_V)
+    assert max_err(out, ref) <= TOL_BF16
