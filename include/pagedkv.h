@@ -288,6 +288,27 @@ kvp_status paged_decode_attention_append(kvp_pool* pool, const void* q, const vo
                                          const kvp_decode_desc* desc, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as paged_decode_attention_append, with the split partials and
+ * records in a library-owned static device buffer instead of a caller
+ * workspace.  The buffer holds 64 MiB (67108864 bytes) per device, from
+ * the library's load until the process ends; a description whose
+ * paged_decode_workspace_size exceeds that returns KVP_ERR_UNSUPPORTED
+ * with a message and enqueues nothing.  The call allocates nothing (no
+ * hipMalloc, no allocating library routine); its first call on a device
+ * looks up that device's buffer address once.  Every call on a device
+ * shares the device's one buffer, which keeps the last call's contents (no
+ * kernel reads a byte of it that the same call did not write first):
+ * calls that overlap on one device (different streams, or host threads
+ * without ordering) race and give wrong results; order them on one stream.
+ * Arguments, results and errors otherwise as for
+ * paged_decode_attention_append. */
+kvp_status paged_decode_attention_append_noalloc(kvp_pool* pool, const void* q, const void* k_new,
+                                                 const void* v_new, const int32_t* block_table,
+                                                 const int32_t* context_lens, float scale, void* out,
+                                                 const kvp_decode_desc* desc, void* stream);
+
 /* ------------------------------------------------------------------------
  * Gather (qwbw 3.4: read each physical block through the table): copies
  * rows 0 .. context_lens[b]-1 of every sequence, bit for bit, into

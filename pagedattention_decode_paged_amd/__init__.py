@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
         "paged_decode_attention_mla": (ctypes.c_int, [P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc), P, SZ, P]),
         "paged_decode_attention_append": (ctypes.c_int, [P, P, P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc),
                                                          P, SZ, P]),
+        "paged_decode_attention_append_noalloc": (ctypes.c_int, [P, P, P, P, P, P, F, P,
+                                                                 ctypes.POINTER(_DecodeDesc), P]),
         "paged_gather": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P]),
         "paged_decode_validate": (ctypes.c_int, [P, P, ctypes.POINTER(_DecodeDesc), I64, P]),
     }
@@ -96,7 +98,8 @@ EXPORTED_SYMBOLS = (
     "kv_pool_view_get", "paged_slot_mapping", "reshape_and_cache", "paged_decode_workspace_size",
     "paged_decode_split_tokens", "paged_decode_mla_workgroups", "paged_decode_attention",
     "paged_decode_attention_int8",
-    "paged_decode_attention_mla", "paged_decode_attention_append", "paged_gather", "paged_decode_validate",
+    "paged_decode_attention_mla", "paged_decode_attention_append", "paged_decode_attention_append_noalloc",
+    "paged_gather", "paged_decode_validate",
 )
 
 
@@ -364,6 +367,20 @@ def paged_decode_attention_append(pool: KVPool, q, k_new, v_new, block_table, co
     _check(_lib.paged_decode_attention_append(pool.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
                                               _ptr(block_table), _ptr(context_lens), float(scale),
                                               _ptr(out), ctypes.byref(desc), _ptr(ws), wsb, _stream(dev)))
+    return out
+
+
+def paged_decode_attention_append_noalloc(pool: KVPool, q, k_new, v_new, block_table, context_lens,
+                                          scale, out, *, max_context_len, split_tokens=0,
+                                          total_context_len=0, workgroups=0):
+    """``paged_decode_attention_append`` with the library's static scratch
+    instead of a workspace: allocates nothing (``out`` is the caller's)."""
+    dev = _need_cuda(q, k_new, block_table, context_lens, out)
+    desc = _append_desc(pool, q, block_table, context_lens, max_context_len, split_tokens,
+                        total_context_len, workgroups)
+    _check(_lib.paged_decode_attention_append_noalloc(pool.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                                      _ptr(block_table), _ptr(context_lens), float(scale),
+                                                      _ptr(out), ctypes.byref(desc), _stream(dev)))
     return out
 
 

@@ -803,12 +803,14 @@ kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
                        workspace_bytes, stream);
 }
 
-kvp_status paged_decode_attention_append(kvp_pool* pool, const void* q, const void* k_new,
-                                         const void* v_new, const int32_t* block_table,
-                                         const int32_t* context_lens, float scale, void* out,
-                                         const kvp_decode_desc* desc, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
-  const char* fn = "paged_decode_attention_append";
+}  // extern "C"
+
+namespace {
+
+kvp_status append_impl(const char* fn, kvp_pool* pool, const void* q, const void* k_new,
+                       const void* v_new, const int32_t* block_table, const int32_t* context_lens,
+                       float scale, void* out, const kvp_decode_desc* desc, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (!pool) return fail(KVP_ERR_INVALID_ARG, "%s: pool is NULL", fn);
   if (const char* e = decode_desc_error(desc)) return fail(KVP_ERR_INVALID_ARG, "%s: %s", fn, e);
   const kvp_pool_desc& pd = pool->desc;
@@ -833,6 +835,75 @@ kvp_status paged_decode_attention_append(kvp_pool* pool, const void* q, const vo
                          desc, workspace, workspace_bytes, stream, &app);
   return decode_common(var, fn, q, v.k, v.v, nullptr, nullptr, block_table, context_lens, scale, out,
                        desc, workspace, workspace_bytes, stream, &app);
+}
+
+// ---- static scratch of paged_decode_attention_append_noalloc
+//
+// One array per device, held from the library's load until the process
+// ends.  Host code never uses the array's name as an address (on the host it
+// names a stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+kvp_status scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVP_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!ptr || !aligned(ptr, 256)) return fail(KVP_ERR_HIP, "%s: scratch address %p is not usable", fn, ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvp_status paged_decode_attention_append(kvp_pool* pool, const void* q, const void* k_new,
+                                         const void* v_new, const int32_t* block_table,
+                                         const int32_t* context_lens, float scale, void* out,
+                                         const kvp_decode_desc* desc, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return append_impl("paged_decode_attention_append", pool, q, k_new, v_new, block_table, context_lens,
+                     scale, out, desc, workspace, workspace_bytes, stream);
+}
+
+kvp_status paged_decode_attention_append_noalloc(kvp_pool* pool, const void* q, const void* k_new,
+                                                 const void* v_new, const int32_t* block_table,
+                                                 const int32_t* context_lens, float scale, void* out,
+                                                 const kvp_decode_desc* desc, void* stream) {
+  const char* fn = "paged_decode_attention_append_noalloc";
+  if (const char* e = decode_desc_error(desc)) return fail(KVP_ERR_INVALID_ARG, "%s: %s", fn, e);
+  const size_t need = workspace_for(desc, variant_of(desc));
+  if (need > kScratchBytes)
+    return fail(KVP_ERR_UNSUPPORTED,
+                "%s: the call needs %zu bytes of scratch, the static buffer holds %zu "
+                "(use paged_decode_attention_append with a workspace)", fn, need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const kvp_status rc = scratch_address(fn, &ws);
+    if (rc != KVP_OK) return rc;
+  }
+  return append_impl(fn, pool, q, k_new, v_new, block_table, context_lens, scale, out, desc, ws,
+                     need > 0 ? kScratchBytes : 0, stream);
 }
 
 kvp_status paged_gather(const void* pool, int32_t elem_bytes, int32_t block_size, int32_t n_kv,
