@@ -206,6 +206,23 @@ typedef struct {
                                   the current device (at most the number of
                                   32-token context tiles).  Ignored by the
                                   other entry points. */
+  int32_t shared_prefix_tokens; /* optional host hint (0 = none): the first
+                                  tokens of the sequences are expected to sit
+                                  in the same physical blocks (a shared
+                                  prompt prefix; hx 4.2, faulkner prefix
+                                  caching).  Used by paged_decode_attention on
+                                  bf16 pools with d = 128, g in {4, 8}, even
+                                  n_kv, B <= 512 and no forced split (other
+                                  calls ignore it): the hint, rounded down to
+                                  a multiple of 64 and at most
+                                  max_context_len, is cut into chunks, and
+                                  each chunk's K/V rows are read once for
+                                  every sequence whose block-table entries
+                                  over its tokens in the chunk equal those of
+                                  the longest sequence (checked on the
+                                  device); any other sequence's chunk is read
+                                  from its own blocks.  A wrong value costs
+                                  time, never results. */
 } kvp_decode_desc;
 
 /* Workspace bytes the call needs for this description (split partials).

@@ -51,7 +51,7 @@ class _DecodeDesc(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
                 ("split_tokens", ctypes.c_int32), ("total_context_len", ctypes.c_int64),
-                ("workgroups", ctypes.c_int32)]
+                ("workgroups", ctypes.c_int32), ("shared_prefix_tokens", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -254,11 +254,11 @@ def paged_gather(pool: torch.Tensor, block_table: torch.Tensor, context_lens: to
 # --------------------------------------------------------------------- decode
 
 def _desc(q, block_table, context_lens, n_kv, d_k, d_v, block_size, kv_dtype, max_context_len,
-          split_tokens, total_context_len, workgroups=0) -> _DecodeDesc:
+          split_tokens, total_context_len, workgroups=0, shared_prefix_tokens=0) -> _DecodeDesc:
     B, n_h, _ = q.shape
     return _DecodeDesc(B, n_h, n_kv, d_k, d_v, block_size, block_table.shape[1], int(max_context_len),
                        _TORCH_TO_KVP[q.dtype], kv_dtype, int(split_tokens), int(total_context_len),
-                       int(workgroups))
+                       int(workgroups), int(shared_prefix_tokens))
 
 
 def decode_workspace_size(desc: _DecodeDesc) -> int:
@@ -292,14 +292,17 @@ def _workspace(desc, workspace, dev):
 
 
 def paged_decode_attention(q, k_pool, v_pool, block_table, context_lens, scale, out=None, *,
-                           max_context_len, split_tokens=0, total_context_len=0, workspace=None):
+                           max_context_len, split_tokens=0, total_context_len=0, workspace=None,
+                           shared_prefix_tokens=0):
     """``out[b, h] = softmax(scale * q[b, h] . K) V`` over each sequence's
-    paged K/V (pools ``[num_blocks, block_size, n_kv, d]``)."""
+    paged K/V (pools ``[num_blocks, block_size, n_kv, d]``).
+    ``shared_prefix_tokens``: a hint that the sequences' first tokens share
+    physical blocks (read once for all of them; checked on the device)."""
     dev = _need_cuda(q, k_pool, v_pool, block_table, context_lens)
     _, bs, n_kv, d_k = k_pool.shape
     d_v = v_pool.shape[3]
     desc = _desc(q, block_table, context_lens, n_kv, d_k, d_v, bs, _TORCH_TO_KVP[k_pool.dtype],
-                 max_context_len, split_tokens, total_context_len)
+                 max_context_len, split_tokens, total_context_len, 0, shared_prefix_tokens)
     if out is None:
         out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=dev)
     ws, wsb = _workspace(desc, workspace, dev)
@@ -385,10 +388,11 @@ def paged_decode_attention_append_noalloc(pool: KVPool, q, k_new, v_new, block_t
 
 
 def make_desc(*, B, n_h, n_kv, d_k, d_v, block_size, max_blocks_per_seq, max_context_len,
-              q_dtype, kv_dtype, split_tokens=0, total_context_len=0, workgroups=0) -> _DecodeDesc:
+              q_dtype, kv_dtype, split_tokens=0, total_context_len=0, workgroups=0,
+              shared_prefix_tokens=0) -> _DecodeDesc:
     """A decode description from plain values (dtype codes KVP_F32/BF16/INT8)."""
     return _DecodeDesc(B, n_h, n_kv, d_k, d_v, block_size, max_blocks_per_seq, max_context_len,
-                       q_dtype, kv_dtype, split_tokens, total_context_len, workgroups)
+                       q_dtype, kv_dtype, split_tokens, total_context_len, workgroups, shared_prefix_tokens)
 
 
 def paged_decode_validate(block_table, context_lens, desc: _DecodeDesc, num_blocks: int) -> None:
@@ -416,11 +420,13 @@ class PreparedCall:
 
 
 def prepare_decode(q, k_pool, v_pool, block_table, context_lens, scale, out, *, max_context_len,
-                   split_tokens=0, total_context_len=0, workspace=None) -> PreparedCall:
+                   split_tokens=0, total_context_len=0, workspace=None,
+                   shared_prefix_tokens=0) -> PreparedCall:
     dev = _need_cuda(q, k_pool, v_pool, block_table, context_lens, out)
     _, bs, n_kv, d_k = k_pool.shape
     desc = _desc(q, block_table, context_lens, n_kv, d_k, v_pool.shape[3], bs,
-                 _TORCH_TO_KVP[k_pool.dtype], max_context_len, split_tokens, total_context_len)
+                 _TORCH_TO_KVP[k_pool.dtype], max_context_len, split_tokens, total_context_len, 0,
+                 shared_prefix_tokens)
     ws, wsb = _workspace(desc, workspace, dev)
     args = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(context_lens),
             ctypes.c_float(scale), _ptr(out), ctypes.byref(desc), _ptr(ws), wsb, None)

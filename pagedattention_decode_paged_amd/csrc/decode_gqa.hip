@@ -520,27 +520,42 @@ __global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_k
 }
 
 // The same merge for the LDS-ring kernel's stream grid: row (b, h) takes the
-// pieces j + b of workgroups j = jf .. jl, [jf, jl] = seq_meta[b] (nothing
-// when jf == jl: the sequence was written whole, or is empty).  Piece p's
-// partials sit at row p * n_h + h.
+// pieces j + b of workgroups j = jf .. jl, [jf, jl] = seq_meta[b].  Without
+// a shared prefix, jf == jl means nothing to merge (the sequence was written
+// whole, or is empty).  With one (prefix_tokens > 0) every sequence with
+// tokens is merged: first its prefix pieces stream_wgs + B + c * B + b for
+// the chunks c < ceil(min(ctx, prefix_tokens) / prefix_chunk), then its
+// stream pieces [jf, jl] (none when jl < jf).  Piece p's partials sit at row
+// p * n_h + h.
 __global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_stream_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_meta, void* __restrict__ out, int rows, int n_h, int d_v,
-    int out_bf16) {
+    const int32_t* __restrict__ seq_meta, const int32_t* __restrict__ context_lens, void* __restrict__ out,
+    int rows, int n_h, int d_v, int out_bf16, int B, int stream_wgs, int prefix_tokens, int prefix_chunk) {
   const int bh = blockIdx.x * kReduceWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kReduceThreads);
   if (bh >= rows) return;
   const int b = bh / n_h, h = bh % n_h;
   const int lane = threadIdx.x % kReduceThreads;
   const int jf = seq_meta[2 * b], jl = seq_meta[2 * b + 1];
-  if (jl <= jf) return;
+  int npre = 0;
+  if (prefix_tokens > 0) {
+    const int ctx = context_lens[b];
+    if (ctx <= 0) return;                       // zeroed by the decode kernel
+    npre = (min(ctx, prefix_tokens) + prefix_chunk - 1) / prefix_chunk;
+  } else if (jl <= jf) {
+    return;
+  }
+  const int n = npre + (jl >= jf ? jl - jf + 1 : 0);
+  const int64_t pre0 = (int64_t)stream_wgs + B;
   const bool c0 = lane < d_v, c1 = lane + kReduceThreads < d_v;
   float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int j0 = jf; j0 <= jl; j0 += kFewSplits) {
+  for (int k0 = 0; k0 < n; k0 += kFewSplits) {
     float m[kFewSplits], l[kFewSplits], v0[kFewSplits], v1[kFewSplits];
 #pragma unroll
     for (int k = 0; k < kFewSplits; ++k) {
-      const bool in = j0 + k <= jl;
-      const int64_t pi = (int64_t)(j0 + k + b) * n_h + h;
+      const int kk = k0 + k;
+      const bool in = kk < n;
+      const int64_t piece = kk < npre ? pre0 + (int64_t)kk * B + b : (int64_t)(jf + kk - npre + b);
+      const int64_t pi = piece * n_h + h;
       m[k] = in ? part_ml[2 * pi] : -INFINITY;
       l[k] = in ? part_ml[2 * pi + 1] : 0.f;
       v0[k] = in && c0 ? part_o[pi * d_v + lane] : 0.f;
@@ -637,8 +652,8 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
   if (e == hipSuccess && p.stream_wgs != 0) {
     hipLaunchKernelGGL(decode_reduce_stream_kernel, dim3((unsigned)((rows + kReduceWaves - 1) / kReduceWaves)),
                        dim3(kReduceThreads * kReduceWaves), 0, stream, (const float*)p.part_o,
-                       (const float*)p.part_ml, (const int32_t*)p.seq_meta, p.out, rows, p.n_h, p.d_v,
-                       p.q_bf16 ? 1 : 0);
+                       (const float*)p.part_ml, (const int32_t*)p.seq_meta, p.context_lens, p.out, rows,
+                       p.n_h, p.d_v, p.q_bf16 ? 1 : 0, p.B, p.stream_wgs, p.prefix_tokens, p.prefix_chunk);
     return hipGetLastError();
   }
   if (e != hipSuccess || p.num_splits == 1) return e;

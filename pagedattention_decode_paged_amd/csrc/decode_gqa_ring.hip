@@ -55,7 +55,7 @@
 // stages (two workgroups resident per compute unit).
 constexpr int kWaves = 4;
 constexpr int kRing = 2;
-constexpr int kGridSplit = 0, kGridCompact = 1, kGridStream = 2;
+constexpr int kGridSplit = 0, kGridCompact = 1, kGridStream = 2, kGridStreamPrefix = 3;
 // bf16 with d = 128: two adjacent KV heads per workgroup
 // (512 contiguous bytes per token per DMA row), when n_kv is even
 #ifndef PKV_GQA_PAIR
@@ -189,14 +189,20 @@ __device__ __forceinline__ void widen_codes(const u32x4_t c, u32x4_t& lo, u32x4_
 }
 
 // INT8: registers for three waves per SIMD (at most 168, no AGPR copies;
-// on the skewed INT8 batch 81.4 against 84.7 us with 136 + 40 AGPRs)
+// on the skewed INT8 batch 81.4 against 84.7 us with 136 + 40 AGPRs).  The
+// shared-prefix instance: at most 256 registers, so that two workgroups stay
+// resident per compute unit (the prefix pass alone would take 357).
 // GRID: kGridSplit (KV head group, sequence, split), kGridCompact (KV head
-// group, unit: the splits that exist) or kGridStream (KV head group, equal
-// token ranges).
+// group, unit: the splits that exist), kGridStream (KV head group, equal
+// token ranges) or kGridStreamPrefix (the stream grid after a shared prefix,
+// plus the prefix workgroups).
 template <int D, int G, int NW, int RING, bool Q8, int GRID, int KH>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Q8 ? 3 : 1)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(Q8 ? 3 : (GRID == kGridStreamPrefix ? 2 : 1))))
 void decode_gqa_ring_kernel(const DecodeParams p) {
   using R = Ring<D, NW, Q8, KH>;
+  constexpr bool kStreamLike = GRID == kGridStream || GRID == kGridStreamPrefix;
+  static_assert(GRID != kGridStreamPrefix || (!Q8 && KH == 2 && D == 128), "shared prefix: bf16, two KV heads");
   constexpr int kStageTok = R::kStageTok;
   constexpr int kThr = 64 * NW;
   static_assert(NW == 4 && G <= 16, "four waves of 16 tokens per stage, g <= 16");
@@ -230,13 +236,13 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
 
   // ---- one unit of work: tokens [t_begin, t_end) of sequence b (ctx > 0
   // tokens).  Its per-head result is the output itself when the unit is the
-  // whole sequence, else a partial at row pmul * row + padd of the
-  // workspace (row = b * n_h + head).  In the compact and stream grids the
+  // whole sequence and direct_ok, else a partial at row pmul * row + padd of
+  // the workspace (row = b * n_h + head).  In the compact and stream grids the
   // thread index is an opaque copy, so that the lane-dependent offsets below
   // are formed per unit rather than hoisted out of the loop over units and
   // kept live across it.
   auto unit = [&](const int b, const int t_begin, const int t_end, const int ctx, const int64_t pmul,
-                  const int64_t padd) {
+                  const int64_t padd, const bool direct_ok) __attribute__((always_inline)) {
   int tid = threadIdx.x;
   if constexpr (GRID != kGridSplit) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
@@ -258,7 +264,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
   // a chunk's block-table entries into LDS (and, for the chunk that holds
   // the sequence's last token, the appended rows), ready for its DMA
   auto begin_chunk = [&]() {
-    ce = GRID != kGridStream ? t_end : min(t_end, cb + chunk);   // a split is one chunk
+    ce = !kStreamLike ? t_end : min(t_end, cb + chunk);   // a split is one chunk
     lb0 = cb >> shift;
     {
       const int nblk = ((ce - 1) >> shift) - lb0 + 1;
@@ -604,7 +610,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
         if (s0 + u < n_stages) stage(s0 + u, u);
     }
   };
-  if constexpr (GRID != kGridStream) {
+  if constexpr (!kStreamLike) {
     run_chunk();
   } else {
     for (cb = t_begin; cb < t_end; cb += chunk) {
@@ -669,7 +675,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
     }
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     const int64_t row = (int64_t)b * n_h + (int64_t)(kvh * KH + kh) * G + h;
-    if (t_begin == 0 && t_end == ctx) {
+    if (direct_ok && t_begin == 0 && t_end == ctx) {
       uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * D + d0;
 #pragma unroll
       for (int c = 0; c < kCpt; ++c) o[c] = f32_to_bf16_rne(num[c] * inv);
@@ -682,6 +688,357 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
   }
   };
 
+  // ---- stream grid: workgroup j of nwg.  The tokens [S, ctx) of every
+  // sequence (S = 0, or the shared prefix's length), each sequence's part
+  // padded to a multiple of 16, are laid end to end and cut into nwg equal
+  // ranges of T tokens (a multiple of 16); workgroup j takes range j, i.e.
+  // its share of every sequence the range overlaps.  Each share is a unit
+  // whose partial goes to piece j + b (distinct for every (j, b) that has a
+  // share: the ranges and the sequences are both in order), and the
+  // workgroup holding a sequence's first share records its first and last
+  // workgroup for the merge.  Wave 0 forms the padded prefix (8 sequences
+  // per lane).  With S > 0 no share is a whole sequence (the prefix pieces
+  // are merged too), and a sequence with no tokens past S records none.
+  auto stream_part = [&](const int j, const int nwg, const int S) {
+    if constexpr (kStreamLike) {
+    if (wave == 0) {
+      const int lane = threadIdx.x & 63;
+      int len[8];
+      int sum = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sb = 8 * lane + k;
+        const int c = sb < p.B ? p.context_lens[sb] : 0;
+        len[k] = (max(c - S, 0) + 15) & ~15;
+        sum += len[k];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      int run = incl - sum;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        s_upre[8 * lane + k] = run;
+        run += len[k];
+      }
+      if (lane == kWave - 1) s_upre[kCompactMaxB] = incl;
+    }
+    __syncthreads();
+    const int total = __builtin_amdgcn_readfirstlane(s_upre[p.B]);
+    const int T = max(16, ((total + nwg - 1) / nwg + 15) & ~15);
+    const int64_t r0 = (int64_t)j * T, r1 = r0 + T;
+    // empty sequences: zeroed by workgroup b mod nwg (one piece, done); with
+    // a prefix, sequences with no tokens past it record no stream pieces
+    for (int b = j; b < p.B; b += nwg) {
+      const int cx = p.context_lens[b];
+      if (cx <= 0) {
+        zero_out(b);
+        if (kvh == 0 && threadIdx.x == 0) { p.seq_meta[2 * b] = 0; p.seq_meta[2 * b + 1] = S > 0 ? -1 : 0; }
+      } else if (cx <= S) {
+        if (kvh == 0 && threadIdx.x == 0) { p.seq_meta[2 * b] = 0; p.seq_meta[2 * b + 1] = -1; }
+      }
+    }
+    // the first sequence that can overlap the range: the largest b with
+    // s_upre[b] <= r0
+    int lo = 0, hi = p.B;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_upre[mid] <= r0) lo = mid; else hi = mid - 1;
+    }
+    for (int b = __builtin_amdgcn_readfirstlane(lo); b < p.B; ++b) {
+      const int st = __builtin_amdgcn_readfirstlane(s_upre[b]);
+      if (st >= r1) break;
+      const int ctx = p.context_lens[b];
+      const int L = ctx - S;                        // this sequence's tokens past the prefix
+      const int a = (int)max(r0 - st, (int64_t)0), e = (int)min(r1 - st, (int64_t)L);
+      if (L <= 0 || a >= e) continue;
+      if (a == 0 && kvh == 0 && threadIdx.x == 0) {
+        p.seq_meta[2 * b] = j;
+        p.seq_meta[2 * b + 1] = (st + L - 1) / T;
+      }
+      unit(b, S + a, S + e, ctx, 1, (int64_t)j * p.n_h, S == 0);
+      __syncthreads();                              // the unit's LDS is free again
+    }
+    }
+  };
+
+  // ---- shared prefix: workgroup y of the prefix ones takes KV head
+  // kvh * KH + (y & 1), chunk c = [c * CH, min((c + 1) * CH, S)) of the
+  // prefix and sequence group cg (y >> 1 = c * groups + cg).  The chunk's
+  // rows come from the longest sequence (the reference); a sequence of the
+  // group whose block-table entries over the tokens it has in the chunk are
+  // the reference's is a member, and its query columns take part in one
+  // pass over those rows: each of the four waves holds two 16-column
+  // matrix-core blocks (32 / g sequences x g heads) and walks every token of
+  // a 64-token stage, S^T = K Q^T then O^T += V^T P^T, with one online
+  // softmax per column (tokens at or past a member's length are masked).
+  // Each member's partial goes to piece stream_wgs + B + c * B + b.  A
+  // sequence with tokens in the chunk whose entries differ runs the chunk
+  // on its own blocks (the workgroup of the pair's first head does it for
+  // both heads), into the same piece.
+  auto prefix_unit = [&](const int y) {
+    if constexpr (GRID == kGridStreamPrefix) {
+      using RP = Ring<D, NW, false, 1>;                // one KV head: 64-token stages of 256-byte rows
+      static_assert(RP::kMatBytes == kRingBytes && RP::kStageTok == 64, "prefix stages fill the ring slots");
+      constexpr int kSpw = 32 / G;                      // sequences per wave (two column blocks)
+      constexpr int kSpg = NW * kSpw;                   // sequences per workgroup
+      constexpr int kCpb = 16 / G;                      // sequences per column block
+      static_assert(kSpg == prefix_seqs_per_wg(G) && 3 * kSpg <= kCompactMaxB, "prefix sequence groups");
+      const int lane = threadIdx.x & 63, tid = threadIdx.x;
+      const int B = p.B, n_h = p.n_h;
+      const int ncg = (B + kSpg - 1) / kSpg;
+      const int hp = y & 1, cg = (y >> 1) % ncg, c = (y >> 1) / ncg;
+      const int kvh_abs = kvh * KH + hp;
+      const int S = p.prefix_tokens, CH = p.prefix_chunk;
+      const int c0 = c * CH, c1 = min(S, c0 + CH);
+      const int shift = p.block_shift, bmask = (1 << shift) - 1;
+      int* s_mis = s_upre;                              // [kSpg]: a block of the chunk is not the reference's
+      int* s_cl = s_upre + kSpg;                        // [kSpg]: context lengths of the group
+      int* s_ref = s_upre + 2 * kSpg;                   // reference sequence and its length
+      if (wave == 0) {
+        // the reference: the longest sequence (the first of that length)
+        int best = -1, bi = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int sb = 8 * lane + k;
+          const int cx = sb < B ? p.context_lens[sb] : -1;
+          if (cx > best) { best = cx; bi = sb; }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const int ob = __shfl_xor(best, off), oi = __shfl_xor(bi, off);
+          if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+        }
+        if (lane == 0) { s_ref[0] = bi; s_ref[1] = best; }
+      }
+      if (tid < kSpg) {
+        const int b = cg * kSpg + tid;
+        s_mis[tid] = 0;
+        s_cl[tid] = b < B ? p.context_lens[b] : 0;
+      }
+      __syncthreads();
+      const int ref = __builtin_amdgcn_readfirstlane(s_ref[0]);
+      const int ctx_ref = __builtin_amdgcn_readfirstlane(s_ref[1]);
+      const int ce = min(c1, ctx_ref);
+      if (ce <= c0) return;                             // no sequence reaches this chunk
+      const int lb0 = c0 >> shift;
+      const int nblk = ((ce - 1) >> shift) - lb0 + 1;
+      {
+        const int32_t* row = p.block_table + (int64_t)ref * p.max_blocks_per_seq + lb0;
+        for (int i = tid; i < nblk; i += kThr) s_bt[i] = row[i];
+      }
+      __syncthreads();
+      // DMA of the first stage(s) and the query loads go out before the
+      // membership check (its table reads), so that the three are in
+      // flight together
+      const int ml16 = lane & 15, mg = lane >> 4;
+      const int j0 = wave * RP::kDmaPerWave;             // 8 instructions of 4 rows per wave: waves 0-1 K, 2-3 V
+      const bool dma_v = j0 >= RP::kDmaPerMat;
+      const int jbase = j0 % RP::kDmaPerMat;
+      const int64_t slot_stride = (int64_t)p.n_kv * RP::kHeadRow;
+      const uint8_t* mat = reinterpret_cast<const uint8_t*>(dma_v ? p.v : p.k) + (int64_t)kvh_abs * RP::kHeadRow;
+      const uint32_t lds_mat =
+          (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&s_dma[dma_v ? 1 : 0][0][0];
+      const int lrow = lane / RP::kSrcPieces, lpiece = lane % RP::kSrcPieces;
+      auto spiece = [&](int r) { return lpiece ^ (dma_v ? RP::swz_v(r) : RP::swz_k(r)); };
+      constexpr int kPer = 4;                            // the permutations repeat every 4 instructions (16 rows)
+      static_assert(RP::kDmaPerWave % kPer == 0 && RP::kRowsPerDma * kPer == 16, "offset period");
+      uint32_t pvoff[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        pvoff[i] = (uint32_t)(lrow * slot_stride) + (uint32_t)spiece((jbase + i) * RP::kRowsPerDma + lrow) * 16u;
+      const bool pfast = (1 << shift) >= RP::kRowsPerDma;
+      const int n_st = (ce - c0 + 63) / 64;
+      auto pissue = [&](int s, int slot) {
+        const int tile0 = c0 + s * 64;
+        const uint32_t dst0 = lds_mat + (uint32_t)(slot * kRingBytes);
+        if (pfast && tile0 + 64 <= ce) {
+#pragma unroll
+          for (int jj = 0; jj < RP::kDmaPerWave; ++jj) {
+            const int jm = jbase + jj;
+            const int t0 = tile0 + jm * RP::kRowsPerDma;
+            const int32_t phys = __builtin_amdgcn_readfirstlane(s_bt[(t0 >> shift) - lb0]);
+            const uint8_t* sb = mat + (((int64_t)phys << shift) + (t0 & bmask)) * slot_stride;
+            dma16(sb, pvoff[jj % kPer], dst0 + (uint32_t)(jm * 1024));
+          }
+        } else {
+          int32_t ph[RP::kDmaPerWave];
+#pragma unroll
+          for (int jj = 0; jj < RP::kDmaPerWave; ++jj) {
+            const int r = (jbase + jj) * RP::kRowsPerDma + lrow;
+            ph[jj] = s_bt[(min(tile0 + r, ce - 1) >> shift) - lb0];
+          }
+#pragma unroll
+          for (int jj = 0; jj < RP::kDmaPerWave; ++jj) {
+            const int jm = jbase + jj;
+            const int r = jm * RP::kRowsPerDma + lrow;
+            const int t = min(tile0 + r, ce - 1);
+            const int64_t sl = ((int64_t)ph[jj] << shift) + (t & bmask);
+            dma16(mat + sl * slot_stride + spiece(r) * 16, dst0 + (uint32_t)(jm * 1024));
+          }
+        }
+      };
+#pragma unroll
+      for (int s = 0; s < RING - 1; ++s)
+        if (s < n_st) pissue(s, s);
+      // the lane's two columns (one per block): sequence bl of the group,
+      // query head ml16 % g of KV head kvh_abs
+      int bcol[2];
+      u32x4_t qf2[2][kKs];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        bcol[cb] = cg * kSpg + wave * kSpw + cb * kCpb + ml16 / G;
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) +
+                              ((int64_t)min(bcol[cb], B - 1) * n_h + (int64_t)kvh_abs * G + ml16 % G) * D * 2;
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks)
+          qf2[cb][ks] = *reinterpret_cast<const u32x4_t*>(qrow + (32 * ks + 8 * mg) * 2);
+      }
+      for (int i = tid; i < kSpg * nblk; i += kThr) {
+        const int bl = i / nblk, jj = i % nblk;
+        const int lim = min(s_cl[bl], ce);
+        if (lim > c0 && jj <= ((lim - 1) >> shift) - lb0) {
+          const int b = cg * kSpg + bl;
+          if (p.block_table[(int64_t)b * p.max_blocks_per_seq + lb0 + jj] != s_bt[jj]) s_mis[bl] = 1;
+        }
+      }
+      const int any_member =
+          __builtin_amdgcn_readfirstlane(__syncthreads_or(tid < kSpg && s_cl[tid] > c0 && s_mis[tid] == 0));
+      const int64_t piece0 = (int64_t)p.stream_wgs + B + (int64_t)c * B;   // + b: this chunk's piece
+      if (!any_member) wait_vm_imm<0>();                  // the first stages' DMA lands before the ring is reused
+      if (any_member) {
+        int lim[2];
+        bool mem[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const int bl = bcol[cb] - cg * kSpg;
+          mem[cb] = s_cl[bl] > c0 && s_mis[bl] == 0;
+          lim[cb] = mem[cb] ? min(s_cl[bl], ce) : 0;
+#pragma unroll
+          for (int ks = 0; ks < kKs; ++ks)
+            if (!mem[cb]) qf2[cb][ks] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+        f32x4_t acc2[2][kCb];
+        float mm2[2] = {-INFINITY, -INFINITY}, ml2[2] = {0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int db = 0; db < kCb; ++db) acc2[cb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        const float qscale = p.scale * kLog2e;
+        auto pstage = [&](int s, int slot) {
+          wait_vm(min(RING - 2, n_st - 1 - s) * RP::kDmaPerWave);
+          lds_barrier();
+          if (s + RING - 1 < n_st) pissue(s + RING - 1, (slot + RING - 1) % RING);
+          const uint8_t* kst = &s_dma[0][slot][0];
+          const uint8_t* vst = &s_dma[1][slot][0];
+          const int tile0 = c0 + s * 64;
+          const uint32_t vbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)vst;
+          const int cp = ml16 & 3;
+          // the stage's four 16-token blocks in turn: scores of both column
+          // blocks (one K fragment per k-step serves both), the online
+          // softmax per column, then the values (a loop, not unrolled: the
+          // reads of one block in flight at a time keep the registers within
+          // two waves per SIMD)
+#pragma unroll 1
+          for (int tb = 0; tb < 4; ++tb) {
+            f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+            const int row = 16 * tb + ml16;
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) {
+              const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
+                  kst + row * RP::kRowBytes + (((4 * ks + mg) ^ RP::swz_k(row)) * 16));
+#pragma unroll
+              for (int cb = 0; cb < 2; ++cb)
+                sacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qf2[cb][ks]), sacc[cb], 0, 0, 0);
+            }
+            i16x4_t pb[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+              float sc[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                sc[i] = tile0 + 16 * tb + 4 * mg + i < lim[cb] ? sacc[cb][i] * qscale : -INFINITY;
+              float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+              {
+                const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+                smax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+                const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+                smax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+              }
+              constexpr float kSlack = 8.f;
+              if (mm2[cb] == -INFINITY) {
+                mm2[cb] = smax;
+              } else if (__builtin_amdgcn_ballot_w64(smax > mm2[cb] + kSlack)) {
+                const float m_new = fmaxf(mm2[cb], smax);
+                const float alpha = __builtin_amdgcn_exp2f(mm2[cb] - m_new);
+                ml2[cb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < kCb; ++db) acc2[cb][db] *= alpha;
+                mm2[cb] = m_new;
+              }
+              float pr[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                pr[i] = sc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[i] - mm2[cb]);
+              const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{pr[0], pr[1]}), bf16x2_t));
+              const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{pr[2], pr[3]}), bf16x2_t));
+              ml2[cb] += (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23));
+              pb[cb] = __builtin_bit_cast(i16x4_t, (u32x2_t{p01, p23}));
+            }
+            // V^T fragments by transposed reads, each used for both column blocks
+            const int tv = 16 * tb + 4 * mg + (ml16 >> 2);
+            const uint32_t vrow = vbase + (uint32_t)(tv * RP::kRowBytes + 8 * (cp & 1));
+            const int svz = RP::swz_v(tv);
+#pragma unroll
+            for (int db = 0; db < kCb; ++db) {
+              const uint32_t a = vrow + (uint32_t)((((2 * db + (cp >> 1)) ^ svz)) * 16);
+              const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a);
+#pragma unroll
+              for (int cb = 0; cb < 2; ++cb)
+                acc2[cb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[cb], acc2[cb][db], 0, 0, 0);
+            }
+          }
+        };
+        for (int s0 = 0; s0 < n_st; s0 += RING) {
+#pragma unroll
+          for (int u = 0; u < RING; ++u)
+            if (s0 + u < n_st) pstage(s0 + u, u);
+        }
+        // each member column's partial: (max, sum) and the output over the sum
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          float L = ml2[cb];
+          L += __shfl_xor(L, 16);
+          L += __shfl_xor(L, 32);
+          if (mem[cb]) {
+            const int64_t pr = (piece0 + bcol[cb]) * n_h + (int64_t)kvh_abs * G + ml16 % G;
+            const float inv = 1.0f / L;
+#pragma unroll
+            for (int db = 0; db < kCb; ++db)
+              *reinterpret_cast<f32x4_t*>(&p.part_o[pr * D + 16 * db + 4 * mg]) = acc2[cb][db] * inv;
+            if (mg == 0) { p.part_ml[2 * pr] = mm2[cb]; p.part_ml[2 * pr + 1] = L; }
+          }
+        }
+      }
+      // sequences whose blocks in the chunk are their own
+      if (hp == 0) {
+#pragma unroll 1
+        for (int bl = 0; bl < kSpg; ++bl) {
+          const int cx = __builtin_amdgcn_readfirstlane(s_cl[bl]);
+          if (cx > c0 && __builtin_amdgcn_readfirstlane(s_mis[bl])) {
+            __syncthreads();                            // the ring and block table are free
+            unit(cg * kSpg + bl, c0, min(c1, cx), cx, 1, piece0 * n_h, false);
+          }
+        }
+      }
+    }
+  };
+
   if constexpr (GRID == kGridSplit) {
     // grid (KV head, sequence, split)
     const int b = blockIdx.y, split = blockIdx.z, ctx = p.context_lens[b];
@@ -689,7 +1046,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
     if (t_begin >= ctx) {
       if (split == 0) zero_out(b);
     } else {
-      unit(b, t_begin, min(ctx, t_begin + p.split_tokens), ctx, p.num_splits, split);
+      unit(b, t_begin, min(ctx, t_begin + p.split_tokens), ctx, p.num_splits, split, true);
     }
   } else if constexpr (GRID == kGridCompact) {
     // Grid (KV head, unit) for ragged batches, a unit being one split of one
@@ -740,77 +1097,16 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       if (t_begin >= ctx) {
         if (split == 0) zero_out(b);
       } else {
-        unit(b, t_begin, min(ctx, t_begin + p.split_tokens), ctx, p.num_splits, split);
+        unit(b, t_begin, min(ctx, t_begin + p.split_tokens), ctx, p.num_splits, split, true);
       }
       __syncthreads();                              // the unit's LDS is free again
     }
   } else {
-    // Stream grid (KV head, workgroup j of gridDim.y) for ragged batches
-    // (B <= kCompactMaxB).  The batch's tokens, each sequence padded to a
-    // multiple of 16, are laid end to end and cut into gridDim.y equal ranges
-    // of T tokens (a multiple of 16); workgroup j takes range j, i.e. its
-    // share of every sequence the range overlaps.  Each share is a unit whose
-    // partial goes to piece j + b (distinct for every (j, b) that has a
-    // share: the ranges and the sequences are both in order), and the
-    // workgroup holding a sequence's first share records its first and last
-    // workgroup for the merge.  Wave 0 forms the padded prefix (8 sequences
-    // per lane).
-    if (wave == 0) {
-      const int lane = threadIdx.x & 63;
-      int len[8];
-      int sum = 0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int sb = 8 * lane + k;
-        const int c = sb < p.B ? p.context_lens[sb] : 0;
-        len[k] = (max(c, 0) + 15) & ~15;
-        sum += len[k];
-      }
-      int incl = sum;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-      }
-      int run = incl - sum;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        s_upre[8 * lane + k] = run;
-        run += len[k];
-      }
-      if (lane == kWave - 1) s_upre[kCompactMaxB] = incl;
-    }
-    __syncthreads();
-    const int nwg = gridDim.y, j = blockIdx.y;
-    const int total = __builtin_amdgcn_readfirstlane(s_upre[p.B]);
-    const int T = max(16, ((total + nwg - 1) / nwg + 15) & ~15);
-    const int64_t r0 = (int64_t)j * T, r1 = r0 + T;
-    // empty sequences: zeroed by workgroup b mod gridDim.y (one piece, done)
-    for (int b = j; b < p.B; b += nwg) {
-      if (p.context_lens[b] <= 0) {
-        zero_out(b);
-        if (kvh == 0 && threadIdx.x == 0) { p.seq_meta[2 * b] = 0; p.seq_meta[2 * b + 1] = 0; }
-      }
-    }
-    // the first sequence that can overlap the range: the largest b with
-    // s_upre[b] <= r0
-    int lo = 0, hi = p.B;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_upre[mid] <= r0) lo = mid; else hi = mid - 1;
-    }
-    for (int b = __builtin_amdgcn_readfirstlane(lo); b < p.B; ++b) {
-      const int st = __builtin_amdgcn_readfirstlane(s_upre[b]);
-      if (st >= r1) break;
-      const int ctx = p.context_lens[b];
-      const int a = (int)max(r0 - st, (int64_t)0), e = (int)min(r1 - st, (int64_t)ctx);
-      if (ctx <= 0 || a >= e) continue;
-      if (a == 0 && kvh == 0 && threadIdx.x == 0) {
-        p.seq_meta[2 * b] = j;
-        p.seq_meta[2 * b + 1] = (st + ctx - 1) / T;
-      }
-      unit(b, a, e, ctx, 1, (int64_t)j * p.n_h);
-      __syncthreads();                              // the unit's LDS is free again
+    if constexpr (GRID == kGridStreamPrefix) {
+      if ((int)blockIdx.y < p.prefix_wgs) prefix_unit(blockIdx.y);
+      else stream_part(blockIdx.y - p.prefix_wgs, gridDim.y - p.prefix_wgs, p.prefix_tokens);
+    } else {
+      stream_part(blockIdx.y, gridDim.y, 0);
     }
   }
 }
@@ -848,10 +1144,22 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
   if ((q8 && p.stream_wgs != 0) || (!q8 && p.compact_units != 0)) return hipErrorInvalidValue;
   // a split's blocks must fit the staged block table (one chunk)
   if ((p.split_tokens >> p.block_shift) > (q8 ? kBtSlotsInt8 : kBtSlots)) return hipErrorInvalidValue;
-  const dim3 grid = p.stream_wgs != 0     ? dim3(groups, (unsigned)p.stream_wgs, 1u)
+  // shared prefix: bf16 with two KV heads per workgroup, on the stream grid,
+  // no append, chunks of whole 64-token stages whose blocks fit the table
+  if (p.prefix_tokens != 0 &&
+      (q8 || kh != 2 || p.d_k != 128 || p.stream_wgs <= 0 || p.prefix_wgs <= 0 || p.prefix_tokens < 0 ||
+       p.prefix_tokens % 64 || p.prefix_chunk <= 0 || p.prefix_chunk % 64 || p.k_new != nullptr ||
+       (p.prefix_chunk >> p.block_shift) + 2 > kBtSlots ||
+       (int64_t)p.stream_wgs + p.prefix_wgs > 65535 ||
+       p.prefix_wgs != 2 * ((p.prefix_tokens + p.prefix_chunk - 1) / p.prefix_chunk) *
+                           ((p.B + prefix_seqs_per_wg(g) - 1) / prefix_seqs_per_wg(g))))
+    return hipErrorInvalidValue;
+  const dim3 grid = p.stream_wgs != 0     ? dim3(groups, (unsigned)(p.stream_wgs + (p.prefix_tokens ? p.prefix_wgs : 0)), 1u)
                     : p.compact_units != 0 ? dim3(groups, (unsigned)p.compact_units, 1u)
                                            : dim3(groups, (unsigned)p.B, (unsigned)p.num_splits);
-  const int mode = p.stream_wgs != 0 ? kGridStream : (p.compact_units != 0 ? kGridCompact : kGridSplit);
+  const int mode = p.prefix_tokens != 0 ? kGridStreamPrefix
+                   : p.stream_wgs != 0  ? kGridStream
+                                        : (p.compact_units != 0 ? kGridCompact : kGridSplit);
 #define PKV_RING(D_, G_, Q8_, KH_)                                                                 \
   do {                                                                                              \
     constexpr int kRagged = Q8_ ? kGridCompact : kGridStream;                                       \
@@ -862,17 +1170,27 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, kGridSplit, KH_>), grid, \
                          dim3(64 * kWaves), 0, stream, p);                                         \
   } while (0)
+  // bf16, two KV heads per workgroup: the grids above plus the shared prefix
+#define PKV_RING_PAIR(G_)                                                                           \
+  do {                                                                                              \
+    if (mode == kGridStreamPrefix)                                                                  \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<128, G_, kWaves, kRing, false, kGridStreamPrefix, 2>), \
+                         grid, dim3(64 * kWaves), 0, stream, p);                                   \
+    else                                                                                           \
+      PKV_RING(128, G_, false, 2);                                                                 \
+  } while (0)
+  if (p.prefix_tokens != 0 && !(p.d_k == 128 && (g == 4 || g == 8) && !q8 && kh == 2)) return hipErrorInvalidValue;
   if (p.d_k == 128 && g == 8) {
     if (q8 && kh == 4) PKV_RING(128, 8, true, 4);
     else if (q8 && kh == 2) PKV_RING(128, 8, true, 2);
     else if (q8) PKV_RING(128, 8, true, 1);
-    else if (kh == 2) PKV_RING(128, 8, false, 2);
+    else if (kh == 2) PKV_RING_PAIR(8);
     else PKV_RING(128, 8, false, 1);
   } else if (p.d_k == 128 && g == 4) {
     if (q8 && kh == 4) PKV_RING(128, 4, true, 4);
     else if (q8 && kh == 2) PKV_RING(128, 4, true, 2);
     else if (q8) PKV_RING(128, 4, true, 1);
-    else if (kh == 2) PKV_RING(128, 4, false, 2);
+    else if (kh == 2) PKV_RING_PAIR(4);
     else PKV_RING(128, 4, false, 1);
   } else if (p.d_k == 64 && g == 8) {
     if (q8) PKV_RING(64, 8, true, 1);
@@ -883,6 +1201,7 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
   } else {
     return hipErrorInvalidValue;
   }
+#undef PKV_RING_PAIR
 #undef PKV_RING
   return hipGetLastError();
 }

@@ -100,7 +100,25 @@ struct DecodeParams {
   // first and last workgroup.
   int32_t compact_units;
   int32_t stream_wgs;
+  // Shared prefix (bf16 LDS-ring kernel with two KV heads per workgroup,
+  // stream grid only; prefix_tokens = 0: off).  Tokens [0, prefix_tokens) of
+  // every sequence are handled by prefix_wgs extra workgroups per KV-head
+  // group (grid.y = stream_wgs + prefix_wgs, the prefix ones first), each
+  // taking one KV head, one chunk of prefix_chunk tokens and a group of
+  // sequences: the chunk's rows of the longest sequence are read once and
+  // serve every sequence whose block-table entries over the chunk are the
+  // same blocks (checked on the device); any other sequence's chunk runs on
+  // its own blocks in the same workgroup.  The stream workgroups take
+  // tokens [prefix_tokens, ctx) of each sequence.  Prefix partials of chunk
+  // c and sequence b go to piece stream_wgs + B + c * B + b.
+  int32_t prefix_tokens;
+  int32_t prefix_chunk;
+  int32_t prefix_wgs;
 };
+
+// Sequences one prefix workgroup serves: four waves of 32 query columns
+// (two 16-column matrix-core blocks), g columns per sequence.
+constexpr int prefix_seqs_per_wg(int g) { return 4 * (32 / g); }
 
 constexpr int kCompactMaxB = 512;
 

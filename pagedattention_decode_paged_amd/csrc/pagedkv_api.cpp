@@ -249,6 +249,7 @@ const char* decode_desc_error(const kvp_decode_desc* d) {
   if (d->split_tokens < 0) return "split_tokens must be >= 0";
   if (d->total_context_len < 0) return "total_context_len must be >= 0";
   if (d->workgroups < 0) return "workgroups must be >= 0";
+  if (d->shared_prefix_tokens < 0) return "shared_prefix_tokens must be >= 0";
   return nullptr;
 }
 
@@ -425,19 +426,84 @@ int32_t num_splits_of(const kvp_decode_desc* d, int32_t split) {
   return (d->max_context_len + split - 1) / split;
 }
 
-// Stream grid workspace: [part_o (wgs + B) x n_h x d_v][part_ml (wgs + B) x
-// n_h x 2][seq_meta B x 2 int32], each region 256-byte aligned.
+// Shared prefix on the stream grid (paged_decode_attention, bf16, two KV
+// heads per workgroup): the hint rounded down to whole 64-token stages,
+// chunks of kPrefixChunk tokens (128: 33.7 us on the 8B-shaped layer against
+// 36.6 at 256 and 51.6 at 512), two prefix workgroups (one per KV head of
+// the pair) per chunk and group of prefix_seqs_per_wg(g) sequences, and the
+// stream workgroups for the tokens past the prefix filling the rest of one
+// round of two workgroups per compute unit.
+#ifndef PKV_PREFIX_CHUNK
+#define PKV_PREFIX_CHUNK 128
+#endif
+#ifndef PKV_PREFIX_ROUND
+#define PKV_PREFIX_ROUND 2
+#endif
+constexpr int32_t kPrefixChunk = PKV_PREFIX_CHUNK;
+
+struct PrefixPlan {
+  int32_t tokens = 0, chunk = 0, wgs = 0, stream = 0;
+  int32_t pieces(const kvp_decode_desc* d) const {   // prefix pieces: chunks x B
+    return tokens ? (tokens + chunk - 1) / chunk * d->B : 0;
+  }
+};
+
+PrefixPlan prefix_plan(const kvp_decode_desc* d, Variant v) {
+  PrefixPlan pp;
+  if (d->shared_prefix_tokens <= 0 || v != Variant::Float || d->kv_dtype != KVP_BF16 ||
+      d->q_dtype != KVP_BF16 || d->split_tokens > 0 || d->B <= 0 || d->B > pkv::kCompactMaxB ||
+      d->d_k != 128 || d->d_v != 128 || ring_kv_group(d, v) != 2)
+    return pp;
+  const int g = d->n_h / d->n_kv;
+  if (g != 4 && g != 8) return pp;
+  if ((int64_t)d->B * ((int64_t)d->max_context_len + 15) >= ((int64_t)1 << 31)) return pp;
+  const int32_t S = std::min(d->shared_prefix_tokens, d->max_context_len) & ~63;
+  if (S < 64) return pp;
+  int32_t ch = kPrefixChunk;
+  while (ch > 64 && (ch >> log2i(d->block_size)) + 2 > kBtSlots) ch -= 64;
+  const int64_t nc = (S + ch - 1) / ch;
+  const int64_t ncg = (d->B + pkv::prefix_seqs_per_wg(g) - 1) / pkv::prefix_seqs_per_wg(g);
+  const int64_t wgs = 2 * nc * ncg;
+  const int64_t groups = d->n_kv / 2;
+  const int64_t total = d->total_context_len > 0 ? d->total_context_len : (int64_t)d->B * d->max_context_len;
+  int64_t w = PKV_PREFIX_ROUND * (int64_t)device_cus() / groups - wgs;
+  const int64_t by_len = (total + kStreamMinTokens - 1) / kStreamMinTokens;
+  if (w > by_len) w = by_len;
+  if (w < 1) w = 1;
+  if (w + wgs > 65535) return pp;
+  pp.tokens = S;
+  pp.chunk = ch;
+  pp.wgs = (int32_t)wgs;
+  pp.stream = (int32_t)w;
+  return pp;
+}
+
+// Stream grid workspace: [part_o pieces x n_h x d_v][part_ml pieces x n_h x
+// 2][seq_meta B x 2 int32], each region 256-byte aligned; pieces = wgs + B
+// (+ the prefix pieces).
 struct StreamWorkspace {
   size_t o_bytes, ml_bytes, meta_bytes;
   size_t total() const { return o_bytes + ml_bytes + meta_bytes; }
 };
-StreamWorkspace stream_workspace(const kvp_decode_desc* d, int32_t wgs) {
-  const size_t rows = ((size_t)wgs + d->B) * d->n_h;
+StreamWorkspace stream_workspace(const kvp_decode_desc* d, int32_t wgs, int32_t extra_pieces = 0) {
+  const size_t rows = ((size_t)wgs + d->B + (size_t)extra_pieces) * d->n_h;
   return {round_up(rows * d->d_v * sizeof(float), 256), round_up(rows * 2 * sizeof(float), 256),
           round_up((size_t)d->B * 2 * sizeof(int32_t), 256)};
 }
 
+size_t workspace_plain(const kvp_decode_desc* d, Variant v);
+
+// The shared-prefix hint applies to paged_decode_attention only; the same
+// description on another entry point runs without it, so the size covers
+// both.
 size_t workspace_for(const kvp_decode_desc* d, Variant v) {
+  const size_t plain = workspace_plain(d, v);
+  const PrefixPlan pp = prefix_plan(d, v);
+  if (pp.tokens == 0) return plain;
+  return std::max(plain, stream_workspace(d, pp.stream, pp.pieces(d)).total());
+}
+
+size_t workspace_plain(const kvp_decode_desc* d, Variant v) {
   if (v == Variant::Mla) return d->B > 0 ? mla_workspace(d).total() : 0;
   const int32_t sw = stream_wgs(d, v);
   if (sw > 0) return stream_workspace(d, sw).total();
@@ -680,7 +746,9 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
       return fail(KVP_ERR_INVALID_ARG, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
     if (!aligned(workspace, 256)) return fail(KVP_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   }
-  const int32_t sw = stream_wgs(d, var);
+  // the shared prefix (plain calls only: an append runs without it)
+  const PrefixPlan pp = app ? PrefixPlan{} : prefix_plan(d, var);
+  const int32_t sw = pp.tokens ? pp.stream : stream_wgs(d, var);
   if (sw == 0 && ns > 1024)
     return fail(KVP_ERR_UNSUPPORTED, "%s: more than 1024 context splits (raise split_tokens)", fn);
 
@@ -694,12 +762,15 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   p.context_lens = context_lens;
   p.out = out;
   if (sw > 0) {
-    const StreamWorkspace sws = stream_workspace(d, sw);
+    const StreamWorkspace sws = stream_workspace(d, sw, pp.pieces(d));
     uint8_t* w = static_cast<uint8_t*>(workspace);
     p.part_o = reinterpret_cast<float*>(w);
     p.part_ml = reinterpret_cast<float*>(w + sws.o_bytes);
     p.seq_meta = reinterpret_cast<int32_t*>(w + sws.o_bytes + sws.ml_bytes);
     p.stream_wgs = sw;
+    p.prefix_tokens = pp.tokens;
+    p.prefix_chunk = pp.chunk;
+    p.prefix_wgs = pp.wgs;
   } else if (need > 0) {
     const size_t rows = (size_t)d->B * d->n_h * ns;
     // [part_o][part_ml]

@@ -175,6 +175,33 @@ def custom_structure(context_lens, block_size: int, num_blocks: int | None = Non
     return Structure(ctx, _tables_from_counts(counts, perm, block_size, mb), nb)
 
 
+def shared_prefix_structure(context_lens, block_size: int, shared_blocks: int, seed: int = 11,
+                            diverge=(), pad_blocks: int = 0) -> Structure:
+    """Tables whose first ``shared_blocks`` logical blocks are one shared set
+    of physical blocks (as in the 8B-shaped workload), a random permutation
+    of a pool sized to the total.  ``diverge`` lists (sequence, logical
+    block) pairs inside the shared range that get a block of their own
+    instead (a sequence that only partly shares the prefix)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctx = np.asarray(context_lens, dtype=np.int32)
+    nbs = [_blocks_needed(c, block_size) for c in ctx]
+    own = set((int(b), int(j)) for b, j in diverge)
+    private = [sum(1 for j in range(n) if j >= shared_blocks or (b, j) in own) for b, n in enumerate(nbs)]
+    n_blocks = shared_blocks + int(sum(private))
+    perm = rng.permutation(n_blocks).astype(np.int32)
+    mb = max(max(nbs) if nbs else 1, 1) + pad_blocks
+    bt = np.full((len(ctx), mb), -1, dtype=np.int32)
+    pos = shared_blocks
+    for b, n in enumerate(nbs):
+        for j in range(n):
+            if j < shared_blocks and (b, j) not in own:
+                bt[b, j] = perm[j]
+            else:
+                bt[b, j] = perm[pos]
+                pos += 1
+    return Structure(ctx, bt, n_blocks, shared_blocks=shared_blocks)
+
+
 # --------------------------------------------------------------------------
 # token lists (structure only: which sequence and position each token has)
 # --------------------------------------------------------------------------

@@ -212,3 +212,32 @@ def test_ragged_planning_with_total_hint():
     assert pk.decode_split_tokens(d_q8) == split
     ns = -(-mc // split)
     assert pk.decode_workspace_size(d_q8) == _r256(B * n_h * ns * d * 4) + _r256(B * n_h * ns * 2 * 4)
+
+
+def test_shared_prefix_planning():
+    """The shared-prefix plan on the host (256 compute units without a GPU):
+    the 8B-shaped layer with a 2048-token hint takes 16 chunks of 128 tokens,
+    two prefix workgroups per chunk (one per KV head of a pair) for its one
+    group of 32 sequences, and the stream workgroups fill the rest of one
+    round of two per compute unit; the workspace holds the stream pieces
+    (workgroups + B) and the prefix pieces (chunks x B).  The hint is
+    rounded down to a multiple of 64, and it is ignored (the plain plan) for
+    INT8 pools, d = 64 and forced splits."""
+    B, n_h, n_kv, mc, total = 32, 32, 8, 4060, 77726
+    kw = dict(B=B, n_h=n_h, n_kv=n_kv, max_blocks_per_seq=254, max_context_len=mc, total_context_len=total)
+    plain = pk.decode_workspace_size(_desc(**kw))
+    for hint, S in ((2048, 2048), (2100, 2048), (5000, 4032)):
+        nc = -(-S // 128)
+        wgs = 2 * nc
+        w = min(2 * 256 // 4 - wgs, -(-total // 256))
+        rows = (w + B + nc * B) * n_h
+        want = _r256(rows * 128 * 4) + _r256(rows * 8) + _r256(B * 8)
+        assert pk.decode_workspace_size(_desc(shared_prefix_tokens=hint, **kw)) == max(plain, want), hint
+    assert pk.decode_workspace_size(_desc(shared_prefix_tokens=63, **kw)) == plain
+    q8 = dict(kw, kv_dtype=pk.KVP_INT8)
+    assert pk.decode_workspace_size(_desc(shared_prefix_tokens=2048, **q8)) == pk.decode_workspace_size(_desc(**q8))
+    assert (pk.decode_workspace_size(_desc(shared_prefix_tokens=2048, split_tokens=512, **kw)) ==
+            pk.decode_workspace_size(_desc(split_tokens=512, **kw)))
+    d64 = dict(kw, d_k=64, d_v=64)
+    assert pk.decode_workspace_size(_desc(shared_prefix_tokens=2048, **d64)) == pk.decode_workspace_size(_desc(**d64))
+    assert _call_decode(_desc(shared_prefix_tokens=-1, max_context_len=200)) == pk.KVP_ERR_INVALID_ARG
