@@ -36,13 +36,26 @@ from .paged_attention import (  # noqa: F401
     gather_sequence,
     softmax_weights,
     decode_attention_contiguous,
+    window_start,
     paged_decode_attention,
     quantize_int8_rows,
     dequantize_int8,
     paged_decode_attention_int8,
+    quantize_int4_rows,
+    pack_int4,
+    unpack_int4,
+    paged_decode_attention_int4,
+    paged_prefill_attention,
     paged_decode_attention_mla,
     split_partials,
     merge_partials,
     kv_cache_bytes,
     decode_attention_intensity,
+)
+from .block_allocator import (  # noqa: F401
+    block_hash,
+    BlockAllocator,
+    copy_blocks,
+    swap_out,
+    swap_in,
 )

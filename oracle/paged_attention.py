@@ -173,8 +173,21 @@ def decode_attention_contiguous(q: np.ndarray, K: np.ndarray, V: np.ndarray,
     return out
 
 
+def window_start(L: int, window: int) -> int:
+    """First position a query at the end of a sequence of ``L`` tokens sees.
+
+    guijiagi section 5.1 (sliding window cache): with window size w only
+    the most recent w tokens are kept and attended, i.e. positions
+    ``L - w .. L - 1`` (all of them when ``L <= w``).  ``window = 0`` means
+    no window (the whole context).
+    """
+    if window < 0:
+        raise ValueError("window must be >= 0")
+    return max(0, L - window) if window > 0 else 0
+
+
 def paged_decode_attention(q, k_pool, v_pool, block_table, context_lens,
-                           scale: float) -> np.ndarray:
+                           scale: float, window: int = 0) -> np.ndarray:
     """Decode attention over a paged KV cache, float64 ``[B, n_h, d_v]``.
 
     qwbw section 3.4: for each sequence, gather its K and V through the
@@ -183,7 +196,8 @@ def paged_decode_attention(q, k_pool, v_pool, block_table, context_lens,
     paging changes only where rows live (hx section 4.2: physical
     non-contiguity is invisible to the kernel).  ``context_lens[b]`` counts
     every cached token of sequence b, the token being decoded included
-    (qwbw section 1.2 appends K/V before attending).
+    (qwbw section 1.2 appends K/V before attending).  With ``window > 0``
+    only the last ``window`` positions take part (:func:`window_start`).
     """
     q = np.asarray(q)
     B = q.shape[0]
@@ -192,7 +206,8 @@ def paged_decode_attention(q, k_pool, v_pool, block_table, context_lens,
         L = int(context_lens[b])
         K = gather_sequence(k_pool, block_table[b], L)
         V = gather_sequence(v_pool, block_table[b], L)
-        out.append(decode_attention_contiguous(q[b], K, V, scale))
+        w0 = window_start(L, window)
+        out.append(decode_attention_contiguous(q[b], K[w0:], V[w0:], scale))
     return np.stack(out, axis=0)
 
 
@@ -240,7 +255,8 @@ def dequantize_int8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
 
 
 def paged_decode_attention_int8(q, k_codes, k_scales, v_codes, v_scales,
-                                block_table, context_lens, scale: float) -> np.ndarray:
+                                block_table, context_lens, scale: float,
+                                window: int = 0) -> np.ndarray:
     """Decode attention over an INT8 paged cache with per-(slot, head) scales.
 
     Pools: codes ``int8 [NB, bs, n_kv, d]``, scales ``float32 [NB, n_kv, bs]``
@@ -251,7 +267,123 @@ def paged_decode_attention_int8(q, k_codes, k_scales, v_codes, v_scales,
     """
     k = dequantize_int8(k_codes, np.swapaxes(np.asarray(k_scales), 1, 2))
     v = dequantize_int8(v_codes, np.swapaxes(np.asarray(v_scales), 1, 2))
-    return paged_decode_attention(q, k, v, block_table, context_lens, scale)
+    return paged_decode_attention(q, k, v, block_table, context_lens, scale, window)
+
+
+# --------------------------------------------------------------------------
+# INT4 KV cache with an unquantized attention sink
+# --------------------------------------------------------------------------
+
+def quantize_int4_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric per-row INT4 quantization in IEEE binary32 arithmetic.
+
+    guijiagi section 4.2 (quantization method, 4-bit branch): the scale is
+    the absolute maximum over the last dimension divided by 7; the code is
+    x / scale rounded to nearest and clamped to [-8, 7].  Taken in float32
+    step by step as in :func:`quantize_int8_rows` (correctly rounded
+    divisions, round-half-to-even); an all-zero row gets scale 0 and codes
+    0.  Returns ``(codes int8 [..., d] in [-8, 7], scale float32 [...])``.
+    """
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        x32 = (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    else:
+        x32 = np.asarray(x, dtype=np.float32)
+    a = np.max(np.abs(x32), axis=-1)
+    scale = (a / np.float32(7.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    quo = (x32 / safe[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(quo), -8, 7)
+    codes = np.where(scale[..., None] > 0, codes, 0).astype(np.int8)
+    return codes, scale.astype(np.float32)
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte (guijiagi section 4.2 gives the 4x memory
+    saving of 4-bit storage but no byte order): element 2i in the low
+    nibble and element 2i + 1 in the high nibble of byte i, each as a 4-bit
+    two's complement value.  ``[..., d]`` int8 -> ``[..., d / 2]`` uint8."""
+    c = np.asarray(codes, dtype=np.int8)
+    if c.shape[-1] % 2:
+        raise ValueError("an even number of codes per row")
+    u = c.astype(np.uint8) & np.uint8(0x0F)
+    return (u[..., 0::2] | (u[..., 1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`pack_int4`: ``[..., d / 2]`` uint8 -> ``[..., d]`` int8."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lo = (p & np.uint8(0x0F)).astype(np.int16)
+    hi = (p >> np.uint8(4)).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def paged_decode_attention_int4(q, k_packed, k_scales, v_packed, v_scales, sink_k, sink_v,
+                                block_table, context_lens, scale: float) -> np.ndarray:
+    """Decode attention over an INT4 paged cache whose first tokens are kept
+    unquantized.
+
+    guijiagi section 4.3 (attention sink): the first k tokens of a sequence
+    draw attention from every later token, so their quantization error is
+    amplified; they are kept at full precision (k = 4 is typical).  Here
+    ``sink_k``/``sink_v`` ``[B, n_sink, n_kv, d]`` hold positions
+    ``0 .. n_sink - 1`` of each sequence (bf16 bits or floats); every other
+    position comes from the paged INT4 pool (codes packed by
+    :func:`pack_int4` ``[NB, bs, n_kv, d / 2]``, scales ``float32 [NB, n_kv,
+    bs]``), dequantized as ``code * scale``.  The pool's rows at sink
+    positions are not read.
+    """
+    q = np.asarray(q)
+    k = dequantize_int8(unpack_int4(k_packed), np.swapaxes(np.asarray(k_scales), 1, 2))
+    v = dequantize_int8(unpack_int4(v_packed), np.swapaxes(np.asarray(v_scales), 1, 2))
+    sk, sv = widen(sink_k), widen(sink_v)
+    n_sink = sk.shape[1]
+    out = []
+    for b in range(q.shape[0]):
+        L = int(context_lens[b])
+        K = gather_sequence(k, block_table[b], L).copy()
+        V = gather_sequence(v, block_table[b], L).copy()
+        ns = min(L, n_sink)
+        K[:ns] = sk[b, :ns]
+        V[:ns] = sv[b, :ns]
+        out.append(decode_attention_contiguous(q[b], K, V, scale))
+    return np.stack(out, axis=0)
+
+
+# --------------------------------------------------------------------------
+# chunked prefill over the paged cache
+# --------------------------------------------------------------------------
+
+def paged_prefill_attention(q, k_pool, v_pool, block_table, start_pos, chunk_lens,
+                            scale: float) -> np.ndarray:
+    """Causal attention of a chunk of new tokens over a paged cache.
+
+    faulkner, continuous batching section (chunked prefill): a long prompt
+    is processed a fixed number of tokens per step, each chunk attending to
+    everything cached before it plus itself, causally.  Sequence b's chunk
+    holds ``chunk_lens[b]`` query tokens at positions ``start_pos[b] + i``;
+    their K/V are already in the cache (written before the attention, as
+    in qwbw section 1.2), and query i sees positions ``0 .. start_pos[b] +
+    i``.  ``q [B, C, n_h, d_k]`` -> ``[B, C, n_h, d_v]`` float64 (rows past
+    a chunk's length are zero).
+    """
+    q = np.asarray(q)
+    B, C = q.shape[0], q.shape[1]
+    out = np.zeros((B, C, q.shape[2], np.asarray(v_pool).shape[3]), dtype=np.float64)
+    for b in range(B):
+        p0, n = int(start_pos[b]), int(chunk_lens[b])
+        if n == 0:
+            continue
+        K = gather_sequence(k_pool, block_table[b], p0 + n)
+        V = gather_sequence(v_pool, block_table[b], p0 + n)
+        for i in range(n):
+            out[b, i] = decode_attention_contiguous(q[b, i], K[:p0 + i + 1], V[:p0 + i + 1], scale)
+    return out
 
 
 # --------------------------------------------------------------------------
