@@ -223,6 +223,18 @@ typedef struct {
                                   device); any other sequence's chunk is read
                                   from its own blocks.  A wrong value costs
                                   time, never results. */
+  int32_t window;              /* sliding window (guijiagi 5.1; 0 = none):
+                                  a sequence of L tokens attends to its last
+                                  min(L, window) positions only, and blocks
+                                  before them are not read.  The block table
+                                  must map every position from max(0, L -
+                                  window) rounded down to a multiple of 16.
+                                  Supported on paged_decode_attention,
+                                  paged_decode_attention_int8 and
+                                  paged_decode_attention_append for g in
+                                  {4, 8}, d in {64, 128} (bf16 and INT8
+                                  pools); other shapes and MLA return
+                                  KVP_ERR_UNSUPPORTED. */
 } kvp_decode_desc;
 
 /* Workspace bytes the call needs for this description (split partials).

@@ -51,7 +51,8 @@ class _DecodeDesc(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
                 ("split_tokens", ctypes.c_int32), ("total_context_len", ctypes.c_int64),
-                ("workgroups", ctypes.c_int32), ("shared_prefix_tokens", ctypes.c_int32)]
+                ("workgroups", ctypes.c_int32), ("shared_prefix_tokens", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -254,11 +255,11 @@ def paged_gather(pool: torch.Tensor, block_table: torch.Tensor, context_lens: to
 # --------------------------------------------------------------------- decode
 
 def _desc(q, block_table, context_lens, n_kv, d_k, d_v, block_size, kv_dtype, max_context_len,
-          split_tokens, total_context_len, workgroups=0, shared_prefix_tokens=0) -> _DecodeDesc:
+          split_tokens, total_context_len, workgroups=0, shared_prefix_tokens=0, window=0) -> _DecodeDesc:
     B, n_h, _ = q.shape
     return _DecodeDesc(B, n_h, n_kv, d_k, d_v, block_size, block_table.shape[1], int(max_context_len),
                        _TORCH_TO_KVP[q.dtype], kv_dtype, int(split_tokens), int(total_context_len),
-                       int(workgroups), int(shared_prefix_tokens))
+                       int(workgroups), int(shared_prefix_tokens), int(window))
 
 
 def decode_workspace_size(desc: _DecodeDesc) -> int:
@@ -293,16 +294,17 @@ def _workspace(desc, workspace, dev):
 
 def paged_decode_attention(q, k_pool, v_pool, block_table, context_lens, scale, out=None, *,
                            max_context_len, split_tokens=0, total_context_len=0, workspace=None,
-                           shared_prefix_tokens=0):
+                           shared_prefix_tokens=0, window=0):
     """``out[b, h] = softmax(scale * q[b, h] . K) V`` over each sequence's
     paged K/V (pools ``[num_blocks, block_size, n_kv, d]``).
     ``shared_prefix_tokens``: a hint that the sequences' first tokens share
-    physical blocks (read once for all of them; checked on the device)."""
+    physical blocks (read once for all of them; checked on the device).
+    ``window``: attend to each sequence's last ``window`` tokens only."""
     dev = _need_cuda(q, k_pool, v_pool, block_table, context_lens)
     _, bs, n_kv, d_k = k_pool.shape
     d_v = v_pool.shape[3]
     desc = _desc(q, block_table, context_lens, n_kv, d_k, d_v, bs, _TORCH_TO_KVP[k_pool.dtype],
-                 max_context_len, split_tokens, total_context_len, 0, shared_prefix_tokens)
+                 max_context_len, split_tokens, total_context_len, 0, shared_prefix_tokens, window)
     if out is None:
         out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=dev)
     ws, wsb = _workspace(desc, workspace, dev)
@@ -314,12 +316,12 @@ def paged_decode_attention(q, k_pool, v_pool, block_table, context_lens, scale, 
 
 def paged_decode_attention_int8(q, k_codes, k_scale, v_codes, v_scale, block_table, context_lens,
                                 scale, out=None, *, max_context_len, split_tokens=0,
-                                total_context_len=0, workspace=None):
+                                total_context_len=0, workspace=None, window=0):
     dev = _need_cuda(q, k_codes, k_scale, v_codes, v_scale, block_table, context_lens)
     _, bs, n_kv, d_k = k_codes.shape
     d_v = v_codes.shape[3]
     desc = _desc(q, block_table, context_lens, n_kv, d_k, d_v, bs, KVP_INT8, max_context_len,
-                 split_tokens, total_context_len)
+                 split_tokens, total_context_len, 0, 0, window)
     if out is None:
         out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=dev)
     ws, wsb = _workspace(desc, workspace, dev)
@@ -349,21 +351,21 @@ def paged_decode_attention_mla(q, latent_pool, block_table, context_lens, scale,
 
 
 def _append_desc(pool: KVPool, q, block_table, context_lens, max_context_len, split_tokens,
-                 total_context_len, workgroups) -> _DecodeDesc:
+                 total_context_len, workgroups, window=0) -> _DecodeDesc:
     kv = KVP_INT8 if pool.dtype == torch.int8 else _TORCH_TO_KVP[pool.dtype]
     return _desc(q, block_table, context_lens, pool.n_kv, pool.d_k, pool.d_v, pool.block_size, kv,
-                 max_context_len, split_tokens, total_context_len, workgroups)
+                 max_context_len, split_tokens, total_context_len, workgroups, 0, window)
 
 
 def paged_decode_attention_append(pool: KVPool, q, k_new, v_new, block_table, context_lens, scale,
                                   out=None, *, max_context_len, split_tokens=0, total_context_len=0,
-                                  workgroups=0, workspace=None):
+                                  workgroups=0, workspace=None, window=0):
     """One decode step: write each sequence's new K/V row (``k_new``/``v_new``
     ``[B, n_kv, d]`` in q's dtype; ``v_new`` None for a latent pool) at position
     ``context_lens[b] - 1``, then attend (the decode call of the pool's kind)."""
     dev = _need_cuda(q, k_new, block_table, context_lens)
     desc = _append_desc(pool, q, block_table, context_lens, max_context_len, split_tokens,
-                        total_context_len, workgroups)
+                        total_context_len, workgroups, window)
     if out is None:
         out = torch.empty((q.shape[0], q.shape[1], pool.d_v), dtype=q.dtype, device=dev)
     ws, wsb = _workspace(desc, workspace, dev)
@@ -389,10 +391,11 @@ def paged_decode_attention_append_noalloc(pool: KVPool, q, k_new, v_new, block_t
 
 def make_desc(*, B, n_h, n_kv, d_k, d_v, block_size, max_blocks_per_seq, max_context_len,
               q_dtype, kv_dtype, split_tokens=0, total_context_len=0, workgroups=0,
-              shared_prefix_tokens=0) -> _DecodeDesc:
+              shared_prefix_tokens=0, window=0) -> _DecodeDesc:
     """A decode description from plain values (dtype codes KVP_F32/BF16/INT8)."""
     return _DecodeDesc(B, n_h, n_kv, d_k, d_v, block_size, max_blocks_per_seq, max_context_len,
-                       q_dtype, kv_dtype, split_tokens, total_context_len, workgroups, shared_prefix_tokens)
+                       q_dtype, kv_dtype, split_tokens, total_context_len, workgroups, shared_prefix_tokens,
+                       window)
 
 
 def paged_decode_validate(block_table, context_lens, desc: _DecodeDesc, num_blocks: int) -> None:

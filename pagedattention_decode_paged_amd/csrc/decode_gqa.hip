@@ -447,7 +447,7 @@ constexpr int kFewSplits = 8;       // splits whose loads are issued together (d
 __global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ context_lens, void* __restrict__ out, int rows, int n_h, int d_v,
-    int num_splits, int split_tokens, int out_bf16) {
+    int num_splits, int split_tokens, int out_bf16, int window) {
   const int bh = blockIdx.x * kReduceWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kReduceThreads);
   if (bh >= rows) return;
   const int b = bh / n_h;
@@ -474,7 +474,8 @@ __global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_k
 #pragma unroll
   for (int k = 0; k < kFewSplits; ++k) PKV_REDUCE_LOAD(k, k, num_splits);   // in flight with ctx
   const int ctx = context_lens[b];
-  const int nsp = min(num_splits, (ctx + split_tokens - 1) / split_tokens);
+  const int a0 = window > 0 ? max(ctx - window, 0) & ~15 : 0;   // first position read (sliding window)
+  const int nsp = min(num_splits, (ctx - a0 + split_tokens - 1) / split_tokens);
   if (nsp <= 1) return;                 // written by the decode kernel itself
   // batches of kFewSplits splits merged online (running max M, sum L, outputs o)
   float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
@@ -632,8 +633,9 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
   // only the bf16 LDS-ring kernel writes appended rows itself
   if (p.k_new && !(p.kv == KV::BF16 && gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)))
     return hipErrorInvalidValue;
-  // the stream grid exists on the LDS-ring kernel only
-  if (p.stream_wgs != 0 && !gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)) return hipErrorInvalidValue;
+  // the stream grid and the sliding window exist on the LDS-ring kernel only
+  if ((p.stream_wgs != 0 || p.window != 0) && !gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g))
+    return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
   if (gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)) {
     e = launch_decode_gqa_ring(p, stream);
@@ -661,7 +663,7 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((rows + kReduceWaves - 1) / kReduceWaves)),
                      dim3(kReduceThreads * kReduceWaves), 0, stream, (const float*)p.part_o,
                      (const float*)p.part_ml, p.context_lens, p.out, rows, p.n_h, p.d_v, p.num_splits,
-                     p.split_tokens, p.q_bf16 ? 1 : 0);
+                     p.split_tokens, p.q_bf16 ? 1 : 0, p.window);
   return hipGetLastError();
 }
 

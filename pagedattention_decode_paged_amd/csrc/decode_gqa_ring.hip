@@ -247,6 +247,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
   if constexpr (GRID != kGridSplit) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int n_h = p.n_h;
+  const int lo = window_lo(p, ctx);                  // positions below it are masked (sliding window)
   const int shift = p.block_shift;
   const int bmask = (1 << shift) - 1;
   // The tokens go in chunks [cb, ce) whose blocks fit the staged block table
@@ -338,7 +339,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
     const int tile0 = cb + s * kStageTok;
     const int t_last = ce - 1;
     const uint32_t dst0 = lds_mat + (uint32_t)(slot * kRingBytes);
-    if (fast_ok && tile0 + kStageTok <= ce) {
+    if (fast_ok && tile0 + kStageTok <= ce && tile0 >= lo) {
       // whole stage: one block per instruction, address base on the scalar unit
 #pragma unroll
       for (int jj = 0; jj < R::kDmaPerWave; ++jj) {
@@ -349,19 +350,19 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
         dma16(sb, voff[jj % kVoffN], dst0 + (uint32_t)(jm * 1024));
       }
     } else {
-      // last (partial) stage or tiny blocks: per-lane rows, clamped to the
-      // last valid token
+      // last (partial) stage, the first stage of a window or tiny blocks:
+      // per-lane rows, clamped to the attended positions
       int32_t ph[R::kDmaPerWave];
 #pragma unroll
       for (int jj = 0; jj < R::kDmaPerWave; ++jj) {
         const int r = (jbase + jj) * R::kRowsPerDma + lrow;
-        ph[jj] = s_bt[(min(tile0 + r, t_last) >> shift) - lb0];
+        ph[jj] = s_bt[(max(min(tile0 + r, t_last), lo) >> shift) - lb0];
       }
 #pragma unroll
       for (int jj = 0; jj < R::kDmaPerWave; ++jj) {
         const int jm = jbase + jj;
         const int r = jm * R::kRowsPerDma + lrow;
-        const int t = min(tile0 + r, t_last);
+        const int t = max(min(tile0 + r, t_last), lo);
         const int64_t sl = ((int64_t)ph[jj] << shift) + (t & bmask);
         dma16(mat + sl * slot_stride + src_piece(r) * 16, dst0 + (uint32_t)(jm * 1024));
       }
@@ -370,7 +371,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       if (wave < R::kScaleWaves) {
         // scales [num_blocks, n_kv, block_size]: a block's scales of the
         // group's heads are adjacent, so the stage's scales are whole runs
-        const int t = min(tile0 + scl_t, t_last);
+        const int t = max(min(tile0 + scl_t, t_last), lo);
         const int64_t si =
             (((int64_t)s_bt[(t >> shift) - lb0] * p.n_kv + kvh * KH + scl_h) << shift) + (t & bmask);
         dma4(scl_src + si, lds_scl + (uint32_t)(slot * KH * kStageTok * 4));
@@ -542,7 +543,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float raw = Q8 ? sacc[i] * (sk[i] * qk) : sacc[i] * qscale;
-        sc4[i] = tile0 + tl0 + i < ce ? raw : -INFINITY;
+        sc4[i] = tile0 + tl0 + i < ce && tile0 + tl0 + i >= lo ? raw : -INFINITY;
       }
       // maximum of the head over the wave's 16 tokens (lanes l16 + 16 j)
       float smax = fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3]));
@@ -675,7 +676,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
     }
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     const int64_t row = (int64_t)b * n_h + (int64_t)(kvh * KH + kh) * G + h;
-    if (direct_ok && t_begin == 0 && t_end == ctx) {
+    if (direct_ok && t_begin <= lo && t_end == ctx) {
       uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * D + d0;
 #pragma unroll
       for (int c = 0; c < kCpt; ++c) o[c] = f32_to_bf16_rne(num[c] * inv);
@@ -709,7 +710,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       for (int k = 0; k < 8; ++k) {
         const int sb = 8 * lane + k;
         const int c = sb < p.B ? p.context_lens[sb] : 0;
-        len[k] = (max(c - S, 0) + 15) & ~15;
+        len[k] = (max(c - (S > 0 ? S : window_a0(p, c)), 0) + 15) & ~15;
         sum += len[k];
       }
       int incl = sum;
@@ -752,14 +753,15 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       const int st = __builtin_amdgcn_readfirstlane(s_upre[b]);
       if (st >= r1) break;
       const int ctx = p.context_lens[b];
-      const int L = ctx - S;                        // this sequence's tokens past the prefix
+      const int s0 = S > 0 ? S : window_a0(p, ctx);  // first position of its part (prefix or window)
+      const int L = ctx - s0;                       // this sequence's tokens in the stream part
       const int a = (int)max(r0 - st, (int64_t)0), e = (int)min(r1 - st, (int64_t)L);
       if (L <= 0 || a >= e) continue;
       if (a == 0 && kvh == 0 && threadIdx.x == 0) {
         p.seq_meta[2 * b] = j;
         p.seq_meta[2 * b + 1] = (st + L - 1) / T;
       }
-      unit(b, S + a, S + e, ctx, 1, (int64_t)j * p.n_h, S == 0);
+      unit(b, s0 + a, s0 + e, ctx, 1, (int64_t)j * p.n_h, S == 0);
       __syncthreads();                              // the unit's LDS is free again
     }
     }
@@ -1042,7 +1044,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
   if constexpr (GRID == kGridSplit) {
     // grid (KV head, sequence, split)
     const int b = blockIdx.y, split = blockIdx.z, ctx = p.context_lens[b];
-    const int t_begin = split * p.split_tokens;
+    const int t_begin = window_a0(p, ctx) + split * p.split_tokens;
     if (t_begin >= ctx) {
       if (split == 0) zero_out(b);
     } else {
@@ -1064,7 +1066,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       for (int k = 0; k < 8; ++k) {
         const int sb = 8 * lane + k;
         const int c = sb < p.B ? p.context_lens[sb] : 0;
-        cnt[k] = sb < p.B ? max(1, (c + p.split_tokens - 1) / p.split_tokens) : 0;
+        cnt[k] = sb < p.B ? max(1, (c - window_a0(p, c) + p.split_tokens - 1) / p.split_tokens) : 0;
         sum += cnt[k];
       }
       int incl = sum;
@@ -1093,7 +1095,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       const int b = __builtin_amdgcn_readfirstlane(lo);
       const int split = __builtin_amdgcn_readfirstlane(u - s_upre[b]);
       const int ctx = p.context_lens[b];
-      const int t_begin = split * p.split_tokens;
+      const int t_begin = window_a0(p, ctx) + split * p.split_tokens;
       if (t_begin >= ctx) {
         if (split == 0) zero_out(b);
       } else {
@@ -1143,11 +1145,14 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
   // ones (each measured the faster there)
   if ((q8 && p.stream_wgs != 0) || (!q8 && p.compact_units != 0)) return hipErrorInvalidValue;
   // a split's blocks must fit the staged block table (one chunk)
-  if ((p.split_tokens >> p.block_shift) > (q8 ? kBtSlotsInt8 : kBtSlots)) return hipErrorInvalidValue;
+  // (a windowed split starts anywhere in a block: one block more)
+  if ((p.split_tokens >> p.block_shift) + (p.window ? 1 : 0) > (q8 ? kBtSlotsInt8 : kBtSlots))
+    return hipErrorInvalidValue;
   // shared prefix: bf16 with two KV heads per workgroup, on the stream grid,
   // no append, chunks of whole 64-token stages whose blocks fit the table
+  if (p.window < 0) return hipErrorInvalidValue;
   if (p.prefix_tokens != 0 &&
-      (q8 || kh != 2 || p.d_k != 128 || p.stream_wgs <= 0 || p.prefix_wgs <= 0 || p.prefix_tokens < 0 ||
+      (p.window != 0 || q8 || kh != 2 || p.d_k != 128 || p.stream_wgs <= 0 || p.prefix_wgs <= 0 || p.prefix_tokens < 0 ||
        p.prefix_tokens % 64 || p.prefix_chunk <= 0 || p.prefix_chunk % 64 || p.k_new != nullptr ||
        (p.prefix_chunk >> p.block_shift) + 2 > kBtSlots ||
        (int64_t)p.stream_wgs + p.prefix_wgs > 65535 ||

@@ -114,7 +114,20 @@ struct DecodeParams {
   int32_t prefix_tokens;
   int32_t prefix_chunk;
   int32_t prefix_wgs;
+  // Sliding window (LDS-ring kernel only; 0: the whole context): a sequence
+  // of ctx tokens attends to positions [max(0, ctx - window), ctx).  The
+  // kernels start reading at that position rounded down to a multiple of 16
+  // (whole DMA rows), mask the positions below it, and skip every block
+  // before it.
+  int32_t window;
 };
+
+// First attended position of a sequence of ctx tokens, and the position the
+// kernels start reading at (a multiple of 16).
+__device__ __forceinline__ int window_lo(const DecodeParams& p, int ctx) {
+  return p.window > 0 ? max(ctx - p.window, 0) : 0;
+}
+__device__ __forceinline__ int window_a0(const DecodeParams& p, int ctx) { return window_lo(p, ctx) & ~15; }
 
 // Sequences one prefix workgroup serves: four waves of 32 query columns
 // (two 16-column matrix-core blocks), g columns per sequence.

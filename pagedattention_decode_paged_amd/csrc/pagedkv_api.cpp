@@ -250,7 +250,22 @@ const char* decode_desc_error(const kvp_decode_desc* d) {
   if (d->total_context_len < 0) return "total_context_len must be >= 0";
   if (d->workgroups < 0) return "workgroups must be >= 0";
   if (d->shared_prefix_tokens < 0) return "shared_prefix_tokens must be >= 0";
+  if (d->window < 0) return "window must be >= 0";
   return nullptr;
+}
+
+// The description the work is planned on: with a sliding window a sequence
+// is read from its window's start rounded down to 16, so its length for
+// planning is at most window + 15.
+kvp_decode_desc planning_desc(const kvp_decode_desc* d) {
+  kvp_decode_desc e = *d;
+  if (d->window > 0) {
+    const int64_t span = (int64_t)d->window + 15;
+    if (e.max_context_len > span) e.max_context_len = (int32_t)span;
+    if (e.total_context_len > 0 && e.total_context_len > (int64_t)d->B * span) e.total_context_len = (int64_t)d->B * span;
+    e.shared_prefix_tokens = 0;
+  }
+  return e;
 }
 
 Variant variant_of(const kvp_decode_desc* d) {
@@ -343,7 +358,9 @@ constexpr int32_t kBtSlots = 512;
 constexpr int32_t kBtSlotsInt8 = 256;
 
 int32_t max_split(const kvp_decode_desc* d, Variant v) {
-  const int64_t cap = (int64_t)(v == Variant::Int8 ? kBtSlotsInt8 : kBtSlots) * d->block_size;
+  // a windowed split starts anywhere in a block, so it may touch one block more
+  const int64_t cap = (int64_t)((v == Variant::Int8 ? kBtSlotsInt8 : kBtSlots) - (d->window > 0 ? 1 : 0)) *
+                      d->block_size;
   return (int32_t)(cap < kMaxSplit ? cap : kMaxSplit);
 }
 
@@ -694,6 +711,12 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
                   d->n_h, d->d_k, d->d_v, d->block_size);
   }
 
+  if (d->window > 0) {
+    if (var == Variant::Mla || !pkv::gqa_ring_supported(var == Variant::Int8 ? pkv::KV::INT8 : pkv::KV::BF16, q_bf16,
+                                                         d->d_k, d->d_v, g) ||
+        (var == Variant::Float && d->kv_dtype != KVP_BF16))
+      return fail(KVP_ERR_UNSUPPORTED, "%s: a sliding window needs bf16 or INT8 pools with g in {4, 8} and d in {64, 128}", fn);
+  }
   if (validate_mode()) {
     int64_t nb;
     if (app) {
@@ -733,6 +756,9 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
 
   if (var == Variant::Mla) return launch_mla(fn, q, k, block_table, context_lens, scale, out, d,
                                              workspace, workspace_bytes, stream);
+  const kvp_decode_desc pdesc = planning_desc(d);
+  const kvp_decode_desc* const dd = d;
+  d = &pdesc;                                     // planning from here on (validation is done)
   const int gr = granule(var);
   if (d->split_tokens > 0 && (d->split_tokens % gr || d->split_tokens > max_split(d, var)))
     return fail(KVP_ERR_INVALID_ARG, "%s: split_tokens must be a multiple of %d and <= %d", fn, gr,
@@ -791,6 +817,7 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   p.num_splits = ns;
   p.q_bf16 = q_bf16;
   p.kv = var == Variant::Int8 ? pkv::KV::INT8 : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
+  p.window = dd->window;
   if (fused_append) {
     p.k_new = app->k_new;
     p.v_new = app->v_new;
@@ -826,11 +853,14 @@ kvp_status reshape_and_cache(kvp_pool* pool, const void* k_new, const void* v_ne
 
 size_t paged_decode_workspace_size(const kvp_decode_desc* desc) {
   if (decode_desc_error(desc)) return 0;
-  return workspace_for(desc, variant_of(desc));
+  const kvp_decode_desc pd = planning_desc(desc);
+  return workspace_for(&pd, variant_of(desc));
 }
 
-int32_t paged_decode_split_tokens(const kvp_decode_desc* desc) {
-  if (decode_desc_error(desc)) return 0;
+int32_t paged_decode_split_tokens(const kvp_decode_desc* desc_in) {
+  if (decode_desc_error(desc_in)) return 0;
+  const kvp_decode_desc pd = planning_desc(desc_in);
+  const kvp_decode_desc* desc = &pd;
   if (variant_of(desc) == Variant::Mla) return pkv::kMlaTileTokens;
   const int32_t sw = stream_wgs(desc, variant_of(desc));
   if (sw > 0) {
@@ -963,7 +993,8 @@ kvp_status paged_decode_attention_append_noalloc(kvp_pool* pool, const void* q, 
                                                  const kvp_decode_desc* desc, void* stream) {
   const char* fn = "paged_decode_attention_append_noalloc";
   if (const char* e = decode_desc_error(desc)) return fail(KVP_ERR_INVALID_ARG, "%s: %s", fn, e);
-  const size_t need = workspace_for(desc, variant_of(desc));
+  const kvp_decode_desc pd = planning_desc(desc);
+  const size_t need = workspace_for(&pd, variant_of(desc));
   if (need > kScratchBytes)
     return fail(KVP_ERR_UNSUPPORTED,
                 "%s: the call needs %zu bytes of scratch, the static buffer holds %zu "
