@@ -339,6 +339,97 @@ kvp_status paged_decode_attention_append_noalloc(kvp_pool* pool, const void* q, 
                                                  const kvp_decode_desc* desc, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Block allocator (host side; faulkner, "Prefix Caching 与 Copy-on-Write"
+ * and the allocator reference section; qwbw 4.3).  It hands out the
+ * physical blocks the tables above name: reference counts per block, a
+ * chained hash H_k = BLAKE2b-64(H_{k-1} as 8 little-endian bytes, then the
+ * block's token ids as 4 little-endian bytes each), H_{-1} = 0, on every
+ * full block of a prompt; blocks whose count drops to zero keep their hash
+ * and are parked in an LRU list of evictable blocks, from whose least
+ * recently used end fresh blocks are taken (losing their hash).  A new
+ * prompt reuses its leading full blocks found by hash (a hit increments the
+ * count); copy-on-write splits a partly filled tail block shared by several
+ * sequences when one of them appends.  An allocator is used by one thread
+ * at a time; its calls never touch device memory.  A call that cannot be
+ * met returns a status, leaves the allocator unchanged and sets
+ * kvp_last_error(); KVP_ERR_OUT_OF_MEMORY means no free block is left (the
+ * allocator's MemoryError).
+ * ---------------------------------------------------------------------- */
+typedef struct kvp_allocator kvp_allocator;
+
+/* num_blocks blocks of block_size slots.  initial_order (host int32
+ * [num_blocks], NULL = 0, 1, ...) is a permutation giving the evictable
+ * list's order from least to most recently used. */
+kvp_status kvp_allocator_create(int64_t num_blocks, int32_t block_size, const int32_t* initial_order,
+                                kvp_allocator** out);
+void kvp_allocator_destroy(kvp_allocator* allocator);
+
+/* One step of the chained block hash (parent hash, n token ids). */
+uint64_t kvp_block_hash(uint64_t parent, const int32_t* token_ids, int32_t n);
+
+/* Blocks for a new prompt of num_tokens token ids (host int32): writes
+ * ceil(num_tokens / block_size) entries of block_table (host int32, room
+ * for max_blocks), their number to *num_blocks and the tokens found cached
+ * (leading full blocks reused) to *cached_tokens. */
+kvp_status kvp_allocate_prompt(kvp_allocator* allocator, const int32_t* token_ids, int64_t num_tokens,
+                               int32_t* block_table, int32_t max_blocks, int32_t* num_blocks,
+                               int64_t* cached_tokens);
+
+/* The slot of one decoded token appended to a sequence whose table (host
+ * int32, *num_blocks entries, room for max_blocks) is updated in place: a
+ * full tail takes a fresh block; a partly filled tail held by several
+ * sequences is copied on write: *cow_src / *cow_dst name the block whose
+ * rows the caller copies with copy_blocks before writing the token (both
+ * -1 otherwise).  *slot receives block * block_size + offset. */
+kvp_status kvp_append_slot(kvp_allocator* allocator, int32_t* block_table, int32_t* num_blocks,
+                           int32_t max_blocks, int64_t* slot, int32_t* cow_src, int32_t* cow_dst);
+
+/* Another sequence sharing every block of a table (parallel sampling, beam
+ * search: qwbw 4.3): each block's count grows by one. */
+kvp_status kvp_fork_sequence(kvp_allocator* allocator, const int32_t* block_table, int32_t num_blocks);
+
+/* Release a sequence: each block's count drops by one; blocks reaching
+ * zero are parked at the most recently used end, keeping their hash. */
+kvp_status kvp_free_sequence(kvp_allocator* allocator, const int32_t* block_table, int32_t num_blocks);
+
+/* State of one block (for inspection and tests). */
+kvp_status kvp_allocator_block_state(const kvp_allocator* allocator, int32_t block, int32_t* ref_count,
+                                     int32_t* fill, int32_t* hashed, uint64_t* hash);
+
+/* The evictable blocks from least to most recently used: writes up to
+ * capacity ids to out (may be NULL) and returns their total number (-1 for
+ * a NULL allocator). */
+int64_t kvp_allocator_evictable(const kvp_allocator* allocator, int32_t* out, int64_t capacity);
+
+/* ------------------------------------------------------------------------
+ * Block copies and swaps on the device (faulkner, copy-on-write; qwbw 4.3
+ * and faulkner's preemption section: a preempted sequence's blocks move to
+ * host memory and back).
+ * ---------------------------------------------------------------------- */
+
+/* Bytes one block occupies over all of the pool's regions (K, V and, for
+ * INT8, both scale arrays). */
+size_t kv_pool_block_bytes(const kvp_pool* pool);
+
+/* For each pair (device int32 [num_pairs, 2]: src, dst) every slot of block
+ * src is copied onto block dst, in every region of the pool, bit for bit.
+ * A pair with a block outside [0, num_blocks) is skipped.  Pairs must have
+ * distinct dst blocks none of which is a src of another pair (copy-on-write
+ * targets are fresh blocks); otherwise the result is unspecified. */
+kvp_status copy_blocks(kvp_pool* pool, const int32_t* pairs, int64_t num_pairs, void* stream);
+
+/* Swap out: the blocks listed in blocks (device int32 [n]) are gathered into
+ * staging (device, n * kv_pool_block_bytes bytes, 16-byte aligned), block i
+ * at offset i * kv_pool_block_bytes, regions in the order K, V, K scales, V
+ * scales, then copied to host_dst (host, same size; pinned memory keeps the
+ * copy asynchronous).  Swap in is the inverse: host_src -> staging ->
+ * blocks.  Entries outside [0, num_blocks) are skipped. */
+kvp_status swap_out_blocks(const kvp_pool* pool, const int32_t* blocks, int64_t n, void* staging,
+                           void* host_dst, void* stream);
+kvp_status swap_in_blocks(kvp_pool* pool, const int32_t* blocks, int64_t n, void* staging,
+                          const void* host_src, void* stream);
+
+/* ------------------------------------------------------------------------
  * Gather (qwbw 3.4: read each physical block through the table): copies
  * rows 0 .. context_lens[b]-1 of every sequence, bit for bit, into
  * out [B, max_context_len, n_kv, d] (device, elem_bytes per element);

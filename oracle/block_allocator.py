@@ -22,7 +22,13 @@ behaviour the pages describe, step by step, with plain Python containers:
   prompt are registered under their hashes; freeing a sequence decrements
   each of its blocks and parks the ones that reach zero at the most
   recently used end; appending a token to a full tail block takes a new
-  block.
+  block.  Where a hash was registered again on a fresh block (after the
+  first block of that chain was evicted), taking the older block removes
+  the index entry only if it still names that block.  The listing raises
+  partway through a prompt; here an allocation
+  that cannot be met changes nothing (the blocks a failed prompt would have
+  taken would otherwise stay owned by no sequence), the plainest reading
+  that keeps the reference counts exact.
 * qwbw section 4.3: sequences sharing a prompt prefix point their block
   tables at the same physical blocks (copy-on-write), and preempted
   sequences' blocks can be swapped out to host memory and back.
@@ -71,7 +77,11 @@ class BlockAllocator:
             raise MemoryError("out of KV cache blocks")
         blk, _ = self.evictable.popitem(last=False)
         if self.hash[blk] is not None:
-            self.by_hash.pop(self.hash[blk], None)
+            # the index entry goes only if it still names this block: after an
+            # eviction a later prompt can register the same hash on a fresh
+            # block, and that entry must stay
+            if self.by_hash.get(self.hash[blk]) == blk:
+                del self.by_hash[self.hash[blk]]
             self.hash[blk] = None
         self.tokens[blk] = []
         self.ref[blk] = 1
@@ -81,6 +91,23 @@ class BlockAllocator:
         """Block table of a new prompt and how many of its tokens were found
         cached."""
         bs = self.block_size
+        # all or nothing: count the leading hits (and those parked in the
+        # evictable pool, which leave it), then the fresh blocks still needed
+        hits, parked, parent = 0, set(), 0
+        for start in range(0, len(token_ids), bs):
+            chunk = [int(t) for t in token_ids[start:start + bs]]
+            if len(chunk) < bs:
+                break
+            parent = block_hash(parent, chunk)
+            hit = self.by_hash.get(parent)
+            if hit is None:
+                break
+            hits += 1
+            if self.ref[hit] == 0:
+                parked.add(hit)
+        need = -(-len(token_ids) // bs) - hits
+        if need > len(self.evictable) - len(parked):
+            raise MemoryError("out of KV cache blocks")
         table: list[int] = []
         cached = 0
         parent = 0
@@ -121,8 +148,8 @@ class BlockAllocator:
             table.append(blk)
             return None
         if self.ref[last] > 1:
-            self.ref[last] -= 1
             blk = self._take()
+            self.ref[last] -= 1
             self.tokens[blk] = list(self.tokens[last]) + [int(token)]
             table[-1] = blk
             return (last, blk)

@@ -83,6 +83,21 @@ def _load() -> ctypes.CDLL:
         "paged_decode_attention_append_noalloc": (ctypes.c_int, [P, P, P, P, P, P, F, P,
                                                                  ctypes.POINTER(_DecodeDesc), P]),
         "paged_gather": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P]),
+        "kvp_allocator_create": (ctypes.c_int, [I64, I32, P, ctypes.POINTER(P)]),
+        "kvp_allocator_destroy": (None, [P]),
+        "kvp_block_hash": (ctypes.c_uint64, [ctypes.c_uint64, P, I32]),
+        "kvp_allocate_prompt": (ctypes.c_int, [P, P, I64, P, I32, ctypes.POINTER(I32), ctypes.POINTER(I64)]),
+        "kvp_append_slot": (ctypes.c_int, [P, P, ctypes.POINTER(I32), I32, ctypes.POINTER(I64),
+                                           ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "kvp_fork_sequence": (ctypes.c_int, [P, P, I32]),
+        "kvp_free_sequence": (ctypes.c_int, [P, P, I32]),
+        "kvp_allocator_block_state": (ctypes.c_int, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                                     ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_uint64)]),
+        "kvp_allocator_evictable": (I64, [P, P, I64]),
+        "kv_pool_block_bytes": (SZ, [P]),
+        "copy_blocks": (ctypes.c_int, [P, P, I64, P]),
+        "swap_out_blocks": (ctypes.c_int, [P, P, I64, P, P, P]),
+        "swap_in_blocks": (ctypes.c_int, [P, P, I64, P, P, P]),
         "paged_decode_validate": (ctypes.c_int, [P, P, ctypes.POINTER(_DecodeDesc), I64, P]),
     }
     for name, (res, args) in sig.items():
@@ -101,6 +116,9 @@ EXPORTED_SYMBOLS = (
     "paged_decode_attention_int8",
     "paged_decode_attention_mla", "paged_decode_attention_append", "paged_decode_attention_append_noalloc",
     "paged_gather", "paged_decode_validate",
+    "kvp_allocator_create", "kvp_allocator_destroy", "kvp_block_hash", "kvp_allocate_prompt", "kvp_append_slot",
+    "kvp_fork_sequence", "kvp_free_sequence", "kvp_allocator_block_state", "kvp_allocator_evictable",
+    "kv_pool_block_bytes", "copy_blocks", "swap_out_blocks", "swap_in_blocks",
 )
 
 
@@ -402,6 +420,109 @@ def paged_decode_validate(block_table, context_lens, desc: _DecodeDesc, num_bloc
     dev = _need_cuda(block_table, context_lens)
     _check(_lib.paged_decode_validate(_ptr(block_table), _ptr(context_lens), ctypes.byref(desc),
                                       int(num_blocks), _stream(dev)))
+
+
+# --------------------------------------------------------------------- block allocator
+
+def _i32_array(values):
+    arr = (ctypes.c_int32 * max(1, len(values)))(*[int(v) for v in values])
+    return arr
+
+
+def block_hash(parent: int, token_ids) -> int:
+    """One step of the allocator's chained block hash (BLAKE2b-64)."""
+    arr = _i32_array(token_ids)
+    return int(_lib.kvp_block_hash(ctypes.c_uint64(parent), arr, len(token_ids)))
+
+
+class BlockAllocator:
+    """The library's host block allocator (``kvp_allocator_*``): reference
+    counts, chained-hash prefix reuse, an LRU list of evictable blocks and
+    copy-on-write.  Block tables are Python lists of block ids."""
+
+    def __init__(self, num_blocks: int, block_size: int, order=None, max_blocks_per_seq: int = 1 << 16):
+        self.block_size = block_size
+        self.max_blocks = max_blocks_per_seq
+        h = ctypes.c_void_p()
+        arr = None if order is None else _i32_array(order)
+        _check(_lib.kvp_allocator_create(num_blocks, block_size, arr, ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.kvp_allocator_destroy(h)
+            self._h = ctypes.c_void_p(None)
+
+    def allocate_prompt(self, token_ids) -> tuple[list[int], int]:
+        toks = _i32_array(token_ids)
+        out = (ctypes.c_int32 * self.max_blocks)()
+        nb, cached = ctypes.c_int32(), ctypes.c_int64()
+        _check(_lib.kvp_allocate_prompt(self._h, toks, len(token_ids), out, self.max_blocks, ctypes.byref(nb),
+                                        ctypes.byref(cached)))
+        return list(out[:nb.value]), int(cached.value)
+
+    def append_slot(self, table: list[int]):
+        """Slot of one appended token; ``table`` is updated in place.
+        Returns ``(slot, (src, dst) or None)``."""
+        arr = (ctypes.c_int32 * self.max_blocks)(*table)
+        nb = ctypes.c_int32(len(table))
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.kvp_append_slot(self._h, arr, ctypes.byref(nb), self.max_blocks, ctypes.byref(slot),
+                                    ctypes.byref(src), ctypes.byref(dst)))
+        table[:] = list(arr[:nb.value])
+        return int(slot.value), (None if src.value < 0 else (int(src.value), int(dst.value)))
+
+    def fork(self, table: list[int]) -> list[int]:
+        _check(_lib.kvp_fork_sequence(self._h, _i32_array(table), len(table)))
+        return list(table)
+
+    def free_sequence(self, table) -> None:
+        _check(_lib.kvp_free_sequence(self._h, _i32_array(table), len(table)))
+
+    def block_state(self, block: int):
+        """``(ref_count, fill, hashed, hash)`` of one block."""
+        r, f, hd, hv = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_uint64()
+        _check(_lib.kvp_allocator_block_state(self._h, block, ctypes.byref(r), ctypes.byref(f), ctypes.byref(hd),
+                                              ctypes.byref(hv)))
+        return int(r.value), int(f.value), bool(hd.value), int(hv.value)
+
+    def evictable(self) -> list[int]:
+        n = int(_lib.kvp_allocator_evictable(self._h, None, 0))
+        out = (ctypes.c_int32 * max(1, n))()
+        _lib.kvp_allocator_evictable(self._h, out, n)
+        return list(out[:n])
+
+
+# --------------------------------------------------------------------- block copies and swaps
+
+def kv_pool_block_bytes(pool: KVPool) -> int:
+    return int(_lib.kv_pool_block_bytes(pool.handle))
+
+
+def copy_blocks(pool: KVPool, pairs: torch.Tensor) -> None:
+    """Copy block src onto block dst for each row (src, dst) of ``pairs``
+    (device int32 ``[n, 2]``), in every region of the pool."""
+    dev = _need_cuda(pairs)
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [n, 2]")
+    _check(_lib.copy_blocks(pool.handle, _ptr(pairs), pairs.shape[0], _stream(dev)))
+
+
+def swap_out_blocks(pool: KVPool, blocks: torch.Tensor, staging: torch.Tensor, host: torch.Tensor) -> None:
+    """Blocks (device int32 ``[n]``) -> ``host`` (pinned uint8, ``n *
+    kv_pool_block_bytes`` bytes) through the device ``staging`` buffer."""
+    dev = _need_cuda(blocks, staging)
+    if host.is_cuda or not host.is_contiguous():
+        raise ValueError("host must be a contiguous host tensor")
+    _check(_lib.swap_out_blocks(pool.handle, _ptr(blocks), blocks.numel(), _ptr(staging), _ptr(host), _stream(dev)))
+
+
+def swap_in_blocks(pool: KVPool, blocks: torch.Tensor, staging: torch.Tensor, host: torch.Tensor) -> None:
+    dev = _need_cuda(blocks, staging)
+    if host.is_cuda or not host.is_contiguous():
+        raise ValueError("host must be a contiguous host tensor")
+    _check(_lib.swap_in_blocks(pool.handle, _ptr(blocks), blocks.numel(), _ptr(staging), _ptr(host), _stream(dev)))
 
 
 # --------------------------------------------------------------------- prepared calls

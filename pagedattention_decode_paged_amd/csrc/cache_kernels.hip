@@ -187,4 +187,67 @@ hipError_t launch_gather(const void* pool, int64_t row_bytes, int32_t shift,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- block copies
+
+namespace {
+
+// One workgroup per (pair or block, region): 16-byte moves when the region's
+// block is a multiple of 16 bytes, else 4-byte ones.  Blocks outside the
+// pool are skipped.
+__device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, int64_t bytes) {
+  if ((bytes & 15) == 0) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
+    for (int64_t i = threadIdx.x; i < bytes / 16; i += blockDim.x) d4[i] = s4[i];
+  } else {
+    const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src);
+    uint32_t* d1 = reinterpret_cast<uint32_t*>(dst);
+    for (int64_t i = threadIdx.x; i < bytes / 4; i += blockDim.x) d1[i] = s1[i];
+  }
+}
+
+__global__ void copy_blocks_kernel(PoolRegions r, const int32_t* __restrict__ pairs) {
+  const int64_t i = blockIdx.x;
+  const int reg = blockIdx.y;
+  const int64_t bytes = r.bytes[reg];
+  if (bytes == 0) return;
+  const int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+  if (src < 0 || dst < 0 || src >= r.num_blocks || dst >= r.num_blocks) return;
+  copy_bytes(r.base[reg] + (int64_t)dst * bytes, r.base[reg] + (int64_t)src * bytes, bytes);
+}
+
+__global__ void stage_blocks_kernel(PoolRegions r, const int32_t* __restrict__ blocks, uint8_t* staging,
+                                    int64_t total, int to_staging) {
+  const int64_t i = blockIdx.x;
+  const int reg = blockIdx.y;
+  const int64_t bytes = r.bytes[reg];
+  if (bytes == 0) return;
+  const int32_t b = blocks[i];
+  if (b < 0 || b >= r.num_blocks) return;
+  int64_t off = 0;
+  for (int k = 0; k < reg; ++k) off += r.bytes[k];
+  uint8_t* st = staging + i * total + off;
+  uint8_t* pb = r.base[reg] + (int64_t)b * bytes;
+  if (to_staging) copy_bytes(st, pb, bytes);
+  else copy_bytes(pb, st, bytes);
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const PoolRegions& r, const int32_t* pairs, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (n > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n, 4u), dim3(256), 0, stream, r, pairs);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_blocks(const PoolRegions& r, const int32_t* blocks, int64_t n, uint8_t* staging,
+                               int64_t total, bool to_staging, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (n > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stage_blocks_kernel, dim3((unsigned)n, 4u), dim3(256), 0, stream, r, blocks, staging, total,
+                     to_staging ? 1 : 0);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -8,6 +8,9 @@
 
 namespace pkv {
 
+// The per-thread message kvp_last_error() returns (set by every entry point).
+void set_last_error(const char* msg);
+
 // ---------------------------------------------------------------- cache ops
 hipError_t launch_slot_mapping(const int32_t* block_table, int32_t max_blocks_per_seq,
                                int32_t block_shift, const int32_t* seq_ids,
@@ -50,6 +53,21 @@ hipError_t launch_cache_quant_int8(int8_t* k_codes, float* k_scales, const void*
                                    int8_t* v_codes, float* v_scales, const void* v_src, int32_t d_v,
                                    bool src_bf16, const SlotSource& slots, int64_t num_tokens,
                                    int32_t n_kv, int32_t block_shift, hipStream_t stream);
+
+// Block copies over up to four regions of a pool (K, V, K scales, V
+// scales): region r of block b is base[r] + b * bytes[r] (bytes[r] a
+// multiple of 4, 0 for an absent region).
+struct PoolRegions {
+  uint8_t* base[4];
+  int64_t bytes[4];
+  int64_t num_blocks;
+};
+// pairs [n, 2] (src, dst): block src -> block dst in every region.
+hipError_t launch_copy_blocks(const PoolRegions& r, const int32_t* pairs, int64_t n, hipStream_t stream);
+// blocks [n]: block blocks[i] <-> staging + i * total, regions in order
+// (to_staging: gather, else scatter).
+hipError_t launch_stage_blocks(const PoolRegions& r, const int32_t* blocks, int64_t n, uint8_t* staging,
+                               int64_t total, bool to_staging, hipStream_t stream);
 
 hipError_t launch_gather(const void* pool, int64_t row_bytes, int32_t block_shift,
                          const int32_t* block_table, int32_t max_blocks_per_seq,

@@ -104,6 +104,10 @@ PoolLayout pool_layout(const kvp_pool_desc* d) {
 
 }  // namespace
 
+namespace pkv {
+void set_last_error(const char* msg) { g_last_error = msg; }
+}  // namespace pkv
+
 struct kvp_pool {
   kvp_pool_desc desc;
   PoolLayout layout;
@@ -1006,6 +1010,90 @@ kvp_status paged_decode_attention_append_noalloc(kvp_pool* pool, const void* q, 
   }
   return append_impl(fn, pool, q, k_new, v_new, block_table, context_lens, scale, out, desc, ws,
                      need > 0 ? kScratchBytes : 0, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The pool's regions block by block: K, V, K scales, V scales.
+pkv::PoolRegions pool_regions(const kvp_pool* pool) {
+  pkv::PoolRegions r{};
+  const kvp_pool_desc& d = pool->desc;
+  const PoolLayout& L = pool->layout;
+  const int64_t slots_per_block = d.block_size;
+  const size_t eb = dtype_bytes(d.dtype);
+  r.num_blocks = d.num_blocks;
+  r.base[0] = pool->base + L.k_off;
+  r.bytes[0] = slots_per_block * d.n_kv * d.d_k * (int64_t)eb;
+  if (!d.latent) {
+    r.base[1] = pool->base + L.v_off;
+    r.bytes[1] = slots_per_block * d.n_kv * d.d_v * (int64_t)eb;
+  }
+  if (d.dtype == KVP_INT8) {
+    r.base[2] = pool->base + L.ks_off;
+    r.bytes[2] = slots_per_block * d.n_kv * 4;
+    if (!d.latent) {
+      r.base[3] = pool->base + L.vs_off;
+      r.bytes[3] = slots_per_block * d.n_kv * 4;
+    }
+  }
+  return r;
+}
+
+int64_t regions_total(const pkv::PoolRegions& r) { return r.bytes[0] + r.bytes[1] + r.bytes[2] + r.bytes[3]; }
+
+}  // namespace
+
+extern "C" {
+
+size_t kv_pool_block_bytes(const kvp_pool* pool) {
+  if (!pool) return 0;
+  return (size_t)regions_total(pool_regions(pool));
+}
+
+kvp_status copy_blocks(kvp_pool* pool, const int32_t* pairs, int64_t num_pairs, void* stream) {
+  if (!pool) return fail(KVP_ERR_INVALID_ARG, "copy_blocks: pool is NULL");
+  if (num_pairs < 0) return fail(KVP_ERR_INVALID_ARG, "copy_blocks: num_pairs < 0");
+  if (num_pairs == 0) return ok();
+  if (!pairs || !aligned(pairs, 4)) return fail(KVP_ERR_INVALID_ARG, "copy_blocks: pairs NULL or misaligned");
+  if (num_pairs > 0x7fffffff) return fail(KVP_ERR_UNSUPPORTED, "copy_blocks: too many pairs");
+  return hip_status(pkv::launch_copy_blocks(pool_regions(pool), pairs, num_pairs, static_cast<hipStream_t>(stream)),
+                    "copy_blocks");
+}
+
+kvp_status swap_out_blocks(const kvp_pool* pool, const int32_t* blocks, int64_t n, void* staging, void* host_dst,
+                           void* stream) {
+  const char* fn = "swap_out_blocks";
+  if (!pool) return fail(KVP_ERR_INVALID_ARG, "%s: pool is NULL", fn);
+  if (n < 0) return fail(KVP_ERR_INVALID_ARG, "%s: n < 0", fn);
+  if (n == 0) return ok();
+  if (!blocks || !staging || !host_dst) return fail(KVP_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned(blocks, 4) || !aligned(staging, 16)) return fail(KVP_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  if (n > 0x7fffffff) return fail(KVP_ERR_UNSUPPORTED, "%s: too many blocks", fn);
+  const pkv::PoolRegions r = pool_regions(pool);
+  const int64_t total = regions_total(r);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = pkv::launch_stage_blocks(r, blocks, n, static_cast<uint8_t*>(staging), total, true, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(host_dst, staging, (size_t)(n * total), hipMemcpyDeviceToHost, st);
+  return hip_status(e, fn);
+}
+
+kvp_status swap_in_blocks(kvp_pool* pool, const int32_t* blocks, int64_t n, void* staging, const void* host_src,
+                          void* stream) {
+  const char* fn = "swap_in_blocks";
+  if (!pool) return fail(KVP_ERR_INVALID_ARG, "%s: pool is NULL", fn);
+  if (n < 0) return fail(KVP_ERR_INVALID_ARG, "%s: n < 0", fn);
+  if (n == 0) return ok();
+  if (!blocks || !staging || !host_src) return fail(KVP_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned(blocks, 4) || !aligned(staging, 16)) return fail(KVP_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  if (n > 0x7fffffff) return fail(KVP_ERR_UNSUPPORTED, "%s: too many blocks", fn);
+  const pkv::PoolRegions r = pool_regions(pool);
+  const int64_t total = regions_total(r);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(staging, host_src, (size_t)(n * total), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = pkv::launch_stage_blocks(r, blocks, n, static_cast<uint8_t*>(staging), total, false, st);
+  return hip_status(e, fn);
 }
 
 kvp_status paged_gather(const void* pool, int32_t elem_bytes, int32_t block_size, int32_t n_kv,

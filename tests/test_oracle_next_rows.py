@@ -311,11 +311,22 @@ def test_copy_on_write_of_a_shared_tail_block():
     assert a.append_token(t, 10) is None and len(t) == 3              # full tail: a new block
 
 
-def test_running_out_of_blocks_raises_memory_error():
-    a = oracle.BlockAllocator(3, 4)
-    a.allocate_prompt(list(range(8)))
+def test_running_out_of_blocks_raises_memory_error_and_changes_nothing():
+    a = oracle.BlockAllocator(4, 4)
+    t, _ = a.allocate_prompt(list(range(6)))              # blocks 0, 1 (tail holds 2)
+    snap = lambda: (list(a.ref), list(a.hash), [list(x) for x in a.tokens], list(a.evictable), dict(a.by_hash))
+    before = snap()
     with pytest.raises(MemoryError):
-        a.allocate_prompt(list(range(100, 109)))
+        a.allocate_prompt(list(range(100, 109)))          # needs 3 fresh blocks, 2 are left
+    assert snap() == before
+    u = a.fork(t)
+    a.allocate_prompt([7, 7, 7, 7, 7, 7, 7, 7])            # the last two blocks
+    before = snap()
+    with pytest.raises(MemoryError):                      # copy-on-write of the shared tail needs a block
+        a.append_token(u, 9)
+    assert snap() == before and a.ref[t[1]] == 2
+    a.free_sequence(u)
+    assert a.append_token(t, 9) is None                   # sole owner again: in place
 
 
 def test_internal_waste_is_below_one_block_per_sequence():
