@@ -338,6 +338,28 @@ kvp_status paged_decode_attention_append_noalloc(kvp_pool* pool, const void* q, 
                                                  const int32_t* context_lens, float scale, void* out,
                                                  const kvp_decode_desc* desc, void* stream);
 
+/* Chunked prefill over the paged cache (faulkner, continuous batching
+ * section: a long prompt is taken a fixed number of tokens per step, each
+ * chunk attending causally to the cache before it and to itself).  For
+ * every sequence b and query token i < chunk_lens[b] at position
+ * start_pos[b] + i, with K/V rows for every position up to start_pos[b] +
+ * chunk_lens[b] - 1 already in the pool (written by reshape_and_cache):
+ *   out[b][i][h] = sum_j softmax_j(scale * q[b][i][h] . K_j) V_j,
+ *                  j = 0 .. start_pos[b] + i
+ * through the block table (kvh = h / (n_h / n_kv)).
+ *   q, out: device [B, max_chunk, n_h, 128] bf16; rows at or past
+ *           chunk_lens[b] are not written.
+ *   start_pos, chunk_lens: device int32 [B].
+ *   desc: B, n_h, n_kv, d_k = d_v = 128, block_size, max_blocks_per_seq,
+ *         bf16 q and pool; max_context_len (host bound of start_pos[b] +
+ *         chunk_lens[b]) <= max_blocks_per_seq * block_size.  g = n_h /
+ *         n_kv in {1, 2, 4, 8, 16}; other shapes KVP_ERR_UNSUPPORTED.
+ * No workspace; asynchronous on the stream. */
+kvp_status paged_prefill_attention(const void* q, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table, const int32_t* start_pos,
+                                   const int32_t* chunk_lens, float scale, void* out,
+                                   const kvp_decode_desc* desc, int32_t max_chunk, void* stream);
+
 /* ------------------------------------------------------------------------
  * Block allocator (host side; faulkner, "Prefix Caching 与 Copy-on-Write"
  * and the allocator reference section; qwbw 4.3).  It hands out the

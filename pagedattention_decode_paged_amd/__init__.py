@@ -83,6 +83,7 @@ def _load() -> ctypes.CDLL:
         "paged_decode_attention_append_noalloc": (ctypes.c_int, [P, P, P, P, P, P, F, P,
                                                                  ctypes.POINTER(_DecodeDesc), P]),
         "paged_gather": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P]),
+        "paged_prefill_attention": (ctypes.c_int, [P, P, P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc), I32, P]),
         "kvp_allocator_create": (ctypes.c_int, [I64, I32, P, ctypes.POINTER(P)]),
         "kvp_allocator_destroy": (None, [P]),
         "kvp_block_hash": (ctypes.c_uint64, [ctypes.c_uint64, P, I32]),
@@ -118,7 +119,7 @@ EXPORTED_SYMBOLS = (
     "paged_gather", "paged_decode_validate",
     "kvp_allocator_create", "kvp_allocator_destroy", "kvp_block_hash", "kvp_allocate_prompt", "kvp_append_slot",
     "kvp_fork_sequence", "kvp_free_sequence", "kvp_allocator_block_state", "kvp_allocator_evictable",
-    "kv_pool_block_bytes", "copy_blocks", "swap_out_blocks", "swap_in_blocks",
+    "kv_pool_block_bytes", "copy_blocks", "swap_out_blocks", "swap_in_blocks", "paged_prefill_attention",
 )
 
 
@@ -420,6 +421,24 @@ def paged_decode_validate(block_table, context_lens, desc: _DecodeDesc, num_bloc
     dev = _need_cuda(block_table, context_lens)
     _check(_lib.paged_decode_validate(_ptr(block_table), _ptr(context_lens), ctypes.byref(desc),
                                       int(num_blocks), _stream(dev)))
+
+
+def paged_prefill_attention(q, k_pool, v_pool, block_table, start_pos, chunk_lens, scale, out=None, *,
+                            max_context_len):
+    """Causal attention of each sequence's chunk of new tokens (``q [B, C,
+    n_h, 128]`` bf16, positions ``start_pos[b] + i`` for ``i <
+    chunk_lens[b]``) over its paged cache, the chunk's own K/V included."""
+    dev = _need_cuda(q, k_pool, v_pool, block_table, start_pos, chunk_lens)
+    B, C, n_h, d = q.shape
+    _, bs, n_kv, d_k = k_pool.shape
+    desc = _DecodeDesc(B, n_h, n_kv, d_k, v_pool.shape[3], bs, block_table.shape[1], int(max_context_len),
+                       _TORCH_TO_KVP[q.dtype], _TORCH_TO_KVP[k_pool.dtype], 0, 0, 0, 0, 0)
+    if out is None:
+        out = torch.zeros((B, C, n_h, v_pool.shape[3]), dtype=q.dtype, device=dev)
+    _check(_lib.paged_prefill_attention(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(start_pos),
+                                        _ptr(chunk_lens), float(scale), _ptr(out), ctypes.byref(desc), C,
+                                        _stream(dev)))
+    return out
 
 
 # --------------------------------------------------------------------- block allocator

@@ -153,6 +153,24 @@ constexpr int prefix_seqs_per_wg(int g) { return 4 * (32 / g); }
 
 constexpr int kCompactMaxB = 512;
 
+// Chunked prefill (bf16, d = 128): q, out [B, max_chunk, n_h, d]; sequence
+// b's chunk_lens[b] query tokens sit at positions start_pos[b] + i.
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* start_pos;
+  const int32_t* chunk_lens;
+  void* out;
+  float scale;
+  int32_t B, max_chunk, n_h, n_kv, d_k, d_v;
+  int32_t block_shift;
+  int32_t max_blocks_per_seq;
+};
+bool prefill_supported(int d_k, int d_v, int g);
+hipError_t launch_prefill_paged(const PrefillParams& p, hipStream_t stream);
+
 // GQA/MQA/MHA over float, bf16 or INT8 pools: routes the shapes the
 // LDS-ring kernel covers there and the others to the general kernels, then
 // launches the split reduce.  Returns hipErrorInvalidValue for a

@@ -1047,6 +1047,59 @@ int64_t regions_total(const pkv::PoolRegions& r) { return r.bytes[0] + r.bytes[1
 
 extern "C" {
 
+kvp_status paged_prefill_attention(const void* q, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table, const int32_t* start_pos,
+                                   const int32_t* chunk_lens, float scale, void* out,
+                                   const kvp_decode_desc* d, int32_t max_chunk, void* stream) {
+  const char* fn = "paged_prefill_attention";
+  if (const char* e = decode_desc_error(d)) return fail(KVP_ERR_INVALID_ARG, "%s: %s", fn, e);
+  if (max_chunk < 0) return fail(KVP_ERR_INVALID_ARG, "%s: max_chunk < 0", fn);
+  if (d->B == 0 || max_chunk == 0) return ok();
+  if (!q || !k_pool || !v_pool || !block_table || !start_pos || !chunk_lens || !out)
+    return fail(KVP_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return fail(KVP_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_table, 4) || !aligned(start_pos, 4) || !aligned(chunk_lens, 4))
+    return fail(KVP_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  const int g = d->n_h / d->n_kv;
+  if (d->q_dtype != KVP_BF16 || d->kv_dtype != KVP_BF16 || !pkv::prefill_supported(d->d_k, d->d_v, g))
+    return fail(KVP_ERR_UNSUPPORTED, "%s: bf16 with d_k = d_v = 128 and g in {1, 2, 4, 8, 16} only", fn);
+  if (d->B > 65535 || d->n_kv > 65535 || max_chunk > 65535 * 8)
+    return fail(KVP_ERR_UNSUPPORTED, "%s: B, n_kv or max_chunk too large", fn);
+  if (validate_mode()) {
+    // the positions each chunk reaches, checked like a decode of length start + chunk
+    std::vector<int32_t> sp(d->B), cl(d->B);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(sp.data(), start_pos, sp.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(cl.data(), chunk_lens, cl.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_status(e, fn);
+    for (int32_t b = 0; b < d->B; ++b)
+      if (sp[b] < 0 || cl[b] < 0 || cl[b] > max_chunk || (int64_t)sp[b] + cl[b] > d->max_context_len)
+        return fail(KVP_ERR_INVALID_ARG, "%s: start_pos[%d] = %d, chunk_lens[%d] = %d out of range", fn, b, sp[b], b,
+                    cl[b]);
+  }
+  pkv::PrefillParams p{};
+  p.q = q;
+  p.k = k_pool;
+  p.v = v_pool;
+  p.block_table = block_table;
+  p.start_pos = start_pos;
+  p.chunk_lens = chunk_lens;
+  p.out = out;
+  p.scale = scale;
+  p.B = d->B;
+  p.max_chunk = max_chunk;
+  p.n_h = d->n_h;
+  p.n_kv = d->n_kv;
+  p.d_k = d->d_k;
+  p.d_v = d->d_v;
+  p.block_shift = log2i(d->block_size);
+  p.max_blocks_per_seq = d->max_blocks_per_seq;
+  return hip_status(pkv::launch_prefill_paged(p, static_cast<hipStream_t>(stream)), fn);
+}
+
 size_t kv_pool_block_bytes(const kvp_pool* pool) {
   if (!pool) return 0;
   return (size_t)regions_total(pool_regions(pool));
