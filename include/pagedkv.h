@@ -58,7 +58,10 @@ typedef enum {
 typedef enum {
   KVP_F32 = 0,   /* IEEE binary32 */
   KVP_BF16 = 1,  /* bfloat16 (top half of binary32), round-to-nearest-even */
-  KVP_INT8 = 2   /* signed 8-bit codes with one fp32 scale per (slot, KV head) */
+  KVP_INT8 = 2,  /* signed 8-bit codes with one fp32 scale per (slot, KV head) */
+  KVP_INT4 = 3   /* signed 4-bit codes, two per byte (element 2i in the low
+                    nibble of byte i, two's complement), one fp32 scale per
+                    (slot, KV head) */
 } kvp_dtype;
 
 /* ------------------------------------------------------------------------
@@ -69,7 +72,8 @@ typedef enum {
  * Layout, row-major (talentme chapter 3, the NumPy pool class):
  *   K codes/values  [num_blocks, block_size, n_kv, d_k]
  *   V codes/values  [num_blocks, block_size, n_kv, d_v]
- *   K, V scales     [num_blocks, n_kv, block_size] float   (KVP_INT8 only)
+ *   K, V scales     [num_blocks, n_kv, block_size] float   (KVP_INT8, KVP_INT4)
+ * (KVP_INT4 rows hold d / 2 bytes: two codes per byte.)
  * Slot s is block s / block_size, offset s % block_size.  The scales are
  * paged like the codes (one per slot and KV head); inside a block, one
  * head's scales are adjacent so that a kernel working on one KV head reads
@@ -149,7 +153,9 @@ kvp_status paged_slot_mapping(const int32_t* block_table, int32_t max_blocks_per
  * pool dtype).  An INT8 pool quantizes on write (guijiagi 4.2): per (token,
  * head) row, scale = fl32(absmax / 127) and code = clamp(rint(fl32(x /
  * scale)), -128, 127) in IEEE binary32 with round-half-to-even; a zero row
- * gets scale 0 and codes 0.  in_dtype F32 or BF16 (widened exactly).
+ * gets scale 0 and codes 0.  An INT4 pool the same with absmax / 7 and
+ * [-8, 7] (the 4-bit branch), packed two per byte.  in_dtype F32 or BF16
+ * (widened exactly).
  * Two tokens mapped to one slot race; the result is one of the rows.
  * ---------------------------------------------------------------------- */
 kvp_status reshape_and_cache(kvp_pool* pool, const void* k_new, const void* v_new,
@@ -270,6 +276,24 @@ kvp_status paged_decode_attention_int8(const void* q, const int8_t* k_codes,
                                        const kvp_decode_desc* desc, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* INT4 pools with an attention sink (guijiagi 4.2, 4-bit branch, and 4.3):
+ * codes [num_blocks, block_size, n_kv, d / 2] (two per byte) and fp32
+ * scales [num_blocks, n_kv, block_size], dequantized (code * scale) inside
+ * the kernel, except that positions 0 .. n_sink - 1 of every sequence come
+ * unquantized from sink_k / sink_v (device bf16 [B, n_sink, n_kv, d]; the
+ * first tokens draw attention from every later one, so their quantization
+ * error would be amplified).  The pool must still hold a row (any finite
+ * values) at every position below the context length.  0 <= n_sink <= 64
+ * (sink arrays may be NULL when 0).  desc->kv_dtype == KVP_INT4; bf16 q and
+ * out, d_k = d_v = 128, g in {4, 8}, even n_kv; no sliding window.  Other
+ * shapes KVP_ERR_UNSUPPORTED. */
+kvp_status paged_decode_attention_int4(const void* q, const uint8_t* k_codes, const float* k_scale,
+                                       const uint8_t* v_codes, const float* v_scale, const void* sink_k,
+                                       const void* sink_v, int32_t n_sink, const int32_t* block_table,
+                                       const int32_t* context_lens, float scale, void* out,
+                                       const kvp_decode_desc* desc, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* Absorbed MLA over a latent pool (faulkner, matrix absorption and
  * decoupled RoPE): q [B, n_h, d_k] already carries W^UK; the pool holds
  * one [c | k_rope] row of d_k bf16 per token (n_kv = 1); the value is the
@@ -310,7 +334,8 @@ kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
  * pools with g in {4, 8} the rows are written by the attention kernel
  * itself (one launch); otherwise by the cache kernel just before it.
  * Errors as for the decode calls, plus KVP_ERR_INVALID_ARG for a NULL pool
- * or rows, a pool that does not match desc, or misaligned rows. */
+ * or rows, a pool that does not match desc, or misaligned rows.  INT4 pools
+ * (whose decode takes sink rows) are not taken here: KVP_ERR_UNSUPPORTED. */
 kvp_status paged_decode_attention_append(kvp_pool* pool, const void* q, const void* k_new,
                                          const void* v_new, const int32_t* block_table,
                                          const int32_t* context_lens, float scale, void* out,

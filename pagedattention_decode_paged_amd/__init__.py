@@ -21,7 +21,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PAGEDKV_LIBRARY") or os.path.join(_HERE, "libpagedkv.so")
 
 KVP_OK, KVP_ERR_INVALID_ARG, KVP_ERR_OUT_OF_MEMORY, KVP_ERR_UNSUPPORTED, KVP_ERR_HIP = 0, -1, -2, -3, -4
-KVP_F32, KVP_BF16, KVP_INT8 = 0, 1, 2
+KVP_F32, KVP_BF16, KVP_INT8, KVP_INT4 = 0, 1, 2, 3
+
+# the pool dtype of an INT4 cache (torch has no 4-bit type: its codes are
+# viewed as uint8, two per byte)
+INT4 = "int4"
 
 _TORCH_TO_KVP = {torch.float32: KVP_F32, torch.bfloat16: KVP_BF16, torch.int8: KVP_INT8}
 _KVP_TO_TORCH = {v: k for k, v in _TORCH_TO_KVP.items()}
@@ -78,6 +82,8 @@ def _load() -> ctypes.CDLL:
         "paged_decode_attention_int8": (ctypes.c_int, [P, P, P, P, P, P, P, F, P,
                                                        ctypes.POINTER(_DecodeDesc), P, SZ, P]),
         "paged_decode_attention_mla": (ctypes.c_int, [P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc), P, SZ, P]),
+        "paged_decode_attention_int4": (ctypes.c_int, [P, P, P, P, P, P, P, I32, P, P, F, P,
+                                                       ctypes.POINTER(_DecodeDesc), P, SZ, P]),
         "paged_decode_attention_append": (ctypes.c_int, [P, P, P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc),
                                                          P, SZ, P]),
         "paged_decode_attention_append_noalloc": (ctypes.c_int, [P, P, P, P, P, P, F, P,
@@ -116,7 +122,7 @@ EXPORTED_SYMBOLS = (
     "paged_decode_split_tokens", "paged_decode_mla_workgroups", "paged_decode_attention",
     "paged_decode_attention_int8",
     "paged_decode_attention_mla", "paged_decode_attention_append", "paged_decode_attention_append_noalloc",
-    "paged_gather", "paged_decode_validate",
+    "paged_gather", "paged_decode_validate", "paged_decode_attention_int4",
     "kvp_allocator_create", "kvp_allocator_destroy", "kvp_block_hash", "kvp_allocate_prompt", "kvp_append_slot",
     "kvp_fork_sequence", "kvp_free_sequence", "kvp_allocator_block_state", "kvp_allocator_evictable",
     "kv_pool_block_bytes", "copy_blocks", "swap_out_blocks", "swap_in_blocks", "paged_prefill_attention",
@@ -185,16 +191,20 @@ class KVPool:
             self.handle = ctypes.c_void_p(None)
 
 
+def _kvp_dtype(dtype) -> int:
+    return KVP_INT4 if dtype == INT4 else _TORCH_TO_KVP[dtype]
+
+
 def kv_pool_required_bytes(num_blocks, block_size, n_kv, d_k, d_v, dtype, latent=False) -> int:
-    d = _PoolDesc(num_blocks, block_size, n_kv, d_k, d_v, _TORCH_TO_KVP[dtype], int(latent))
+    d = _PoolDesc(num_blocks, block_size, n_kv, d_k, d_v, _kvp_dtype(dtype), int(latent))
     return int(_lib.kv_pool_required_bytes(ctypes.byref(d)))
 
 
 def kv_pool_create(num_blocks: int, block_size: int, n_kv: int, d_k: int, d_v: int,
                    dtype: torch.dtype, latent: bool = False, device="cuda") -> KVPool:
-    if dtype not in _TORCH_TO_KVP:
+    if dtype != INT4 and dtype not in _TORCH_TO_KVP:
         raise ValueError(f"unsupported pool dtype {dtype}")
-    d = _PoolDesc(num_blocks, block_size, n_kv, d_k, d_v, _TORCH_TO_KVP[dtype], int(latent))
+    d = _PoolDesc(num_blocks, block_size, n_kv, d_k, d_v, _kvp_dtype(dtype), int(latent))
     nbytes = int(_lib.kv_pool_required_bytes(ctypes.byref(d)))
     if nbytes == 0:
         # let the library name the problem
@@ -215,8 +225,12 @@ def kv_pool_create(num_blocks: int, block_size: int, n_kv: int, d_k: int, d_v: i
         return storage[off:off + nb].view(dt).view(shape)
 
     slots = num_blocks * block_size
-    k = sub(view.k, slots * n_kv * d_k, dtype, (num_blocks, block_size, n_kv, d_k))
-    v = k if latent else sub(view.v, slots * n_kv * d_v, dtype, (num_blocks, block_size, n_kv, d_v))
+    if dtype == INT4:      # codes as uint8, two per byte
+        k = sub(view.k, slots * n_kv * d_k // 2, torch.uint8, (num_blocks, block_size, n_kv, d_k // 2))
+        v = sub(view.v, slots * n_kv * d_v // 2, torch.uint8, (num_blocks, block_size, n_kv, d_v // 2))
+    else:
+        k = sub(view.k, slots * n_kv * d_k, dtype, (num_blocks, block_size, n_kv, d_k))
+        v = k if latent else sub(view.v, slots * n_kv * d_v, dtype, (num_blocks, block_size, n_kv, d_v))
     ks = sub(view.k_scale, slots * n_kv, torch.float32, (num_blocks, n_kv, block_size))
     vs = sub(view.v_scale, slots * n_kv, torch.float32, (num_blocks, n_kv, block_size))
     return KVPool(h, storage, k, v, ks, vs, num_blocks, block_size, n_kv, d_k, d_v, dtype, latent)
@@ -351,6 +365,29 @@ def paged_decode_attention_int8(q, k_codes, k_scale, v_codes, v_scale, block_tab
     return out
 
 
+def paged_decode_attention_int4(q, k_codes, k_scale, v_codes, v_scale, sink_k, sink_v, block_table, context_lens,
+                                scale, out=None, *, max_context_len, split_tokens=0, total_context_len=0,
+                                workspace=None):
+    """INT4 cache (codes ``uint8 [NB, bs, n_kv, d / 2]``, two per byte) with
+    the first ``sink_k.shape[1]`` positions of every sequence taken
+    unquantized from ``sink_k`` / ``sink_v`` (``bf16 [B, n_sink, n_kv, d]``;
+    None for no sink)."""
+    dev = _need_cuda(q, k_codes, k_scale, v_codes, v_scale, block_table, context_lens, sink_k, sink_v)
+    _, bs, n_kv, half = k_codes.shape
+    d = 2 * half
+    desc = _desc(q, block_table, context_lens, n_kv, d, d, bs, KVP_INT4, max_context_len, split_tokens,
+                 total_context_len)
+    n_sink = 0 if sink_k is None else int(sink_k.shape[1])
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], d), dtype=q.dtype, device=dev)
+    ws, wsb = _workspace(desc, workspace, dev)
+    _check(_lib.paged_decode_attention_int4(_ptr(q), _ptr(k_codes), _ptr(k_scale), _ptr(v_codes), _ptr(v_scale),
+                                            _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(block_table),
+                                            _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(desc),
+                                            _ptr(ws), wsb, _stream(dev)))
+    return out
+
+
 def paged_decode_attention_mla(q, latent_pool, block_table, context_lens, scale, d_v, out=None, *,
                                max_context_len, total_context_len=0, workgroups=0, workspace=None):
     """Absorbed MLA: ``out[b, h] = softmax(scale * q[b, h] . C) C[:, :d_v]``
@@ -371,7 +408,7 @@ def paged_decode_attention_mla(q, latent_pool, block_table, context_lens, scale,
 
 def _append_desc(pool: KVPool, q, block_table, context_lens, max_context_len, split_tokens,
                  total_context_len, workgroups, window=0) -> _DecodeDesc:
-    kv = KVP_INT8 if pool.dtype == torch.int8 else _TORCH_TO_KVP[pool.dtype]
+    kv = KVP_INT8 if pool.dtype == torch.int8 else _kvp_dtype(pool.dtype)
     return _desc(q, block_table, context_lens, pool.n_kv, pool.d_k, pool.d_v, pool.block_size, kv,
                  max_context_len, split_tokens, total_context_len, workgroups, 0, window)
 

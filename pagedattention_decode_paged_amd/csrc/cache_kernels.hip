@@ -102,6 +102,52 @@ __global__ void cache_quant_int8_kernel(QuantJob kj, QuantJob vj, int bf16, Slot
   if (lane == 0) scales[out_scale] = scale;
 }
 
+// guijiagi 4.2, 4-bit branch, in binary32 as for INT8: scale = fl32(absmax /
+// 7), code = clamp(rint(fl32(x / scale)), -8, 7) (a zero row: scale 0, codes
+// 0); two codes per byte, element 2i in the low and 2i + 1 in the high
+// nibble of byte i.  One wavefront per (token, head) row, each lane two
+// adjacent elements at a time.
+struct Quant4Job {
+  uint8_t* codes;             // [slots, n_kv, d / 2]
+  float* scales;
+  const void* src;
+  int32_t d;
+};
+
+__global__ void cache_quant_int4_kernel(Quant4Job kj, Quant4Job vj, int bf16, SlotSource slots,
+                                        int64_t num_rows, int32_t n_kv, int32_t bshift) {
+  const Quant4Job j = blockIdx.y == 0 ? kj : vj;
+  const int32_t d = j.d;
+  const void* __restrict__ src = j.src;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= num_rows) return;
+  const int64_t t = row / n_kv;
+  const int32_t h = (int32_t)(row - t * n_kv);
+  const int64_t s = slot_of(slots, t);
+  if (s < 0) return;
+  const int64_t in_base = row * d;
+  float amax = 0.f;
+  for (int i = lane; i < d; i += 64) amax = fmaxf(amax, fabsf(load_as_f32(src, in_base + i, bf16)));
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax / 7.0f;
+  const int64_t out_row = s * n_kv + h;
+  uint8_t* crow = j.codes + out_row * (d / 2);
+  const int64_t out_scale = (((s >> bshift) * n_kv + h) << bshift) + (s & ((1 << bshift) - 1));
+  for (int i = 2 * lane; i < d; i += 128) {
+    int c[2] = {0, 0};
+    if (scale > 0.f) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float r = fminf(fmaxf(rintf(load_as_f32(src, in_base + i + k, bf16) / scale), -8.f), 7.f);
+        c[k] = (int)r;
+      }
+    }
+    crow[i / 2] = (uint8_t)((c[0] & 0xF) | ((c[1] & 0xF) << 4));
+  }
+  if (lane == 0) j.scales[out_scale] = scale;
+}
+
 // qwbw 3.4: walk each sequence's table and copy its rows in logical order.
 template <typename V>
 __global__ void gather_kernel(const uint8_t* __restrict__ pool, int64_t row_bytes, int32_t shift,
@@ -150,6 +196,20 @@ hipError_t launch_cache_copy(void* k_pool, const void* k_src, int64_t k_row_byte
     hipLaunchKernelGGL(cache_copy_kernel<uint4>, grid, dim3(threads), 0, stream, kj, vj, slots);
   else
     hipLaunchKernelGGL(cache_copy_kernel<uint32_t>, grid, dim3(threads), 0, stream, kj, vj, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_quant_int4(uint8_t* k_codes, float* k_scales, const void* k_src, int32_t d_k,
+                                   uint8_t* v_codes, float* v_scales, const void* v_src, int32_t d_v,
+                                   bool src_bf16, const SlotSource& slots, int64_t num_tokens,
+                                   int32_t n_kv, int32_t block_shift, hipStream_t stream) {
+  const int64_t rows = num_tokens * n_kv;
+  if (rows == 0) return hipSuccess;
+  const int waves = 4;
+  dim3 grid((unsigned)((rows + waves - 1) / waves), 2u);
+  hipLaunchKernelGGL(cache_quant_int4_kernel, grid, dim3(64 * waves), 0, stream,
+                     Quant4Job{k_codes, k_scales, k_src, d_k}, Quant4Job{v_codes, v_scales, v_src, d_v},
+                     src_bf16 ? 1 : 0, slots, rows, n_kv, block_shift);
   return hipGetLastError();
 }
 

@@ -622,6 +622,7 @@ bool gqa_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
   if (kv == KV::BF16) return q_bf16 && (d_k == 64 || d_k == 128);
   if (kv == KV::F32) return !q_bf16 && (d_k == 32 || d_k == 64);
   if (kv == KV::INT8) return int8_supported(q_bf16, d_k, d_v, g);
+  if (kv == KV::INT4) return gqa_ring_supported(kv, q_bf16, d_k, d_v, g);
   return false;
 }
 

@@ -56,6 +56,9 @@
 // stages (two workgroups resident per compute unit).
 constexpr int kWaves = 4;
 constexpr int kRing = 2;
+// INT4 stages are 4 KiB of codes per matrix: four in the ring (three in
+// flight), which also leaves room for the four waves' merge buffers
+constexpr int kRingQ4 = 4;
 constexpr int kGridSplit = 0, kGridCompact = 1, kGridStream = 2, kGridStreamPrefix = 3;
 // bf16 with d = 128: two adjacent KV heads per workgroup
 // (512 contiguous bytes per token per DMA row), when n_kv is even
@@ -85,10 +88,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 // path): a token's rows of those heads are adjacent in the pool, so the DMA
 // moves KH rows of 256 (bf16) or 128 (INT8) contiguous bytes per token.  A
 // stage holds 64 / KH tokens.
-template <int D, int NW, bool Q8, int KH = 1>
+template <int D, int NW, bool Q8, int KH = 1, bool Q4 = false>
 struct Ring {
   static constexpr int kStageTok = 64 / KH;                   // tokens per stage
-  static constexpr int kHeadRow = Q8 ? D : D * 2;             // bytes of one head's row in the pool
+  static constexpr int kHeadRow = Q4 ? D / 2 : (Q8 ? D : D * 2);   // bytes of one head's row in the pool
   static constexpr int kRowBytes = KH * D * 2;                // bf16 row of the LDS tiles (KH heads)
   static constexpr int kPieces = D * 2 / 16;                  // 16-byte pieces per head row (bf16)
   static constexpr int kSrcRow = KH * kHeadRow;               // bytes per token moved by the DMA
@@ -105,6 +108,7 @@ struct Ring {
   static_assert(D == 64 || D == 128, "row must be 64 or 128 elements");
   static_assert(KH == 1 || (D == 128 && (KH == 2 || (Q8 && KH == 4))),
                 "KV-head groups: d = 128, two heads (bf16, INT8) or four (INT8)");
+  static_assert(!Q4 || (Q8 && D == 128 && KH == 2), "INT4: d = 128, two KV heads per workgroup");
   static_assert(kDmaPerMat % kDmaPerWave == 0, "a wave issues K or V instructions only");
   // Piece permutations of the bf16 tiles (row r's logical piece p of a head
   // sits at position p ^ swz(r) of that head's pieces; every swz is below
@@ -145,19 +149,39 @@ __device__ __forceinline__ void widen_codes(const u32x4_t c, u32x4_t& lo, u32x4_
   hi = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
+// Thirty-two int4 codes (a 16-byte piece, element 2i in the low and 2i + 1
+// in the high nibble of byte i) -> thirty-two bf16 values 136 + code, as four
+// 16-byte pieces in element order.  With n = code + 8 in [0, 15], the bf16
+// bits of 128 + n are 0x4300 | n (exponent 7, mantissa n), so each byte
+// becomes one bf16 pair by a byte permute and an or.
+__device__ __forceinline__ void widen_int4(const u32x4_t c, u32x4_t (&out)[4]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t u = c[w] ^ 0x88888888u;             // every nibble + 8 (mod 16)
+    const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)                        // byte k of lo to byte 0, of hi to byte 2
+      o[k] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | (uint32_t)k | ((uint32_t)(4 + k) << 16)) | 0x43004300u;
+    out[w] = u32x4_t{o[0], o[1], o[2], o[3]};
+  }
+}
+
 // INT8: registers for three waves per SIMD (at most 168, no AGPR copies;
 // on the skewed INT8 batch 81.4 against 84.7 us with 136 + 40 AGPRs).  The
 // shared-prefix instance: at most 256 registers, so that two workgroups stay
-// resident per compute unit (the prefix pass alone would take 357).
+// resident per compute unit (the prefix pass alone would take 357).  INT4:
+// its LDS (four stages, ~54 KB) allows two workgroups per compute unit, so
+// up to 256 registers (at 168 the compact grid spilled).
 // GRID: kGridSplit (KV head group, sequence, split), kGridCompact (KV head
 // group, unit: the splits that exist), kGridStream (KV head group, equal
 // token ranges) or kGridStreamPrefix (the stream grid after a shared prefix,
 // plus the prefix workgroups).
-template <int D, int G, int NW, int RING, bool Q8, int GRID, int KH>
+template <int D, int G, int NW, int RING, bool Q8, int GRID, int KH, bool Q4 = false>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(Q8 ? 3 : (GRID == kGridStreamPrefix ? 2 : 1))))
+__attribute__((amdgpu_waves_per_eu(Q4 ? 2 : (Q8 ? 3 : (GRID == kGridStreamPrefix ? 2 : 1)))))
 void decode_gqa_ring_kernel(const DecodeParams p) {
-  using R = Ring<D, NW, Q8, KH>;
+  using R = Ring<D, NW, Q8, KH, Q4>;
   constexpr bool kStreamLike = GRID == kGridStream || GRID == kGridStreamPrefix;
   static_assert(GRID != kGridStreamPrefix || (!Q8 && KH == 2 && D == 128), "shared prefix: bf16, two KV heads");
   constexpr int kStageTok = R::kStageTok;
@@ -205,6 +229,8 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
   const int lane = tid & 63;
   const int n_h = p.n_h;
   const int lo = window_lo(p, ctx);                  // positions below it are masked (sliding window)
+  // INT4: the first n_sink positions come from the sink rows, not the codes
+  const int mlo = Q4 ? max(lo, p.n_sink) : lo;
   const int shift = p.block_shift;
   const int bmask = (1 << shift) - 1;
   // The tokens go in chunks [cb, ce) whose blocks fit the staged block table
@@ -385,15 +411,26 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       amax = fmaxf(amax, __shfl_xor(amax, 32));
       const float inv = amax > 0.f ? 127.f / amax : 0.f;
       qk = amax * (1.f / 127.f) * qscale;
-      // byte m of piece j pairs with code 16 j + m of the lane's quarter
-      // row: element (D / 4) mg + 16 j + m, i.e. k-step 2 j + m / 8
+      // INT8: byte m of piece j pairs with code 16 j + m of the lane's
+      // quarter row: element (D / 4) mg + 16 j + m, i.e. k-step 2 j + m / 8.
+      // INT4: the quarter's 16 packed bytes unpack to the even elements
+      // (piece 0) and the odd ones (piece 1): byte m of piece j pairs with
+      // element (D / 4) mg + 2 m + j, the low (j = 0) or high half of
+      // dword m % 4 of k-step m / 4.
 #pragma unroll
       for (int j = 0; j < kLp; ++j) {
         uint32_t w1[4], w2[4], w3[4];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const uint32_t bits = qf[2 * j + d / 2][2 * (d % 2)], bits2 = qf[2 * j + d / 2][2 * (d % 2) + 1];
-          const float x[4] = {bf_lo(bits) * inv, bf_hi(bits) * inv, bf_lo(bits2) * inv, bf_hi(bits2) * inv};
+          float x[4] = {bf_lo(bits) * inv, bf_hi(bits) * inv, bf_lo(bits2) * inv, bf_hi(bits2) * inv};
+          if constexpr (Q4) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const uint32_t w = qf[d][m];              // byte 4 d + m: dword m of k-step d
+              x[m] = (j == 0 ? bf_lo(w) : bf_hi(w)) * inv;
+            }
+          }
           uint32_t a = 0u, c = 0u, e = 0u;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
@@ -412,6 +449,48 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
         q1f[j] = i32x4_t{(int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
         q2f[j] = i32x4_t{(int)w2[0], (int)w2[1], (int)w2[2], (int)w2[3]};
         q3f[j] = i32x4_t{(int)w3[0], (int)w3[1], (int)w3[2], (int)w3[3]};
+      }
+    }
+  }
+  // INT4 attention sink (guijiagi 4.3): positions [t_begin, min(n_sink,
+  // t_end)) come from the unquantized sink rows (bf16 [B, n_sink, n_kv, D]),
+  // taken by the first wave of each KV head before the stages: the score of
+  // the lane's head on the VALU, folded into its softmax state, and the row's
+  // values added to the accumulators in the matrix-core layout (lane (mg,
+  // ml16) holds columns 16 c + 4 mg .. + 3 of head ml16).  The stages mask
+  // these positions.
+  if constexpr (Q4) {
+    constexpr int kWphS = NW / KH;
+    const int se = min(p.n_sink, t_end);
+    if (t_begin < se && wave % kWphS == 0) {
+      const int kv_w = kvh * KH + wave / kWphS;
+      const uint8_t* qr = reinterpret_cast<const uint8_t*>(p.q) +
+                          ((int64_t)b * n_h + (int64_t)kv_w * G + min(ml16, G - 1)) * D * 2;
+      for (int j = t_begin; j < se; ++j) {
+        const int64_t srow = (((int64_t)b * p.n_sink + j) * p.n_kv + kv_w) * D * 2;
+        const uint8_t* kr = reinterpret_cast<const uint8_t*>(p.sink_k) + srow;
+        const uint8_t* vr = reinterpret_cast<const uint8_t*>(p.sink_v) + srow;
+        float dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+          const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(qr + 16 * c);
+          const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kr + 16 * c);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) dot = dot2_bf16(qv[w], kv[w], dot);
+        }
+        const float sc = dot * qscale;
+        const float m_new = fmaxf(mm_run, sc);
+        const float alpha = mm_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm_run - m_new);
+        const float wgt = __builtin_amdgcn_exp2f(sc - m_new);
+        ml_run = ml_run * alpha + (mg == 0 ? wgt : 0.f);     // the four lane groups are summed at the end
+        mps_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < kCb; ++c) {
+          const u32x2_t v2 = *reinterpret_cast<const u32x2_t*>(vr + (16 * c + 4 * mg) * 2);
+          const f32x4_t vv = {bf_lo(v2[0]), bf_hi(v2[0]), bf_lo(v2[1]), bf_hi(v2[1])};
+          macc[c] = macc[c] * alpha + vv * wgt;
+        }
+        mm_run = m_new;
       }
     }
   }
@@ -437,7 +516,42 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       const int hoff = khw * (D * 2);
       const int row = tb + ml16;                     // K row of this lane (A operand)
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (Q8) {
+      if constexpr (Q4) {
+        // The lane's codes: the 16 packed bytes of elements (D / 4) mg ..
+        // + D / 4 - 1 of row `row` of its KV head, for K and V.
+        constexpr int kHeadPieces = D / 32;                 // 16-byte code pieces per head row
+        const int cz = R::swz_c(row);
+        const int pc = (khw * kHeadPieces + mg) ^ cz;
+        const u32x4_t kc = *reinterpret_cast<const u32x4_t*>(&s_dma[0][slot][row * R::kSrcRow + pc * 16]);
+        const u32x4_t vc = *reinterpret_cast<const u32x4_t*>(&s_dma[1][slot][row * R::kSrcRow + pc * 16]);
+        // V codes -> this wave's rows of the bf16 V tile as 136 + code
+        uint8_t* vrow_w = &s_tile[row * R::kRowBytes + hoff];
+        const int sv = R::swz_v(row);
+        u32x4_t wv[4];
+        widen_int4(vc, wv);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4_t*>(vrow_w + ((4 * mg + k) ^ sv) * 16) = wv[k];
+        // K codes as 16 x code in int8 (the low nibbles shifted up: the even
+        // elements; the high nibbles in place: the odd ones)
+        i32x4_t ke, ko;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          ke[w] = (int)((kc[w] << 4) & 0xF0F0F0F0u);
+          ko[w] = (int)(kc[w] & 0xF0F0F0F0u);
+        }
+        i32x4_t a1 = {0, 0, 0, 0}, a2 = {0, 0, 0, 0}, a3 = {0, 0, 0, 0};
+        a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ke, q1f[0], a1, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ke, q2f[0], a2, 0, 0, 0);
+        a3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ke, q3f[0], a3, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ko, q1f[1], a1, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ko, q2f[1], a2, 0, 0, 0);
+        a3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ko, q3f[1], a3, 0, 0, 0);
+        // |a_i| <= 128 * 127 * 128 < 2^24: exact in fp32; the 16 comes off exactly
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sacc[i] = (1.f / 16.f) * fmaf((float)a3[i], 1.f / (kQb * kQb), fmaf((float)a2[i], 1.f / kQb, (float)a1[i]));
+        asm volatile("" ::: "memory");               // the V tile stores stay before its reads
+      } else if constexpr (Q8) {
         // The lane's codes: elements (D / 4) mg .. + D / 4 - 1 of row `row`
         // of its KV head, for K and V (kLp 16-byte pieces each; the k index
         // of the score product is permuted the same way in qf).
@@ -500,7 +614,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float raw = Q8 ? sacc[i] * (sk[i] * qk) : sacc[i] * qscale;
-        sc4[i] = tile0 + tl0 + i < ce && tile0 + tl0 + i >= lo ? raw : -INFINITY;
+        sc4[i] = tile0 + tl0 + i < ce && tile0 + tl0 + i >= mlo ? raw : -INFINITY;
       }
       // maximum of the head over the wave's 16 tokens (lanes l16 + 16 j)
       float smax = fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3]));
@@ -528,7 +642,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         pr[i] = sc4[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc4[i] - mm_run);
-        pw[i] = Q8 ? pr[i] * svv[i] : pr[i];
+        pw[i] = Q8 ? (Q4 && pr[i] == 0.f ? 0.f : pr[i] * svv[i]) : pr[i];
       }
       const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{pw[0], pw[1]}), bf16x2_t));
       const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{pw[2], pw[3]}), bf16x2_t));
@@ -626,7 +740,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       const float mw = s_mml[w * G + h];
       const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       den = fmaf(f, s_mml[NW * G + w * G + h], den);
-      const float off = Q8 ? 128.f * s_mml[2 * NW * G + w * G + h] : 0.f;
+      const float off = Q8 ? (Q4 ? 136.f : 128.f) * s_mml[2 * NW * G + w * G + h] : 0.f;
       const float* ow = &s_mo[(w * G + h) * D + d0];
 #pragma unroll
       for (int c = 0; c < kCpt; ++c) num[c] = fmaf(f, ow[c] - off, num[c]);
@@ -1073,6 +1187,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
 }  // namespace
 
 bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
+  if (kv == KV::INT4) return q_bf16 && d_k == 128 && d_v == 128 && (g == 4 || g == 8);
   return (kv == KV::BF16 || kv == KV::INT8) && q_bf16 && d_k == d_v && (d_k == 64 || d_k == 128) &&
          (g == 4 || g == 8);
 }
@@ -1080,6 +1195,7 @@ bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
 int gqa_ring_kv_group(KV kv, bool q_bf16, int d_k, int d_v, int g, int n_kv) {
   if (!q_bf16 || d_k != 128 || d_v != 128 || !(g == 4 || g == 8)) return 1;
   if (kv == KV::BF16) return PKV_GQA_PAIR && n_kv % 2 == 0 ? 2 : 1;
+  if (kv == KV::INT4) return n_kv % 2 == 0 ? 2 : 0;      // INT4: pairs of KV heads only
   if (kv == KV::INT8) {
     if (PKV_Q8_KH >= 4 && n_kv % 4 == 0) return 4;
     if (PKV_Q8_KH >= 2 && n_kv % 2 == 0) return 2;
@@ -1097,7 +1213,11 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
   const int g = p.n_h / p.n_kv;
   const int kh = gqa_ring_kv_group(p.kv, p.q_bf16, p.d_k, p.d_v, g, p.n_kv);
   const unsigned groups = (unsigned)(p.n_kv / kh);
-  const bool q8 = p.kv == KV::INT8;
+  if (kh == 0) return hipErrorInvalidValue;
+  const bool q4 = p.kv == KV::INT4;
+  const bool q8 = p.kv == KV::INT8 || q4;
+  if (q4 && (p.window != 0 || p.n_sink < 0 || p.n_sink > kMaxSink || (p.n_sink > 0 && (!p.sink_k || !p.sink_v))))
+    return hipErrorInvalidValue;
   // ragged batches: the compact grid on INT8 pools, the stream grid on bf16
   // ones (each measured the faster there)
   if ((q8 && p.stream_wgs != 0) || (!q8 && p.compact_units != 0)) return hipErrorInvalidValue;
@@ -1142,6 +1262,24 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
       PKV_RING(128, G_, false, 2);                                                                 \
   } while (0)
   if (p.prefix_tokens != 0 && !(p.d_k == 128 && (g == 4 || g == 8) && !q8 && kh == 2)) return hipErrorInvalidValue;
+  // INT4 (two KV heads per workgroup, d = 128): the split or compact grid
+#define PKV_RING_Q4(G_)                                                                             \
+  do {                                                                                              \
+    if (mode != kGridSplit)                                                                         \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<128, G_, kWaves, kRingQ4, true, kGridCompact, 2, true>), grid, \
+                         dim3(64 * kWaves), 0, stream, p);                                         \
+    else                                                                                           \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<128, G_, kWaves, kRingQ4, true, kGridSplit, 2, true>), grid, \
+                         dim3(64 * kWaves), 0, stream, p);                                         \
+  } while (0)
+  if (q4) {
+    if (p.d_k != 128 || kh != 2) return hipErrorInvalidValue;
+    if (g == 8) PKV_RING_Q4(8);
+    else if (g == 4) PKV_RING_Q4(4);
+    else return hipErrorInvalidValue;
+#undef PKV_RING_Q4
+    return hipGetLastError();
+  }
   if (p.d_k == 128 && g == 8) {
     if (q8 && kh == 4) PKV_RING(128, 8, true, 4);
     else if (q8 && kh == 2) PKV_RING(128, 8, true, 2);

@@ -69,13 +69,20 @@ hipError_t launch_copy_blocks(const PoolRegions& r, const int32_t* pairs, int64_
 hipError_t launch_stage_blocks(const PoolRegions& r, const int32_t* blocks, int64_t n, uint8_t* staging,
                                int64_t total, bool to_staging, hipStream_t stream);
 
+// INT4 (two codes per byte, element 2i in the low nibble of byte i): codes
+// [slots, n_kv, d / 2] uint8, scales as for INT8.
+hipError_t launch_cache_quant_int4(uint8_t* k_codes, float* k_scales, const void* k_src, int32_t d_k,
+                                   uint8_t* v_codes, float* v_scales, const void* v_src, int32_t d_v,
+                                   bool src_bf16, const SlotSource& slots, int64_t num_tokens,
+                                   int32_t n_kv, int32_t block_shift, hipStream_t stream);
+
 hipError_t launch_gather(const void* pool, int64_t row_bytes, int32_t block_shift,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t B, int32_t max_context_len,
                          void* out, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode
-enum class KV { F32, BF16, INT8 };
+enum class KV { F32, BF16, INT8, INT4 };
 
 struct DecodeParams {
   const void* q;
@@ -138,6 +145,12 @@ struct DecodeParams {
   // (whole DMA rows), mask the positions below it, and skip every block
   // before it.
   int32_t window;
+  // INT4 pools (LDS-ring kernel): the first n_sink positions of each
+  // sequence are taken from unquantized rows, sink_k / sink_v bf16
+  // [B, n_sink, n_kv, d] (null when n_sink is 0).
+  const void* sink_k;
+  const void* sink_v;
+  int32_t n_sink;
 };
 
 // First attended position of a sequence of ctx tokens, and the position the
@@ -152,6 +165,7 @@ __device__ __forceinline__ int window_a0(const DecodeParams& p, int ctx) { retur
 constexpr int prefix_seqs_per_wg(int g) { return 4 * (32 / g); }
 
 constexpr int kCompactMaxB = 512;
+constexpr int kMaxSink = 64;        // INT4 pools: most unquantized sink positions
 
 // Chunked prefill (bf16, d = 128): q, out [B, max_chunk, n_h, d]; sequence
 // b's chunk_lens[b] query tokens sit at positions start_pos[b] + i.

@@ -56,11 +56,17 @@ size_t dtype_bytes(kvp_dtype t) {
     case KVP_F32: return 4;
     case KVP_BF16: return 2;
     case KVP_INT8: return 1;
+    case KVP_INT4: return 1;   // two codes per byte: rows are row_bytes(), not d * this
   }
   return 0;
 }
 
-bool dtype_valid(int t) { return t == KVP_F32 || t == KVP_BF16 || t == KVP_INT8; }
+bool dtype_valid(int t) { return t == KVP_F32 || t == KVP_BF16 || t == KVP_INT8 || t == KVP_INT4; }
+
+bool quantized(kvp_dtype t) { return t == KVP_INT8 || t == KVP_INT4; }
+
+// Bytes of one head's row of d elements.
+size_t row_bytes(kvp_dtype t, int64_t d) { return t == KVP_INT4 ? (size_t)d / 2 : (size_t)d * dtype_bytes(t); }
 
 struct PoolLayout {
   size_t k_off = 0, v_off = 0, ks_off = 0, vs_off = 0, total = 0;
@@ -77,9 +83,10 @@ const char* pool_desc_error(const kvp_pool_desc* d) {
   if (d->latent != 0 && d->latent != 1) return "latent must be 0 or 1";
   if (d->latent && d->n_kv != 1) return "a latent pool has n_kv == 1";
   if (d->latent && d->d_v > d->d_k) return "a latent pool needs d_v <= d_k";
-  if (d->latent && d->dtype == KVP_INT8) return "INT8 latent pools are not supported";
+  if (d->latent && quantized(d->dtype)) return "INT8 and INT4 latent pools are not supported";
+  if (d->dtype == KVP_INT4 && (d->d_k % 8 || d->d_v % 8)) return "INT4 rows need d a multiple of 8";
   const size_t eb = dtype_bytes(d->dtype);
-  if ((d->d_k * eb) % 4 || (d->d_v * eb) % 4) return "row bytes must be a multiple of 4";
+  if (row_bytes(d->dtype, d->d_k) % 4 || row_bytes(d->dtype, d->d_v) % 4) return "row bytes must be a multiple of 4";
   // K + V + scales per slot, times the slots, must stay far from size_t's end
   const double per_slot = (double)d->n_kv * ((double)(d->d_k + d->d_v) * eb + 8.0);
   if ((double)d->num_blocks * d->block_size * per_slot > 1.0e18) return "pool larger than 1e18 bytes";
@@ -88,11 +95,10 @@ const char* pool_desc_error(const kvp_pool_desc* d) {
 
 PoolLayout pool_layout(const kvp_pool_desc* d) {
   PoolLayout L;
-  const size_t eb = dtype_bytes(d->dtype);
   const size_t slots = (size_t)d->num_blocks * (size_t)d->block_size;
-  L.k_bytes = slots * d->n_kv * d->d_k * eb;
-  L.v_bytes = d->latent ? 0 : slots * d->n_kv * d->d_v * eb;
-  L.s_bytes = d->dtype == KVP_INT8 ? slots * d->n_kv * sizeof(float) : 0;
+  L.k_bytes = slots * d->n_kv * row_bytes(d->dtype, d->d_k);
+  L.v_bytes = d->latent ? 0 : slots * d->n_kv * row_bytes(d->dtype, d->d_v);
+  L.s_bytes = quantized(d->dtype) ? slots * d->n_kv * sizeof(float) : 0;
   size_t off = 0;
   L.k_off = off; off = round_up(off + L.k_bytes, 256);
   L.v_off = off; off = round_up(off + L.v_bytes, 256);
@@ -206,8 +212,8 @@ kvp_status kv_pool_view_get(const kvp_pool* pool, kvp_pool_view* out) {
   const PoolLayout& L = pool->layout;
   out->k = pool->base + L.k_off;
   out->v = pool->desc.latent ? out->k : pool->base + L.v_off;
-  out->k_scale = pool->desc.dtype == KVP_INT8 ? reinterpret_cast<float*>(pool->base + L.ks_off) : nullptr;
-  out->v_scale = (pool->desc.dtype == KVP_INT8 && !pool->desc.latent)
+  out->k_scale = quantized(pool->desc.dtype) ? reinterpret_cast<float*>(pool->base + L.ks_off) : nullptr;
+  out->v_scale = (quantized(pool->desc.dtype) && !pool->desc.latent)
                      ? reinterpret_cast<float*>(pool->base + L.vs_off) : nullptr;
   out->total_bytes = L.total;
   out->desc = pool->desc;
@@ -235,7 +241,9 @@ kvp_status paged_slot_mapping(const int32_t* block_table, int32_t max_blocks_per
 // ---------------------------------------------------------------- decode
 namespace {
 
-enum class Variant { Float, Int8, Mla };
+enum class Variant { Float, Int8, Int4, Mla };
+
+bool quant_variant(Variant v) { return v == Variant::Int8 || v == Variant::Int4; }
 
 const char* decode_desc_error(const kvp_decode_desc* d) {
   if (!d) return "decode description is NULL";
@@ -274,6 +282,7 @@ kvp_decode_desc planning_desc(const kvp_decode_desc* d) {
 
 Variant variant_of(const kvp_decode_desc* d) {
   if (d->kv_dtype == KVP_INT8) return Variant::Int8;
+  if (d->kv_dtype == KVP_INT4) return Variant::Int4;
   if (d->n_kv == 1 && d->d_k != d->d_v) return Variant::Mla;
   return Variant::Float;
 }
@@ -363,7 +372,7 @@ constexpr int32_t kBtSlotsInt8 = 256;
 
 int32_t max_split(const kvp_decode_desc* d, Variant v) {
   // a windowed split starts anywhere in a block, so it may touch one block more
-  const int64_t cap = (int64_t)((v == Variant::Int8 ? kBtSlotsInt8 : kBtSlots) - (d->window > 0 ? 1 : 0)) *
+  const int64_t cap = (int64_t)((quant_variant(v) ? kBtSlotsInt8 : kBtSlots) - (d->window > 0 ? 1 : 0)) *
                       d->block_size;
   return (int32_t)(cap < kMaxSplit ? cap : kMaxSplit);
 }
@@ -371,10 +380,10 @@ int32_t max_split(const kvp_decode_desc* d, Variant v) {
 // KV heads per workgroup of the LDS-ring kernel for this description, 0 when
 // the description does not run on it.
 int ring_kv_group(const kvp_decode_desc* d, Variant v) {
-  if (!(v == Variant::Float || v == Variant::Int8) || d->n_kv <= 0) return 0;
+  if (!(v == Variant::Float || quant_variant(v)) || d->n_kv <= 0) return 0;
   const int gq = d->n_h / d->n_kv;
   const bool qb = d->q_dtype == KVP_BF16;
-  const pkv::KV kv = v == Variant::Int8 ? pkv::KV::INT8
+  const pkv::KV kv = v == Variant::Int4 ? pkv::KV::INT4 : v == Variant::Int8 ? pkv::KV::INT8
                                         : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
   if (!pkv::gqa_ring_supported(kv, qb, d->d_k, d->d_v, gq)) return 0;
   return pkv::gqa_ring_kv_group(kv, qb, d->d_k, d->d_v, gq, d->n_kv);
@@ -412,7 +421,7 @@ int32_t stream_wgs(const kvp_decode_desc* d, Variant v) {
 // forced, B <= kCompactMaxB): the compact grid, which launches only the
 // splits that exist.
 bool compact_ok(const kvp_decode_desc* d, Variant v) {
-  return v == Variant::Int8 && d->split_tokens == 0 && d->total_context_len > 0 && d->B > 0 &&
+  return quant_variant(v) && d->split_tokens == 0 && d->total_context_len > 0 && d->B > 0 &&
          d->B <= pkv::kCompactMaxB && 4 * d->total_context_len < 3 * (int64_t)d->B * d->max_context_len &&
          ring_kv_group(d, v) > 0;
 }
@@ -595,8 +604,18 @@ kvp_status write_rows(kvp_pool* pool, const void* k_new, const void* v_new, kvp_
   hipStream_t st = static_cast<hipStream_t>(stream);
   kvp_pool_view v;
   kv_pool_view_get(pool, &v);
+  if (d.dtype == KVP_INT4) {
+    if (in_dtype != KVP_F32 && in_dtype != KVP_BF16)
+      return fail(KVP_ERR_INVALID_ARG, "%s: INT4 pools take F32 or BF16 rows", fn);
+    return hip_status(pkv::launch_cache_quant_int4(static_cast<uint8_t*>(v.k), v.k_scale, k_new, d.d_k,
+                                                  static_cast<uint8_t*>(v.v), v.v_scale, v_new, d.d_v,
+                                                  in_dtype == KVP_BF16, slots, num_tokens, d.n_kv,
+                                                  __builtin_ctz((unsigned)d.block_size), st),
+                      fn);
+  }
   if (d.dtype == KVP_INT8) {
-    if (in_dtype == KVP_INT8) return fail(KVP_ERR_INVALID_ARG, "%s: INT8 pools take F32 or BF16 rows", fn);
+    if (in_dtype == KVP_INT8 || in_dtype == KVP_INT4)
+      return fail(KVP_ERR_INVALID_ARG, "%s: INT8 pools take F32 or BF16 rows", fn);
     const bool bf = in_dtype == KVP_BF16;
     return hip_status(pkv::launch_cache_quant_int8(static_cast<int8_t*>(v.k), v.k_scale, k_new, d.d_k,
                                                   static_cast<int8_t*>(v.v), v.v_scale, v_new, d.d_v,
@@ -665,6 +684,13 @@ int64_t blocks_reachable(const void* ptr, size_t block_bytes) {
   return used >= size ? 0 : (int64_t)((size - used) / block_bytes);
 }
 
+// INT4 sink rows of paged_decode_attention_int4.
+struct SinkRows {
+  const void* k;
+  const void* v;
+  int32_t n;
+};
+
 // The append request of paged_decode_attention_append (null for a plain decode).
 struct AppendRows {
   kvp_pool* pool;
@@ -676,10 +702,13 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
                          const void* v, const float* ks, const float* vs,
                          const int32_t* block_table, const int32_t* context_lens, float scale,
                          void* out, const kvp_decode_desc* d, void* workspace,
-                         size_t workspace_bytes, void* stream, const AppendRows* app = nullptr) {
+                         size_t workspace_bytes, void* stream, const AppendRows* app = nullptr,
+                         const SinkRows* sink = nullptr) {
   if (const char* e = decode_desc_error(d)) return fail(KVP_ERR_INVALID_ARG, "%s: %s", fn, e);
   if (variant_of(d) != var) {
     if (var == Variant::Int8) return fail(KVP_ERR_INVALID_ARG, "%s: desc->kv_dtype must be KVP_INT8", fn);
+    if (var == Variant::Int4) return fail(KVP_ERR_INVALID_ARG, "%s: desc->kv_dtype must be KVP_INT4", fn);
+    if (d->kv_dtype == KVP_INT4) return fail(KVP_ERR_INVALID_ARG, "%s: use paged_decode_attention_int4 for INT4 pools", fn);
     if (var == Variant::Mla) return fail(KVP_ERR_INVALID_ARG, "%s: MLA needs n_kv == 1 and d_v < d_k", fn);
     if (d->kv_dtype == KVP_INT8) return fail(KVP_ERR_INVALID_ARG, "%s: use paged_decode_attention_int8 for INT8 pools", fn);
     return fail(KVP_ERR_INVALID_ARG, "%s: n_kv == 1 with d_v != d_k is the MLA layout; use paged_decode_attention_mla", fn);
@@ -687,7 +716,14 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   if (d->B == 0) return ok();
   if (!q || !k || !block_table || !context_lens || !out) return fail(KVP_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (var != Variant::Mla && !v) return fail(KVP_ERR_INVALID_ARG, "%s: v pool is NULL", fn);
-  if (var == Variant::Int8 && (!ks || !vs)) return fail(KVP_ERR_INVALID_ARG, "%s: NULL scale array", fn);
+  if (quant_variant(var) && (!ks || !vs)) return fail(KVP_ERR_INVALID_ARG, "%s: NULL scale array", fn);
+  if (var == Variant::Int4) {
+    if (!sink || sink->n < 0 || sink->n > pkv::kMaxSink)
+      return fail(KVP_ERR_INVALID_ARG, "%s: n_sink must be in [0, %d]", fn, pkv::kMaxSink);
+    if (sink->n > 0 && (!sink->k || !sink->v || !aligned(sink->k, 16) || !aligned(sink->v, 16)))
+      return fail(KVP_ERR_INVALID_ARG, "%s: sink rows NULL or not 16-byte aligned", fn);
+    if (app) return fail(KVP_ERR_UNSUPPORTED, "%s: INT4 pools decode through paged_decode_attention_int4", fn);
+  }
   if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
     return fail(KVP_ERR_INVALID_ARG, "%s: scale must be finite", fn);
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k, 16) || (v && !aligned(v, 16)))
@@ -709,6 +745,10 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
     if (!pkv::gqa_supported(pkv::KV::INT8, q_bf16, d->d_k, d->d_v, g))
       return fail(KVP_ERR_UNSUPPORTED, "%s: no INT8 kernel for q dtype %d, d_k %d, d_v %d, g %d", fn,
                   (int)d->q_dtype, d->d_k, d->d_v, g);
+  } else if (var == Variant::Int4) {
+    if (!pkv::gqa_supported(pkv::KV::INT4, q_bf16, d->d_k, d->d_v, g) || d->n_kv % 2)
+      return fail(KVP_ERR_UNSUPPORTED, "%s: INT4 needs bf16 q, d_k = d_v = 128, g in {4, 8} and even n_kv", fn);
+    if (d->window > 0) return fail(KVP_ERR_UNSUPPORTED, "%s: no sliding window on INT4 pools", fn);
   } else {
     if (d->kv_dtype != KVP_BF16 || !q_bf16 || !pkv::mla_supported(d->d_k, d->d_v, d->n_h, d->block_size))
       return fail(KVP_ERR_UNSUPPORTED, "%s: no MLA kernel for n_h %d, d_k %d, d_v %d, block %d", fn,
@@ -726,14 +766,13 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
     if (app) {
       nb = app->pool->desc.num_blocks;
     } else {
-      const size_t eb = dtype_bytes(d->kv_dtype);
       const size_t bsz = (size_t)d->block_size * d->n_kv;
-      nb = blocks_reachable(k, bsz * d->d_k * eb);
+      nb = blocks_reachable(k, bsz * row_bytes(d->kv_dtype, d->d_k));
       if (var != Variant::Mla) {
-        const int64_t nv = blocks_reachable(v, bsz * d->d_v * eb);
+        const int64_t nv = blocks_reachable(v, bsz * row_bytes(d->kv_dtype, d->d_v));
         if (nv < nb) nb = nv;
       }
-      if (var == Variant::Int8) {
+      if (quant_variant(var)) {
         const int64_t ns = std::min(blocks_reachable(ks, bsz * 4), blocks_reachable(vs, bsz * 4));
         if (ns < nb) nb = ns;
       }
@@ -820,7 +859,14 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   p.split_tokens = split;
   p.num_splits = ns;
   p.q_bf16 = q_bf16;
-  p.kv = var == Variant::Int8 ? pkv::KV::INT8 : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
+  p.kv = var == Variant::Int4   ? pkv::KV::INT4
+         : var == Variant::Int8 ? pkv::KV::INT8
+                                : (d->kv_dtype == KVP_BF16 ? pkv::KV::BF16 : pkv::KV::F32);
+  if (sink) {
+    p.sink_k = sink->k;
+    p.sink_v = sink->v;
+    p.n_sink = sink->n;
+  }
   p.window = dd->window;
   if (fused_append) {
     p.k_new = app->k_new;
@@ -899,6 +945,18 @@ kvp_status paged_decode_attention_int8(const void* q, const int8_t* k_codes, con
                        workspace_bytes, stream);
 }
 
+kvp_status paged_decode_attention_int4(const void* q, const uint8_t* k_codes, const float* k_scale,
+                                       const uint8_t* v_codes, const float* v_scale, const void* sink_k,
+                                       const void* sink_v, int32_t n_sink, const int32_t* block_table,
+                                       const int32_t* context_lens, float scale, void* out,
+                                       const kvp_decode_desc* desc, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  const SinkRows sink{sink_k, sink_v, n_sink};
+  return decode_common(Variant::Int4, "paged_decode_attention_int4", q, k_codes, v_codes, k_scale, v_scale,
+                       block_table, context_lens, scale, out, desc, workspace, workspace_bytes, stream, nullptr,
+                       &sink);
+}
+
 kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
                                       const int32_t* block_table, const int32_t* context_lens,
                                       float scale, void* out, const kvp_decode_desc* desc,
@@ -923,6 +981,9 @@ kvp_status append_impl(const char* fn, kvp_pool* pool, const void* q, const void
       pd.block_size != desc->block_size || pd.dtype != desc->kv_dtype)
     return fail(KVP_ERR_INVALID_ARG, "%s: the pool's n_kv, d_k, d_v, block_size or dtype differs from desc", fn);
   const Variant var = variant_of(desc);
+  if (var == Variant::Int4)
+    return fail(KVP_ERR_UNSUPPORTED, "%s: INT4 pools decode through paged_decode_attention_int4 "
+                "(write the rows with reshape_and_cache)", fn);
   if (pd.latent != (var == Variant::Mla))
     return fail(KVP_ERR_INVALID_ARG, "%s: a latent pool goes with an MLA description and only with one", fn);
   if (desc->B == 0) return ok();

@@ -47,6 +47,10 @@ def test_pool_sizes():
     # latent pool: one region
     nl = pk.kv_pool_required_bytes(4, 64, 1, 576, 512, pk.torch.bfloat16, latent=True)
     assert nl == 4 * 64 * 576 * 2
+    # INT4: two codes per byte plus the same scales as INT8
+    n4 = pk.kv_pool_required_bytes(10, 16, 8, 128, 128, pk.INT4)
+    assert n4 == 2 * (codes // 2) + 2 * ((scales + 255) // 256 * 256)
+    assert pk.kv_pool_required_bytes(10, 16, 8, 12, 12, pk.INT4) == 0     # d must be a multiple of 8
     # invalid descriptions size to 0
     assert pk.kv_pool_required_bytes(16, 12, 2, 64, 64, pk.torch.float32) == 0   # block not pow2
     assert pk.kv_pool_required_bytes(0, 16, 2, 64, 64, pk.torch.float32) == 0
