@@ -51,6 +51,8 @@ def parse():
                     help="CPU budget of the oracle baseline sample")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the secondary workloads (8B-shaped layer, INT8 cache, MLA)")
+    ap.add_argument("--only", choices=sorted(LEGS), default=None,
+                    help="run one secondary workload alone and print its record (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -80,6 +82,9 @@ def main():
               "(the path shards by sequence or KV head with no exchange, see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+    cpu_pool = None
+    if not args.no_cpu_baseline and not args.only:
+        cpu_pool, cpu_cores = start_cpu_workers()
 
     import torch
     import pagedattention_decode_paged_amd as pk
@@ -89,6 +94,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        print(json.dumps({"leg": args.only, **LEGS[args.only](dev)}), flush=True)
+        return
     cfg = CONFIGS["llama70b"]
     L = args.layers
     B, n_h, n_kv, d = cfg.B, cfg.n_h, cfg.n_kv, cfg.d_k
@@ -228,9 +236,22 @@ def main():
     if not args.headline_only:
         del layers, calls_rc, calls_dec, calls_app, calls_attn
         torch.cuda.empty_cache()
-        result["secondary"] = [bench_llama8b(dev), bench_int8(dev), bench_mla(dev)]
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        result["secondary"] = []
+        for name in ("llama8b", "int8", "mla", "window", "int4", "prefill", "blocks"):
+            print(f"[bench] secondary: {name}", file=sys.stderr, flush=True)
+            result["secondary"].append(LEGS[name](dev))
+            torch.cuda.empty_cache()
+        torch.cuda.empty_cache()
+    ceiling = read_ceiling(dev)
+    result["read_ceiling"] = ceiling
+    result["pct_of_read_ceiling"] = round(100 * gbs / ceiling["gbs"], 2)
+    result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
+    if cpu_pool is not None:
+        try:
+            result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, cpu_pool, cpu_cores)
+        finally:
+            cpu_pool.terminate()
+            cpu_pool.join()
     print(json.dumps(result), flush=True)
 
 
@@ -344,8 +365,7 @@ def bench_int8(dev, instances=4, cycles=10):
     us = _time_calls(calls, cycles)
     total = int(s.context_lens.sum())
     kv = total * cfg.n_kv * 2 * (cfg.d_k + 4)                  # codes + one fp32 scale, K and V
-    return {"workload": cfg.desc, "instances": instances, "shared_prefix_hint": shared_prefix_tokens,
-            "us_per_call": round(us, 2), "us_per_call_without_hint": round(us_plain, 2),
+    return {"workload": cfg.desc, "instances": instances, "us_per_call": round(us, 2),
             "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
             "pct_hbm_peak": round(100 * kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "token_heads_per_s": float(f"{total * cfg.n_h / (us * 1e-6):.4g}"), "kv_bytes": kv}
@@ -383,14 +403,215 @@ def bench_mla(dev, instances=4, cycles=10):
     us = _time_calls(calls, cycles)
     kv = total * cfg.d_k * 2
     flops = total * cfg.n_h * 2 * (cfg.d_k + cfg.d_v)
-    return {"workload": cfg.desc, "instances": instances, "shared_prefix_hint": shared_prefix_tokens,
-            "us_per_call": round(us, 2), "us_per_call_without_hint": round(us_plain, 2),
+    return {"workload": cfg.desc, "instances": instances, "us_per_call": round(us, 2),
             "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
             "pct_hbm_peak": round(100 * kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 1),
             "pct_mfma_bf16_peak": round(100 * flops / (us * 1e-6) / 2.5e15, 2),
             "token_heads_per_s": float(f"{total * cfg.n_h / (us * 1e-6):.4g}"), "kv_bytes": kv,
             "flops": flops}
+
+
+def bench_window(dev, instances=4, cycles=10, window=4096):
+    """Sliding-window decode on the 70B-shaped layer (B=16, n_h=64, n_kv=8,
+    d=128, every context 8192): each sequence attends to its last 4096
+    positions; 4 pools of identical structure cycled."""
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    from synth import CONFIGS, structure, device_normal_
+    cfg = CONFIGS["llama70b"]
+    s = structure(cfg, layer=0)
+    bt = torch.from_numpy(s.block_table).to(dev)
+    ctx = torch.from_numpy(s.context_lens).to(dev)
+    calls, keep = [], []
+    for i in range(instances):
+        pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v, torch.bfloat16,
+                                 device=dev)
+        device_normal_(pool.storage.view(torch.bfloat16), cfg.seed * 100 + 70 + i)
+        q = device_normal_(torch.empty((cfg.B, cfg.n_h, cfg.d_k), dtype=torch.bfloat16, device=dev),
+                           cfg.seed * 100 + 80 + i)
+        out = torch.empty((cfg.B, cfg.n_h, cfg.d_v), dtype=torch.bfloat16, device=dev)
+        desc = pk.make_desc(B=cfg.B, n_h=cfg.n_h, n_kv=cfg.n_kv, d_k=cfg.d_k, d_v=cfg.d_v,
+                            block_size=cfg.block_size, max_blocks_per_seq=s.max_blocks_per_seq,
+                            max_context_len=8192, q_dtype=pk.KVP_BF16, kv_dtype=pk.KVP_BF16, window=window)
+        ws = pk.alloc_workspace(desc, dev)
+        calls.append(lambda q=q, pool=pool, out=out, ws=ws: pk.paged_decode_attention(
+            q, pool.k, pool.v, bt, ctx, cfg.scale, out, max_context_len=8192, window=window, workspace=ws))
+        keep.append((pool, q, out, ws))
+    torch.cuda.synchronize()
+    us = _time_calls(calls, cycles)
+    tokens = int(np.minimum(s.context_lens, window).sum())
+    kv = tokens * cfg.n_kv * cfg.d_k * 2 * 2
+    return {"workload": f"bf16 B=16 n_h=64 n_kv=8 d=128 bs=16 S=8192, window {window}",
+            "instances": instances, "us_per_call": round(us, 2),
+            "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "token_heads_per_s": float(f"{tokens * cfg.n_h / (us * 1e-6):.4g}"), "kv_bytes": kv}
+
+
+def bench_int4(dev, instances=4, cycles=10, n_sink=4):
+    """INT4 cache with a 4-token unquantized sink, on the INT8 workload's
+    shape (B=32, n_h=64, n_kv=8, d=128, contexts log-uniform in [50, 32768]):
+    codes and scales written by reshape_and_cache from bf16 N(0,1) rows,
+    sink rows bf16 N(0,1); 4 instances cycled."""
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    from synth import CONFIGS, structure, device_normal_
+    from synth.workloads import prefill_tokens
+    cfg = CONFIGS["int8_70b"]
+    s = structure(cfg)
+    bt = torch.from_numpy(s.block_table).to(dev)
+    ctx = torch.from_numpy(s.context_lens).to(dev)
+    seq, pos = prefill_tokens(s.context_lens)
+    slots = pk.paged_slot_mapping(bt, torch.from_numpy(seq).to(dev), torch.from_numpy(pos).to(dev),
+                                  cfg.block_size)
+    total = int(s.context_lens.sum())
+    calls, keep = [], []
+    for i in range(instances):
+        pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v, pk.INT4, device=dev)
+        src = device_normal_(torch.empty((2, len(seq), cfg.n_kv, cfg.d_k), dtype=torch.bfloat16,
+                                         device=dev), cfg.seed * 100 + 20 + i)
+        pk.reshape_and_cache(pool, src[0], src[1], slots)
+        del src
+        sink = device_normal_(torch.empty((2, cfg.B, n_sink, cfg.n_kv, cfg.d_k), dtype=torch.bfloat16,
+                                          device=dev), cfg.seed * 100 + 30 + i)
+        q = device_normal_(torch.empty((cfg.B, cfg.n_h, cfg.d_k), dtype=torch.bfloat16, device=dev),
+                           cfg.seed * 100 + 40 + i)
+        out = torch.empty((cfg.B, cfg.n_h, cfg.d_v), dtype=torch.bfloat16, device=dev)
+        desc = pk.make_desc(B=cfg.B, n_h=cfg.n_h, n_kv=cfg.n_kv, d_k=cfg.d_k, d_v=cfg.d_v,
+                            block_size=cfg.block_size, max_blocks_per_seq=s.max_blocks_per_seq,
+                            max_context_len=s.max_context_len, q_dtype=pk.KVP_BF16,
+                            kv_dtype=pk.KVP_INT4, total_context_len=total)
+        ws = pk.alloc_workspace(desc, dev)
+        calls.append(lambda q=q, pool=pool, out=out, ws=ws, sink=sink: pk.paged_decode_attention_int4(
+            q, pool.k, pool.k_scale, pool.v, pool.v_scale, sink[0], sink[1], bt, ctx, cfg.scale, out,
+            max_context_len=s.max_context_len, total_context_len=total, workspace=ws))
+        keep.append((pool, sink, q, out, ws))
+    torch.cuda.synchronize()
+    us = _time_calls(calls, cycles)
+    sink_tokens = int(np.minimum(s.context_lens, n_sink).sum())
+    kv = (total - sink_tokens) * cfg.n_kv * 2 * (cfg.d_k // 2 + 4) + sink_tokens * cfg.n_kv * 2 * cfg.d_k * 2
+    return {"workload": f"int4 KV + {n_sink}-token bf16 sink, B=32 n_h=64 n_kv=8 d=128 bs=16 "
+                        "ctx log-U[50,32768]",
+            "instances": instances, "us_per_call": round(us, 2),
+            "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "token_heads_per_s": float(f"{total * cfg.n_h / (us * 1e-6):.4g}"), "kv_bytes": kv,
+            "note": "kv bytes: codes (d/2 per row) + one fp32 scale per row, K and V; sink rows bf16"}
+
+
+def bench_prefill(dev, instances=4, cycles=10):
+    """Chunked prefill on 70B-shaped heads (n_h=64, n_kv=8, d=128, block 16):
+    four 512-token chunks starting at positions 0, 1024, 4096 and 7680, each
+    attending causally to its cache and itself; 4 instances cycled."""
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    from synth import device_normal_
+    from synth.workloads import custom_structure
+    starts, chunks, n_h, n_kv, d, bs = [0, 1024, 4096, 7680], [512] * 4, 64, 8, 128, 16
+    ends = [a + c for a, c in zip(starts, chunks)]
+    st = custom_structure(ends, bs, seed=31, pad_blocks=1)
+    bt = torch.from_numpy(st.block_table).to(dev)
+    sp = torch.tensor(starts, dtype=torch.int32, device=dev)
+    cl = torch.tensor(chunks, dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    calls, keep = [], []
+    for i in range(instances):
+        pool = pk.kv_pool_create(st.num_blocks, bs, n_kv, d, d, torch.bfloat16, device=dev)
+        device_normal_(pool.storage.view(torch.bfloat16), 900 + i)
+        q = device_normal_(torch.empty((4, 512, n_h, d), dtype=torch.bfloat16, device=dev), 910 + i)
+        out = torch.empty_like(q)
+        calls.append(lambda q=q, pool=pool, out=out: pk.paged_prefill_attention(
+            q, pool.k, pool.v, bt, sp, cl, scale, out, max_context_len=max(ends)))
+        keep.append((pool, q, out))
+    torch.cuda.synchronize()
+    us = _time_calls(calls, cycles)
+    pairs = sum(sum(a + j + 1 for j in range(c)) for a, c in zip(starts, chunks))   # (query, key) pairs
+    flops = pairs * n_h * 4 * d                                 # q.k and p.v, 2 flops per MAC
+    kv = sum(ends) * n_kv * d * 2 * 2
+    return {"workload": "chunked prefill bf16 n_h=64 n_kv=8 d=128 bs=16, chunks of 512 at 0/1024/4096/7680",
+            "instances": instances, "us_per_call": round(us, 2),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "pct_mfma_bf16_peak": round(100 * flops / (us * 1e-6) / 2.5e15, 2),
+            "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1), "flops": flops, "kv_bytes": kv,
+            "note": "flops count every causal (query, key) pair of the chunks, 4*d per pair and head"}
+
+
+def bench_blocks(dev, n_pairs=2048, n_swap=1024, cycles=10):
+    """Block moves on a 70B-shaped layer pool (8192 blocks of 64 KiB, K and
+    V): copy_blocks of 2048 (src, dst) pairs with distinct random blocks, and
+    swap_out_blocks / swap_in_blocks of 1024 random blocks through pinned
+    host memory."""
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    from synth import device_normal_
+    nb, bs, n_kv, d = 8192, 16, 8, 128
+    pool = pk.kv_pool_create(nb, bs, n_kv, d, d, torch.bfloat16, device=dev)
+    device_normal_(pool.storage.view(torch.bfloat16), 77)
+    bb = pk.kv_pool_block_bytes(pool)
+    perm = np.random.default_rng(5).permutation(nb).astype(np.int32)
+    pairs = torch.from_numpy(perm[:2 * n_pairs].reshape(2, n_pairs).T.copy()).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / reps
+
+    us_copy = timed(lambda: pk.copy_blocks(pool, pairs), cycles)
+    blocks = torch.from_numpy(perm[:n_swap].copy()).to(dev)
+    staging = torch.empty(n_swap * bb, dtype=torch.uint8, device=dev)
+    host = torch.empty(n_swap * bb, dtype=torch.uint8, pin_memory=True)
+    us_out = timed(lambda: pk.swap_out_blocks(pool, blocks, staging, host), cycles)
+    us_in = timed(lambda: pk.swap_in_blocks(pool, blocks, staging, host), cycles)
+    moved = n_pairs * bb
+    sw = n_swap * bb
+    return {"workload": f"block moves, 70B-shaped layer pool ({nb} blocks of {bb} bytes)",
+            "copy_blocks_pairs": n_pairs, "copy_blocks_us": round(us_copy, 2),
+            "copy_blocks_gbs": round(2 * moved / (us_copy * 1e-6) / 1e9, 1),
+            "copy_blocks_pct_hbm_peak": round(100 * 2 * moved / (us_copy * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "swap_blocks": n_swap, "swap_out_us": round(us_out, 1), "swap_in_us": round(us_in, 1),
+            "swap_out_gbs": round(sw / (us_out * 1e-6) / 1e9, 2),
+            "swap_in_gbs": round(sw / (us_in * 1e-6) / 1e9, 2),
+            "note": "copy GB/s counts bytes read + written; swap GB/s counts the host bytes "
+                    "(gather/scatter through HBM staging + one PCIe copy)"}
+
+
+def read_ceiling(dev, gib=4, reps=10):
+    """A plain streaming read of a 4 GiB buffer (kvp_stream_read) at a few
+    grid sizes: the HBM read rate this device reaches with the simplest
+    kernel, against which the decode kernels' rates are put."""
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream()
+    best, sweep = 0.0, {}
+    for per_cu in (2, 4, 8, 16):
+        wg = per_cu * cus
+        pk.stream_read(buf, sink, wg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pk.stream_read(buf, sink, wg)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbs = buf.numel() / (1e-3 * e0.elapsed_time(e1) / reps) / 1e9
+        sweep[str(wg)] = round(gbs, 1)
+        best = max(best, gbs)
+    del buf
+    torch.cuda.empty_cache()
+    return {"gbs": round(best, 1), "pct_hbm_peak": round(100 * best / HBM_PEAK_GBS, 2),
+            "bytes": gib << 30, "gbs_by_workgroups": sweep,
+            "kernel": "stream_read_kernel: 8 x 16-byte loads in flight per lane, grid-stride"}
 
 
 def measured_traffic():
@@ -411,48 +632,117 @@ def measured_traffic():
     return None
 
 
-def cpu_baseline(budget_s):
-    """The fp64 oracle, as it stands, on a bounded sample of the same
-    workload: whole sequences of layer 0 (all 64 query heads, its K/V drawn
-    with the bench's seeds) until the CPU budget is spent; single-threaded
-    BLAS."""
-    import torch
+def _cpu_cores():
+    """Host cores the baseline may use: this process's CPU affinity, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:                                # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _cpu_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:                                   # pragma: no cover
+        pass
+    import oracle  # noqa: F401
+
+
+def _cpu_worker(task):
+    """Oracle calls on (sequence, KV head) units of one layer until the
+    budget is spent: each unit is decode attention of the g query heads
+    that share one KV head over the sequence's whole context."""
     import oracle
+    d, items, budget = task
+    k = np.load(os.path.join(d, "k.npy"), mmap_mode="r")
+    v = np.load(os.path.join(d, "v.npy"), mmap_mode="r")
+    q = np.load(os.path.join(d, "q.npy"))
+    bt = np.load(os.path.join(d, "bt.npy"))
+    ctx = np.load(os.path.join(d, "ctx.npy"))
+    scale = float(np.load(os.path.join(d, "scale.npy")))
+    g = q.shape[1] // k.shape[2]
+    done, kv_bytes = 0, 0
+    t0 = time.perf_counter()
+    for b, h in items:
+        if time.perf_counter() - t0 >= budget:
+            break
+        oracle.paged_decode_attention(q[b:b + 1, h * g:(h + 1) * g], k[:, :, h:h + 1], v[:, :, h:h + 1],
+                                      bt[b:b + 1], ctx[b:b + 1], scale)
+        done += 1
+        kv_bytes += int(ctx[b]) * (k.shape[3] + v.shape[3]) * 2
+    return done, kv_bytes, time.perf_counter() - t0
+
+
+def start_cpu_workers():
+    """The baseline's worker processes, started before this process touches
+    the GPU (they only ever run the CPU oracle)."""
+    import multiprocessing as mp
+    cores = _cpu_cores()
+    return mp.get_context("spawn").Pool(cores, initializer=_cpu_worker_init), cores
+
+
+def cpu_baseline(budget_s, pool, cores):
+    """The fp64 oracle, as it stands, on a bounded sample of the same
+    workload: layer 0 of the 70B-shaped step (its K/V drawn with the bench's
+    seeds on the device, then held in host memory), split into its 128
+    (sequence, KV head) units, dealt round-robin to one single-threaded
+    process per core and cycled until the CPU budget is spent."""
+    import shutil
+    import tempfile
+    import torch
     import pagedattention_decode_paged_amd as pk
     from synth import CONFIGS, structure, device_normal_
     cfg = CONFIGS["llama70b"]
     s = structure(cfg, layer=0)
-    pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v, torch.bfloat16)
-    device_normal_(pool.k, cfg.seed * 1000)
-    device_normal_(pool.v, cfg.seed * 1000 + 1)
+    kvp = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v, torch.bfloat16)
+    device_normal_(kvp.k, cfg.seed * 1000)
+    device_normal_(kvp.v, cfg.seed * 1000 + 1)
     q = device_normal_(torch.empty((cfg.B, cfg.n_h, cfg.d_k), dtype=torch.bfloat16, device="cuda"),
                        cfg.seed * 1000 + 2)
-    layer = {"s": s, "pool": pool, "q": q}
+    base = "/dev/shm" if os.access("/dev/shm", os.W_OK) else None
+    d = tempfile.mkdtemp(prefix="pkv_cpu_baseline_", dir=base)
     try:
-        from threadpoolctl import threadpool_limits
-        limit = threadpool_limits(limits=1)
-    except Exception:                                   # pragma: no cover
-        limit = None
-    s = layer["s"]
-    kh = layer["pool"].k.cpu().view(torch.int16).numpy().view(np.uint16)
-    vh = layer["pool"].v.cpu().view(torch.int16).numpy().view(np.uint16)
-    qh = layer["q"].cpu().view(torch.int16).numpy().view(np.uint16)
-    done = 0
-    t0 = time.perf_counter()
-    for b in range(cfg.B):
-        oracle.paged_decode_attention(qh[b:b + 1], kh, vh, s.block_table[b:b + 1],
-                                      s.context_lens[b:b + 1], cfg.scale)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    if limit is not None:
-        limit.unregister() if hasattr(limit, "unregister") else None
-    kv_bytes = done * int(s.context_lens[0]) * cfg.n_kv * cfg.d_k * 2 * 2
-    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0, {done} of {cfg.B} sequences x 8192 tokens x {cfg.n_kv} KV heads, "
-                      f"all {cfg.n_h} query heads ({kv_bytes} KV bytes in {dt:.2f} s)",
-            "tokens_per_s_equiv": round(done / dt / 80.0, 6)}
+        t_copy = time.perf_counter()
+        for name, t in (("k", kvp.k), ("v", kvp.v), ("q", q)):
+            np.save(os.path.join(d, f"{name}.npy"), t.cpu().view(torch.int16).numpy().view(np.uint16))
+        t_copy = time.perf_counter() - t_copy
+        del kvp, q
+        np.save(os.path.join(d, "bt.npy"), s.block_table)
+        np.save(os.path.join(d, "ctx.npy"), s.context_lens)
+        np.save(os.path.join(d, "scale.npy"), np.float64(cfg.scale))
+        units = [(b, h) for b in range(cfg.B) for h in range(cfg.n_kv)]
+        cap = 64 * len(units)
+        tasks = [(d, [units[i % len(units)] for i in range(w, cap, cores)], budget_s) for w in range(cores)]
+        print(f"[bench] cpu baseline: {cores} processes, {budget_s:.0f} s", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        # bounded wait: a pool whose workers cannot start never finishes a map
+        res = pool.map_async(_cpu_worker, tasks, chunksize=1).get(timeout=budget_s + 120)
+        wall = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    done = sum(r[0] for r in res)
+    kv_bytes = sum(r[1] for r in res)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:                                     # pragma: no cover
+        pass
+    tokens_equiv = kv_bytes / (cfg.n_kv * cfg.d_k * 2 * 2 * 8192 * 80)   # whole 80-layer decode steps of one sequence
+    return {"value": round(kv_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"layer 0 of the 70B-shaped step: {done} (sequence, KV head) units of 8192 tokens x "
+                      f"8 query heads ({len(units)} distinct, cycled) on {cores} single-threaded processes, "
+                      f"{kv_bytes} KV bytes in {wall:.2f} s",
+            "cpu_model": model, "host_copy_s": round(t_copy, 2),
+            "tokens_per_s_equiv": round(tokens_equiv / wall, 6)}
+
+
+LEGS = {"llama8b": bench_llama8b, "int8": bench_int8, "mla": bench_mla, "window": bench_window,
+        "int4": bench_int4, "prefill": bench_prefill, "blocks": bench_blocks, "ceiling": read_ceiling}
 
 
 if __name__ == "__main__":

@@ -496,6 +496,14 @@ kvp_status paged_decode_validate(const int32_t* block_table, const int32_t* cont
                                  const kvp_decode_desc* desc, int64_t num_blocks,
                                  void* stream);
 
+/* Measurement aid, not part of the decode path: a plain streaming read of
+ * buf (device, 16-byte aligned, bytes a multiple of 16) by `workgroups`
+ * workgroups of 256 lanes (0 = two per compute unit), each lane with eight
+ * 16-byte loads in flight; sink (device, 4 bytes) is written only if the
+ * data fold to a fixed key.  Timing it gives the read-bandwidth ceiling of
+ * the device that the decode kernels' HBM rates are compared with. */
+kvp_status kvp_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* kvp_last_error(void);
 

@@ -89,6 +89,7 @@ def _load() -> ctypes.CDLL:
         "paged_decode_attention_append_noalloc": (ctypes.c_int, [P, P, P, P, P, P, F, P,
                                                                  ctypes.POINTER(_DecodeDesc), P]),
         "paged_gather": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P]),
+        "kvp_stream_read": (ctypes.c_int, [P, SZ, P, I32, P]),
         "paged_prefill_attention": (ctypes.c_int, [P, P, P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc), I32, P]),
         "kvp_allocator_create": (ctypes.c_int, [I64, I32, P, ctypes.POINTER(P)]),
         "kvp_allocator_destroy": (None, [P]),
@@ -126,6 +127,7 @@ EXPORTED_SYMBOLS = (
     "kvp_allocator_create", "kvp_allocator_destroy", "kvp_block_hash", "kvp_allocate_prompt", "kvp_append_slot",
     "kvp_fork_sequence", "kvp_free_sequence", "kvp_allocator_block_state", "kvp_allocator_evictable",
     "kv_pool_block_bytes", "copy_blocks", "swap_out_blocks", "swap_in_blocks", "paged_prefill_attention",
+    "kvp_stream_read",
 )
 
 
@@ -476,6 +478,12 @@ def paged_prefill_attention(q, k_pool, v_pool, block_table, start_pos, chunk_len
                                         _ptr(chunk_lens), float(scale), _ptr(out), ctypes.byref(desc), C,
                                         _stream(dev)))
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0) -> None:
+    """The read-ceiling probe: a plain streaming read of ``buf``."""
+    dev = _need_cuda(buf, sink)
+    _check(_lib.kvp_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), workgroups, _stream(dev)))
 
 
 # --------------------------------------------------------------------- block allocator

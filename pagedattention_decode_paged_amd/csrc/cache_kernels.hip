@@ -310,4 +310,40 @@ hipError_t launch_stage_blocks(const PoolRegions& r, const int32_t* blocks, int6
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- read ceiling
+
+namespace {
+
+// A plain streaming read of a buffer: each lane keeps eight 16-byte loads in
+// flight, grid-stride over the buffer; the words are folded into one value
+// that is stored only if it equals a key no data produces, so the loads
+// stay.  Its rate is the ceiling the decode kernels' HBM rates are read
+// against.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                          uint32_t* __restrict__ sink, uint32_t key) {
+  constexpr int kIn = 8;
+  uint32_t acc = 0;
+  const int64_t step = (int64_t)gridDim.x * 256 * kIn;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kIn + threadIdx.x; base < n16; base += step) {
+    uint4 r[kIn];
+#pragma unroll
+    for (int i = 0; i < kIn; ++i) {
+      const int64_t idx = base + (int64_t)i * 256;
+      r[i] = idx < n16 ? src[idx] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kIn; ++i) acc ^= r[i].x ^ r[i].y ^ r[i].z ^ r[i].w;
+  }
+  if (acc == key) sink[0] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream) {
+  if (bytes < 16 || workgroups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(buf), bytes / 16, sink, 0x9E3779B9u);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -76,6 +76,10 @@ hipError_t launch_cache_quant_int4(uint8_t* k_codes, float* k_scales, const void
                                    bool src_bf16, const SlotSource& slots, int64_t num_tokens,
                                    int32_t n_kv, int32_t block_shift, hipStream_t stream);
 
+// Streaming read of bytes (16-byte aligned) with workgroups workgroups of
+// 256 lanes (the read-bandwidth ceiling probe).
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
+
 hipError_t launch_gather(const void* pool, int64_t row_bytes, int32_t block_shift,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t B, int32_t max_context_len,

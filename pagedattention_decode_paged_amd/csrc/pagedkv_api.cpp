@@ -1161,6 +1161,14 @@ kvp_status paged_prefill_attention(const void* q, const void* k_pool, const void
   return hip_status(pkv::launch_prefill_paged(p, static_cast<hipStream_t>(stream)), fn);
 }
 
+kvp_status kvp_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+  if (!buf || !sink || !aligned(buf, 16) || bytes % 16 || workgroups < 0)
+    return fail(KVP_ERR_INVALID_ARG, "kvp_stream_read: NULL or misaligned buffer, or bytes not a multiple of 16");
+  const int wg = workgroups > 0 ? workgroups : 2 * device_cus();
+  return hip_status(pkv::launch_stream_read(buf, (int64_t)bytes, sink, wg, static_cast<hipStream_t>(stream)),
+                    "kvp_stream_read");
+}
+
 size_t kv_pool_block_bytes(const kvp_pool* pool) {
   if (!pool) return 0;
   return (size_t)regions_total(pool_regions(pool));
