@@ -148,6 +148,126 @@ __global__ void cache_quant_int4_kernel(Quant4Job kj, Quant4Job vj, int bf16, Sl
   if (lane == 0) j.scales[out_scale] = scale;
 }
 
+// The same two quantizers (same binary32 operations per element, so the same
+// bits) for rows whose width d is 8 << lpr_shift (64 ... 512): a row is spread
+// over d / 8 lanes with eight elements each (one 16-byte load of bf16, two of
+// f32), so one wavefront quantizes 64 / (d / 8) rows at once and each lane
+// stores its eight codes in one 8-byte (INT8) or 4-byte (INT4) store.  A
+// wavefront takes kQuantBatches batches of kQuantGroups adjacent row groups,
+// the loads of a batch issued before any of its arithmetic.
+constexpr int kQuantGroups = 4;
+constexpr int kQuantBatches = 4;
+template <bool Q4, bool BF16>
+__global__ __launch_bounds__(256) void cache_quant_vec_kernel(QuantJob kj, QuantJob vj, SlotSource slots,
+                                                              int64_t num_rows, int32_t n_kv, int32_t bshift,
+                                                              int32_t lpr_shift) {
+  const QuantJob j = blockIdx.y == 0 ? kj : vj;
+  const int32_t d = j.d;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & ((1 << lpr_shift) - 1);             // lane within its row
+  const int64_t rpw = 64 >> lpr_shift;                        // rows per wavefront per group
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+#pragma unroll 1
+  for (int batch = 0; batch < kQuantBatches; ++batch) {
+    const int64_t first = (wave * kQuantBatches + batch) * kQuantGroups;   // first row group of the batch
+    if (first * rpw >= num_rows) break;
+    float x[kQuantGroups][8];
+#pragma unroll
+    for (int u = 0; u < kQuantGroups; ++u) {
+      const int64_t row = (first + u) * rpw + (lane >> lpr_shift);
+      if (row < num_rows) {
+        const int64_t e0 = row * d + sub * 8;
+        if (BF16) {
+          const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(j.src) + e0);
+          const uint32_t p[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            x[u][2 * k] = __uint_as_float(p[k] << 16);
+            x[u][2 * k + 1] = __uint_as_float(p[k] & 0xFFFF0000u);
+          }
+        } else {
+          const float4* f = reinterpret_cast<const float4*>(static_cast<const float*>(j.src) + e0);
+          const float4 a = f[0], b = f[1];
+          x[u][0] = a.x; x[u][1] = a.y; x[u][2] = a.z; x[u][3] = a.w;
+          x[u][4] = b.x; x[u][5] = b.y; x[u][6] = b.z; x[u][7] = b.w;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[u][k] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantGroups; ++u) {
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[u][k]));
+      for (int off = 1; off < (1 << lpr_shift); off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      const int64_t row = (first + u) * rpw + (lane >> lpr_shift);
+      if (row >= num_rows) continue;
+      // 32-bit division whenever the row count allows it (the 64-bit one is a long sequence)
+      const int64_t t = num_rows <= 0xFFFFFFFFll ? (int64_t)((uint32_t)row / (uint32_t)n_kv) : row / n_kv;
+      const int32_t h = (int32_t)(row - t * n_kv);
+      const int64_t s = slot_of(slots, t);
+      if (s < 0) continue;
+      const float scale = amax / (Q4 ? 7.0f : 127.0f);
+      int c[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        c[k] = 0;
+        if (scale > 0.f) {
+          const float r = rintf(x[u][k] / scale);
+          c[k] = (int)(Q4 ? fminf(fmaxf(r, -8.f), 7.f) : fminf(fmaxf(r, -128.f), 127.f));
+        }
+      }
+      const int64_t out_row = s * n_kv + h;
+      if (Q4) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) packed |= (uint32_t)(c[k] & 0xF) << (4 * k);
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(j.codes) + out_row * (d / 2) + sub * 4) = packed;
+      } else {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          lo |= (uint32_t)(c[k] & 0xFF) << (8 * k);
+          hi |= (uint32_t)(c[k + 4] & 0xFF) << (8 * k);
+        }
+        *reinterpret_cast<uint2*>(j.codes + out_row * d + sub * 8) = uint2{lo, hi};
+      }
+      if (sub == 0) j.scales[(((s >> bshift) * n_kv + h) << bshift) + (s & ((1 << bshift) - 1))] = scale;
+    }
+  }
+}
+
+// lanes per row as a power of two for the vectorised quantizers, -1 when
+// the rows do not fit them (d not in {64, 128, 256, 512}, K and V widths
+// differ, or a pointer is not 16-byte aligned).
+int quant_vec_shift(int32_t d_k, int32_t d_v, const void* k_src, const void* v_src, const void* k_codes,
+                    const void* v_codes, bool q4) {
+  if (d_k != d_v) return -1;
+  int sh = -1;
+  for (int s = 3; s <= 6; ++s)
+    if (d_k == (8 << s)) sh = s;
+  auto al = [](const void* p, uintptr_t a) { return p == nullptr || (uintptr_t)p % a == 0; };
+  const uintptr_t code_align = q4 ? 4 : 8;
+  if (sh < 0 || !al(k_src, 16) || !al(v_src, 16) || !al(k_codes, code_align) || !al(v_codes, code_align)) return -1;
+  return sh;
+}
+
+template <bool Q4>
+hipError_t launch_quant_vec(const QuantJob& kj, const QuantJob& vj, bool bf16, const SlotSource& slots,
+                            int64_t rows, int32_t n_kv, int32_t bshift, int sh, hipStream_t stream) {
+  const int64_t rows_per_wg = (int64_t)4 * kQuantBatches * kQuantGroups * (64 >> sh);   // 4 wavefronts
+  dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg), 2u);
+  if (bf16)
+    hipLaunchKernelGGL((cache_quant_vec_kernel<Q4, true>), grid, dim3(256), 0, stream, kj, vj, slots, rows, n_kv,
+                       bshift, sh);
+  else
+    hipLaunchKernelGGL((cache_quant_vec_kernel<Q4, false>), grid, dim3(256), 0, stream, kj, vj, slots, rows, n_kv,
+                       bshift, sh);
+  return hipGetLastError();
+}
+
 // qwbw 3.4: walk each sequence's table and copy its rows in logical order.
 template <typename V>
 __global__ void gather_kernel(const uint8_t* __restrict__ pool, int64_t row_bytes, int32_t shift,
@@ -205,6 +325,11 @@ hipError_t launch_cache_quant_int4(uint8_t* k_codes, float* k_scales, const void
                                    int32_t n_kv, int32_t block_shift, hipStream_t stream) {
   const int64_t rows = num_tokens * n_kv;
   if (rows == 0) return hipSuccess;
+  const int sh = quant_vec_shift(d_k, d_v, k_src, v_src, k_codes, v_codes, true);
+  if (sh >= 0)
+    return launch_quant_vec<true>(QuantJob{reinterpret_cast<int8_t*>(k_codes), k_scales, k_src, d_k},
+                                  QuantJob{reinterpret_cast<int8_t*>(v_codes), v_scales, v_src, d_v}, src_bf16,
+                                  slots, rows, n_kv, block_shift, sh, stream);
   const int waves = 4;
   dim3 grid((unsigned)((rows + waves - 1) / waves), 2u);
   hipLaunchKernelGGL(cache_quant_int4_kernel, grid, dim3(64 * waves), 0, stream,
@@ -219,6 +344,10 @@ hipError_t launch_cache_quant_int8(int8_t* k_codes, float* k_scales, const void*
                                    int32_t n_kv, int32_t block_shift, hipStream_t stream) {
   const int64_t rows = num_tokens * n_kv;
   if (rows == 0) return hipSuccess;
+  const int sh = quant_vec_shift(d_k, d_v, k_src, v_src, k_codes, v_codes, false);
+  if (sh >= 0)
+    return launch_quant_vec<false>(QuantJob{k_codes, k_scales, k_src, d_k}, QuantJob{v_codes, v_scales, v_src, d_v},
+                                   src_bf16, slots, rows, n_kv, block_shift, sh, stream);
   const int waves = 4;
   dim3 grid((unsigned)((rows + waves - 1) / waves), 2u);
   hipLaunchKernelGGL(cache_quant_int8_kernel, grid, dim3(64 * waves), 0, stream,
