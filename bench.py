@@ -277,42 +277,48 @@ def _time_calls(calls, cycles, warm=3):
 
 def bench_llama8b(dev, instances=16, cycles=20, shared_prefix_tokens=2048):
     """8B-shaped layer (B=32, n_h=32, n_kv=8, d=128, contexts U[512, 4096],
-    2K prefix shared by all sequences), 16 instances of identical structure
-    and different contents cycled.  The calls pass the shared prefix's
-    length as a hint (the prefix rows are then read once for all
-    sequences); the same calls without it are timed too."""
+    2K system prompt shared by all sequences) with its block tables built by
+    the library's block allocator from the prompts' token ids (the shared
+    prompt's full blocks are found by prefix caching and shared), 16
+    instances of identical structure and different contents cycled.  The
+    calls pass the shared prefix's length as a hint (the prefix rows are
+    then read once for all sequences); the same calls without it are timed
+    too."""
     import torch
     import pagedattention_decode_paged_amd as pk
-    from synth import CONFIGS, structure, device_normal_
+    from synth import CONFIGS, device_normal_
+    from synth.workloads import shared_prefix_prompts
     cfg = CONFIGS["llama8b"]
-    s = structure(cfg)
-    bt = torch.from_numpy(s.block_table).to(dev)
-    ctx = torch.from_numpy(s.context_lens).to(dev)
+    prompts, num_blocks, order = shared_prefix_prompts(cfg, shared_prefix_tokens)
+    table, ctx_np, cached = pk.BlockAllocator(num_blocks, cfg.block_size, order=order).allocate_batch(prompts)
+    bt = torch.from_numpy(table).to(dev)
+    ctx = torch.from_numpy(ctx_np).to(dev)
+    max_ctx = int(ctx_np.max())
+    total = int(ctx_np.sum())
     calls, calls_plain = [], []
     keep = []
     for i in range(instances):
-        pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v,
-                                 torch.bfloat16, device=dev)
+        pool = pk.kv_pool_create(num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v, torch.bfloat16, device=dev)
         device_normal_(pool.storage.view(torch.bfloat16), cfg.seed * 100 + i)
         q = device_normal_(torch.empty((cfg.B, cfg.n_h, cfg.d_k), dtype=torch.bfloat16, device=dev),
                            cfg.seed * 100 + 50 + i)
         out = torch.empty((cfg.B, cfg.n_h, cfg.d_v), dtype=torch.bfloat16, device=dev)
-        calls.append(pk.prepare_decode(q, pool.k, pool.v, bt, ctx, cfg.scale, out,
-                                       max_context_len=s.max_context_len,
-                                       total_context_len=int(s.context_lens.sum()),
-                                       shared_prefix_tokens=shared_prefix_tokens))
-        calls_plain.append(pk.prepare_decode(q, pool.k, pool.v, bt, ctx, cfg.scale, out,
-                                             max_context_len=s.max_context_len,
-                                             total_context_len=int(s.context_lens.sum())))
+        calls.append(pk.prepare_decode(q, pool.k, pool.v, bt, ctx, cfg.scale, out, max_context_len=max_ctx,
+                                       total_context_len=total, shared_prefix_tokens=shared_prefix_tokens))
+        calls_plain.append(pk.prepare_decode(q, pool.k, pool.v, bt, ctx, cfg.scale, out, max_context_len=max_ctx,
+                                             total_context_len=total))
         keep.append((pool, q, out))
     us = _time_calls(calls, cycles)
     us_plain = _time_calls(calls_plain, cycles)
     row = cfg.n_kv * cfg.d_k * 2 * 2                            # K + V bytes per token
-    total = int(s.context_lens.sum())
     logical = total * row
-    unique_tokens = int(min(2048, s.context_lens.max())) + int(np.maximum(s.context_lens - 2048, 0).sum())
-    unique = unique_tokens * row
-    return {"workload": cfg.desc, "instances": instances, "shared_prefix_hint": shared_prefix_tokens,
+    pos = np.concatenate([np.arange(c) for c in ctx_np])
+    seq = np.repeat(np.arange(cfg.B), ctx_np)
+    distinct_rows = np.unique(table[seq, pos // cfg.block_size].astype(np.int64) * cfg.block_size
+                              + pos % cfg.block_size).size
+    unique = int(distinct_rows) * row
+    return {"workload": cfg.desc + ", tables from the block allocator", "instances": instances,
+            "shared_prefix_hint": shared_prefix_tokens, "prefix_tokens_cached": int(sum(cached)),
             "us_per_call": round(us, 2), "us_per_call_without_hint": round(us_plain, 2),
             "kv_gbs_logical": round(logical / (us * 1e-6) / 1e9, 1),
             "kv_gbs_unique": round(unique / (us * 1e-6) / 1e9, 1),
@@ -320,9 +326,9 @@ def bench_llama8b(dev, instances=16, cycles=20, shared_prefix_tokens=2048):
             "pct_hbm_peak_unique": round(100 * unique / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "token_heads_per_s": float(f"{total * cfg.n_h / (us * 1e-6):.4g}"),
             "logical_kv_bytes": logical, "unique_kv_bytes": unique,
-            "note": "logical bytes count every sequence's view of the shared prefix; with the hint "
-                    "the prefix rows are read once for all sequences, without it each sequence reads "
-                    "them (after the first from cache)"}
+            "note": "logical bytes count every sequence's view of the shared prefix; unique bytes count each "
+                    "distinct cached row once; with the hint the prefix rows are read once for all sequences, "
+                    "without it each sequence reads them (after the first mostly from cache)"}
 
 
 def bench_int8(dev, instances=4, cycles=10):

@@ -13,6 +13,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -525,6 +526,23 @@ class BlockAllocator:
         _check(_lib.kvp_allocate_prompt(self._h, toks, len(token_ids), out, self.max_blocks, ctypes.byref(nb),
                                         ctypes.byref(cached)))
         return list(out[:nb.value]), int(cached.value)
+
+    def allocate_batch(self, prompts):
+        """Tables of a batch of new prompts, allocated in order (a prompt
+        that repeats an earlier one's leading full blocks shares them):
+        ``(block_table int32 [B, max blocks] padded with -1, context_lens
+        int32 [B], tokens found cached per prompt)``."""
+        tables, cached = [], []
+        for p in prompts:
+            t, c = self.allocate_prompt(p)
+            tables.append(t)
+            cached.append(c)
+        width = max([len(t) for t in tables] + [1])
+        bt = np.full((len(tables), width), -1, dtype=np.int32)
+        for b, t in enumerate(tables):
+            bt[b, :len(t)] = t
+        ctx = np.array([len(p) for p in prompts], dtype=np.int32)
+        return bt, ctx, cached
 
     def append_slot(self, table: list[int]):
         """Slot of one appended token; ``table`` is updated in place.

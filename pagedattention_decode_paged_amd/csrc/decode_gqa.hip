@@ -531,7 +531,8 @@ __global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_k
 __global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_stream_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_meta, const int32_t* __restrict__ context_lens, void* __restrict__ out,
-    int rows, int n_h, int d_v, int out_bf16, int B, int stream_wgs, int prefix_tokens, int prefix_chunk) {
+    int rows, int n_h, int d_v, int out_bf16, int B, int stream_wgs, int prefix_tokens, int prefix_chunk,
+    int block_shift) {
   const int bh = blockIdx.x * kReduceWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kReduceThreads);
   if (bh >= rows) return;
   const int b = bh / n_h, h = bh % n_h;
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(kReduceThreads * kReduceWaves) void decode_reduce_s
   if (prefix_tokens > 0) {
     const int ctx = context_lens[b];
     if (ctx <= 0) return;                       // zeroed by the decode kernel
-    npre = (min(ctx, prefix_tokens) + prefix_chunk - 1) / prefix_chunk;
+    npre = (prefix_end(ctx, prefix_tokens, block_shift) + prefix_chunk - 1) / prefix_chunk;
   } else if (jl <= jf) {
     return;
   }
@@ -656,7 +657,8 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(decode_reduce_stream_kernel, dim3((unsigned)((rows + kReduceWaves - 1) / kReduceWaves)),
                        dim3(kReduceThreads * kReduceWaves), 0, stream, (const float*)p.part_o,
                        (const float*)p.part_ml, (const int32_t*)p.seq_meta, p.context_lens, p.out, rows,
-                       p.n_h, p.d_v, p.q_bf16 ? 1 : 0, p.B, p.stream_wgs, p.prefix_tokens, p.prefix_chunk);
+                       p.n_h, p.d_v, p.q_bf16 ? 1 : 0, p.B, p.stream_wgs, p.prefix_tokens, p.prefix_chunk,
+                       p.block_shift);
     return hipGetLastError();
   }
   if (e != hipSuccess || p.num_splits == 1) return e;

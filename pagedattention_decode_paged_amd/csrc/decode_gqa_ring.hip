@@ -781,7 +781,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       for (int k = 0; k < 8; ++k) {
         const int sb = 8 * lane + k;
         const int c = sb < p.B ? p.context_lens[sb] : 0;
-        len[k] = (max(c - (S > 0 ? S : window_a0(p, c)), 0) + 15) & ~15;
+        len[k] = (max(c - (S > 0 ? prefix_end(c, S, p.block_shift) : window_a0(p, c)), 0) + 15) & ~15;
         sum += len[k];
       }
       int incl = sum;
@@ -809,7 +809,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       if (cx <= 0) {
         zero_out(b);
         if (kvh == 0 && threadIdx.x == 0) { p.seq_meta[2 * b] = 0; p.seq_meta[2 * b + 1] = S > 0 ? -1 : 0; }
-      } else if (cx <= S) {
+      } else if (S > 0 && prefix_end(cx, S, p.block_shift) == cx) {
         if (kvh == 0 && threadIdx.x == 0) { p.seq_meta[2 * b] = 0; p.seq_meta[2 * b + 1] = -1; }
       }
     }
@@ -824,7 +824,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       const int st = __builtin_amdgcn_readfirstlane(s_upre[b]);
       if (st >= r1) break;
       const int ctx = p.context_lens[b];
-      const int s0 = S > 0 ? S : window_a0(p, ctx);  // first position of its part (prefix or window)
+      const int s0 = S > 0 ? prefix_end(ctx, S, p.block_shift) : window_a0(p, ctx);   // its part starts here
       const int L = ctx - s0;                       // this sequence's tokens in the stream part
       const int a = (int)max(r0 - st, (int64_t)0), e = (int)min(r1 - st, (int64_t)L);
       if (L <= 0 || a >= e) continue;
@@ -895,7 +895,7 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       __syncthreads();
       const int ref = __builtin_amdgcn_readfirstlane(s_ref[0]);
       const int ctx_ref = __builtin_amdgcn_readfirstlane(s_ref[1]);
-      const int ce = min(c1, ctx_ref);
+      const int ce = min(c1, prefix_end(ctx_ref, S, shift));
       if (ce <= c0) return;                             // no sequence reaches this chunk
       const int lb0 = c0 >> shift;
       const int nblk = ((ce - 1) >> shift) - lb0 + 1;
@@ -972,14 +972,15 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
       }
       for (int i = tid; i < kSpg * nblk; i += kThr) {
         const int bl = i / nblk, jj = i % nblk;
-        const int lim = min(s_cl[bl], ce);
+        const int lim = min(prefix_end(s_cl[bl], S, shift), ce);
         if (lim > c0 && jj <= ((lim - 1) >> shift) - lb0) {
           const int b = cg * kSpg + bl;
           if (p.block_table[(int64_t)b * p.max_blocks_per_seq + lb0 + jj] != s_bt[jj]) s_mis[bl] = 1;
         }
       }
       const int any_member =
-          __builtin_amdgcn_readfirstlane(__syncthreads_or(tid < kSpg && s_cl[tid] > c0 && s_mis[tid] == 0));
+          __builtin_amdgcn_readfirstlane(__syncthreads_or(tid < kSpg && prefix_end(s_cl[tid], S, shift) > c0 &&
+                                                          s_mis[tid] == 0));
       const int64_t piece0 = (int64_t)p.stream_wgs + B + (int64_t)c * B;   // + b: this chunk's piece
       if (!any_member) wait_vm_imm<0>();                  // the first stages' DMA lands before the ring is reused
       if (any_member) {
@@ -988,8 +989,9 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
           const int bl = bcol[cb] - cg * kSpg;
-          mem[cb] = s_cl[bl] > c0 && s_mis[bl] == 0;
-          lim[cb] = mem[cb] ? min(s_cl[bl], ce) : 0;
+          const int pe = prefix_end(s_cl[bl], S, shift);
+          mem[cb] = pe > c0 && s_mis[bl] == 0;
+          lim[cb] = mem[cb] ? min(pe, ce) : 0;
 #pragma unroll
           for (int ks = 0; ks < kKs; ++ks)
             if (!mem[cb]) qf2[cb][ks] = u32x4_t{0u, 0u, 0u, 0u};
@@ -1103,9 +1105,10 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
 #pragma unroll 1
         for (int bl = 0; bl < kSpg; ++bl) {
           const int cx = __builtin_amdgcn_readfirstlane(s_cl[bl]);
-          if (cx > c0 && __builtin_amdgcn_readfirstlane(s_mis[bl])) {
+          const int pe = prefix_end(cx, S, shift);
+          if (pe > c0 && __builtin_amdgcn_readfirstlane(s_mis[bl])) {
             __syncthreads();                            // the ring and block table are free
-            unit(cg * kSpg + bl, c0, min(c1, cx), cx, 1, piece0 * n_h, false);
+            unit(cg * kSpg + bl, c0, min(c1, pe), cx, 1, piece0 * n_h, false);
           }
         }
       }

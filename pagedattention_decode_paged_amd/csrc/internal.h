@@ -164,6 +164,16 @@ __device__ __forceinline__ int window_lo(const DecodeParams& p, int ctx) {
 }
 __device__ __forceinline__ int window_a0(const DecodeParams& p, int ctx) { return window_lo(p, ctx) & ~15; }
 
+// End of a sequence's part in the shared prefix of S tokens (S > 0, a
+// multiple of 64): S for a sequence that reaches it, else its tokens up to
+// the last boundary of a whole block and of 16 tokens.  A partly filled
+// last block is never shared by a block allocator (only full blocks are
+// found by prefix caching), so it joins the sequence's own part instead of
+// failing the prefix pass's table check; parts start at multiples of 16.
+__device__ __forceinline__ int prefix_end(int ctx, int S, int shift) {
+  return ctx >= S ? S : ctx & ~((1 << max(shift, 4)) - 1);
+}
+
 // Sequences one prefix workgroup serves: four waves of 32 query columns
 // (two 16-column matrix-core blocks), g columns per sequence.
 constexpr int prefix_seqs_per_wg(int g) { return 4 * (32 / g); }

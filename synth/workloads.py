@@ -202,6 +202,28 @@ def shared_prefix_structure(context_lens, block_size: int, shared_blocks: int, s
     return Structure(ctx, bt, n_blocks, shared_blocks=shared_blocks)
 
 
+def shared_prefix_prompts(cfg: Config, prefix_tokens: int = 2048, vocab: int = 32000):
+    """Token ids of the 8B-shaped batch, for building its tables with a
+    block allocator: the context lengths of ``structure(cfg)``; every prompt
+    starts with one shared ``prefix_tokens``-token system prompt (a shorter
+    prompt is that prompt's first tokens) followed by its own random ids.
+    Also the allocator's initial free order (a seeded permutation of the
+    pool, so physical placement is random) and a pool size with one block of
+    headroom per sequence (a partly filled last block is never shared)."""
+    rng = np.random.Generator(np.random.PCG64(cfg.seed))
+    ctx = rng.integers(512, 4097, size=cfg.B).astype(np.int32)          # as structure(cfg)
+    trng = np.random.Generator(np.random.PCG64([cfg.seed, 7]))
+    shared = trng.integers(0, vocab, size=prefix_tokens).astype(np.int32)
+    prompts = [np.concatenate([shared[:min(int(c), prefix_tokens)],
+                               trng.integers(0, vocab, size=max(0, int(c) - prefix_tokens)).astype(np.int32)])
+               for c in ctx]
+    bs = cfg.block_size
+    n_blocks = _blocks_needed(prefix_tokens, bs) + sum(_blocks_needed(max(0, int(c) - prefix_tokens), bs)
+                                                       for c in ctx) + cfg.B
+    order = np.random.Generator(np.random.PCG64([cfg.seed, 8])).permutation(n_blocks).astype(np.int32)
+    return prompts, n_blocks, order
+
+
 # --------------------------------------------------------------------------
 # token lists (structure only: which sequence and position each token has)
 # --------------------------------------------------------------------------

@@ -99,3 +99,25 @@ def test_errors_leave_the_allocator_unchanged():
     assert ([a.block_state(b) for b in range(4)], a.evictable()) == before
     with pytest.raises(pk.PagedKVError):
         pk.BlockAllocator(4, 4, order=[0, 1, 1, 3])
+
+
+def test_shared_prefix_batch_tables_match_the_oracle():
+    """The 8B-shaped batch's tables as the bench and the GPU tests build
+    them (the library's allocator over the prompts' token ids): identical to
+    the oracle allocator's from the same free order, and every full block
+    of the shared 2K system prompt is one physical block for all."""
+    from synth import CONFIGS
+    from synth.workloads import shared_prefix_prompts
+    cfg = CONFIGS["llama8b"]
+    prompts, nb, order = shared_prefix_prompts(cfg)
+    bt, ctx, cached = pk.BlockAllocator(nb, cfg.block_size, order=order).allocate_batch(prompts)
+    ref = oracle.BlockAllocator(nb, cfg.block_size, order=order)
+    for b, p in enumerate(prompts):
+        table, c = ref.allocate_prompt(p)
+        assert list(bt[b, :len(table)]) == table and np.all(bt[b, len(table):] == -1)
+        assert cached[b] == c
+    assert list(ctx) == [len(p) for p in prompts]
+    full = np.minimum(ctx, 2048) // cfg.block_size
+    longest = int(np.argmax(full))
+    for b in range(cfg.B):
+        assert np.array_equal(bt[b, :full[b]], bt[longest, :full[b]])

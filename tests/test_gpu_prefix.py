@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from synth import CONFIGS, structure, device_normal_
-from synth.workloads import shared_prefix_structure
+from synth.workloads import Structure, shared_prefix_prompts, shared_prefix_structure
 
 from parity_support import TOL_BF16, host, max_err, owned_slots, poison_unowned_, tables_to_device
 
@@ -74,6 +74,31 @@ def test_llama8b_shared_prefix_hint_full_size(hint):
     torch.cuda.synchronize()
     ref = oracle.paged_decode_attention(host(q), host(pool.k), host(pool.v), s.block_table, s.context_lens,
                                         cfg.scale)
+    assert max_err(out, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("hint", [2048, 0])
+def test_llama8b_allocator_tables_full_size(hint):
+    """The 8B-shaped batch with its tables built by the library's block
+    allocator from the prompts' token ids: the shared 2K system prompt's
+    full blocks are found by prefix caching and shared by every sequence (a
+    prompt shorter than 2K keeps its partly filled last block to itself).
+    Full size, every output element, with the hint and without."""
+    cfg = CONFIGS["llama8b"]
+    prompts, nb, order = shared_prefix_prompts(cfg)
+    bt_np, ctx_np, cached = pk.BlockAllocator(nb, cfg.block_size, order=order).allocate_batch(prompts)
+    full = np.minimum(ctx_np, 2048) // 16
+    for b in range(1, cfg.B):                   # every full prefix block is shared with sequence 0's
+        n = min(full[b], full[0])
+        assert np.array_equal(bt_np[b, :n], bt_np[0, :n])
+    assert cached[0] == 0 and sum(cached) > 0
+    s = Structure(ctx_np, bt_np, nb)
+    pool, q = _case(s, cfg.n_h, cfg.n_kv, cfg.block_size, 77 + hint)
+    bt, ctx = tables_to_device(s)
+    out = pk.paged_decode_attention(q, pool.k, pool.v, bt, ctx, cfg.scale, max_context_len=s.max_context_len,
+                                    total_context_len=int(ctx_np.sum()), shared_prefix_tokens=hint)
+    torch.cuda.synchronize()
+    ref = oracle.paged_decode_attention(host(q), host(pool.k), host(pool.v), bt_np, ctx_np, cfg.scale)
     assert max_err(out, ref) <= TOL_BF16
 
 
