@@ -429,8 +429,11 @@ bool compact_ok(const kvp_decode_desc* d, Variant v) {
 int32_t plan_split(const kvp_decode_desc* d, Variant v) {
   const int g = granule(v);
   if (d->split_tokens > 0) return d->split_tokens;
-  const int64_t total = d->total_context_len > 0 ? d->total_context_len
-                                                 : (int64_t)d->B * d->max_context_len;
+  int64_t total = d->total_context_len > 0 ? d->total_context_len : (int64_t)d->B * d->max_context_len;
+  // a sliding window reads at most window + 15 tokens (the start rounds down
+  // to 16), the grid covering them; the work is sized by the window itself,
+  // so an aligned window splits evenly (4096 -> 8 x 512 rather than 8 x 576)
+  if (d->window > 0) total = std::min(total, (int64_t)d->B * d->window);
   int64_t heads = v == Variant::Mla ? 1 : d->n_kv;
   const int kh = ring_kv_group(d, v);
   if (kh > 0) heads /= kh;                      // the ring kernel's KV-head groups
