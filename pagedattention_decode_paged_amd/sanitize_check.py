@@ -2,8 +2,9 @@
 
 Builds the library with the sanitizers on its host code only (each
 ``-fsanitize=`` right after ``-Xarch_host``; the GPU code is built as usual)
-into ``_build/asan/``, then runs the CPU tests of the boundary
-(``tests/test_abi.py``) against that build in a child process with the ASan
+into ``_build/asan/``, then runs the CPU tests of the boundary and of the
+host block allocator (``tests/test_abi.py``, ``tests/test_allocator.py``)
+against that build in a child process with the ASan
 runtime preloaded (Python itself is not instrumented, so leak checking is
 off).  Exits with the test run's status; a sanitizer report aborts the run.
 
@@ -48,8 +49,9 @@ def main() -> int:
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_abi.py")], env=env, cwd=ROOT)
-    print(f"sanitized C-ABI tests: exit {r.returncode} ({lib})")
+                        os.path.join(ROOT, "tests", "test_abi.py"), os.path.join(ROOT, "tests", "test_allocator.py")],
+                       env=env, cwd=ROOT)
+    print(f"sanitized C-ABI and allocator tests: exit {r.returncode} ({lib})")
     return r.returncode
 
 
