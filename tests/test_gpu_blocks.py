@@ -85,6 +85,42 @@ def test_swap_out_and_in_round_trip(kind, bs, n_kv, d_k, d_v, latent):
         assert np.array_equal(got, arr)
 
 
+def test_block_moves_at_the_bench_size():
+    """The bench's block-move workload: a 70B-shaped layer pool (8192 blocks
+    of 64 KiB), copy_blocks of 2048 (src, dst) pairs of distinct random
+    blocks, then a swap out and back in of 1024 random blocks: every byte
+    of the pool against the oracle's copy, the host rows against its swap."""
+    nb = 8192
+    pool = _pool("bf16", nb, 16, 8, 128, 128, False, 5)
+    before = _arrays(pool)
+    perm = np.random.default_rng(5).permutation(nb).astype(np.int32)
+    pairs = perm[:4096].reshape(2, 2048).T.copy()
+    pk.copy_blocks(pool, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    after = _arrays(pool)
+    for got, arr in zip(after, before):
+        assert np.array_equal(got, oracle.copy_blocks(arr, pairs.tolist()))
+    blocks = perm[:1024]
+    bb = pk.kv_pool_block_bytes(pool)
+    staging = torch.empty(len(blocks) * bb, dtype=torch.uint8, device="cuda")
+    hbuf = torch.empty(len(blocks) * bb, dtype=torch.uint8, pin_memory=True)
+    bl = torch.from_numpy(blocks.copy()).cuda()
+    pk.swap_out_blocks(pool, bl, staging, hbuf)
+    torch.cuda.synchronize()
+    hb = hbuf.numpy().reshape(len(blocks), bb)
+    off = 0
+    for arr in after:
+        w = arr.shape[1]
+        assert np.array_equal(hb[:, off:off + w], oracle.swap_out(arr, blocks.tolist()))
+        off += w
+    for arr_t in (pool.k, pool.v):
+        arr_t.view(torch.uint8)[bl.long()] = 0xFF
+    pk.swap_in_blocks(pool, bl, staging.zero_(), hbuf)
+    torch.cuda.synchronize()
+    for got, arr in zip(_arrays(pool), after):
+        assert np.array_equal(got, arr)
+
+
 def _write_tokens(pool, tables, lens, seed):
     """K/V rows for every token of every sequence, written through
     reshape_and_cache at the slots the tables give."""

@@ -184,3 +184,19 @@ def test_pool_create_reports_out_of_memory():
     lib.kv_pool_destroy(h)
     x = torch.ones(1024, device="cuda")
     assert float(x.sum()) == 1024.0
+
+
+def test_stream_read_probe():
+    """The read-ceiling probe (kvp_stream_read): reads the buffer, leaves the
+    sink alone (a buffer of ones never folds to the key), and refuses a
+    misaligned buffer or a size that is not a multiple of 16 bytes."""
+    buf = torch.ones(1 << 22, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for wg in (0, 1, 7, 4096):
+        pk.stream_read(buf, sink, wg)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    with pytest.raises(pk.PagedKVError):
+        pk.stream_read(buf[1:17], sink)
+    with pytest.raises(pk.PagedKVError):
+        pk.stream_read(buf[:24], sink)
