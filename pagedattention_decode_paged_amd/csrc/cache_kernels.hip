@@ -445,9 +445,9 @@ namespace {
 
 // A plain streaming read of a buffer: each lane keeps eight 16-byte loads in
 // flight, grid-stride over the buffer; the words are folded into one value
-// that is stored only if it equals a key no data produces, so the loads
-// stay.  Its rate is the ceiling the decode kernels' HBM rates are read
-// against.
+// that is stored only if it equals a fixed key, so the compiler keeps the
+// loads (and almost no run writes anything).  Its rate is the ceiling the
+// decode kernels' HBM rates are read against.
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
                                                           uint32_t* __restrict__ sink, uint32_t key) {
   constexpr int kIn = 8;
