@@ -246,9 +246,17 @@ def main():
     result["read_ceiling"] = ceiling
     result["pct_of_read_ceiling"] = round(100 * gbs / ceiling["gbs"], 2)
     result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
+    mfma = mfma_ceiling(dev)
+    result["mfma_ceiling"] = mfma
+    for leg in result.get("secondary", []):
+        if "mfma_tflops" in leg:
+            leg["pct_of_mfma_ceiling"] = round(100 * leg["mfma_tflops"] / mfma["tflops"], 2)
+        if "tflops" in leg:
+            leg["pct_of_mfma_ceiling"] = round(100 * leg["tflops"] / mfma["tflops"], 2)
     if cpu_pool is not None:
         try:
             result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, cpu_pool, cpu_cores)
+            result["cpu_baseline"]["gpu_over_oracle"] = round(gbs / result["cpu_baseline"]["value"], 1)
         finally:
             cpu_pool.terminate()
             cpu_pool.join()
@@ -620,6 +628,34 @@ def read_ceiling(dev, gib=4, reps=10):
             "kernel": "stream_read_kernel: 8 x 16-byte loads in flight per lane, grid-stride"}
 
 
+def mfma_ceiling(dev, iterations=4096, reps=5):
+    """The bf16 matrix-core rate this device reaches with back-to-back
+    independent v_mfma_f32_16x16x32_bf16 on register operands
+    (kvp_mfma_peak), at 4, 8 and 16 workgroups of four wavefronts per CU."""
+    import torch
+    import pagedattention_decode_paged_amd as pk
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream()
+    best, sweep = 0.0, {}
+    for per_cu in (4, 8, 16):
+        wg = per_cu * cus
+        flops = pk.mfma_peak(sink, wg, iterations)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pk.mfma_peak(sink, wg, iterations)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tf = flops / (1e-3 * e0.elapsed_time(e1) / reps) / 1e12
+        sweep[str(wg)] = round(tf, 1)
+        best = max(best, tf)
+    return {"tflops": round(best, 1), "pct_of_dense_bf16_peak": round(100 * best / 2500.0, 2),
+            "tflops_by_workgroups": sweep,
+            "kernel": "mfma_peak_kernel: 8 independent v_mfma_f32_16x16x32_bf16 chains per wavefront"}
+
+
 def measured_traffic():
     """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE record, if the kernel sources it was taken on are unchanged
@@ -748,7 +784,8 @@ def cpu_baseline(budget_s, pool, cores):
 
 
 LEGS = {"llama8b": bench_llama8b, "int8": bench_int8, "mla": bench_mla, "window": bench_window,
-        "int4": bench_int4, "prefill": bench_prefill, "blocks": bench_blocks, "ceiling": read_ceiling}
+        "int4": bench_int4, "prefill": bench_prefill, "blocks": bench_blocks, "ceiling": read_ceiling,
+        "mfma": mfma_ceiling}
 
 
 if __name__ == "__main__":

@@ -504,6 +504,15 @@ kvp_status paged_decode_validate(const int32_t* block_table, const int32_t* cont
  * the device that the decode kernels' HBM rates are compared with. */
 kvp_status kvp_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
 
+/* Measurement aid, not part of the decode path: `workgroups` workgroups of
+ * four wavefronts (0 = four per compute unit), each wavefront running
+ * `iterations` rounds of eight independent bf16 matrix instructions
+ * (v_mfma_f32_16x16x32_bf16, 16,384 FLOPs each) on register operands; sink
+ * (device, 4 bytes) is never written in practice.  FLOPs per call =
+ * workgroups x 4 x iterations x 8 x 16384; timing it gives the bf16
+ * matrix-core ceiling that the MLA and prefill FLOP rates are compared with. */
+kvp_status kvp_mfma_peak(float* sink, int32_t workgroups, int32_t iterations, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* kvp_last_error(void);
 

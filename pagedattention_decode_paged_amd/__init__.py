@@ -91,6 +91,7 @@ def _load() -> ctypes.CDLL:
                                                                  ctypes.POINTER(_DecodeDesc), P]),
         "paged_gather": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P]),
         "kvp_stream_read": (ctypes.c_int, [P, SZ, P, I32, P]),
+        "kvp_mfma_peak": (ctypes.c_int, [P, I32, I32, P]),
         "paged_prefill_attention": (ctypes.c_int, [P, P, P, P, P, P, F, P, ctypes.POINTER(_DecodeDesc), I32, P]),
         "kvp_allocator_create": (ctypes.c_int, [I64, I32, P, ctypes.POINTER(P)]),
         "kvp_allocator_destroy": (None, [P]),
@@ -128,7 +129,7 @@ EXPORTED_SYMBOLS = (
     "kvp_allocator_create", "kvp_allocator_destroy", "kvp_block_hash", "kvp_allocate_prompt", "kvp_append_slot",
     "kvp_fork_sequence", "kvp_free_sequence", "kvp_allocator_block_state", "kvp_allocator_evictable",
     "kv_pool_block_bytes", "copy_blocks", "swap_out_blocks", "swap_in_blocks", "paged_prefill_attention",
-    "kvp_stream_read",
+    "kvp_stream_read", "kvp_mfma_peak",
 )
 
 
@@ -485,6 +486,14 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0) -> N
     """The read-ceiling probe: a plain streaming read of ``buf``."""
     dev = _need_cuda(buf, sink)
     _check(_lib.kvp_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), workgroups, _stream(dev)))
+
+
+def mfma_peak(sink: torch.Tensor, workgroups: int = 0, iterations: int = 4096) -> int:
+    """The matrix-core probe; returns the FLOPs the call performs."""
+    dev = _need_cuda(sink)
+    _check(_lib.kvp_mfma_peak(_ptr(sink), workgroups, iterations, _stream(dev)))
+    wg = workgroups if workgroups > 0 else 4 * torch.cuda.get_device_properties(dev).multi_processor_count
+    return wg * 4 * iterations * 8 * 16384
 
 
 # --------------------------------------------------------------------- block allocator

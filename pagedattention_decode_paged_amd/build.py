@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
-SOURCES = ["pagedkv_api.cpp", "block_allocator.cpp", "cache_kernels.hip", "decode_gqa.hip", "decode_gqa_ring.hip", "decode_int8.hip", "decode_mla.hip", "prefill_paged.hip"]
+SOURCES = ["pagedkv_api.cpp", "block_allocator.cpp", "cache_kernels.hip", "decode_gqa.hip", "decode_gqa_ring.hip", "decode_int8.hip", "decode_mla.hip", "prefill_paged.hip", "probes.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

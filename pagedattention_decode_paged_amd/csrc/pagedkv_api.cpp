@@ -14,6 +14,7 @@
 
 #include "../../include/pagedkv.h"
 #include "internal.h"
+#include "probes.h"
 
 namespace {
 
@@ -1170,6 +1171,13 @@ kvp_status kvp_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_
   const int wg = workgroups > 0 ? workgroups : 2 * device_cus();
   return hip_status(pkv::launch_stream_read(buf, (int64_t)bytes, sink, wg, static_cast<hipStream_t>(stream)),
                     "kvp_stream_read");
+}
+
+kvp_status kvp_mfma_peak(float* sink, int32_t workgroups, int32_t iterations, void* stream) {
+  if (!sink || !aligned(sink, 4) || workgroups < 0 || iterations <= 0)
+    return fail(KVP_ERR_INVALID_ARG, "kvp_mfma_peak: NULL or misaligned sink, workgroups < 0 or iterations <= 0");
+  const int wg = workgroups > 0 ? workgroups : 4 * device_cus();
+  return hip_status(pkv::launch_mfma_peak(sink, wg, iterations, static_cast<hipStream_t>(stream)), "kvp_mfma_peak");
 }
 
 size_t kv_pool_block_bytes(const kvp_pool* pool) {

@@ -200,3 +200,16 @@ def test_stream_read_probe():
         pk.stream_read(buf[1:17], sink)
     with pytest.raises(pk.PagedKVError):
         pk.stream_read(buf[:24], sink)
+
+
+def test_mfma_peak_probe():
+    """The matrix-core probe (kvp_mfma_peak): runs, never writes the sink,
+    reports the FLOPs of the call, and refuses a bad sink or iteration count."""
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    flops = pk.mfma_peak(sink, 8, 16)
+    torch.cuda.synchronize()
+    assert flops == 8 * 4 * 16 * 8 * 16384 and float(sink.item()) == 0.0
+    with pytest.raises(pk.PagedKVError):
+        pk.mfma_peak(sink, 8, 0)
+    with pytest.raises(pk.PagedKVError):
+        pk.mfma_peak(torch.zeros(2, dtype=torch.uint8, device="cuda")[1:], 8, 16)
