@@ -374,7 +374,10 @@ kvp_status paged_decode_attention_append_noalloc(kvp_pool* pool, const void* q, 
  * through the block table (kvh = h / (n_h / n_kv)).
  *   q, out: device [B, max_chunk, n_h, 128] bf16; rows at or past
  *           chunk_lens[b] are not written.
- *   start_pos, chunk_lens: device int32 [B].
+ *   start_pos, chunk_lens: device int32 [B], start_pos[b] >= 0 and
+ *           chunk_lens[b] <= max_chunk (device data: checked only under
+ *           PAGEDKV_VALIDATE; a sequence outside these bounds or whose
+ *           chunk runs past its table is skipped, its rows not written).
  *   desc: B, n_h, n_kv, d_k = d_v = 128, block_size, max_blocks_per_seq,
  *         bf16 q and pool; max_context_len (host bound of start_pos[b] +
  *         chunk_lens[b]) <= max_blocks_per_seq * block_size.  g = n_h /

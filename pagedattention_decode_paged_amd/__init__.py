@@ -595,24 +595,34 @@ def copy_blocks(pool: KVPool, pairs: torch.Tensor) -> None:
     """Copy block src onto block dst for each row (src, dst) of ``pairs``
     (device int32 ``[n, 2]``), in every region of the pool."""
     dev = _need_cuda(pairs)
-    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
-        raise ValueError("pairs must be int32 [n, 2]")
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
+        raise ValueError("pairs must be a contiguous int32 [n, 2] tensor")
     _check(_lib.copy_blocks(pool.handle, _ptr(pairs), pairs.shape[0], _stream(dev)))
+
+
+def _swap_args(pool: KVPool, blocks: torch.Tensor, staging: torch.Tensor, host: torch.Tensor):
+    dev = _need_cuda(blocks, staging)
+    if blocks.dtype != torch.int32 or blocks.dim() != 1 or not blocks.is_contiguous():
+        raise ValueError("blocks must be a contiguous int32 [n] tensor")
+    if host.is_cuda or not host.is_contiguous():
+        raise ValueError("host must be a contiguous host tensor")
+    need = blocks.numel() * kv_pool_block_bytes(pool)
+    for name, t in (("staging", staging), ("host", host)):
+        if not t.is_contiguous() or t.numel() * t.element_size() < need:
+            raise ValueError(f"{name} must be contiguous with at least {need} bytes")
+    return dev
 
 
 def swap_out_blocks(pool: KVPool, blocks: torch.Tensor, staging: torch.Tensor, host: torch.Tensor) -> None:
     """Blocks (device int32 ``[n]``) -> ``host`` (pinned uint8, ``n *
     kv_pool_block_bytes`` bytes) through the device ``staging`` buffer."""
-    dev = _need_cuda(blocks, staging)
-    if host.is_cuda or not host.is_contiguous():
-        raise ValueError("host must be a contiguous host tensor")
+    dev = _swap_args(pool, blocks, staging, host)
     _check(_lib.swap_out_blocks(pool.handle, _ptr(blocks), blocks.numel(), _ptr(staging), _ptr(host), _stream(dev)))
 
 
 def swap_in_blocks(pool: KVPool, blocks: torch.Tensor, staging: torch.Tensor, host: torch.Tensor) -> None:
-    dev = _need_cuda(blocks, staging)
-    if host.is_cuda or not host.is_contiguous():
-        raise ValueError("host must be a contiguous host tensor")
+    """The inverse of :func:`swap_out_blocks`: ``host`` -> staging -> blocks."""
+    dev = _swap_args(pool, blocks, staging, host)
     _check(_lib.swap_in_blocks(pool.handle, _ptr(blocks), blocks.numel(), _ptr(staging), _ptr(host), _stream(dev)))
 
 

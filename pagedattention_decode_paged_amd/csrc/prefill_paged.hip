@@ -59,9 +59,13 @@ void prefill_paged_kernel(const PrefillParams p) {
   __shared__ __align__(16) int32_t s_bt[kBtSlots];
 
   const int kvh = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
+  // a chunk longer than the q rows, a negative start or one that runs past
+  // the table is outside the contract: nothing is read or written for it
   const int n = p.chunk_lens[b], p0 = p.start_pos[b];
   const int i0 = tile * kQt;
-  if (i0 >= n || n <= 0) return;
+  if (i0 >= n || n <= 0 || n > p.max_chunk || p0 < 0 ||
+      (int64_t)p0 + n > ((int64_t)p.max_blocks_per_seq << p.block_shift))
+    return;
   const int t_end = p0 + min(i0 + kQt, n);   // positions the workgroup reads: [0, t_end)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -120,3 +120,24 @@ def test_prefill_70b_shaped_chunks_sampled():
             ref = oracle.paged_decode_attention(qh[b, i][None], kh, vh, st.block_table[b:b + 1],
                                                 [starts[b] + i + 1], scale)
             assert max_err(out[b, i:i + 1], ref) <= TOL_BF16, (b, i)
+
+
+def test_prefill_skips_sequences_outside_the_contract():
+    """A chunk longer than the q rows, a negative start and a chunk running
+    past its block table are skipped (their rows keep the fill); the other
+    sequences are still computed against the oracle."""
+    starts, chunks = [0, 40, 0, 30], [20, 30, 10, 16]
+    st, pool, q, bt, sp, cl, mx = _case(starts, chunks, 8, 2, 16, 44, C=32)
+    scale = 1.0 / math.sqrt(128)
+    bad_cl = cl.clone()
+    bad_cl[1] = 33                                  # longer than the 32 q rows
+    bad_sp = sp.clone()
+    bad_sp[2] = -5                                  # negative start
+    bad_sp[3] = st.max_blocks_per_seq * 16 - 8      # 16 tokens from 8 before the table's end
+    out = torch.full_like(q, float("nan"))
+    pk.paged_prefill_attention(q, pool.k, pool.v, bt, bad_sp, bad_cl, scale, out, max_context_len=mx)
+    torch.cuda.synchronize()
+    ref = oracle.paged_prefill_attention(host(q), host(pool.k), host(pool.v), st.block_table, starts, chunks, scale)
+    assert max_err(out[0, :20], ref[0, :20]) <= TOL_BF16
+    for b in (1, 2, 3):
+        assert bool(torch.isnan(out[b].float()).all()), b
