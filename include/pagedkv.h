@@ -227,7 +227,12 @@ typedef struct {
                                   over its tokens in the chunk equal those of
                                   the longest sequence (checked on the
                                   device); any other sequence's chunk is read
-                                  from its own blocks.  A wrong value costs
+                                  from its own blocks.  A sequence shorter
+                                  than the hint takes part up to its last
+                                  whole block and 16-token boundary (a partly
+                                  filled last block is never shared by an
+                                  allocator); its remaining tokens are read
+                                  with its own part.  A wrong value costs
                                   time, never results. */
   int32_t window;              /* sliding window (guijiagi 5.1; 0 = none):
                                   a sequence of L tokens attends to its last
