@@ -39,6 +39,7 @@ def _case(g, n_kv, kind, seed):
     else:
         from synth.workloads import prefill_tokens
         pool = pk.kv_pool_create(s.num_blocks, bs, n_kv, d, d, torch.int8)
+        pool.storage.zero_()                       # slots no token owns: codes and scales 0
         seq, pos = prefill_tokens(s.context_lens)
         slots = pk.paged_slot_mapping(bt, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), bs)
         rows = device_normal_(torch.empty((2, len(seq), n_kv, d), dtype=torch.bfloat16, device="cuda"), seed + 2)
