@@ -743,7 +743,13 @@ def cpu_baseline(budget_s, pool, cores):
     device_normal_(kvp.v, cfg.seed * 1000 + 1)
     q = device_normal_(torch.empty((cfg.B, cfg.n_h, cfg.d_k), dtype=torch.bfloat16, device="cuda"),
                        cfg.seed * 1000 + 2)
-    base = "/dev/shm" if os.access("/dev/shm", os.W_OK) else None
+    need = 2 * s.num_blocks * cfg.block_size * cfg.n_kv * cfg.d_k * 2 + (64 << 20)
+    base = None                                       # the default temp dir unless /dev/shm has the room
+    try:
+        if os.access("/dev/shm", os.W_OK) and shutil.disk_usage("/dev/shm").free > 2 * need:
+            base = "/dev/shm"
+    except OSError:                                   # pragma: no cover
+        pass
     d = tempfile.mkdtemp(prefix="pkv_cpu_baseline_", dir=base)
     try:
         t_copy = time.perf_counter()
