@@ -273,7 +273,9 @@ kvp_status paged_decode_attention(const void* q, const void* k_pool, const void*
 
 /* INT8 pools: codes as in the pool layout plus fp32 scales
  * [num_blocks, n_kv, block_size]; dequantization (code * scale,
- * guijiagi 4.2) happens inside the kernel.  desc->kv_dtype == KVP_INT8. */
+ * guijiagi 4.2) happens inside the kernel.  desc->kv_dtype == KVP_INT8.
+ * Scale arrays must be 4-byte aligned (else KVP_ERR_INVALID_ARG; the same for
+ * INT4). */
 kvp_status paged_decode_attention_int8(const void* q, const int8_t* k_codes,
                                        const float* k_scale, const int8_t* v_codes,
                                        const float* v_scale, const int32_t* block_table,

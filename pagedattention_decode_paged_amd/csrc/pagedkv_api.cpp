@@ -721,6 +721,8 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   if (!q || !k || !block_table || !context_lens || !out) return fail(KVP_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (var != Variant::Mla && !v) return fail(KVP_ERR_INVALID_ARG, "%s: v pool is NULL", fn);
   if (quant_variant(var) && (!ks || !vs)) return fail(KVP_ERR_INVALID_ARG, "%s: NULL scale array", fn);
+  if (quant_variant(var) && (!aligned(ks, 4) || !aligned(vs, 4)))
+    return fail(KVP_ERR_INVALID_ARG, "%s: scale arrays must be 4-byte aligned", fn);
   if (var == Variant::Int4) {
     if (!sink || sink->n < 0 || sink->n > pkv::kMaxSink)
       return fail(KVP_ERR_INVALID_ARG, "%s: n_sink must be in [0, %d]", fn, pkv::kMaxSink);

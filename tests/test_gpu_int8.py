@@ -3,6 +3,7 @@ against the oracle's fp32-step quantizer, and decode attention with the
 dequantization fused into the kernel against the oracle's attention over the
 dequantized cache (bf16 q and output: max abs error <= 2e-2)."""
 
+import ctypes
 import math
 
 import numpy as np
@@ -124,3 +125,44 @@ def test_int8_query_outliers(d, g):
     scale = 1.0 / math.sqrt(d)
     _check_attention(pool, q, bt, ctx, s, scale)
     _check_attention(pool, q, bt, ctx, s, scale, split_tokens=256)
+
+
+@pytest.mark.parametrize("g,bs", [(8, 16), (4, 64)])
+def test_int8_scales_not_16_byte_aligned(g, bs):
+    """Scale arrays 4- but not 16-byte aligned (the kernel fetches one fp32
+    per lane and token): the outputs are bit-identical to those from the
+    aligned arrays, with every unowned scale slot NaN.  A scale array that is
+    not 4-byte aligned is refused with a message."""
+    ctxs = [1, 15, 17, 300, 1025, 64]
+    s = custom_structure(ctxs, bs, seed=g + bs, pad_blocks=1)
+    s.extra["bs"] = bs
+    n_kv, d = 2, 128
+    pool, q, bt, ctx = _int8_case(s, n_kv * g, n_kv, d, 900 + g + bs)
+    scale = 1.0 / math.sqrt(d)
+    out_a = _check_attention(pool, q, bt, ctx, s, scale, total_context_len=int(s.context_lens.sum()))
+    outs = {}
+    for name, shift in (("aligned", 0), ("offset4", 1)):
+        ks = torch.empty(pool.k_scale.numel() + 4, dtype=torch.float32, device="cuda")
+        vs = torch.empty_like(ks)
+        k_sc = ks[shift:shift + pool.k_scale.numel()].view(pool.k_scale.shape)
+        v_sc = vs[shift:shift + pool.v_scale.numel()].view(pool.v_scale.shape)
+        k_sc.copy_(pool.k_scale)
+        v_sc.copy_(pool.v_scale)
+        assert (k_sc.data_ptr() % 16 == 0) == (shift == 0)
+        for split in (0, 256):
+            outs[(name, split)] = pk.paged_decode_attention_int8(
+                q, pool.k, k_sc, pool.v, v_sc, bt, ctx, scale, max_context_len=s.max_context_len,
+                split_tokens=split, total_context_len=int(s.context_lens.sum()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[("aligned", 0)], out_a)
+    for split in (0, 256):
+        assert torch.equal(outs[("offset4", split)], outs[("aligned", split)])
+    raw = torch.empty(pool.k_scale.numel() * 4 + 8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pk.PagedKVError, match="4-byte aligned"):
+        pk._check(pk._lib.paged_decode_attention_int8(
+            pk._ptr(q), pk._ptr(pool.k), ctypes.c_void_p(raw.data_ptr() + 2), pk._ptr(pool.v),
+            pk._ptr(pool.v_scale), pk._ptr(bt), pk._ptr(ctx), ctypes.c_float(scale),
+            pk._ptr(torch.empty_like(q)), ctypes.byref(pk.make_desc(
+                B=len(ctxs), n_h=n_kv * g, n_kv=n_kv, d_k=d, d_v=d, block_size=bs,
+                max_blocks_per_seq=s.max_blocks_per_seq, max_context_len=s.max_context_len,
+                q_dtype=pk.KVP_BF16, kv_dtype=pk.KVP_INT8)), None, 0, None))
