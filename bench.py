@@ -234,14 +234,14 @@ def main():
     }
 
     if not args.headline_only:
+        # The memory freed here stays in torch's cache for the later legs:
+        # handed back to the driver, tens of GiB are cleared in the background
+        # for up to a minute, and the device reads ~5-10 % slower meanwhile.
         del layers, calls_rc, calls_dec, calls_app, calls_attn
-        torch.cuda.empty_cache()
         result["secondary"] = []
         for name in ("llama8b", "int8", "mla", "window", "int4", "prefill", "blocks"):
             print(f"[bench] secondary: {name}", file=sys.stderr, flush=True)
             result["secondary"].append(LEGS[name](dev))
-            torch.cuda.empty_cache()
-        torch.cuda.empty_cache()
     ceiling = read_ceiling(dev)
     result["read_ceiling"] = ceiling
     result["pct_of_read_ceiling"] = round(100 * gbs / ceiling["gbs"], 2)
@@ -263,16 +263,22 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def _time_calls(calls, cycles, warm=3):
+def _time_calls(calls, cycles, warm=3, warm_s=0.1):
     """Average device time of one call, cycling through independent
     instances (so that repeated calls do not find their data in the
-    256 MB last-level cache); HIP events on the launch stream."""
+    256 MB last-level cache); HIP events on the launch stream.  The calls
+    run for at least warm_s seconds first: after the idle set-up of a leg
+    the device needs tens of milliseconds of load to reach its steady
+    clock (the INT8 leg's first 4 ms ran ~10 % slower than later ones)."""
     import torch
     stream = torch.cuda.current_stream()
-    for _ in range(warm):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warm or time.perf_counter() - t0 < warm_s:
         for c in calls:
             c()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        n += 1
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(cycles):
@@ -567,9 +573,13 @@ def bench_blocks(dev, n_pairs=2048, n_swap=1024, cycles=10):
     pairs = torch.from_numpy(perm[:2 * n_pairs].reshape(2, n_pairs).T.copy()).to(dev)
     stream = torch.cuda.current_stream()
 
-    def timed(fn, reps):
-        fn()
-        torch.cuda.synchronize()
+    def timed(fn, reps, warm_s=0.1):
+        t0 = time.perf_counter()                    # to the steady clock first (see _time_calls)
+        while True:
+            fn()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= warm_s:
+                break
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
@@ -622,7 +632,6 @@ def read_ceiling(dev, gib=4, reps=10):
         sweep[str(wg)] = round(gbs, 1)
         best = max(best, gbs)
     del buf
-    torch.cuda.empty_cache()
     return {"gbs": round(best, 1), "pct_hbm_peak": round(100 * best / HBM_PEAK_GBS, 2),
             "bytes": gib << 30, "gbs_by_workgroups": sweep,
             "kernel": "stream_read_kernel: 8 x 16-byte loads in flight per lane, grid-stride"}
