@@ -462,13 +462,16 @@ int32_t num_splits_of(const kvp_decode_desc* d, int32_t split) {
 
 // Shared prefix on the stream grid (paged_decode_attention, bf16, two KV
 // heads per workgroup): the hint rounded down to whole 64-token stages,
-// chunks of kPrefixChunk tokens (128: 33.7 us on the 8B-shaped layer against
-// 36.6 at 256 and 51.6 at 512), two prefix workgroups (one per KV head of
+// chunks of kPrefixChunk tokens, two prefix workgroups (one per KV head of
 // the pair) per chunk and group of prefix_seqs_per_wg(g) sequences, and the
 // stream workgroups for the tokens past the prefix filling the rest of one
-// round of two workgroups per compute unit.
+// round of two workgroups per compute unit.  On the 8B-shaped layer with
+// allocator-built tables and per-sequence stream pieces, 128 / 192 / 256-token
+// chunks ran 34.9 / 32.7 / 33.0 us (fewer prefix workgroups leave more for
+// the stream pieces, and fewer prefix pieces to merge), and a third
+// workgroup per compute unit 41.1 us.
 #ifndef PKV_PREFIX_CHUNK
-#define PKV_PREFIX_CHUNK 128
+#define PKV_PREFIX_CHUNK 192
 #endif
 #ifndef PKV_PREFIX_ROUND
 #define PKV_PREFIX_ROUND 2

@@ -220,7 +220,7 @@ def test_ragged_planning_with_total_hint():
 
 def test_shared_prefix_planning():
     """The shared-prefix plan on the host (256 compute units without a GPU):
-    the 8B-shaped layer with a 2048-token hint takes 16 chunks of 128 tokens,
+    the 8B-shaped layer with a 2048-token hint takes 11 chunks of 192 tokens,
     two prefix workgroups per chunk (one per KV head of a pair) for its one
     group of 32 sequences, and the stream workgroups fill the rest of one
     round of two per compute unit; the workspace holds the stream pieces
@@ -231,7 +231,7 @@ def test_shared_prefix_planning():
     kw = dict(B=B, n_h=n_h, n_kv=n_kv, max_blocks_per_seq=254, max_context_len=mc, total_context_len=total)
     plain = pk.decode_workspace_size(_desc(**kw))
     for hint, S in ((2048, 2048), (2100, 2048), (5000, 4032)):
-        nc = -(-S // 128)
+        nc = -(-S // 192)
         wgs = 2 * nc
         w = min(2 * 256 // 4 - wgs, -(-total // 256))
         rows = (w + B + nc * B) * n_h

@@ -36,8 +36,8 @@ def _case(s, n_h, n_kv, bs, seed):
     return pool, q
 
 
-def _prefix_ws(B, n_h, n_kv, hint, max_ctx, total, bs=16, cus=256, chunk=128):
-    """Workspace of the prefix plan: 128-token chunks, stream workgroups
+def _prefix_ws(B, n_h, n_kv, hint, max_ctx, total, bs=16, cus=256, chunk=192):
+    """Workspace of the prefix plan: 192-token chunks, stream workgroups
     filling one round of two per compute unit after the prefix ones, pieces
     (stream + B + chunks * B)."""
     g = n_h // n_kv
