@@ -132,6 +132,34 @@ def test_prefix_partly_shared_ragged(g, bs, hint):
     assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[17]) == 0
 
 
+@pytest.mark.parametrize("case", ["pieces", "equal_ranges"])
+def test_prefix_stream_parts_both_cuts(case):
+    """The stream parts after a shared prefix are cut per sequence (each
+    workgroup one piece of one sequence) while fewer sequences have a part
+    than there are stream workgroups, and into equal ranges of their
+    concatenation otherwise.  "pieces": 64 sequences of one KV-head pair,
+    most parts a few tokens or blocks long, some thousands; "equal_ranges":
+    512 sequences over four KV-head pairs, each with a part past a 64-token
+    hint (more parts than the 96 stream workgroups of a pair)."""
+    rng = np.random.default_rng(7 if case == "pieces" else 8)
+    if case == "pieces":
+        n_kv, g, shared, hint = 2, 8, 64, 1024
+        ctxs = [int(x) for x in rng.choice([1025, 1030, 1040, 1100, 1300, 2000, 4500], size=64)]
+        ctxs[5], ctxs[9] = 1024, 700                   # no part past the prefix, shorter than it
+    else:
+        n_kv, g, shared, hint = 8, 4, 4, 64
+        ctxs = [int(x) for x in rng.integers(65, 400, size=512)]
+    s = shared_prefix_structure(ctxs, 16, shared, seed=len(ctxs), pad_blocks=1)
+    pool, q = _case(s, g * n_kv, n_kv, 16, 300 + len(ctxs))
+    bt, ctx = tables_to_device(s)
+    scale = 1.0 / math.sqrt(128.0)
+    out = pk.paged_decode_attention(q, pool.k, pool.v, bt, ctx, scale, max_context_len=max(ctxs),
+                                    total_context_len=int(sum(ctxs)), shared_prefix_tokens=hint)
+    torch.cuda.synchronize()
+    ref = oracle.paged_decode_attention(host(q), host(pool.k), host(pool.v), s.block_table, s.context_lens, scale)
+    assert max_err(out, ref) <= TOL_BF16
+
+
 def test_prefix_with_more_kv_heads_and_one_sequence():
     """n_kv = 8 (four KV-head pairs) with g = 4, a batch of one sequence
     (the reference itself), and a batch where every context ends inside the
