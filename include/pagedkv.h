@@ -183,6 +183,9 @@ kvp_status reshape_and_cache(kvp_pool* pool, const void* k_new, const void* v_ne
  *   max_context_len: a host-side upper bound of every context_lens[b]
  *          (used to size the launch without reading device memory);
  *          must be <= max_blocks_per_seq * block_size.
+ * Shapes (g = n_h / n_kv, an integer): bf16 and INT8 pools d_k = d_v in
+ * {64, 128}, g in {1, 2, 4, 8, 16}; F32 pools d_k = d_v in {32, 64}, g in
+ * {1, 2, 4, 8}; others KVP_ERR_UNSUPPORTED.
  *   workspace: device scratch of at least paged_decode_workspace_size()
  *          bytes (may be NULL when that is 0), 256-byte aligned; it holds
  *          the split partials.  Calls that share a workspace must not
@@ -200,7 +203,7 @@ typedef struct {
                                   (0 = unknown; then B * max_context_len is
                                   assumed when sizing splits).  For a ragged
                                   batch (B <= 512) on the GQA path with
-                                  g in {4, 8}: bf16 pools cut the batch's
+                                  g in {4, 8, 16}: bf16 pools cut the batch's
                                   tokens into equal ranges, one per
                                   workgroup (one round of workgroups on the
                                   current device); INT8 pools launch only
@@ -217,7 +220,7 @@ typedef struct {
                                   in the same physical blocks (a shared
                                   prompt prefix; hx 4.2, faulkner prefix
                                   caching).  Used by paged_decode_attention on
-                                  bf16 pools with d = 128, g in {4, 8}, even
+                                  bf16 pools with d = 128, g in {4, 8, 16}, even
                                   n_kv, B <= 512 and no forced split (other
                                   calls ignore it): the hint, rounded down to
                                   a multiple of 64 and at most
@@ -243,7 +246,7 @@ typedef struct {
                                   Supported on paged_decode_attention,
                                   paged_decode_attention_int8 and
                                   paged_decode_attention_append for g in
-                                  {4, 8}, d in {64, 128} (bf16 and INT8
+                                  {4, 8, 16}, d in {64, 128} (bf16 and INT8
                                   pools); other shapes and MLA return
                                   KVP_ERR_UNSUPPORTED. */
 } kvp_decode_desc;
@@ -292,7 +295,7 @@ kvp_status paged_decode_attention_int8(const void* q, const int8_t* k_codes,
  * error would be amplified).  The pool must still hold a row (any finite
  * values) at every position below the context length.  0 <= n_sink <= 64
  * (sink arrays may be NULL when 0).  desc->kv_dtype == KVP_INT4; bf16 q and
- * out, d_k = d_v = 128, g in {4, 8}, even n_kv; no sliding window.  Other
+ * out, d_k = d_v = 128, g in {4, 8, 16}, even n_kv; no sliding window.  Other
  * shapes KVP_ERR_UNSUPPORTED. */
 kvp_status paged_decode_attention_int4(const void* q, const uint8_t* k_codes, const float* k_scale,
                                        const uint8_t* v_codes, const float* v_scale, const void* sink_k,
@@ -338,7 +341,7 @@ kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
  * included (paged_decode_validate checks this), and no other sequence of
  * the call reads the slot a sequence appends to.  A sequence with
  * context_lens[b] = 0 appends nothing and gets a zero output.  For bf16
- * pools with g in {4, 8} the rows are written by the attention kernel
+ * pools with g in {4, 8, 16} the rows are written by the attention kernel
  * itself (one launch); otherwise by the cache kernel just before it.
  * Errors as for the decode calls, plus KVP_ERR_INVALID_ARG for a NULL pool
  * or rows, a pool that does not match desc, or misaligned rows.  INT4 pools

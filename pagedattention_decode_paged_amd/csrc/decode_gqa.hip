@@ -619,6 +619,7 @@ bool pair_ok(const DecodeParams& p) {
 
 bool gqa_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
   if (d_k != d_v) return false;
+  if (g == 16) return gqa_ring_supported(kv, q_bf16, d_k, d_v, g);   // the LDS-ring kernel only
   if (!(g == 1 || g == 2 || g == 4 || g == 8)) return false;
   if (kv == KV::BF16) return q_bf16 && (d_k == 64 || d_k == 128);
   if (kv == KV::F32) return !q_bf16 && (d_k == 32 || d_k == 64);

@@ -726,10 +726,15 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
     }
     __syncthreads();
     // the merge buffers in the ring: the waves' outputs [NW][G][D], then per
-    // wave and head the running maximum, sum (and the INT8 weight sum)
-    static_assert(sizeof(s_dma) >= (NW * G * D + 3 * NW * G) * sizeof(float), "the merge buffers fit the ring");
+    // wave and head the running maximum, sum (and the INT8 weight sum).  At
+    // g = 16 the INT8 ring (codes only) holds just the outputs, and the
+    // statistics go to the bf16 V tile, free as well by now.
+    constexpr bool kStatsInRing = sizeof(s_dma) >= (NW * G * D + 3 * NW * G) * sizeof(float);
+    static_assert(sizeof(s_dma) >= NW * G * D * sizeof(float) &&
+                      (kStatsInRing || sizeof(s_tile) >= 3 * NW * G * sizeof(float)),
+                  "the merge buffers fit the ring (and the V tile)");
     float* s_mo = reinterpret_cast<float*>(&s_dma[0][0][0]);
-    float* s_mml = s_mo + NW * G * D;
+    float* s_mml = kStatsInRing ? s_mo + NW * G * D : reinterpret_cast<float*>(&s_tile[0]);
     if (ml16 < G) {
 #pragma unroll
       for (int c = 0; c < kCb; ++c)
@@ -1285,17 +1290,18 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
 }  // namespace
 
 bool gqa_ring_supported(KV kv, bool q_bf16, int d_k, int d_v, int g) {
-  if (kv == KV::INT4) return q_bf16 && d_k == 128 && d_v == 128 && (g == 4 || g == 8);
-  return (kv == KV::BF16 || kv == KV::INT8) && q_bf16 && d_k == d_v && (d_k == 64 || d_k == 128) &&
-         (g == 4 || g == 8);
+  const bool g_ok = g == 4 || g == 8 || g == 16;
+  if (kv == KV::INT4) return q_bf16 && d_k == 128 && d_v == 128 && g_ok;
+  return (kv == KV::BF16 || kv == KV::INT8) && q_bf16 && d_k == d_v && (d_k == 64 || d_k == 128) && g_ok;
 }
 
 int gqa_ring_kv_group(KV kv, bool q_bf16, int d_k, int d_v, int g, int n_kv) {
-  if (!q_bf16 || d_k != 128 || d_v != 128 || !(g == 4 || g == 8)) return 1;
+  if (!q_bf16 || d_k != 128 || d_v != 128 || !(g == 4 || g == 8 || g == 16)) return 1;
   if (kv == KV::BF16) return PKV_GQA_PAIR && n_kv % 2 == 0 ? 2 : 1;
   if (kv == KV::INT4) return n_kv % 2 == 0 ? 2 : 0;      // INT4: pairs of KV heads only
   if (kv == KV::INT8) {
-    if (PKV_Q8_KH >= 4 && n_kv % 4 == 0) return 4;
+    // g = 16: at most two KV heads (the merge gives each thread 8 KH columns)
+    if (PKV_Q8_KH >= 4 && n_kv % 4 == 0 && g < 16) return 4;
     if (PKV_Q8_KH >= 2 && n_kv % 2 == 0) return 2;
   }
   return 1;
@@ -1359,7 +1365,8 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
     else                                                                                           \
       PKV_RING(128, G_, false, 2);                                                                 \
   } while (0)
-  if (p.prefix_tokens != 0 && !(p.d_k == 128 && (g == 4 || g == 8) && !q8 && kh == 2)) return hipErrorInvalidValue;
+  if (p.prefix_tokens != 0 && !(p.d_k == 128 && (g == 4 || g == 8 || g == 16) && !q8 && kh == 2))
+    return hipErrorInvalidValue;
   // INT4 (two KV heads per workgroup, d = 128): the split or compact grid
 #define PKV_RING_Q4(G_)                                                                             \
   do {                                                                                              \
@@ -1374,6 +1381,7 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
     if (p.d_k != 128 || kh != 2) return hipErrorInvalidValue;
     if (g == 8) PKV_RING_Q4(8);
     else if (g == 4) PKV_RING_Q4(4);
+    else if (g == 16) PKV_RING_Q4(16);
     else return hipErrorInvalidValue;
 #undef PKV_RING_Q4
     return hipGetLastError();
@@ -1390,6 +1398,15 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
     else if (q8) PKV_RING(128, 4, true, 1);
     else if (kh == 2) PKV_RING_PAIR(4);
     else PKV_RING(128, 4, false, 1);
+  } else if (p.d_k == 128 && g == 16) {
+    if (q8 && kh == 2) PKV_RING(128, 16, true, 2);
+    else if (q8 && kh == 1) PKV_RING(128, 16, true, 1);
+    else if (q8) return hipErrorInvalidValue;
+    else if (kh == 2) PKV_RING_PAIR(16);
+    else PKV_RING(128, 16, false, 1);
+  } else if (p.d_k == 64 && g == 16) {
+    if (q8) PKV_RING(64, 16, true, 1);
+    else PKV_RING(64, 16, false, 1);
   } else if (p.d_k == 64 && g == 8) {
     if (q8) PKV_RING(64, 8, true, 1);
     else PKV_RING(64, 8, false, 1);

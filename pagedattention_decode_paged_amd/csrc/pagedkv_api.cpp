@@ -492,7 +492,7 @@ PrefixPlan prefix_plan(const kvp_decode_desc* d, Variant v) {
       d->d_k != 128 || d->d_v != 128 || ring_kv_group(d, v) != 2)
     return pp;
   const int g = d->n_h / d->n_kv;
-  if (g != 4 && g != 8) return pp;
+  if (g != 4 && g != 8 && g != 16) return pp;
   if ((int64_t)d->B * ((int64_t)d->max_context_len + 15) >= ((int64_t)1 << 31)) return pp;
   const int32_t S = std::min(d->shared_prefix_tokens, d->max_context_len) & ~63;
   if (S < 64) return pp;
@@ -756,7 +756,7 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
                   (int)d->q_dtype, d->d_k, d->d_v, g);
   } else if (var == Variant::Int4) {
     if (!pkv::gqa_supported(pkv::KV::INT4, q_bf16, d->d_k, d->d_v, g) || d->n_kv % 2)
-      return fail(KVP_ERR_UNSUPPORTED, "%s: INT4 needs bf16 q, d_k = d_v = 128, g in {4, 8} and even n_kv", fn);
+      return fail(KVP_ERR_UNSUPPORTED, "%s: INT4 needs bf16 q, d_k = d_v = 128, g in {4, 8, 16} and even n_kv", fn);
     if (d->window > 0) return fail(KVP_ERR_UNSUPPORTED, "%s: no sliding window on INT4 pools", fn);
   } else {
     if (d->kv_dtype != KVP_BF16 || !q_bf16 || !pkv::mla_supported(d->d_k, d->d_v, d->n_h, d->block_size))
@@ -768,7 +768,7 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
     if (var == Variant::Mla || !pkv::gqa_ring_supported(var == Variant::Int8 ? pkv::KV::INT8 : pkv::KV::BF16, q_bf16,
                                                          d->d_k, d->d_v, g) ||
         (var == Variant::Float && d->kv_dtype != KVP_BF16))
-      return fail(KVP_ERR_UNSUPPORTED, "%s: a sliding window needs bf16 or INT8 pools with g in {4, 8} and d in {64, 128}", fn);
+      return fail(KVP_ERR_UNSUPPORTED, "%s: a sliding window needs bf16 or INT8 pools with g in {4, 8, 16} and d in {64, 128}", fn);
   }
   if (validate_mode()) {
     int64_t nb;

@@ -133,6 +133,9 @@ def test_decode_rejects_bad_arguments_on_host():
     # shapes without a kernel
     assert _call_decode(_desc(d_k=96, d_v=96, max_context_len=200)) == pk.KVP_ERR_UNSUPPORTED
     assert _call_decode(_desc(q_dtype=pk.KVP_F32, max_context_len=200)) == pk.KVP_ERR_UNSUPPORTED
+    assert _call_decode(_desc(n_h=256, n_kv=8, max_context_len=200)) == pk.KVP_ERR_UNSUPPORTED   # g = 32
+    assert (_call_decode(_desc(n_h=128, n_kv=8, kv_dtype=pk.KVP_F32, q_dtype=pk.KVP_F32, d_k=64, d_v=64,
+                               max_context_len=200)) == pk.KVP_ERR_UNSUPPORTED)             # fp32, g = 16
     # INT8 pools must go through the INT8 entry point; MLA shapes through MLA
     assert _call_decode(_desc(kv_dtype=pk.KVP_INT8, max_context_len=200)) == pk.KVP_ERR_INVALID_ARG
     assert _call_decode(_desc(n_kv=1, d_k=576, d_v=512, max_context_len=200)) == pk.KVP_ERR_INVALID_ARG
@@ -244,4 +247,13 @@ def test_shared_prefix_planning():
             pk.decode_workspace_size(_desc(split_tokens=512, **kw)))
     d64 = dict(kw, d_k=64, d_v=64)
     assert pk.decode_workspace_size(_desc(shared_prefix_tokens=2048, **d64)) == pk.decode_workspace_size(_desc(**d64))
+    # g = 16 (128 query heads on 8 KV heads): eight sequences per prefix
+    # workgroup, so four sequence groups per chunk and KV head
+    g16 = dict(kw, n_h=128)
+    nc, ncg = -(-2048 // 192), B // 8
+    w = min(2 * 256 // 4 - 2 * nc * ncg, -(-total // 256))
+    rows = (w + B + nc * B) * 128
+    want = _r256(rows * 128 * 4) + _r256(rows * 8) + _r256(B * 8)
+    assert pk.decode_workspace_size(_desc(shared_prefix_tokens=2048, **g16)) == \
+        max(pk.decode_workspace_size(_desc(**g16)), want)
     assert _call_decode(_desc(shared_prefix_tokens=-1, max_context_len=200)) == pk.KVP_ERR_INVALID_ARG

@@ -93,6 +93,8 @@ CASES = [
     ("bf16_g2_generic", "bf16", 4, 2, 128, 16, [1, 40, 300], 0),
     ("f32_g1_generic", "f32", 4, 4, 64, 16, [1, 40, 300, 0], 0),
     ("int8_g8", "int8", 16, 2, 128, 16, [1, 40, 300, 0], 0),
+    ("bf16_g16_d128", "bf16", 32, 2, 128, 16, [1, 17, 64, 65, 300, 0, 2049], 0),
+    ("int8_g16", "int8", 32, 2, 128, 16, [1, 40, 300, 0], 0),
 ]
 
 

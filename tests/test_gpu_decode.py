@@ -7,6 +7,7 @@ sequences) with the oracle: max |gpu - oracle| <= 1e-5 for fp32 inputs and
 context length shows up as NaN in the output.
 """
 
+import dataclasses
 import math
 
 import numpy as np
@@ -67,7 +68,8 @@ def test_tiny_fp32_against_oracle_and_contiguous(name):
 
 
 @pytest.mark.parametrize("kind,d,g", [("f32", 64, 2), ("f32", 32, 4), ("bf16", 128, 8),
-                                      ("bf16", 64, 1), ("bf16", 128, 2), ("bf16", 64, 4)])
+                                      ("bf16", 64, 1), ("bf16", 128, 2), ("bf16", 64, 4),
+                                      ("bf16", 128, 16), ("bf16", 64, 16)])
 @pytest.mark.parametrize("bs", [1, 16, 64])
 def test_ragged_contexts(kind, d, g, bs):
     ctxs = [1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 700]
@@ -85,7 +87,7 @@ def test_ragged_contexts(kind, d, g, bs):
     assert max_err(out, ref) <= tol
 
 
-@pytest.mark.parametrize("n_kv,g", [(1, 8), (2, 8), (3, 8), (4, 4), (6, 4), (8, 8)])
+@pytest.mark.parametrize("n_kv,g", [(1, 8), (2, 8), (3, 8), (4, 4), (6, 4), (8, 8), (1, 16), (3, 16), (4, 16)])
 def test_kv_head_groups_bf16(n_kv, g):
     """bf16 with d = 128 runs two adjacent KV heads per workgroup when n_kv
     is even and one otherwise; both against the oracle on the plain grid,
@@ -233,6 +235,38 @@ def test_llama70b_layers_full_shape_append_every_sequence():
         del pool, kh, vh
 
 
+def test_g16_on_the_70b_shaped_pool_full_shape_append():
+    """128 query heads on the 70B-shaped layer's 8 KV heads (g = 16; B = 16,
+    ctx 8192, 8192 permuted blocks) through paged_decode_attention_append
+    with the automatic split, as the 70B-shaped layer runs: every output
+    element against the oracle over the pool as the call left it, and the
+    appended rows bit-exact."""
+    cfg = dataclasses.replace(CONFIGS["llama70b"], n_h=128)
+    s = structure(cfg, layer=3)
+    k, v, q = _big_case(cfg, s, cfg.seed * 100 + 3, poison=False)
+    bt, ctx = tables_to_device(s)
+    pool = pk.kv_pool_create(s.num_blocks, cfg.block_size, cfg.n_kv, cfg.d_k, cfg.d_v, torch.bfloat16)
+    pool.k.copy_(k)
+    pool.v.copy_(v)
+    del k, v
+    kv_new = device_normal_(torch.empty((2, cfg.B, cfg.n_kv, cfg.d_k), dtype=torch.bfloat16, device="cuda"),
+                            cfg.seed * 100 + 10)
+    k0, v0 = host(pool.k), host(pool.v)
+    out = pk.paged_decode_attention_append(pool, q, kv_new[0], kv_new[1], bt, ctx, cfg.scale, max_context_len=8192)
+    torch.cuda.synchronize()
+    seq, pos = decode_positions(s.context_lens)
+    slots = oracle.slot_mapping(s.block_table, seq, pos, cfg.block_size)
+    k1 = oracle.reshape_and_cache(k0, host(kv_new[0]), slots)
+    v1 = oracle.reshape_and_cache(v0, host(kv_new[1]), slots)
+    del k0, v0
+    kh, vh = host(pool.k), host(pool.v)
+    assert np.array_equal(kh, k1) and np.array_equal(vh, v1)
+    del k1, v1
+    ref = oracle.paged_decode_attention(host(q), kh, vh, s.block_table, s.context_lens, cfg.scale)
+    assert ref.shape == (cfg.B, 128, cfg.d_v)
+    assert max_err(out, ref) <= TOL_BF16
+
+
 def test_split_count_invariance():
     cfg = CONFIGS["llama8b"]
     s = structure(cfg)
@@ -274,7 +308,8 @@ def test_one_workspace_serves_calls_of_different_shapes():
 
 
 @pytest.mark.parametrize("kind", ["bf16", "int8"])
-@pytest.mark.parametrize("g,d,bs", [(8, 128, 16), (4, 64, 16), (8, 128, 1), (4, 128, 64)])
+@pytest.mark.parametrize("g,d,bs", [(8, 128, 16), (4, 64, 16), (8, 128, 1), (4, 128, 64), (16, 128, 16),
+                                    (16, 64, 16)])
 def test_ragged_grids_with_total_hint(kind, g, d, bs):
     """Ragged batch with a total-context hint and no split forced.  bf16: the
     LDS-ring kernel's stream grid (the batch's tokens cut into equal ranges,

@@ -76,7 +76,7 @@ def _sinks(s, rows, n_sink, n_kv, seed):
 CTXS = [1, 2, 3, 4, 5, 16, 17, 33, 300, 1000, 2049, 0, 7000, 64]
 
 
-@pytest.mark.parametrize("g,n_kv", [(8, 2), (4, 8), (8, 8)])
+@pytest.mark.parametrize("g,n_kv", [(8, 2), (4, 8), (8, 8), (16, 2)])
 @pytest.mark.parametrize("bs", [16, 64, 1])
 @pytest.mark.parametrize("n_sink", [0, 4, 16])
 @pytest.mark.parametrize("grid", ["split", "compact", "forced"])

@@ -74,7 +74,8 @@ def test_int8_70b_full_size():
 
 
 @pytest.mark.parametrize("d,g,bs", [(128, 8, 16), (128, 1, 16), (64, 4, 16), (64, 2, 16),
-                                    (128, 4, 16), (128, 8, 1), (128, 4, 64), (64, 8, 1), (64, 4, 64)])
+                                    (128, 4, 16), (128, 8, 1), (128, 4, 64), (64, 8, 1), (64, 4, 64),
+                                    (128, 16, 16), (128, 16, 1), (64, 16, 16)])
 def test_int8_ragged(d, g, bs):
     ctxs = [1, 15, 16, 17, 64, 65, 255, 257, 600]
     s = custom_structure(ctxs, bs, seed=d + g + bs, pad_blocks=1)
@@ -86,7 +87,7 @@ def test_int8_ragged(d, g, bs):
     _check_attention(pool, q, bt, ctx, s, 1.0 / math.sqrt(d), split_tokens=256)
 
 
-@pytest.mark.parametrize("n_kv,g", [(1, 8), (2, 8), (4, 8), (6, 4), (8, 4), (12, 8)])
+@pytest.mark.parametrize("n_kv,g", [(1, 8), (2, 8), (4, 8), (6, 4), (8, 4), (12, 8), (1, 16), (4, 16)])
 def test_int8_kv_head_groups(n_kv, g):
     """INT8 with d = 128 runs four adjacent KV heads per workgroup when n_kv
     is a multiple of 4, two when it is even, else one: all against the oracle
@@ -106,7 +107,7 @@ def test_int8_from_fp32_rows():
     _check_attention(pool, q, bt, ctx, s, 0.0883)
 
 
-@pytest.mark.parametrize("d,g", [(128, 8), (128, 4), (64, 8)])
+@pytest.mark.parametrize("d,g", [(128, 8), (128, 4), (64, 8), (128, 16)])
 def test_int8_query_outliers(d, g):
     """Queries with outlier channels (every 37th channel 30 times the rest)
     and one head all zero.  The matrix-core INT8 path holds each head's

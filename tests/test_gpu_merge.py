@@ -62,7 +62,8 @@ def _ref(kind, s, q, pool, scale):
                                               host(pool.v_scale), s.block_table, s.context_lens, scale)
 
 
-@pytest.mark.parametrize("kind,g,n_kv,split", [("bf16", 8, 8, 512), ("bf16", 4, 2, 256), ("int8", 8, 4, 1024)])
+@pytest.mark.parametrize("kind,g,n_kv,split", [("bf16", 8, 8, 512), ("bf16", 4, 2, 256), ("int8", 8, 4, 1024),
+                                                ("int8", 16, 2, 256)])
 def test_merge_with_a_never_cleared_workspace_and_repeated_calls(kind, g, n_kv, split):
     s, bt, ctx, q, pool = _case(g, n_kv, kind, 40 + g + n_kv)
     scale = 1.0 / math.sqrt(128)

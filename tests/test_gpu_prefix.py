@@ -106,7 +106,7 @@ CTXS = [0, 1, 63, 64, 65, 300, 511, 512, 513, 700, 1100, 1, 900, 2000, 64, 129, 
         256, 255, 257, 33, 1800, 640, 960, 12, 450, 1301, 2, 999, 1536, 1537, 16, 17, 3000, 70, 5, 880]
 
 
-@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("g", [4, 8, 16])
 @pytest.mark.parametrize("bs", [16, 64, 1])
 @pytest.mark.parametrize("hint", [1024, 1536, 3000])
 def test_prefix_partly_shared_ragged(g, bs, hint):

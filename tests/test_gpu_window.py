@@ -34,7 +34,7 @@ def _visible_slots(s, bs, window):
     return oracle.slot_mapping(s.block_table, np.asarray(seq, dtype=np.int32), np.asarray(pos, dtype=np.int32), bs)
 
 
-@pytest.mark.parametrize("g,d,bs", [(8, 128, 16), (4, 128, 64), (4, 64, 16), (8, 128, 1)])
+@pytest.mark.parametrize("g,d,bs", [(8, 128, 16), (4, 128, 64), (4, 64, 16), (8, 128, 1), (16, 128, 16)])
 @pytest.mark.parametrize("window", [1, 40, 256, 1000, 5000])
 @pytest.mark.parametrize("grid", ["split", "stream", "forced"])
 def test_window_bf16(g, d, bs, window, grid):
@@ -64,8 +64,9 @@ def test_window_bf16(g, d, bs, window, grid):
 
 @pytest.mark.parametrize("window", [1, 100, 2048])
 @pytest.mark.parametrize("hint", [True, False])
-def test_window_int8(window, hint):
-    n_kv, g, d, bs = 8, 8, 128, 16
+@pytest.mark.parametrize("g", [8, 16])
+def test_window_int8(window, hint, g):
+    n_kv, d, bs = 64 // g, 128, 16
     s = custom_structure(CTXS, bs, seed=window, pad_blocks=1)
     pool = pk.kv_pool_create(s.num_blocks, bs, n_kv, d, d, torch.int8)
     seq, pos = prefill_tokens(s.context_lens)
