@@ -117,12 +117,16 @@ struct Ring {
   // lanes per phase.
   static __device__ __forceinline__ int swz_k(int r) { return (r / kRows256) % kPieces; }
   // V: the two 16-lane groups of a transposed read phase are on rows 4
-  // apart, so the 8 rows of a phase need distinct piece positions.  INT8
-  // (d = 128): the waves write their widened rows 16 rows at a time, so rows
-  // 8 apart also differ (in the lowest bit, constant over a read phase's 8
-  // rows).
+  // apart, so the 8 rows of a phase need distinct piece pairs (swz >> 1
+  // distinct over 8 aligned rows).  INT8 (d = 128): the waves also store
+  // their widened rows, one row per lane, and a 16-byte store is served 8
+  // lanes (128 bytes) at a time, so swz & 7 must be distinct over 8 aligned
+  // rows as well, and all of swz over 16 (r & 7 with bit 3 = bit 0 of
+  // r ^ (r >> 3) does all three; 2 (r & 7) | bit 3 of r, distinct over 16
+  // rows only, cost the INT8 call 2.7e6 conflict cycles).
   static __device__ __forceinline__ int swz_v(int r) {
-    return D == 128 ? (2 * (r & 7) | (Q8 ? (r >> 3) & 1 : 0)) : 2 * ((r >> 1) & 3);
+    if constexpr (D == 128 && Q8) return (r & 7) | (((r ^ (r >> 3)) & 1) << 3);
+    return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
   }
   // INT8 code rows in the staging ring: 16-byte piece p of row r sits at
   // position p ^ swz_c(r).  A wave reads one piece of 16 consecutive rows
