@@ -266,6 +266,12 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
         // Append: the workgroup holding the sequence's last token writes that
         // token's new K and V rows (its KV heads) into its slot, and the store
         // completes before any of the workgroup's DMA can read the slot.
+        // With a ring of two stages every wave waits for all of its memory
+        // operations before the barrier that precedes each stage's DMA issue,
+        // so only a token in the stage issued ahead of the loop needs a wait
+        // here (70B-shaped layer 95.1 -> 94.7 us).
+        static_assert(RING == 2, "the stage loop's waits cover the append store");
+        const bool wait_now = ce - 1 < cb + (RING - 1) * kStageTok;
         if (wave == 0) {
           const int t_last = ce - 1;
           constexpr int kLanesPerRow = R::kSrcRow / 16;     // 16-byte pieces per row
@@ -280,9 +286,9 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
                            sl * slot_stride + off;
             *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
           }
-          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+          if (wait_now) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         }
-        __syncthreads();
+        if (wait_now) __syncthreads();
       }
     }
   };
