@@ -13,8 +13,8 @@
 // wave); the workgroup walks the sequence's K/V rows up to its last query's
 // position in 64-token stages staged by LDS DMA (two stages in flight), and
 // every wave runs S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16
-// / 16x16x16bf16_1k over each 16-token block, with an online softmax per
-// column whose mask is that column's causal limit.  Rows past 511 blocks of
+// over each stage, with one online softmax step per stage and column whose
+// mask is that column's causal limit.  Rows past 511 blocks of
 // the table are taken in chunks (the softmax state carries over).
 #include "internal.h"
 #include "device_common.h"
@@ -152,23 +152,27 @@ void prefill_paged_kernel(const PrefillParams p) {
     const uint32_t vbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&s_dma[1][slot][0];
     const int tile0 = cb0 + s * kStage;
     const int cp = ml16 & 3;
-    // 32 tokens at a time: the scores of two 16-token blocks, one online
-    // softmax step over both, then O^T += V^T P^T on v_mfma_f32_16x16x32_bf16
-    // with k = the 32 tokens (lane group mg holds tokens 4 mg .. + 3 of each
-    // block, in both operands): half the matrix instructions of two
-    // 16x16x16 steps, which take as long as one 16x16x32 each on gfx950.
+    // The whole stage per step: the scores of its four 16-token blocks, one
+    // online softmax step over them, then O^T += V^T P^T on
+    // v_mfma_f32_16x16x32_bf16 over pairs of blocks (k = 32 tokens; lane
+    // group mg holds tokens 4 mg .. + 3 of each block of the pair, in both
+    // operands): half the matrix instructions of 16x16x16 steps, which take
+    // as long as one 16x16x32 each on gfx950 (70B-heads chunk leg: 526.7 us
+    // with 16x16x16 steps per block, 420 with pairs, 403 with whole stages).
+    constexpr int kNB = 4;                            // 16-token blocks per softmax step
 #pragma unroll 1
-    for (int tp = 0; tp < 2; ++tp) {
-      f32x4_t sacc[2][2];
+    for (int tp = 0; tp < 4 / kNB; ++tp) {
+      const int base = 16 * kNB * tp;
+      f32x4_t sacc[kNB][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < kNB; ++h)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) sacc[h][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 32 * tp + 16 * h + ml16;
+        for (int h = 0; h < kNB; ++h) {
+          const int row = base + 16 * h + ml16;
           const u32x4_t ka =
               *reinterpret_cast<const u32x4_t*>(kst + row * kRowBytes + (((4 * ks + mg) ^ swz_k(row)) * 16));
 #pragma unroll
@@ -177,17 +181,18 @@ void prefill_paged_kernel(const PrefillParams p) {
                                                                   __builtin_bit_cast(bf16x8_t, qf[cb][ks]), sacc[h][cb], 0, 0, 0);
         }
       }
-      bf16x8_t pb[2];
+      bf16x8_t pb[kNB / 2][2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        // element 4 h + i: token 32 tp + 16 h + 4 mg + i
-        float sc[8];
+        float sc[4 * kNB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < kNB; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sc[4 * h + i] = tile0 + 32 * tp + 16 * h + 4 * mg + i < lim[cb] ? sacc[h][cb][i] * qscale : -INFINITY;
-        float smax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+            sc[4 * h + i] = tile0 + base + 16 * h + 4 * mg + i < lim[cb] ? sacc[h][cb][i] * qscale : -INFINITY;
+        float smax = sc[0];
+#pragma unroll
+        for (int e = 1; e < 4 * kNB; ++e) smax = fmaxf(smax, sc[e]);
         {
           const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
           smax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
@@ -207,31 +212,41 @@ void prefill_paged_kernel(const PrefillParams p) {
           for (int db = 0; db < kCb; ++db) acc[cb][db] *= alpha;
           mm[cb] = m_new;
         }
-        float pr[8];
+        // weights rounded to bf16 (the running sum adds the rounded values);
+        // pair q: elements 0-3 block 2 q, 4-7 block 2 q + 1
+        float rs = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pr[e] = sc[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[e] - mm[cb]);
-        u32x4_t pw;
+        for (int q = 0; q < kNB / 2; ++q) {
+          u32x4_t pw;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{pr[2 * e], pr[2 * e + 1]}), bf16x2_t));
-        ml[cb] += ((bf_lo(pw[0]) + bf_hi(pw[0])) + (bf_lo(pw[1]) + bf_hi(pw[1]))) +
-                  ((bf_lo(pw[2]) + bf_hi(pw[2])) + (bf_lo(pw[3]) + bf_hi(pw[3])));
-        pb[cb] = __builtin_bit_cast(bf16x8_t, pw);
+          for (int e = 0; e < 4; ++e) {
+            const float a = sc[8 * q + 2 * e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[8 * q + 2 * e] - mm[cb]);
+            const float c = sc[8 * q + 2 * e + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[8 * q + 2 * e + 1] - mm[cb]);
+            pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, c}), bf16x2_t));
+          }
+          rs += ((bf_lo(pw[0]) + bf_hi(pw[0])) + (bf_lo(pw[1]) + bf_hi(pw[1]))) +
+                ((bf_lo(pw[2]) + bf_hi(pw[2])) + (bf_lo(pw[3]) + bf_hi(pw[3])));
+          pb[q][cb] = __builtin_bit_cast(bf16x8_t, pw);
+        }
+        ml[cb] += rs;
       }
-      // V^T fragments: rows 4 mg .. + 3 of each block, column ml16 of the
-      // 16-column block, by two transposed reads 16 rows apart
-      const int tv = 32 * tp + 4 * mg + (ml16 >> 2);
-      const uint32_t vrow = vbase + (uint32_t)(tv * kRowBytes + 8 * (cp & 1));
-      const int svz = swz_v(tv);                       // = swz_v(tv + 16)
+      // V^T fragments: rows 4 mg .. + 3 of each block of pair q, column ml16
+      // of the 16-column block, by two transposed reads 16 rows apart
 #pragma unroll
-      for (int db = 0; db < kCb; ++db) {
-        const uint32_t a = vrow + (uint32_t)((((2 * db + (cp >> 1)) ^ svz)) * 16);
-        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a);
-        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(a + 16 * kRowBytes));
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int q = 0; q < kNB / 2; ++q) {
+        const int tv = base + 32 * q + 4 * mg + (ml16 >> 2);
+        const uint32_t vrow = vbase + (uint32_t)(tv * kRowBytes + 8 * (cp & 1));
+        const int svz = swz_v(tv);                     // = swz_v(tv + 16)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[cb], acc[cb][db], 0, 0, 0);
+        for (int db = 0; db < kCb; ++db) {
+          const uint32_t a = vrow + (uint32_t)((((2 * db + (cp >> 1)) ^ svz)) * 16);
+          const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a);
+          const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(a + 16 * kRowBytes));
+          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[q][cb], acc[cb][db], 0, 0, 0);
+        }
       }
     }
   };
