@@ -78,8 +78,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence or KV head with no exchange, see DESIGN.md)",
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard by sequence or by KV head with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     cpu_pool = None

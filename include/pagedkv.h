@@ -51,7 +51,7 @@ typedef enum {
   KVP_OK = 0,
   KVP_ERR_INVALID_ARG = -1,   /* a null pointer, a bad size or a shape mismatch */
   KVP_ERR_OUT_OF_MEMORY = -2, /* the pool could not be allocated */
-  KVP_ERR_UNSUPPORTED = -3,   /* a valid shape/type this build has no kernel for */
+  KVP_ERR_UNSUPPORTED = -3,   /* a valid shape/type the library has no kernel for */
   KVP_ERR_HIP = -4            /* the HIP runtime reported an error */
 } kvp_status;
 
