@@ -183,3 +183,32 @@ def test_append_on_the_stream_grid():
     assert torch.equal(pa.storage, pb.storage)
     ref = oracle.paged_decode_attention(host(q), host(pb.k), host(pb.v), s.block_table, s.context_lens, 0.0884)
     assert max_err(out_b, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("ctxs,split", [([1, 17, 32, 33, 64, 65, 300, 2049], 0), ([31, 33, 700, 1024, 1025, 3000], 256)])
+def test_append_slot_poisoned_before_the_call(ctxs, split):
+    """The fused bf16 append with every appended slot holding NaN before the
+    call: the attention must see the new rows, whether the sequence's last
+    token falls in the first stage its workgroup reads (the store completes
+    before that stage's DMA) or in a later one (the stage loop's own waits
+    order the store before that DMA).  Equal bit for bit to the separate
+    calls on an identically poisoned pool, and finite."""
+    s = custom_structure(ctxs, 16, seed=71 + split, pad_blocks=1)
+    pa, pb, _ = _two_pools("bf16", s, 16, 2, 128, 128, False, 72)
+    for pool in (pa, pb):
+        for b, c in enumerate(ctxs):
+            blk, off = int(s.block_table[b, (c - 1) // 16]), (c - 1) % 16
+            pool.k[blk, off] = float("nan")
+            pool.v[blk, off] = float("nan")
+    B = len(ctxs)
+    q = device_normal_(torch.empty((B, 16, 128), dtype=torch.bfloat16, device="cuda"), 73)
+    k_new = device_normal_(torch.empty((B, 2, 128), dtype=torch.bfloat16, device="cuda"), 74)
+    v_new = device_normal_(torch.empty((B, 2, 128), dtype=torch.bfloat16, device="cuda"), 75)
+    bt, ctx = tables_to_device(s)
+    out_a = _separate_calls(pa, "bf16", q, k_new, v_new, bt, ctx, s, 0.0884, split, False, 128)
+    out_b = pk.paged_decode_attention_append(pb, q, k_new, v_new, bt, ctx, 0.0884,
+                                             max_context_len=max(ctxs), split_tokens=split)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_b.float()).all()
+    assert torch.equal(_bits(out_a), _bits(out_b))
+    assert torch.equal(pa.storage, pb.storage)
