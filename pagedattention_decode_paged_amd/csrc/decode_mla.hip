@@ -212,8 +212,9 @@ template <int NS>
 __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NS * kStageBytes];
   __shared__ int32_t s_pref[kMlaMaxBatch + 1];
+  __shared__ uint8_t s_fill[kMlaMaxBatch];    // per sequence: (context - 1) mod 32 (its last tile's rows - 1)
   __shared__ TileInfo s_tile[kTileCap + NS];
-  __shared__ int32_t s_scan[kThreadsM];
+  __shared__ int32_t s_scan[kWavesM];
   // probabilities of the tile, one 16-byte B fragment per (head block, lane)
   __shared__ bf16x8_t s_p[kWavesM * 64];
   __shared__ float s_alpha[kHeadsPerGroup];   // rescale factor per head
@@ -228,26 +229,32 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
   const bool score_active = hbase < p.n_h;
   const int B = p.B;
 
-  // ---- tile prefix over the batch (every workgroup computes it) ----
+  // ---- tile prefix over the batch (every workgroup computes it): each
+  // thread sums its share of the sequences, a shuffle scan inside each wave,
+  // then the waves' totals (one barrier; the last tile's fill of each
+  // sequence is kept for the block-id staging below) ----
   {
     const int per = (B + kThreadsM - 1) / kThreadsM;
     const int lo = min(B, tid * per), hi = min(B, lo + per);
     int sum = 0;
     for (int b = lo; b < hi; ++b) sum += (p.context_lens[b] + kTileTok - 1) / kTileTok;
-    s_scan[tid] = sum;
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) s_scan[wave] = incl;
     __syncthreads();
-    for (int off = 1; off < kThreadsM; off <<= 1) {
-      const int v = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    int run = s_scan[tid] - sum;
+    int run = incl - sum;
+    for (int k = 0; k < wave; ++k) run += s_scan[k];
     for (int b = lo; b < hi; ++b) {
+      const int c = p.context_lens[b];
       s_pref[b] = run;
-      run += (p.context_lens[b] + kTileTok - 1) / kTileTok;
+      s_fill[b] = (uint8_t)((c - 1) & (kTileTok - 1));
+      run += (c + kTileTok - 1) / kTileTok;
     }
-    if (tid == kThreadsM - 1) s_pref[B] = s_scan[kThreadsM - 1];
+    if (tid == kThreadsM - 1) s_pref[B] = run;
     __syncthreads();
   }
   const int T = s_pref[B];
@@ -274,14 +281,15 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
       const int x = first + k;
       const int b = seq_of_tile(s_pref, B, x);
       const int tok0 = (x - s_pref[b]) * kTileTok;
-      const int nvalid = min(kTileTok, p.context_lens[b] - tok0);
+      const bool last_tile = x + 1 == s_pref[b + 1];
+      const int nvalid = last_tile ? s_fill[b] + 1 : kTileTok;
       const int kb = tok0 >> p.block_shift;
       const int row0 = tok0 & ((1 << p.block_shift) - 1);
       const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks_per_seq;
       const int32_t b0 = bt[kb];
       const int32_t b1 = (row0 + nvalid > (1 << p.block_shift)) ? bt[kb + 1] : b0;
       const int jt = x - s_pref[b];
-      s_tile[k] = TileInfo{b0, b1, nvalid | (row0 << 8), b, (jt << 1) | (int)(x + 1 == s_pref[b + 1])};
+      s_tile[k] = TileInfo{b0, b1, nvalid | (row0 << 8), b, (jt << 1) | (int)last_tile};
     }
   };
   fill_tiles(c0);
