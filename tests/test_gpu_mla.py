@@ -130,3 +130,21 @@ def test_mla_full_size_every_sequence():
     ref = _oracle(q, pool, s, cfg.scale)
     assert ref.shape == (cfg.B, cfg.n_h, D_V)
     assert max_err(out, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("B", [1300, 4096])
+def test_mla_large_batch_of_short_contexts(B):
+    """Batches past 512 sequences (each of the 512 threads of the tile-prefix
+    scan sums several sequences' tile counts; 4096 is the largest batch),
+    contexts of 0 to 80 tokens with empty sequences among them, block 16:
+    every output row against the oracle, empty sequences zero."""
+    rng = np.random.default_rng(B)
+    ctxs = rng.integers(0, 81, B)
+    ctxs[::97] = 0
+    s = custom_structure(list(ctxs), 16, seed=B + 1, pad_blocks=1)
+    pool, q = _latent_case(s, 16, 16, seed=B + 2)
+    bt, ctx = tables_to_device(s)
+    out = _mla(pool, q, bt, ctx, s, 0.07, total_context_len=int(ctxs.sum()))
+    torch.cuda.synchronize()
+    assert max_err(out, _oracle(q, pool, s, 0.07)) <= TOL_BF16
+    assert torch.count_nonzero(out[::97]) == 0
