@@ -633,8 +633,9 @@ hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream) {
       (p.split_tokens >> p.block_shift) > kBtSlots)
     return hipErrorInvalidValue;
   const int g = p.n_h / p.n_kv;
-  // only the bf16 LDS-ring kernel writes appended rows itself
-  if (p.k_new && !(p.kv == KV::BF16 && gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)))
+  // only the bf16 and INT8 LDS-ring kernels write appended rows themselves
+  if (p.k_new && !((p.kv == KV::BF16 || (p.kv == KV::INT8 && p.q_bf16)) &&
+                   gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g)))
     return hipErrorInvalidValue;
   // the stream grid and the sliding window exist on the LDS-ring kernel only
   if ((p.stream_wgs != 0 || p.window != 0) && !gqa_ring_supported(p.kv, p.q_bf16, p.d_k, p.d_v, g))

@@ -181,7 +181,9 @@ __device__ __forceinline__ void widen_int4(const u32x4_t c, u32x4_t (&out)[4]) {
 // group, unit: the splits that exist), kGridStream (KV head group, equal
 // token ranges) or kGridStreamPrefix (the stream grid after a shared prefix,
 // plus the prefix workgroups).
-template <int D, int G, int NW, int RING, bool Q8, int GRID, int KH, bool Q4 = false>
+// APP: the INT8 instance that also quantizes and writes the appended rows
+// (a separate instance, so that the plain INT8 kernels keep their code).
+template <int D, int G, int NW, int RING, bool Q8, int GRID, int KH, bool Q4 = false, bool APP = false>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(Q4 ? 2 : (Q8 ? 3 : (GRID == kGridStreamPrefix ? 2 : 1)))))
 void decode_gqa_ring_kernel(const DecodeParams p) {
@@ -285,6 +287,60 @@ void decode_gqa_ring_kernel(const DecodeParams p) {
             uint8_t* dst = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(m ? p.v : p.k)) +
                            sl * slot_stride + off;
             *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+          }
+          if (wait_now) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        }
+        if (wait_now) __syncthreads();
+      }
+    } else if constexpr (!Q4 && APP) {
+      if (p.k_new != nullptr && ce == ctx) {
+        // Append (INT8): the new token's K and V rows of this workgroup's KV
+        // heads (bf16), quantized as reshape_and_cache quantizes them
+        // (guijiagi 4.2: scale = absmax / 127 by IEEE division, codes
+        // rint(x / scale) clamped to [-128, 127]; a zero row has scale 0 and
+        // codes 0), so codes and scales are the same bits; eight elements
+        // per thread, a row's absolute maximum reduced over its threads.
+        // The same ordering as the bf16 rows: the stores complete before any
+        // DMA of the workgroup reads the slot.
+        static_assert(RING == 2, "the stage loop's waits cover the append stores");
+        const bool wait_now = ce - 1 < cb + (RING - 1) * kStageTok;
+        constexpr int kLpr = D / 8;                          // threads per row
+        constexpr int kAppThr = 2 * KH * kLpr;               // the K and V rows of the group
+        static_assert(kAppThr <= kThr && kWave % kLpr == 0, "eight elements per thread, rows inside a wave");
+        if (tid < kAppThr) {
+          const int t_last = ce - 1;
+          const int r = tid / kLpr, sub = tid % kLpr;
+          const int m = r / KH, h = kvh * KH + r % KH;       // K or V, KV head
+          const int32_t phys = s_bt[(t_last >> shift) - lb0];
+          const u32x4_t w = *reinterpret_cast<const u32x4_t*>(
+              reinterpret_cast<const uint16_t*>(m ? p.v_new : p.k_new) + ((int64_t)b * p.n_kv + h) * D + sub * 8);
+          float x[8];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            x[2 * k] = bf_lo(w[k]);
+            x[2 * k + 1] = bf_hi(w[k]);
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+          for (int off = 1; off < kLpr; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+          if (phys >= 0) {                                   // an unmapped block is skipped
+            const float qs = amax / 127.0f;
+            uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              int c = 0;
+              if (qs > 0.f) c = (int)fminf(fmaxf(rintf(x[k] / qs), -128.f), 127.f);
+              if (k < 4) lo |= (uint32_t)(c & 0xFF) << (8 * k);
+              else hi |= (uint32_t)(c & 0xFF) << (8 * (k - 4));
+            }
+            const int64_t sl = ((int64_t)phys << shift) + (t_last & bmask);
+            uint8_t* dst = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(m ? p.v : p.k)) +
+                           (sl * p.n_kv + h) * D + sub * 8;
+            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{lo, hi};
+            if (sub == 0)
+              const_cast<float*>(m ? p.v_scale : p.k_scale)[(((int64_t)phys * p.n_kv + h) << shift) + (t_last & bmask)] = qs;
           }
           if (wait_now) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         }
@@ -1378,9 +1434,16 @@ hipError_t launch_decode_gqa_ring(const DecodeParams& p, hipStream_t stream) {
 #define PKV_RING(D_, G_, Q8_, KH_)                                                                 \
   do {                                                                                              \
     constexpr int kRagged = Q8_ ? kGridCompact : kGridStream;                                       \
-    if (mode != kGridSplit)                                                                         \
+    const bool app8 = Q8_ && p.k_new != nullptr;                                                    \
+    if (mode != kGridSplit && app8)                                                                 \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, kRagged, KH_, false, Q8_>), \
+                         grid, dim3(64 * kWaves), 0, stream, p);                                   \
+    else if (mode != kGridSplit)                                                                    \
       hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, kRagged, KH_>), grid,    \
                          dim3(64 * kWaves), 0, stream, p);                                         \
+    else if (app8)                                                                                  \
+      hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, kGridSplit, KH_, false, Q8_>), \
+                         grid, dim3(64 * kWaves), 0, stream, p);                                   \
     else                                                                                           \
       hipLaunchKernelGGL((decode_gqa_ring_kernel<D_, G_, kWaves, kRing, Q8_, kGridSplit, KH_>), grid, \
                          dim3(64 * kWaves), 0, stream, p);                                         \

@@ -790,10 +790,14 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
     if (vs_rc != KVP_OK) return vs_rc;
   }
 
-  // Append: the bf16 LDS-ring kernel writes the new rows itself (one launch);
-  // every other kernel gets them from the cache kernel first.
-  const bool fused_append = app && var == Variant::Float && d->kv_dtype == KVP_BF16 && q_bf16 &&
-                            pkv::gqa_ring_supported(pkv::KV::BF16, true, d->d_k, d->d_v, g);
+  // Append: the bf16 and INT8 LDS-ring kernels write the new rows themselves
+  // (one launch; INT8 quantizes them on the way); every other kernel gets
+  // them from the cache kernel first.
+  const bool fused_append =
+      app && q_bf16 &&
+      ((var == Variant::Float && d->kv_dtype == KVP_BF16 &&
+        pkv::gqa_ring_supported(pkv::KV::BF16, true, d->d_k, d->d_v, g)) ||
+       (var == Variant::Int8 && pkv::gqa_ring_supported(pkv::KV::INT8, true, d->d_k, d->d_v, g)));
   if (app && !fused_append) {
     if (!aligned(app->k_new, 4) || (app->v_new && !aligned(app->v_new, 4)))
       return fail(KVP_ERR_INVALID_ARG, "%s: k_new and v_new must be 4-byte aligned", fn);
