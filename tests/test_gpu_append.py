@@ -212,3 +212,38 @@ def test_append_slot_poisoned_before_the_call(ctxs, split):
     assert torch.isfinite(out_b.float()).all()
     assert torch.equal(_bits(out_a), _bits(out_b))
     assert torch.equal(pa.storage, pb.storage)
+
+
+@pytest.mark.parametrize("n_kv,d,hint", [(4, 128, True), (3, 128, False), (2, 64, True), (4, 128, False)])
+def test_append_int8_fused_with_poisoned_scales(n_kv, d, hint):
+    """INT8 pools, where the attention kernel quantizes and writes the new
+    rows itself (two KV heads per workgroup at n_kv = 4, one at n_kv = 3 or
+    d = 64; the compact grid with a total-context hint, the split grid
+    without), with the scales of every appended slot NaN before the call:
+    the output equals the separate calls bit for bit and is finite, and the
+    pool (codes and scales) equals theirs."""
+    ctxs = [1, 31, 33, 300, 2049, 64, 5000]
+    g = 8
+    s = custom_structure(ctxs, 16, seed=81 + n_kv + d, pad_blocks=1)
+    pa, pb, _ = _two_pools("int8", s, 16, n_kv, d, d, False, 82)
+    for pool in (pa, pb):
+        for b, c in enumerate(ctxs):
+            blk, off = int(s.block_table[b, (c - 1) // 16]), (c - 1) % 16
+            pool.k_scale[blk, :, off] = float("nan")
+            pool.v_scale[blk, :, off] = float("nan")
+    B = len(ctxs)
+    q = device_normal_(torch.empty((B, g * n_kv, d), dtype=torch.bfloat16, device="cuda"), 83)
+    k_new = device_normal_(torch.empty((B, n_kv, d), dtype=torch.bfloat16, device="cuda"), 84)
+    v_new = device_normal_(torch.empty((B, n_kv, d), dtype=torch.bfloat16, device="cuda"), 85)
+    bt, ctx = tables_to_device(s)
+    kw = {"total_context_len": int(sum(ctxs))} if hint else {}
+    seq = torch.arange(B, dtype=torch.int32, device="cuda")
+    slots = pk.paged_slot_mapping(bt, seq, (ctx - 1).to(torch.int32), 16)
+    pk.reshape_and_cache(pa, k_new, v_new, slots)
+    out_a = pk.paged_decode_attention_int8(q, pa.k, pa.k_scale, pa.v, pa.v_scale, bt, ctx, 0.0884,
+                                           max_context_len=max(ctxs), **kw)
+    out_b = pk.paged_decode_attention_append(pb, q, k_new, v_new, bt, ctx, 0.0884, max_context_len=max(ctxs), **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_b.float()).all()
+    assert torch.equal(_bits(out_a), _bits(out_b))
+    assert torch.equal(pa.storage, pb.storage)
