@@ -341,10 +341,10 @@ kvp_status paged_decode_attention_mla(const void* q, const void* latent_pool,
  * included (paged_decode_validate checks this), and no other sequence of
  * the call reads the slot a sequence appends to.  A sequence with
  * context_lens[b] = 0 appends nothing and gets a zero output.  For bf16
- * pools, and INT8 pools with bf16 rows, with g in {4, 8, 16} the rows are
- * written (INT8: quantized, the same codes and scales as reshape_and_cache)
- * by the attention kernel itself (one launch); otherwise by the cache kernel
- * just before it.
+ * pools and INT8 pools with bf16 rows (g in {4, 8, 16}), and for latent (MLA)
+ * pools, the rows are written (INT8: quantized, the same codes and scales as
+ * reshape_and_cache) by the attention kernel itself (one launch); otherwise
+ * by the cache kernel just before it.
  * Errors as for the decode calls, plus KVP_ERR_INVALID_ARG for a NULL pool
  * or rows, a pool that does not match desc, or misaligned rows.  INT4 pools
  * (whose decode takes sink rows) are not taken here: KVP_ERR_UNSUPPORTED. */

@@ -91,6 +91,7 @@ struct MlaParams {
   int32_t* seq_meta;        // [B, 2] first and last workgroup holding the sequence
   float scale_log2;         // scale * log2(e)
   int32_t B, n_h, block_shift, max_blocks_per_seq, W;
+  const uint16_t* k_new;    // append: [B, 576] bf16 rows for position context_lens[b] - 1 (or null)
 };
 
 // Chunk permutation of tile row t (inside each aligned group of 8 chunks):
@@ -327,6 +328,31 @@ __global__ void __launch_bounds__(kThreadsM, 1) decode_mla_kernel(MlaParams p) {
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   };
+
+  // ---- append: the workgroup holding a sequence's last tile writes the new
+  // token's latent row into its slot (position context - 1) and the stores
+  // complete before any of its DMA, which reads that slot, is issued ----
+  if (p.k_new != nullptr && n > 0) {
+    const int b_lo = s_tile[0].seq;
+    const int b_hi = seq_of_tile(s_pref, B, end - 1);
+    bool any = false;
+    for (int b = b_lo; b <= b_hi; ++b) {
+      const int nt = s_pref[b + 1] - s_pref[b];
+      if (nt == 0 || s_pref[b + 1] - 1 < start || s_pref[b + 1] - 1 >= end) continue;   // no last tile here
+      any = true;
+      const int pos = (nt - 1) * kTileTok + s_fill[b];
+      const int32_t phys = p.block_table[(int64_t)b * p.max_blocks_per_seq + (pos >> p.block_shift)];
+      if (phys < 0) continue;                                 // an unmapped block is skipped
+      const uint32_t slot = ((uint32_t)phys << p.block_shift) | (uint32_t)(pos & ((1 << p.block_shift) - 1));
+      for (int c = tid; c < kRowChunks; c += kThreadsM)
+        *reinterpret_cast<dev::u32x4_t*>(const_cast<uint8_t*>(p.pool) + (uint64_t)slot * kRowBytes + 16 * c) =
+            *reinterpret_cast<const dev::u32x4_t*>(reinterpret_cast<const uint8_t*>(p.k_new + (int64_t)b * kDk) + 16 * c);
+    }
+    if (any) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    }
+  }
 
   // ---- prologue: first NS - 1 tiles in flight ----
 #pragma unroll
@@ -682,6 +708,7 @@ hipError_t launch_decode_mla(const DecodeParams& d, hipStream_t stream) {
   p.block_shift = d.block_shift;
   p.max_blocks_per_seq = d.max_blocks_per_seq;
   p.W = d.workgroups;
+  p.k_new = static_cast<const uint16_t*>(d.k_new);
   const dim3 grid((unsigned)p.W, (unsigned)mla_head_groups(p.n_h));
   hipLaunchKernelGGL((decode_mla_kernel<kMlaStages>), grid, dim3(kThreadsM), 0, stream, p);
   hipError_t e = hipGetLastError();

@@ -565,7 +565,7 @@ kvp_status check_workspace(const char* fn, size_t need, const void* workspace, s
 kvp_status launch_mla(const char* fn, const void* q, const void* pool, const int32_t* block_table,
                       const int32_t* context_lens, float scale, void* out,
                       const kvp_decode_desc* d, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, const void* k_new = nullptr) {
   if (d->B > pkv::kMlaMaxBatch) return fail(KVP_ERR_UNSUPPORTED, "%s: MLA batch must be <= %d", fn, pkv::kMlaMaxBatch);
   const int64_t per_seq = ((int64_t)d->max_context_len + pkv::kMlaTileTokens - 1) / pkv::kMlaTileTokens;
   if ((int64_t)d->B * per_seq >= ((int64_t)1 << 31))
@@ -596,6 +596,7 @@ kvp_status launch_mla(const char* fn, const void* q, const void* pool, const int
   p.q_bf16 = true;
   p.kv = pkv::KV::BF16;
   p.workgroups = mla_workgroups(d);
+  p.k_new = k_new;
   return hip_status(pkv::launch_decode_mla(p, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -797,7 +798,8 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
       app && q_bf16 &&
       ((var == Variant::Float && d->kv_dtype == KVP_BF16 &&
         pkv::gqa_ring_supported(pkv::KV::BF16, true, d->d_k, d->d_v, g)) ||
-       (var == Variant::Int8 && pkv::gqa_ring_supported(pkv::KV::INT8, true, d->d_k, d->d_v, g)));
+       (var == Variant::Int8 && pkv::gqa_ring_supported(pkv::KV::INT8, true, d->d_k, d->d_v, g)) ||
+       var == Variant::Mla);
   if (app && !fused_append) {
     if (!aligned(app->k_new, 4) || (app->v_new && !aligned(app->v_new, 4)))
       return fail(KVP_ERR_INVALID_ARG, "%s: k_new and v_new must be 4-byte aligned", fn);
@@ -811,7 +813,8 @@ kvp_status decode_common(Variant var, const char* fn, const void* q, const void*
   }
 
   if (var == Variant::Mla) return launch_mla(fn, q, k, block_table, context_lens, scale, out, d,
-                                             workspace, workspace_bytes, stream);
+                                             workspace, workspace_bytes, stream,
+                                             fused_append ? app->k_new : nullptr);
   const kvp_decode_desc pdesc = planning_desc(d);
   const kvp_decode_desc* const dd = d;
   d = &pdesc;                                     // planning from here on (validation is done)
