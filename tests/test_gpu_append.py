@@ -247,3 +247,34 @@ def test_append_int8_fused_with_poisoned_scales(n_kv, d, hint):
     assert torch.isfinite(out_b.float()).all()
     assert torch.equal(_bits(out_a), _bits(out_b))
     assert torch.equal(pa.storage, pb.storage)
+
+
+@pytest.mark.parametrize("n_h,workgroups", [(128, 0), (160, 3), (16, 1), (128, 7)])
+def test_append_mla_fused_with_poisoned_slots(n_h, workgroups):
+    """Latent pools, where the MLA kernel writes the new rows itself (the
+    workgroup holding a sequence's last tile; two head groups at n_h = 160
+    both write the same row), with every appended slot NaN before the call:
+    bit for bit the separate calls on an identically poisoned pool, finite."""
+    ctxs = [1, 33, 300, 64, 0, 2049, 95]
+    s = custom_structure(ctxs, 64, seed=91 + n_h + workgroups, pad_blocks=1)
+    pa, pb, _ = _two_pools("bf16", s, 64, 1, 576, 512, True, 92)
+    for pool in (pa, pb):
+        for b, c in enumerate(ctxs):
+            if c > 0:
+                pool.k[int(s.block_table[b, (c - 1) // 64]), (c - 1) % 64] = float("nan")
+    B = len(ctxs)
+    q = device_normal_(torch.empty((B, n_h, 576), dtype=torch.bfloat16, device="cuda"), 93)
+    k_new = device_normal_(torch.empty((B, 1, 576), dtype=torch.bfloat16, device="cuda"), 94)
+    bt, ctx = tables_to_device(s)
+    scale = 1.0 / math.sqrt(192.0)
+    seq = torch.arange(B, dtype=torch.int32, device="cuda")
+    slots = pk.paged_slot_mapping(bt, seq, (ctx - 1).to(torch.int32), 64)
+    pk.reshape_and_cache(pa, k_new, None, slots)
+    out_a = pk.paged_decode_attention_mla(q, pa.k, bt, ctx, scale, 512, max_context_len=max(ctxs),
+                                          workgroups=workgroups)
+    out_b = pk.paged_decode_attention_append(pb, q, k_new, None, bt, ctx, scale, max_context_len=max(ctxs),
+                                             workgroups=workgroups)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_b.float()).all()
+    assert torch.equal(_bits(out_a), _bits(out_b))
+    assert torch.equal(pa.storage, pb.storage)
