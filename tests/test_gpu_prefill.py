@@ -107,8 +107,10 @@ def test_prefill_long_context_in_table_chunks(bs):
 
 def test_prefill_70b_shaped_chunks_sampled():
     """The chunked-prefill workload: four 512-token chunks of 70B-shaped
-    heads (n_h 64, n_kv 8) at positions 0, 1024, 4096 and 7680; rows sampled
-    across every chunk against decode attention over the same positions."""
+    heads (n_h 64, n_kv 8) at positions 0, 1024, 4096 and 7680; fifteen rows
+    of every chunk (every 37th, which crosses each 64-token stage at a
+    different offset, and the last) against decode attention over the same
+    positions."""
     starts, chunks = [0, 1024, 4096, 7680], [512] * 4
     st, pool, q, bt, sp, cl, mx = _case(starts, chunks, 8, 8, 16, 31)
     scale = 1.0 / math.sqrt(128.0)
@@ -116,7 +118,7 @@ def test_prefill_70b_shaped_chunks_sampled():
     torch.cuda.synchronize()
     kh, vh, qh = host(pool.k), host(pool.v), host(q)
     for b in range(4):
-        for i in (0, 15, 16, 255, 300, 511):
+        for i in list(range(0, 512, 37)) + [511]:
             ref = oracle.paged_decode_attention(qh[b, i][None], kh, vh, st.block_table[b:b + 1],
                                                 [starts[b] + i + 1], scale)
             assert max_err(out[b, i:i + 1], ref) <= TOL_BF16, (b, i)
